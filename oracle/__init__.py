@@ -1,0 +1,254 @@
+"""CPU oracle for the block-scaled FP4 GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this package.  The product path (the HIP
+library and its Python binding) never imports it, and it imports nothing from
+the product path.
+
+``oracle.c`` holds the arithmetic: plain fp64 decode-then-dot-product loops,
+written from the format definitions (E2M1 "Float4E2M1FN" and E4M3 "Float8E4M3FN"
+on the issue page, section "Code Reference"; E8M0 "Float8E8M0FNU" on the
+cute-rs page, section 1; the W4A8 K tile of 128 on the Hopper W4A8 page,
+section "The W4A8 kernel: the same four definitions, with the operands
+swapped").  This module only loads the shared library, marshals numpy arrays
+into it, and holds the comparison rule that turns (D, S) into a pass/fail.
+
+Parity rule (relative to S = sum_k |a_hat * b_hat| with every scale folded in):
+  fp32 output:  |D_gpu - D| <= 1e-5 * S
+  bf16 output:  |D_gpu - D| <= 1e-5 * S + ulp_bf16(D)
+where ulp_bf16(x) = 2^(max(floor(log2|x|), -126) - 7), and 2^-133 at x = 0.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+REL_TOL = 1e-5
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (plain C, OpenMP over rows)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=False)
+    _lib = bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def bind(lib):
+    """Declare the C signatures on a loaded copy of the oracle library."""
+    i64, p, d = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
+    lib.oracle_e2m1.restype = d
+    lib.oracle_e2m1.argtypes = [ctypes.c_uint]
+    lib.oracle_e8m0.restype = d
+    lib.oracle_e8m0.argtypes = [ctypes.c_uint]
+    lib.oracle_e4m3fn.restype = d
+    lib.oracle_e4m3fn.argtypes = [ctypes.c_uint]
+    lib.oracle_int4.restype = ctypes.c_int
+    lib.oracle_int4.argtypes = [ctypes.c_uint]
+    lib.oracle_bf16.restype = d
+    lib.oracle_bf16.argtypes = [ctypes.c_uint16]
+    lib.oracle_mx_gemm_rows.restype = ctypes.c_int
+    lib.oracle_mx_gemm_rows.argtypes = [i64, i64, i64, p, p, p, p, i64, i64, p, p]
+    lib.oracle_nv_gemm_rows.restype = ctypes.c_int
+    lib.oracle_nv_gemm_rows.argtypes = [i64, i64, i64, p, p, d, p, p, d, i64, i64, p, p]
+    lib.oracle_w4a8_gemm_rows.restype = ctypes.c_int
+    lib.oracle_w4a8_gemm_rows.argtypes = [i64, i64, i64, p, p, p, p, i64, i64, p, p]
+    lib.oracle_sampled.restype = ctypes.c_int
+    lib.oracle_sampled.argtypes = [ctypes.c_int, i64, i64, i64, p, p, d, p, p, d, p, p, i64, p, p]
+    return lib
+
+
+def set_threads(n: int) -> None:
+    """Set the OpenMP thread count used by later oracle calls (this process)."""
+    os.environ["OMP_NUM_THREADS"] = str(int(n))
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(int(n))
+    except OSError:
+        pass
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None and a.size else None
+
+
+def _u8(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError(f"expected uint8, got {a.dtype}")
+    return a
+
+
+# ---- scalar decoders (exposed for the pins) -----------------------------------------
+
+def e2m1(code: int) -> float:
+    return _load().oracle_e2m1(code)
+
+
+def e8m0(e: int) -> float:
+    return _load().oracle_e8m0(e)
+
+
+def e4m3fn(b: int) -> float:
+    return _load().oracle_e4m3fn(b)
+
+
+def int4(n: int) -> int:
+    return _load().oracle_int4(n)
+
+
+def bf16(u: int) -> float:
+    return _load().oracle_bf16(u)
+
+
+# ---- full and row-slice products ------------------------------------------------------
+
+def mx_gemm(A, sfA, B, sfB, rows=None):
+    """MXFP4 (V=32, E8M0): A [M][K/2] u8, sfA [M][K/32] u8, B [N][K/2], sfB [N][K/32].
+
+    Returns (D, S) as fp64 [rows][N]; ``rows`` = (row0, row1) or None for all.
+    """
+    A, sfA, B, sfB = _u8(A), _u8(sfA), _u8(B), _u8(sfB)
+    M, N, K = A.shape[0], B.shape[0], A.shape[1] * 2
+    r0, r1 = rows if rows is not None else (0, M)
+    D = np.empty((r1 - r0, N), np.float64)
+    S = np.empty((r1 - r0, N), np.float64)
+    rc = _load().oracle_mx_gemm_rows(M, N, K, _ptr(A), _ptr(sfA), _ptr(B), _ptr(sfB), r0, r1,
+                                     _ptr(D), _ptr(S))
+    if rc:
+        raise ValueError("oracle_mx_gemm_rows: bad arguments")
+    return D, S
+
+
+def nv_gemm(A, sfA, gA, B, sfB, gB, rows=None):
+    """NVFP4 (V=16, E4M3 scales, fp32 global scales gA, gB)."""
+    A, sfA, B, sfB = _u8(A), _u8(sfA), _u8(B), _u8(sfB)
+    M, N, K = A.shape[0], B.shape[0], A.shape[1] * 2
+    r0, r1 = rows if rows is not None else (0, M)
+    D = np.empty((r1 - r0, N), np.float64)
+    S = np.empty((r1 - r0, N), np.float64)
+    rc = _load().oracle_nv_gemm_rows(M, N, K, _ptr(A), _ptr(sfA), float(np.float32(gA)),
+                                     _ptr(B), _ptr(sfB), float(np.float32(gB)), r0, r1,
+                                     _ptr(D), _ptr(S))
+    if rc:
+        raise ValueError("oracle_nv_gemm_rows: bad arguments")
+    return D, S
+
+
+def w4a8_gemm(A, sa, B, sB, rows=None):
+    """W4A8: A [M][K] u8 E4M3, sa [M] fp32, B [N][K/2] u8 INT4, sB [N][K/128] bf16 bits (u16)."""
+    A, B = _u8(A), _u8(B)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sB = np.ascontiguousarray(sB)
+    if sB.dtype != np.uint16:
+        raise TypeError("sB must hold raw bf16 bits as uint16")
+    M, N, K = A.shape[0], B.shape[0], A.shape[1]
+    r0, r1 = rows if rows is not None else (0, M)
+    D = np.empty((r1 - r0, N), np.float64)
+    S = np.empty((r1 - r0, N), np.float64)
+    rc = _load().oracle_w4a8_gemm_rows(M, N, K, _ptr(A), _ptr(sa), _ptr(B), _ptr(sB), r0, r1,
+                                       _ptr(D), _ptr(S))
+    if rc:
+        raise ValueError("oracle_w4a8_gemm_rows: bad arguments")
+    return D, S
+
+
+_KIND = {"mx": 0, "nv": 1, "w4a8": 2}
+
+
+def sampled(kind, inputs, ms, ns):
+    """Evaluate the product only at the pairs (ms[i], ns[i]).  ``inputs`` is the dict
+    made by the input generators (keys A, sfA, B, sfB and, for NVFP4, gA, gB; for
+    W4A8 keys A, sa, B, sB)."""
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    D = np.empty(ms.shape[0], np.float64)
+    S = np.empty(ms.shape[0], np.float64)
+    if kind == "w4a8":
+        A, B = _u8(inputs["A"]), _u8(inputs["B"])
+        sfa = np.ascontiguousarray(inputs["sa"], dtype=np.float32)
+        sfb = np.ascontiguousarray(inputs["sB"], dtype=np.uint16)
+        M, N, K = A.shape[0], B.shape[0], A.shape[1]
+        gA = gB = 1.0
+    else:
+        A, B = _u8(inputs["A"]), _u8(inputs["B"])
+        sfa, sfb = _u8(inputs["sfA"]), _u8(inputs["sfB"])
+        M, N, K = A.shape[0], B.shape[0], A.shape[1] * 2
+        gA = float(np.float32(inputs.get("gA", 1.0)))
+        gB = float(np.float32(inputs.get("gB", 1.0)))
+    rc = _load().oracle_sampled(_KIND[kind], M, N, K, _ptr(A), _ptr(sfa), gA, _ptr(B), _ptr(sfb),
+                                gB, _ptr(ms), _ptr(ns), ms.shape[0], _ptr(D), _ptr(S))
+    if rc:
+        raise ValueError("oracle_sampled: bad arguments")
+    return D, S
+
+
+def run(kind, inputs, rows=None):
+    """Full (or row-slice) product for an input dict of the given kind."""
+    if kind == "mx":
+        return mx_gemm(inputs["A"], inputs["sfA"], inputs["B"], inputs["sfB"], rows)
+    if kind == "nv":
+        return nv_gemm(inputs["A"], inputs["sfA"], inputs.get("gA", 1.0), inputs["B"],
+                       inputs["sfB"], inputs.get("gB", 1.0), rows)
+    if kind == "w4a8":
+        return w4a8_gemm(inputs["A"], inputs["sa"], inputs["B"], inputs["sB"], rows)
+    raise ValueError(kind)
+
+
+# ---- the comparison rule ---------------------------------------------------------------
+
+def ulp_bf16(x):
+    """bf16 unit in the last place of the exact value x (8 significant bits)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(x > 0, x, 1.0)))
+    e = np.maximum(e, -126.0)
+    u = np.ldexp(1.0, (e - 7).astype(np.int64))
+    return np.where(x > 0, u, 2.0 ** -133)
+
+
+def tolerance(D, S, out_dtype: str):
+    tol = REL_TOL * np.asarray(S, dtype=np.float64)
+    if out_dtype == "bf16":
+        tol = tol + ulp_bf16(D)
+    elif out_dtype != "f32":
+        raise ValueError(out_dtype)
+    return tol
+
+
+def parity_ratio(D_gpu, D, S, out_dtype: str) -> float:
+    """max |D_gpu - D| / tol over all elements (<= 1 passes).  NaN in D requires NaN."""
+    D_gpu = np.asarray(D_gpu, dtype=np.float64)
+    D = np.asarray(D, dtype=np.float64)
+    if D_gpu.shape != D.shape:
+        raise ValueError(f"shape mismatch {D_gpu.shape} vs {D.shape}")
+    if D.size == 0:
+        return 0.0
+    nan_ref = np.isnan(D)
+    if np.any(np.isnan(D_gpu) != nan_ref):
+        return float("inf")
+    tol = tolerance(np.where(nan_ref, 0.0, D), np.where(nan_ref, 0.0, S), out_dtype)
+    err = np.abs(np.where(nan_ref, 0.0, D_gpu - D))
+    return float(np.max(err / tol))

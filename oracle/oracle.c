@@ -1,0 +1,273 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for the block-scaled FP4 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant with the HIP library: every decoder below is
+ * written from the bit-field definitions of the formats.
+ *
+ * What it computes (block-scaled contraction):
+ *   D[m][n] = sum_k (a[m][k] * sfa[m][k/V]) * (b[n][k] * sfb[n][k/V])
+ * with a, b E2M1 codes and one scale per V consecutive K elements:
+ *   - MXFP4: V = 32, E8M0 scales (page 3, "Block-Scaled MXFP4 GEMM in cute-rs
+ *     (SM120a)": Float8E8M0FNU scales, one scale pair per K=64 step).
+ *   - NVFP4: V = 16, E4M3 scales (page 1, "Scale Factor Granularity" and the
+ *     "Code Reference" block: sf_dtype Float8E4M3FN, sf_vec_size 16), followed
+ *     by one fp32 global scale per operand.
+ *   - W4A8: FP8 E4M3 activations times signed INT4 weights with one scale per
+ *     weight row per 128-element K tile (page 2, "The W4A8 kernel: the same
+ *     four definitions, with the operands swapped": TileShapeK = 128; and
+ *     "What changes in the W4A8 builder", item 4: one scale per row per K
+ *     tile), and one fp32 scale per activation row.
+ *
+ * Every product and sum is taken in fp64, in increasing k, with no blocking.
+ * Besides D, each routine returns S[m][n] = sum_k |a_hat * b_hat| (all scales
+ * folded in), the magnitude that the parity tolerance is relative to.
+ *
+ * Layouts (the plainest reading; the pages do not fix them):
+ *   FP4 / INT4 operand X[rows][K/2] bytes, row-major, K contiguous; the low
+ *   nibble of byte j holds element 2j, the high nibble element 2j+1.
+ *   Scales sf[rows][K/V] bytes, row-major.  FP8 operand A[M][K] bytes.
+ *   W4A8 group scales sB[N][K/128] as raw bf16 bit patterns.  D[M][N] fp64.
+ *
+ * Return value: 0 on success, -1 on an argument error (K not a multiple of V
+ * or of 2, null pointer, negative size).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---- scalar decoders, each from its format's bit fields ---------------- */
+
+/* E2M1 ("Float4E2M1FN", page 1 "What Works"): 1 sign, 2 exponent bits with
+ * bias 1, 1 mantissa bit; exponent field 0 is subnormal (0.5 * m); no
+ * infinities or NaNs ("FN"). */
+double oracle_e2m1(unsigned code) {
+    unsigned s = (code >> 3) & 1u, e = (code >> 1) & 3u, m = code & 1u;
+    double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+/* E8M0 ("Float8E8M0FNU", page 3 section 1): unsigned power of two, value
+ * 2^(e-127); the all-ones code is NaN, there are no zeros or infinities. */
+double oracle_e8m0(unsigned e) {
+    e &= 0xFFu;
+    if (e == 0xFFu) return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+/* E4M3 with the "FN" convention ("Float8E4M3FN", page 1 "Code Reference"):
+ * 1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
+ * subnormal; exponent 15 with mantissa 7 is NaN; no infinities; max 448. */
+double oracle_e4m3fn(unsigned b) {
+    b &= 0xFFu;
+    unsigned s = b >> 7, E = (b >> 3) & 15u, M = b & 7u;
+    double mag;
+    if (E == 15u && M == 7u) return NAN;
+    if (E == 0u) mag = ldexp((double)M / 8.0, -6);
+    else mag = ldexp(1.0 + (double)M / 8.0, (int)E - 7);
+    return s ? -mag : mag;
+}
+
+/* Signed INT4 ("int4b_t", page 2): two's complement nibble, -8..7. */
+int oracle_int4(unsigned n) {
+    n &= 0xFu;
+    return (n < 8u) ? (int)n : (int)n - 16;
+}
+
+/* bf16: the upper 16 bits of an IEEE binary32. */
+double oracle_bf16(uint16_t u) {
+    uint32_t bits = (uint32_t)u << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Nibble k of a packed row: low nibble = even k. */
+static unsigned nibble(const uint8_t *row, int64_t k) {
+    uint8_t byte = row[k >> 1];
+    return (k & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 0xFu);
+}
+
+/* ---- block-scaled FP4 contraction, generic over (V, scale decoder) ------ */
+
+typedef double (*scale_fn)(unsigned);
+
+/* One output element of the block-scaled FP4 product (rows m of A, n of B). */
+static void fp4_dot(int64_t K, int64_t V, scale_fn dec_scale,
+                    const uint8_t *arow, const uint8_t *sfarow,
+                    const uint8_t *brow, const uint8_t *sfbrow,
+                    double *d, double *s) {
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double a_hat = oracle_e2m1(nibble(arow, k)) * dec_scale(sfarow[k / V]);
+        double b_hat = oracle_e2m1(nibble(brow, k)) * dec_scale(sfbrow[k / V]);
+        double p = a_hat * b_hat;
+        acc += p;
+        mag += fabs(p);
+    }
+    *d = acc;
+    *s = mag;
+}
+
+static int fp4_gemm_rows(int64_t M, int64_t N, int64_t K, int64_t V, scale_fn dec,
+                         const uint8_t *A, const uint8_t *sfA,
+                         const uint8_t *B, const uint8_t *sfB,
+                         int64_t row0, int64_t row1, double *D, double *S) {
+    if (M < 0 || N < 0 || K < 0 || (K % V) != 0 || (K % 2) != 0) return -1;
+    if (row0 < 0 || row1 > M || row0 > row1) return -1;
+    if ((M && N && K) && (!A || !sfA || !B || !sfB)) return -1;
+    if ((row1 > row0 && N) && (!D || !S)) return -1;
+    const int64_t a_ld = K / 2, s_ld = K / V;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = row0; m < row1; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double d, s;
+            fp4_dot(K, V, dec, A + m * a_ld, sfA + m * s_ld, B + n * a_ld, sfB + n * s_ld, &d, &s);
+            D[(m - row0) * N + n] = d;
+            S[(m - row0) * N + n] = s;
+        }
+    }
+    return 0;
+}
+
+/* MXFP4: V = 32, E8M0 scales.  Rows [row0, row1) of D and S are written to
+ * D[0 .. (row1-row0)*N).  The M <= 16 GEMV is the same operation. */
+int oracle_mx_gemm_rows(int64_t M, int64_t N, int64_t K,
+                        const uint8_t *A, const uint8_t *sfA,
+                        const uint8_t *B, const uint8_t *sfB,
+                        int64_t row0, int64_t row1, double *D, double *S) {
+    return fp4_gemm_rows(M, N, K, 32, oracle_e8m0, A, sfA, B, sfB, row0, row1, D, S);
+}
+
+int oracle_mx_gemm(int64_t M, int64_t N, int64_t K,
+                   const uint8_t *A, const uint8_t *sfA,
+                   const uint8_t *B, const uint8_t *sfB, double *D, double *S) {
+    return oracle_mx_gemm_rows(M, N, K, A, sfA, B, sfB, 0, M, D, S);
+}
+
+/* NVFP4: V = 16, E4M3 scales, then D *= gA * gB and S *= |gA * gB|. */
+int oracle_nv_gemm_rows(int64_t M, int64_t N, int64_t K,
+                        const uint8_t *A, const uint8_t *sfA, double gA,
+                        const uint8_t *B, const uint8_t *sfB, double gB,
+                        int64_t row0, int64_t row1, double *D, double *S) {
+    int rc = fp4_gemm_rows(M, N, K, 16, oracle_e4m3fn, A, sfA, B, sfB, row0, row1, D, S);
+    if (rc) return rc;
+    const double g = gA * gB;
+    for (int64_t i = 0; i < (row1 - row0) * N; ++i) {
+        D[i] *= g;
+        S[i] *= fabs(g);
+    }
+    return 0;
+}
+
+int oracle_nv_gemm(int64_t M, int64_t N, int64_t K,
+                   const uint8_t *A, const uint8_t *sfA, double gA,
+                   const uint8_t *B, const uint8_t *sfB, double gB, double *D, double *S) {
+    return oracle_nv_gemm_rows(M, N, K, A, sfA, gA, B, sfB, gB, 0, M, D, S);
+}
+
+/* W4A8: D[m][n] = sa[m] * sum_g bf16(sB[n][g]) * sum_{k in group g}
+ * e4m3(A[m][k]) * int4(B[n][k]), groups of G = 128 consecutive K elements.
+ * S is the same sum with every product in absolute value. */
+#define W4A8_GROUP 128
+int oracle_w4a8_gemm_rows(int64_t M, int64_t N, int64_t K,
+                          const uint8_t *A, const float *sa,
+                          const uint8_t *B, const uint16_t *sB,
+                          int64_t row0, int64_t row1, double *D, double *S) {
+    if (M < 0 || N < 0 || K < 0 || (K % W4A8_GROUP) != 0) return -1;
+    if (row0 < 0 || row1 > M || row0 > row1) return -1;
+    if ((M && N && K) && (!A || !sa || !B || !sB)) return -1;
+    if ((row1 > row0 && N) && (!D || !S)) return -1;
+    const int64_t G = K / W4A8_GROUP;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = row0; m < row1; ++m) {
+        const uint8_t *arow = A + m * K;
+        const double row_scale = (double)sa[m];
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *brow = B + n * (K / 2);
+            double acc = 0.0, mag = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                double part = 0.0, part_mag = 0.0;
+                for (int64_t k = g * W4A8_GROUP; k < (g + 1) * W4A8_GROUP; ++k) {
+                    double p = oracle_e4m3fn(arow[k]) * (double)oracle_int4(nibble(brow, k));
+                    part += p;
+                    part_mag += fabs(p);
+                }
+                double gs = oracle_bf16(sB[n * G + g]);
+                acc += gs * part;
+                mag += fabs(gs) * part_mag;
+            }
+            D[(m - row0) * N + n] = row_scale * acc;
+            S[(m - row0) * N + n] = fabs(row_scale) * mag;
+        }
+    }
+    return 0;
+}
+
+int oracle_w4a8_gemm(int64_t M, int64_t N, int64_t K,
+                     const uint8_t *A, const float *sa,
+                     const uint8_t *B, const uint16_t *sB, double *D, double *S) {
+    return oracle_w4a8_gemm_rows(M, N, K, A, sa, B, sB, 0, M, D, S);
+}
+
+/* Sampled outputs: the same definitions evaluated only at the listed (m, n)
+ * pairs, for shapes whose full product is too slow on the CPU.  kind selects
+ * the operation: 0 = MXFP4, 1 = NVFP4 (gA, gB used), 2 = W4A8 (A is FP8,
+ * sfA is the fp32 row-scale array, sfB the bf16 group scales). */
+int oracle_sampled(int kind, int64_t M, int64_t N, int64_t K,
+                   const void *A, const void *sfA, double gA,
+                   const void *B, const void *sfB, double gB,
+                   const int64_t *ms, const int64_t *ns, int64_t count,
+                   double *D, double *S) {
+    if (count < 0 || (count && (!ms || !ns || !D || !S))) return -1;
+    for (int64_t i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t m = ms[i], n = ns[i];
+        double d = 0.0, s = 0.0;
+        if (kind == 0) {
+            if (K % 32) { bad = 1; continue; }
+            fp4_dot(K, 32, oracle_e8m0, (const uint8_t *)A + m * (K / 2),
+                    (const uint8_t *)sfA + m * (K / 32), (const uint8_t *)B + n * (K / 2),
+                    (const uint8_t *)sfB + n * (K / 32), &d, &s);
+        } else if (kind == 1) {
+            if (K % 16) { bad = 1; continue; }
+            fp4_dot(K, 16, oracle_e4m3fn, (const uint8_t *)A + m * (K / 2),
+                    (const uint8_t *)sfA + m * (K / 16), (const uint8_t *)B + n * (K / 2),
+                    (const uint8_t *)sfB + n * (K / 16), &d, &s);
+            d *= gA * gB;
+            s *= fabs(gA * gB);
+        } else if (kind == 2) {
+            if (K % W4A8_GROUP) { bad = 1; continue; }
+            /* one row of one column: reuse the row routine on a 1x1 view */
+            const uint8_t *arow = (const uint8_t *)A + m * K;
+            const uint8_t *brow = (const uint8_t *)B + n * (K / 2);
+            const uint16_t *srow = (const uint16_t *)sfB + n * (K / W4A8_GROUP);
+            double acc = 0.0, mag = 0.0;
+            for (int64_t g = 0; g < K / W4A8_GROUP; ++g) {
+                double part = 0.0, part_mag = 0.0;
+                for (int64_t k = g * W4A8_GROUP; k < (g + 1) * W4A8_GROUP; ++k) {
+                    double p = oracle_e4m3fn(arow[k]) * (double)oracle_int4(nibble(brow, k));
+                    part += p;
+                    part_mag += fabs(p);
+                }
+                double gs = oracle_bf16(srow[g]);
+                acc += gs * part;
+                mag += fabs(gs) * part_mag;
+            }
+            double rs = (double)((const float *)sfA)[m];
+            d = rs * acc;
+            s = fabs(rs) * mag;
+        } else {
+            bad = 1;
+            continue;
+        }
+        D[i] = d;
+        S[i] = s;
+    }
+    return bad ? -1 : 0;
+}

@@ -1,0 +1,103 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a temporary copy of oracle.c (a dropped term,
+a wrong sign, bias or index, a transposed operand), builds it with gcc on the
+CPU, points the oracle module at the mutant, and runs the quick pins from
+test_oracle_codecs / test_oracle_pins.  At least one pin must fail for every
+mutant.  Nothing here touches the committed oracle or any GPU.
+"""
+import ctypes
+import inspect
+import itertools
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_codecs as codecs
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "nibble-order-swapped": (
+        "return (k & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 0xFu);",
+        "return (k & 1) ? (unsigned)(byte & 0xFu) : (unsigned)(byte >> 4);"),
+    "scale-index-off-by-one": (
+        "double a_hat = oracle_e2m1(nibble(arow, k)) * dec_scale(sfarow[k / V]);",
+        "double a_hat = oracle_e2m1(nibble(arow, k)) * dec_scale(sfarow[(k + 1) / V < K / V ? (k + 1) / V : k / V]);"),
+    "e2m1-exponent-bias": (
+        "ldexp(1.0 + 0.5 * (double)m, (int)e - 1)", "ldexp(1.0 + 0.5 * (double)m, (int)e)"),
+    "e2m1-subnormal": ("? 0.5 * (double)m :", "? 1.0 * (double)m :"),
+    "e2m1-sign-dropped": (
+        "double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);\n    return s ? -mag : mag;",
+        "double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);\n    (void)s; return mag;"),
+    "e4m3-bias": ("ldexp(1.0 + (double)M / 8.0, (int)E - 7)", "ldexp(1.0 + (double)M / 8.0, (int)E - 8)"),
+    "e4m3-subnormal-scale": ("ldexp((double)M / 8.0, -6)", "ldexp((double)M / 8.0, -7)"),
+    "e8m0-bias": ("return ldexp(1.0, (int)e - 127);", "return ldexp(1.0, (int)e - 128);"),
+    "int4-sign": ("(int)n - 16", "(int)n - 15"),
+    "b-scale-dropped": (
+        "double b_hat = oracle_e2m1(nibble(brow, k)) * dec_scale(sfbrow[k / V]);",
+        "double b_hat = oracle_e2m1(nibble(brow, k));"),
+    "b-scale-from-a": (
+        "double b_hat = oracle_e2m1(nibble(brow, k)) * dec_scale(sfbrow[k / V]);",
+        "double b_hat = oracle_e2m1(nibble(brow, k)) * dec_scale(sfarow[k / V]);"),
+    "w4a8-group-scale-index": ("double gs = oracle_bf16(sB[n * G + g]);", "double gs = oracle_bf16(sB[n * G]);"),
+    "w4a8-row-scale-dropped": ("D[(m - row0) * N + n] = row_scale * acc;", "D[(m - row0) * N + n] = acc;"),
+    "w4a8-group-size": ("#define W4A8_GROUP 128", "#define W4A8_GROUP 64"),
+    "nv-global-scale-half": ("D[i] *= g;", "D[i] *= gA;"),
+    "b-row-stride": (
+        "fp4_dot(K, V, dec, A + m * a_ld, sfA + m * s_ld, B + n * a_ld, sfB + n * s_ld, &d, &s);",
+        "fp4_dot(K, V, dec, A + m * a_ld, sfA + m * s_ld, B + n * a_ld, sfB + m * s_ld, &d, &s);"),
+    "abs-sum-signed": ("mag += fabs(p);\n    }\n    *d = acc;", "mag += p;\n    }\n    *d = acc;"),
+}
+
+
+def _quick_pins():
+    """(callable, kwargs) for every quick pin, over all of its parametrisations."""
+    out = []
+    for mod in (codecs, pins):
+        for name, fn in inspect.getmembers(mod, inspect.isfunction):
+            if not name.startswith("test_") or fn.__module__ != mod.__name__:
+                continue
+            grids = [{}]
+            for mk in getattr(fn, "pytestmark", []):
+                if mk.name != "parametrize":
+                    continue
+                argnames, values = mk.args[0], mk.args[1]
+                names = [a.strip() for a in argnames.split(",")] if isinstance(argnames, str) else list(argnames)
+                rows = [dict(zip(names, v if len(names) > 1 else (v,))) for v in values]
+                grids = [dict(g, **r) for g, r in itertools.product(grids, rows)]
+            out.extend((fn, g) for g in grids)
+    return out
+
+
+@pytest.fixture(scope="module")
+def pin_list():
+    return _quick_pins()
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(mutant, tmp_path, pin_list, monkeypatch):
+    old, new = MUTANTS[mutant]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique/found: {mutant}"
+    mpath = tmp_path / "oracle_mut.c"
+    mpath.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
+                    str(mpath), "-lm"], check=True)
+    monkeypatch.setattr(oracle, "_lib", oracle.bind(ctypes.CDLL(str(so))))
+    failed = []
+    for fn, kw in pin_list:
+        try:
+            fn(oracle_lib=oracle, **kw)
+        except (AssertionError, ValueError):   # a failed pin or a rejected result
+            failed.append(fn.__name__)
+    assert failed, f"no pin caught the planted mistake '{mutant}'"
+
+
+def test_unmutated_oracle_passes_every_quick_pin(pin_list):
+    for fn, kw in pin_list:
+        fn(oracle_lib=oracle, **kw)
