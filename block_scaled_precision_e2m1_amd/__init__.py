@@ -1,0 +1,184 @@
+"""Block-scaled FP4 GEMM for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libfp4gemm.so`` (declared in
+``include/fp4gemm.h``).  Each function below has the name of the C entry point
+it calls, checks and marshals its torch arguments (device memory and the
+current stream only), and raises on a non-zero status.  All arithmetic runs in
+the library's HIP kernels; there is no fallback.  If the library has not been
+built, the first call raises ``ImportError`` naming the build step.
+
+Layouts (uint8 tensors unless noted, all contiguous, all on one GPU):
+  mx_fp4_gemm / fp4_gemv : A [M, K/2], sfA [M, K/32], B [N, K/2], sfB [N, K/32]
+  nv_fp4_gemm            : A [M, K/2], sfA [M, K/16], B [N, K/2], sfB [N, K/16],
+                           plus float global scales
+  w4a8_gemm              : A [M, K] (E4M3 codes), sa [M] float32,
+                           B [N, K/2] (INT4 nibbles), sB [N, K/128] bfloat16
+Output D [M, N] float32 or bfloat16, row-major.  Packed nibbles: low nibble =
+even k.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "fp4g_status_string",
+           "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfp4gemm.so")
+SYMBOLS = ("mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "fp4g_status_string")
+
+OUT_F32, OUT_BF16 = 0, 1
+_lib = None
+
+
+class Fp4GemmError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn}: status {status}: {text}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libfp4gemm.so (built by ``__graft_entry__.build()``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`"
+                          " or `python block_scaled_precision_e2m1_amd/_build.py`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, p, c_int, f = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.mx_fp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
+    lib.mx_fp4_gemm.restype = c_int
+    lib.fp4_gemv.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
+    lib.fp4_gemv.restype = c_int
+    lib.nv_fp4_gemm.argtypes = [i64, i64, i64, p, p, f, p, p, f, p, c_int, p]
+    lib.nv_fp4_gemm.restype = c_int
+    lib.w4a8_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
+    lib.w4a8_gemm.restype = c_int
+    lib.fp4g_status_string.argtypes = [c_int]
+    lib.fp4g_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fp4g_status_string(status: int) -> str:
+    return load_library().fp4g_status_string(int(status)).decode()
+
+
+# ---- argument marshalling ------------------------------------------------------------------
+
+def _check(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
+
+
+def _out(out, M, N, out_dtype, device):
+    if out is None:
+        return torch.empty((M, N), dtype=out_dtype, device=device)
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    _check(out, "out", out.dtype, (M, N), device)
+    return out
+
+
+def _device_of(A):
+    if not isinstance(A, torch.Tensor):
+        raise TypeError("A must be a torch.Tensor")
+    if A.device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {A.device}")
+    return A.device
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _raise_on(fn, st):
+    if st != 0:
+        raise Fp4GemmError(fn, st, fp4g_status_string(st))
+
+
+def _fp4_common(fn, V, A, sfA, B, sfB, out, out_dtype, max_m=None):
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape[0], A.shape[1] * 2
+    N = B.shape[0]
+    if K % V:
+        raise ValueError(f"K={K} must be a multiple of {V}")
+    _check(A, "A", torch.uint8, (M, K // 2), device)
+    _check(sfA, "sfA", torch.uint8, (M, K // V), device)
+    _check(B, "B", torch.uint8, (N, K // 2), device)
+    _check(sfB, "sfB", torch.uint8, (N, K // V), device)
+    D = _out(out, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    return lib, device, M, N, K, D, dt
+
+
+def mx_fp4_gemm(A, sfA, B, sfB, out=None, out_dtype=torch.bfloat16):
+    """MXFP4 GEMM (E2M1 codes, E8M0 scale per 32 K elements); returns D [M, N]."""
+    lib, dev, M, N, K, D, dt = _fp4_common("mx_fp4_gemm", 32, A, sfA, B, sfB, out, out_dtype)
+    st = lib.mx_fp4_gemm(M, N, K, _ptr(A), _ptr(sfA), _ptr(B), _ptr(sfB), _ptr(D), dt, _stream(dev))
+    _raise_on("mx_fp4_gemm", st)
+    return D
+
+
+def fp4_gemv(A, sfA, B, sfB, out=None, out_dtype=torch.bfloat16):
+    """MXFP4 GEMV for 1 <= M <= 16 tokens (same layouts as mx_fp4_gemm)."""
+    lib, dev, M, N, K, D, dt = _fp4_common("fp4_gemv", 32, A, sfA, B, sfB, out, out_dtype)
+    st = lib.fp4_gemv(M, N, K, _ptr(A), _ptr(sfA), _ptr(B), _ptr(sfB), _ptr(D), dt, _stream(dev))
+    _raise_on("fp4_gemv", st)
+    return D
+
+
+def nv_fp4_gemm(A, sfA, global_a, B, sfB, global_b, out=None, out_dtype=torch.bfloat16):
+    """NVFP4 GEMM (E2M1 codes, E4M3 scale per 16 K elements, fp32 global scales)."""
+    lib, dev, M, N, K, D, dt = _fp4_common("nv_fp4_gemm", 16, A, sfA, B, sfB, out, out_dtype)
+    st = lib.nv_fp4_gemm(M, N, K, _ptr(A), _ptr(sfA), float(global_a), _ptr(B), _ptr(sfB),
+                         float(global_b), _ptr(D), dt, _stream(dev))
+    _raise_on("nv_fp4_gemm", st)
+    return D
+
+
+def w4a8_gemm(A, sa, B, sB, out=None, out_dtype=torch.bfloat16):
+    """W4A8 GEMM: A [M, K] E4M3 codes (uint8), sa [M] float32, B [N, K/2] INT4 nibbles,
+    sB [N, K/128] bfloat16 group scales."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    N = B.shape[0]
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(A, "A", torch.uint8, (M, K), device)
+    _check(sa, "sa", torch.float32, (M,), device)
+    _check(B, "B", torch.uint8, (N, K // 2), device)
+    _check(sB, "sB", torch.bfloat16, (N, K // 128), device)
+    D = _out(out, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    st = lib.w4a8_gemm(M, N, K, _ptr(A), _ptr(sa), _ptr(B), _ptr(sB), _ptr(D), dt, _stream(device))
+    _raise_on("w4a8_gemm", st)
+    return D

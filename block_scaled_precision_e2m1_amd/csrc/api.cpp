@@ -1,0 +1,128 @@
+// C-ABI entry points: validate on the host, pick a kernel, launch on the
+// caller's stream.  Validation runs before any HIP call, so an invalid call
+// returns its status without touching the device.
+#include "../../include/fp4gemm.h"
+#include "internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+using fp4g::FP4Args;
+using fp4g::W4A8Args;
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // each of M, N, K below 2^31
+
+struct Range { uintptr_t lo, hi; };
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+Range range_of(const void* p, int64_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)bytes};
+}
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shared shape / pointer checks.  `out_elem` is 4 (fp32) or 2 (bf16).
+// Returns FP4G_OK, or the first failing status.  `*empty` is set when the
+// output has no elements (nothing to launch).
+fp4g_status check_common(int64_t M, int64_t N, int64_t K, int d_type, const void* D, bool* empty) {
+  if (M < 0 || N < 0 || K < 0) return FP4G_EINVAL;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP4G_EINVAL;
+  if (d_type != FP4G_OUT_F32 && d_type != FP4G_OUT_BF16) return FP4G_EINVAL;
+  if (K % 128 != 0) return FP4G_EUNSUPPORTED;
+  *empty = (M == 0 || N == 0);
+  if (*empty) return FP4G_OK;
+  if (!D) return FP4G_EINVAL;
+  if (!aligned(D, 16)) return FP4G_EALIGN;
+  return FP4G_OK;
+}
+
+fp4g_status check_fp4_operands(int64_t M, int64_t N, int64_t K, int V, const void* A, const void* sfA,
+                               const void* B, const void* sfB, const void* D, int d_type) {
+  if (K == 0) return FP4G_OK;                       // empty sum: inputs are not read
+  if (!A || !sfA || !B || !sfB) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16)) return FP4G_EALIGN;
+  if (!aligned(sfA, 4) || !aligned(sfB, 4)) return FP4G_EALIGN;
+  const int64_t out_bytes = M * N * (d_type == FP4G_OUT_BF16 ? 2 : 4);
+  const Range d = range_of(D, out_bytes);
+  const Range ins[4] = {range_of(A, M * (K / 2)), range_of(sfA, M * (K / V)),
+                        range_of(B, N * (K / 2)), range_of(sfB, N * (K / V))};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  return FP4G_OK;
+}
+
+fp4g_status finish(hipError_t e) { return e == hipSuccess ? FP4G_OK : FP4G_EHIP; }
+
+fp4g_status run_fp4(int which, int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
+                    float g, const void* B, const void* sfB, void* D, int d_type, void* stream) {
+  const int V = (which == 1) ? 16 : 32;
+  bool empty = false;
+  fp4g_status st = check_common(M, N, K, d_type, D, &empty);
+  if (st != FP4G_OK || empty) return st;
+  if (which == 2 && M > 16) return FP4G_EUNSUPPORTED;
+  st = check_fp4_operands(M, N, K, V, A, sfA, B, sfB, D, d_type);
+  if (st != FP4G_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, M * N, bf16, s));
+  FP4Args a{M, N, K, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(sfA),
+            static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(sfB), g, D, bf16};
+  if (which == 0) return finish(fp4g::launch_mxfp4_gemm(a, s));
+  if (which == 1) return finish(fp4g::launch_nvfp4_gemm(a, s));
+  return finish(fp4g::launch_fp4_gemv(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4g_status mx_fp4_gemm(int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
+                        const void* B, const void* sfB, void* D, int d_type, void* stream) {
+  return run_fp4(0, M, N, K, A, sfA, 1.0f, B, sfB, D, d_type, stream);
+}
+
+fp4g_status nv_fp4_gemm(int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
+                        float global_a, const void* B, const void* sfB, float global_b, void* D,
+                        int d_type, void* stream) {
+  return run_fp4(1, M, N, K, A, sfA, global_a * global_b, B, sfB, D, d_type, stream);
+}
+
+fp4g_status fp4_gemv(int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
+                     const void* B, const void* sfB, void* D, int d_type, void* stream) {
+  return run_fp4(2, M, N, K, A, sfA, 1.0f, B, sfB, D, d_type, stream);
+}
+
+fp4g_status w4a8_gemm(int64_t M, int64_t N, int64_t K, const void* A, const float* sa,
+                      const void* B, const void* sB, void* D, int d_type, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_common(M, N, K, d_type, D, &empty);
+  if (st != FP4G_OK || empty) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, M * N, bf16, s));
+  if (!A || !sa || !B || !sB) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16)) return FP4G_EALIGN;
+  if (!aligned(sa, 4) || !aligned(sB, 4)) return FP4G_EALIGN;
+  const Range d = range_of(D, M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, M * K), range_of(sa, M * 4), range_of(B, N * (K / 2)),
+                        range_of(sB, N * (K / 128) * 2)};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  W4A8Args a{M, N, K, static_cast<const uint8_t*>(A), sa, static_cast<const uint8_t*>(B),
+             static_cast<const uint16_t*>(sB), D, bf16};
+  return finish(fp4g::launch_w4a8_gemm(a, s));
+}
+
+const char* fp4g_status_string(int status) {
+  switch (status) {
+    case FP4G_OK: return "ok";
+    case FP4G_EINVAL: return "invalid argument (null pointer, negative size, bad output type or D overlapping an input)";
+    case FP4G_EUNSUPPORTED: return "unsupported shape (K must be a multiple of 128; GEMV needs M <= 16)";
+    case FP4G_EALIGN: return "misaligned pointer (operands and D need 16-byte, scales 4-byte alignment)";
+    case FP4G_EHIP: return "HIP runtime error at kernel launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Internal interface between the C-ABI entry points (api.cpp) and the kernel
+// launchers.  Arguments reach a launcher only after validation; every
+// launcher enqueues on the given stream and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4g {
+
+struct FP4Args {            // MXFP4 / NVFP4 / GEMV
+  int64_t M, N, K;
+  const uint8_t* A;         // [M][K/2]
+  const uint8_t* sfA;       // [M][K/V]
+  const uint8_t* B;         // [N][K/2]
+  const uint8_t* sfB;       // [N][K/V]
+  float gscale;             // NVFP4: global_a * global_b; unused otherwise
+  void* D;                  // [M][N]
+  bool bf16_out;
+};
+
+struct W4A8Args {
+  int64_t M, N, K;
+  const uint8_t* A;         // [M][K] E4M3
+  const float* sa;          // [M]
+  const uint8_t* B;         // [N][K/2] INT4
+  const uint16_t* sB;       // [N][K/128] bf16
+  void* D;
+  bool bf16_out;
+};
+
+hipError_t launch_mxfp4_gemm(const FP4Args& a, hipStream_t s);
+hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s);
+hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s);
+hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t s);
+// D[M][N] = 0 (the empty-K product); never uses hipMemset so it can be captured.
+hipError_t launch_zero_fill(void* D, int64_t count, bool bf16_out, hipStream_t s);
+
+}  // namespace fp4g

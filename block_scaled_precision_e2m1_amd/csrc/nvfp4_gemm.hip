@@ -1,0 +1,191 @@
+// NVFP4 GEMM for gfx950: E2M1 operands with one E4M3 scale per 16 K elements and
+// one fp32 global scale per operand:
+//   D[m][n] = gA * gB * sum_k e2m1(A[m,k]) e4m3(sfA[m,k/16]) * e2m1(B[n,k]) e4m3(sfB[n,k/16])
+// The 16-element E4M3 scale granularity is the NVFP4 setup of the NVIDIA/cutlass
+// issue "Add FP4 TMA kernel example for Blackwell in CuTe Python DSL" (sections
+// "Scale Factor Granularity" and "Code Reference": sf_dtype Float8E4M3FN,
+// sf_vec_size 16, so a 128-wide K tile carries 8 scales per row).
+//
+// gfx950 has no hardware E4M3-per-16 block scale (its scaled MFMA takes E8M0 per
+// 32), and e2m1 * e4m3 needs up to 6 significant bits, more than any 8-bit
+// float holds.  The exact fold is into bf16 (8 significant bits): each element
+// is widened with v_cvt_scalef32_pk_f32_fp4, multiplied by its decoded fp32
+// scale (exact), and truncated to bf16 (exact, the low 16 bits are zero).  The
+// folded tiles are written to LDS and consumed by v_mfma_f32_16x16x32_bf16 with
+// fp32 accumulation; gA*gB multiplies the accumulator in the epilogue.
+//
+// Structure: one workgroup per BM x BN tile, 4 waves of WM x WN; 64 K elements
+// (32 packed bytes, one scale dword) per row per step; the packed tile for the
+// next step is prefetched into registers while the MFMAs of the current one run;
+// LDS rows are 128 bytes (64 bf16) with 16-byte chunks XOR-swizzled by row.
+#include "common.hpp"
+#include "internal.h"
+
+namespace fp4g {
+namespace {
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+constexpr int kBK = 64;             // K elements per step
+constexpr int kRowBf = kBK * 2;     // 128 bytes of bf16 per LDS row
+
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// Exact E4M3 (OCP, bias 7) decode to fp32.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t s = (b >> 7) & 1u, E = (b >> 3) & 15u, Mt = b & 7u;
+  if (E == 15u && Mt == 7u) return __builtin_nanf("");
+  float mag;
+  if (E == 0u) mag = (float)Mt * 0x1p-9f;
+  else mag = __builtin_bit_cast(float, ((E + 120u) << 23) | (Mt << 20));
+  return s ? -mag : mag;
+}
+
+// 4 packed bytes (8 E2M1 codes) times one fp32 scale -> 8 bf16 in 4 dwords.
+__device__ __forceinline__ void fold8(uint32_t w, float sc, uint32_t* out) {
+#pragma unroll
+  for (int byte = 0; byte < 4; ++byte) {
+    v2f f;
+    if (byte == 0) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    else if (byte == 1) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    else if (byte == 2) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    else f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    const uint32_t lo = __builtin_bit_cast(uint32_t, f[0] * sc);
+    const uint32_t hi = __builtin_bit_cast(uint32_t, f[1] * sc);
+    out[byte] = (hi & 0xFFFF0000u) | (lo >> 16);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool BF16>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
+                  const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, float gscale,
+                  void* __restrict__ D) {
+  constexpr int NWN = BN / WN;
+  constexpr int NT = (BM / WM) * NWN * 64;
+  constexpr int CH = (BM + BN) * 2 / NT;   // 16-byte packed chunks per thread per step
+  constexpr int FI = WM / 16, FJ = WN / 16;
+  static_assert(CH >= 1 && (BM + BN) * 2 % NT == 0, "tile/threads mismatch");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * kRowBf];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int r16 = lane & 15, slot = lane >> 4;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int m0 = (int)(blockIdx.x / tiles_n) * BM, n0 = (int)(blockIdx.x % tiles_n) * BN;
+  const int64_t ld = K / 2, lds_ = K / 16;
+  const int KT = K / kBK;
+
+  // Thread chunk q: packed row (A rows first, then B rows), half c of its 32 bytes.
+  const uint8_t* gsrc[CH];
+  const uint8_t* gscl[CH];
+  int ldst[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int q = tid + i * NT, row = q >> 1, c = q & 1;
+    const bool isA = row < BM;
+    const int grow = isA ? min(m0 + row, M - 1) : min(n0 + row - BM, N - 1);
+    gsrc[i] = (isA ? A : B) + (int64_t)grow * ld + c * 16;
+    gscl[i] = (isA ? sfA : sfB) + (int64_t)grow * lds_ + c * 2;
+    ldst[i] = row * kRowBf + c * 64;   // 32 bf16 = 4 logical 16-byte chunks 4c..4c+3
+  }
+
+  v4i pk[CH];
+  uint32_t ps[CH];
+  auto load_global = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      pk[i] = *reinterpret_cast<const v4i*>(gsrc[i] + (int64_t)kt * 32);
+      ps[i] = *reinterpret_cast<const uint16_t*>(gscl[i] + kt * 4);
+    }
+  };
+  auto store_lds = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int row = (tid + i * NT) >> 1, c = (tid + i * NT) & 1;
+      const float s0 = e4m3_to_f32(ps[i] & 0xFFu), s1 = e4m3_to_f32(ps[i] >> 8);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {   // dword d: elements 8d..8d+7 of the 32
+        uint32_t out[4];
+        fold8((uint32_t)pk[i][d], d < 2 ? s0 : s1, out);
+        const int chunk = 4 * c + d;
+        *reinterpret_cast<v4i*>(&lds[st][row * kRowBf + ((chunk ^ swz8(row)) << 4)]) =
+            v4i{(int)out[0], (int)out[1], (int)out[2], (int)out[3]};
+      }
+    }
+  };
+
+  v4f acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  load_global(0);
+  store_lds(0);
+  if (KT > 1) load_global(1);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt & 1;
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int chunk = 4 * sub + slot;
+      v8bf af[FI], bf[FJ];
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        const int row = wm * WM + i * 16 + r16;
+        af[i] = *reinterpret_cast<const v8bf*>(&lds[st][row * kRowBf + ((chunk ^ swz8(row)) << 4)]);
+      }
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int row = BM + wn * WN + j * 16 + r16;
+        bf[j] = *reinterpret_cast<const v8bf*>(&lds[st][row * kRowBf + ((chunk ^ swz8(row)) << 4)]);
+      }
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) {
+      store_lds(st ^ 1);
+      if (kt + 2 < KT) load_global(kt + 2);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      const int n = n0 + wn * WN + j * 16 + r16;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int m = m0 + wm * WM + i * 16 + 4 * slot + t;
+        if (m < M && n < N) store_out<BF16>(D, (int64_t)m * N + n, acc[i][j][t] * gscale);
+      }
+    }
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
+  constexpr int NT = (BM / WM) * (BN / WN) * 64;
+  const int64_t tiles = ceil_div(a.N, BN) * ceil_div(a.M, BM);
+  if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)tiles);
+  if (a.bf16_out)
+    hipLaunchKernelGGL((nvfp4_gemm_kernel<BM, BN, WM, WN, true>), grid, dim3(NT), 0, s, (int)a.M,
+                       (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.gscale, a.D);
+  else
+    hipLaunchKernelGGL((nvfp4_gemm_kernel<BM, BN, WM, WN, false>), grid, dim3(NT), 0, s, (int)a.M,
+                       (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.gscale, a.D);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s) {
+  if (ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256) return launch_cfg<128, 128, 64, 64>(a, s);
+  return launch_cfg<64, 64, 32, 32>(a, s);
+}
+
+}  // namespace fp4g

@@ -1,0 +1,104 @@
+/*
+ * fp4gemm.h -- C ABI of the block-scaled FP4 GEMM library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (all entry points): an output tile D[M][N] of
+ *   D[m][n] = sum_k  (a[m][k] * sa[m][k / V]) * (b[n][k] * sb[n][k / V])
+ * where a, b are 4-bit E2M1 codes and sa, sb block scales, one per V
+ * consecutive K elements.  The block-scaled MMA and its scale granularity are
+ * the subject of the NVIDIA/cutlass issue "Add FP4 TMA kernel example for
+ * Blackwell in CuTe Python DSL" (sections "What Works", "MMA Instruction K
+ * Constraint", "Scale Factor Granularity" and "Code Reference"); the MXFP4
+ * variant with E8M0 scales is section 1 of the cuda-oxide page "TMA
+ * Pipelines, Tensor Cores, and ctm-rs Interop"; the W4A8 variant is the
+ * Hopper CUTLASS/CuTe DSL blog post, sections "The W4A8 kernel: the same four
+ * definitions, with the operands swapped" and "What changes in the W4A8
+ * builder".
+ *
+ * Layouts (normative; every pointer is device memory owned by the caller):
+ *   FP4 / INT4 operand  X[rows][K/2] bytes, row-major (K contiguous, "K-major"
+ *                       for both operands); the low nibble of byte j holds
+ *                       element 2j, the high nibble element 2j+1.
+ *   E2M1 nibble         sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0;
+ *                       values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *   MX scales           sf[rows][K/32] bytes, row-major; E8M0: value 2^(e-127),
+ *                       0xFF is NaN.
+ *   NV scales           sf[rows][K/16] bytes, row-major; E4M3 (OCP "FN": bias 7,
+ *                       max 448, 0x7F/0xFF NaN, no infinities).
+ *   W4A8 activations    A[M][K] bytes, E4M3 codes; row scales sa[M] fp32.
+ *   W4A8 weights        B[N][K/2] bytes, two's-complement INT4 nibbles
+ *                       (-8..7); group scales sB[N][K/128] bf16.
+ *   Output              D[M][N] row-major (leading dimension N), fp32 or bf16
+ *                       (round to nearest even).  D is only written, never read.
+ *
+ * Calls are asynchronous: each entry point validates its arguments on the
+ * host, then enqueues its kernel on `stream` (a hipStream_t; NULL is the
+ * default stream) and returns.  Faults inside a kernel surface at the
+ * caller's next synchronisation.  The library allocates no memory, keeps no
+ * per-call state, and may be called from several threads at once.
+ * Validation failures return a status code and launch nothing.
+ */
+#ifndef FP4GEMM_H
+#define FP4GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP4G_OK = 0,
+    FP4G_EINVAL = 1,       /* null pointer, size <= 0, bad enum, D overlaps an input */
+    FP4G_EUNSUPPORTED = 2, /* K not a multiple of 128, or GEMV with M > 16 */
+    FP4G_EALIGN = 3,       /* operand / output not 16-byte aligned, scales not 4-byte aligned */
+    FP4G_EHIP = 4          /* the HIP runtime rejected the launch */
+} fp4g_status;
+
+typedef enum {
+    FP4G_OUT_F32 = 0,
+    FP4G_OUT_BF16 = 1
+} fp4g_out;
+
+/* MXFP4 GEMM: V = 32, E8M0 scales.
+ *   A [M][K/2], sfA [M][K/32], B [N][K/2], sfB [N][K/32], D [M][N] of d_type.
+ *   Requires M, N >= 1 and K a positive multiple of 128. */
+fp4g_status mx_fp4_gemm(int64_t M, int64_t N, int64_t K,
+                        const void *A, const void *sfA,
+                        const void *B, const void *sfB,
+                        void *D, int d_type, void *stream);
+
+/* NVFP4 GEMM: V = 16, E4M3 scales, then D *= global_a * global_b.
+ *   A [M][K/2], sfA [M][K/16], B [N][K/2], sfB [N][K/16], D [M][N].
+ *   Requires K a positive multiple of 128. */
+fp4g_status nv_fp4_gemm(int64_t M, int64_t N, int64_t K,
+                        const void *A, const void *sfA, float global_a,
+                        const void *B, const void *sfB, float global_b,
+                        void *D, int d_type, void *stream);
+
+/* W4A8 mixed-input GEMM (FP8 E4M3 activations x INT4 weights):
+ *   D[m][n] = sa[m] * sum_g bf16(sB[n][g]) * sum_{k in group g} e4m3(A[m][k]) * int4(B[n][k])
+ *   with groups of 128 consecutive K elements.
+ *   A [M][K] bytes, sa [M] fp32, B [N][K/2] bytes, sB [N][K/128] bf16 (raw
+ *   16-bit patterns), D [M][N].  Requires K a positive multiple of 128. */
+fp4g_status w4a8_gemm(int64_t M, int64_t N, int64_t K,
+                      const void *A, const float *sa,
+                      const void *B, const void *sB,
+                      void *D, int d_type, void *stream);
+
+/* MXFP4 GEMV for decode (few tokens): the MXFP4 GEMM with 1 <= M <= 16 and the
+ * same layouts, tuned for streaming the weight operand B once from HBM.
+ * Requires K a positive multiple of 128; M > 16 returns FP4G_EUNSUPPORTED. */
+fp4g_status fp4_gemv(int64_t M, int64_t N, int64_t K,
+                     const void *A, const void *sfA,
+                     const void *B, const void *sfB,
+                     void *D, int d_type, void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *fp4g_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4GEMM_H */

@@ -239,7 +239,11 @@ def tolerance(D, S, out_dtype: str):
 
 
 def parity_ratio(D_gpu, D, S, out_dtype: str) -> float:
-    """max |D_gpu - D| / tol over all elements (<= 1 passes).  NaN in D requires NaN."""
+    """max |D_gpu - D| / tol over all elements (<= 1 passes).
+
+    Where the exact result is NaN (a NaN scale code reached it) the GPU value must be
+    NaN too; those positions then carry no error term.  A NaN where the exact result
+    is finite fails (returns inf)."""
     D_gpu = np.asarray(D_gpu, dtype=np.float64)
     D = np.asarray(D, dtype=np.float64)
     if D_gpu.shape != D.shape:
@@ -249,6 +253,8 @@ def parity_ratio(D_gpu, D, S, out_dtype: str) -> float:
     nan_ref = np.isnan(D)
     if np.any(np.isnan(D_gpu) != nan_ref):
         return float("inf")
-    tol = tolerance(np.where(nan_ref, 0.0, D), np.where(nan_ref, 0.0, S), out_dtype)
-    err = np.abs(np.where(nan_ref, 0.0, D_gpu - D))
-    return float(np.max(err / tol))
+    ok = ~nan_ref
+    if not ok.any():
+        return 0.0
+    tol = tolerance(D[ok], np.asarray(S, dtype=np.float64)[ok], out_dtype)
+    return float(np.max(np.abs(D_gpu[ok] - D[ok]) / tol))

@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+that include/fp4gemm.h declares, and rejects invalid arguments with the
+documented status codes before touching any device (no GPU needed: every call
+here fails validation or has an empty output, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_scaled_precision_e2m1_amd as fp4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4gemm.h")
+
+OK, EINVAL, EUNSUP, EALIGN, EHIP = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fp4.load_library()
+
+
+def test_header_declares_the_four_operations():
+    assert declared_functions() == sorted(["mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv",
+                                            "fp4g_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(fp4.SYMBOLS) == set(declared_functions())
+
+
+def test_library_is_gfx950_only():
+    out = os.popen(f"/opt/rocm/bin/roc-obj-ls {fp4.library_path()} 2>/dev/null").read()
+    if not out.strip():
+        pytest.skip("roc-obj-ls unavailable")
+    assert "gfx950" in out
+    assert "gfx942" not in out and "gfx90a" not in out
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert fp4.fp4g_status_string(s)
+    assert fp4.fp4g_status_string(99) == "unknown status"
+
+
+# Fake, aligned, non-overlapping "device" addresses: validation never dereferences them.
+A_, SA_, B_, SB_, D_ = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+
+
+def mx(lib, M, N, K, A=A_, sA=SA_, B=B_, sB=SB_, D=D_, dt=0):
+    return lib.mx_fp4_gemm(M, N, K, A, sA, B, sB, D, dt, None)
+
+
+def test_invalid_sizes(lib):
+    assert mx(lib, -1, 4, 128) == EINVAL
+    assert mx(lib, 4, -1, 128) == EINVAL
+    assert mx(lib, 4, 4, -128) == EINVAL
+    assert mx(lib, 1 << 31, 4, 128) == EINVAL
+    assert mx(lib, 4, 4, 64) == EUNSUP
+    assert mx(lib, 4, 4, 100) == EUNSUP
+
+
+def test_bad_output_type(lib):
+    assert mx(lib, 4, 4, 128, dt=2) == EINVAL
+    assert mx(lib, 4, 4, 128, dt=-1) == EINVAL
+
+
+def test_null_pointers(lib):
+    assert mx(lib, 4, 4, 128, A=None) == EINVAL
+    assert mx(lib, 4, 4, 128, sA=None) == EINVAL
+    assert mx(lib, 4, 4, 128, B=None) == EINVAL
+    assert mx(lib, 4, 4, 128, sB=None) == EINVAL
+    assert mx(lib, 4, 4, 128, D=None) == EINVAL
+
+
+def test_alignment(lib):
+    assert mx(lib, 4, 4, 128, A=A_ + 8) == EALIGN
+    assert mx(lib, 4, 4, 128, B=B_ + 4) == EALIGN
+    assert mx(lib, 4, 4, 128, D=D_ + 2) == EALIGN
+    assert mx(lib, 4, 4, 128, sA=SA_ + 2) == EALIGN
+    assert mx(lib, 4, 4, 128, sB=SB_ + 1) == EALIGN
+
+
+def test_output_overlapping_an_input(lib):
+    assert mx(lib, 4, 4, 128, D=A_) == EINVAL
+    assert mx(lib, 4, 4, 1024, D=SB_ + 64) == EINVAL   # sfB spans 4 * 32 bytes
+    assert mx(lib, 4, 4, 1024, D=B_ + 1024) == EINVAL  # B spans 4 * 512 bytes
+
+
+def test_empty_outputs_are_noops(lib):
+    assert mx(lib, 0, 4, 128, A=None, sA=None, B=None, sB=None, D=None) == OK
+    assert mx(lib, 4, 0, 128, A=None, sA=None, B=None, sB=None, D=None) == OK
+    assert lib.w4a8_gemm(0, 5, 256, None, None, None, None, None, 1, None) == OK
+    assert lib.nv_fp4_gemm(3, 0, 256, None, None, 1.0, None, None, 1.0, None, 1, None) == OK
+
+
+def test_gemv_token_limit(lib):
+    assert lib.fp4_gemv(17, 64, 128, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
+    assert lib.fp4_gemv(4, 64, 96, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
+
+
+def test_nv_and_w4a8_validation(lib):
+    assert lib.nv_fp4_gemm(4, 4, 128, None, SA_, 1.0, B_, SB_, 1.0, D_, 0, None) == EINVAL
+    assert lib.nv_fp4_gemm(4, 4, 192, A_, SA_, 1.0, B_, SB_, 1.0, D_, 0, None) == EUNSUP
+    assert lib.w4a8_gemm(4, 4, 128, A_, None, B_, SB_, D_, 0, None) == EINVAL
+    assert lib.w4a8_gemm(4, 4, 128, A_, SA_ + 2, B_, SB_, D_, 0, None) == EALIGN
+    assert lib.w4a8_gemm(4, 4, 128, A_, SA_, B_, SB_, A_ + 64, 0, None) == EINVAL
+
+
+def test_binding_rejects_host_tensors():
+    A = torch.zeros((4, 64), dtype=torch.uint8)
+    s = torch.zeros((4, 4), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.mx_fp4_gemm(A, s, A, s)
+    with pytest.raises(TypeError):
+        fp4.mx_fp4_gemm(A.numpy(), s, A, s)

@@ -1,0 +1,300 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar (the oracle module's parity rule): fp32 output |D - D_exact| <= 1e-5 * S,
+bf16 output <= 1e-5 * S + one bf16 ulp of D_exact, with S = sum_k |a_hat b_hat|.
+Full products at sizes the oracle finishes in seconds (several tiles plus ragged
+tails); at the workloads' full sizes, in the launch configuration the benchmark
+times, sampled outputs (random pairs plus whole rows and columns at the tile
+edges) evaluated one by one by the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_e2m1_amd as fp4
+import datagen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def up(d):
+    t = {}
+    for k, v in d.items():
+        if not isinstance(v, np.ndarray) or v.ndim == 0:
+            continue
+        if k == "sB":
+            t[k] = torch.from_numpy(v.view(np.int16)).to(DEV).view(torch.bfloat16)
+        else:
+            t[k] = torch.from_numpy(v).to(DEV)
+    return t
+
+
+def run(kind, d, out_dtype, t=None):
+    t = t or up(d)
+    od = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    if kind == "mx":
+        D = fp4.mx_fp4_gemm(t["A"], t["sfA"], t["B"], t["sfB"], out_dtype=od)
+    elif kind == "gemv":
+        D = fp4.fp4_gemv(t["A"], t["sfA"], t["B"], t["sfB"], out_dtype=od)
+    elif kind == "nv":
+        D = fp4.nv_fp4_gemm(t["A"], t["sfA"], float(d["gA"]), t["B"], t["sfB"], float(d["gB"]), out_dtype=od)
+    elif kind == "w4a8":
+        D = fp4.w4a8_gemm(t["A"], t["sa"], t["B"], t["sB"], out_dtype=od)
+    else:
+        raise ValueError(kind)
+    torch.cuda.synchronize(DEV)
+    return D
+
+
+def as_np(D):
+    return D.float().cpu().numpy().astype(np.float64)
+
+
+def okind(kind):
+    return "mx" if kind == "gemv" else kind
+
+
+def check_full(kind, d, out_dtype):
+    D = as_np(run(kind, d, out_dtype))
+    ref, S = oracle.run(okind(kind), d)
+    r = oracle.parity_ratio(D, ref, S, out_dtype)
+    assert r <= 1.0, f"{kind} {d['M']}x{d['N']}x{d['K']} {out_dtype}: max |err|/tol = {r}"
+    return r
+
+
+def sample_pairs(M, N, rng, count, edges=()):
+    ms = list(rng.integers(0, M, count))
+    ns = list(rng.integers(0, N, count))
+    for m in edges:                       # whole rows at tile edges
+        if 0 <= m < M:
+            ms += [m] * N
+            ns += list(range(N))
+    return np.array(ms), np.array(ns)
+
+
+def check_sampled(kind, d, out_dtype, ms, ns, D=None):
+    if D is None:
+        D = run(kind, d, out_dtype)
+    Dn = as_np(D[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)])
+    ref, S = oracle.sampled(okind(kind), d, ms, ns)
+    r = oracle.parity_ratio(Dn, ref, S, out_dtype)
+    assert r <= 1.0, f"{kind} sampled: max |err|/tol = {r}"
+    return r
+
+
+# ---- MXFP4 GEMM ---------------------------------------------------------------------------
+
+def test_mxfp4_256_fp32_full():
+    d = datagen.make("mxfp4_256")
+    print("case mxfp4_256 seed 0", flush=True)
+    check_full("mx", d, "f32")
+
+
+MX_SHAPES = [(1, 1, 128), (7, 33, 256), (33, 7, 128), (64, 64, 128), (100, 300, 384),
+             (255, 257, 256), (257, 129, 512), (128, 128, 1024), (300, 1000, 256), (513, 511, 128)]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", MX_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in MX_SHAPES])
+def test_mxfp4_shapes(shape, out):
+    M, N, K = shape
+    d = datagen.make_shape("mx", M, N, K, seed=M + N + K)
+    check_full("mx", d, out)
+
+
+@pytest.mark.parametrize("shape", [(2048, 2048, 256), (2176, 2100, 384)])
+def test_mxfp4_mid_tile_config_full(shape):
+    M, N, K = shape
+    d = datagen.make_shape("mx", M, N, K, seed=5, dist="gaussian")
+    check_full("mx", d, "bf16")
+
+
+@pytest.mark.parametrize("shape", [(4096, 4096, 256), (4100, 4097, 384)])
+def test_mxfp4_big_tile_config_sampled(shape):
+    M, N, K = shape
+    d = datagen.make_shape("mx", M, N, K, seed=7, dist="gaussian")
+    rng = np.random.default_rng(1)
+    ms, ns = sample_pairs(M, N, rng, 20000, edges=(0, 255, 256, M - 1))
+    check_sampled("mx", d, "bf16", ms, ns)
+    mt, nt = sample_pairs(N, M, rng, 0, edges=(0, 511, N - 1))   # whole columns
+    check_sampled("mx", d, "bf16", nt, mt)
+
+
+def test_mxfp4_8192_sampled_and_repeatable():
+    d = datagen.make("mxfp4_8192")
+    print("case mxfp4_8192 seed 0", flush=True)
+    t = up(d)
+    D1 = run("mx", d, "bf16", t)
+    D2 = run("mx", d, "bf16", t)
+    assert torch.equal(D1.view(torch.int16), D2.view(torch.int16)), "not bitwise repeatable"
+    rng = np.random.default_rng(2)
+    ms, ns = sample_pairs(8192, 8192, rng, 8192, edges=(0, 4095, 8191))
+    check_sampled("mx", d, "bf16", ms, ns, D=D1)
+    cols = np.array([0, 300, 8191])
+    ms2 = np.repeat(np.arange(8192), len(cols))
+    ns2 = np.tile(cols, 8192)
+    check_sampled("mx", d, "bf16", ms2, ns2, D=D1)
+
+
+def test_mxfp4_transpose_identity():
+    d = datagen.make_shape("mx", 200, 130, 256, seed=9)
+    sw = dict(d, A=d["B"], sfA=d["sfB"], B=d["A"], sfB=d["sfA"], M=130, N=200)
+    D = as_np(run("mx", d, "f32"))
+    Dt = as_np(run("mx", sw, "f32"))
+    ref, S = oracle.run("mx", d)
+    assert oracle.parity_ratio(Dt.T, ref, S, "f32") <= 1.0
+    assert oracle.parity_ratio(D, ref, S, "f32") <= 1.0
+
+
+def test_mxfp4_output_guard_rows_untouched():
+    M, N, K = 70, 90, 256
+    d = datagen.make_shape("mx", M, N, K, seed=10)
+    t = up(d)
+    buf = torch.full((M + 3, N), float("nan"), dtype=torch.float32, device=DEV)
+    out = buf[:M]
+    fp4.mx_fp4_gemm(t["A"], t["sfA"], t["B"], t["sfB"], out=out)
+    torch.cuda.synchronize(DEV)
+    assert torch.isfinite(out).all()
+    assert torch.isnan(buf[M:]).all()
+    ref, S = oracle.run("mx", d)
+    assert oracle.parity_ratio(as_np(out), ref, S, "f32") <= 1.0
+
+
+def test_mxfp4_nan_scale_propagates():
+    d = datagen.make_shape("mx", 40, 50, 256, seed=11)
+    d["sfA"][3, 2] = 0xFF
+    D = as_np(run("mx", d, "f32"))
+    ref, S = oracle.run("mx", d)
+    assert np.isnan(ref[3]).all()
+    assert oracle.parity_ratio(D, ref, S, "f32") <= 1.0
+
+
+# ---- GEMV --------------------------------------------------------------------------------
+
+def test_gemv_decode_workload_full():
+    d = datagen.make("mxfp4_gemv_8x14336x4096")
+    print("case gemv 8x14336x4096 seed 0", flush=True)
+    check_full("gemv", d, "bf16")
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 13, 16])
+@pytest.mark.parametrize("NK", [(1, 128), (17, 384), (1000, 256), (4101, 1152)])
+def test_gemv_shapes(M, NK):
+    N, K = NK
+    d = datagen.make_shape("gemv", M, N, K, seed=M * 31 + N)
+    check_full("gemv", d, "f32")
+
+
+def test_gemv_matches_gemm():
+    d = datagen.make_shape("mx", 16, 700, 512, seed=12, dist="gaussian")
+    a = as_np(run("gemv", d, "f32"))
+    b = as_np(run("mx", d, "f32"))
+    ref, S = oracle.run("mx", d)
+    assert np.all(np.abs(a - b) <= 2e-5 * S + 1e-30)
+
+
+# ---- NVFP4 -------------------------------------------------------------------------------
+
+def test_nvfp4_1024_full():
+    d = datagen.make("nvfp4_1024")
+    print("case nvfp4_1024 seed 0", flush=True)
+    check_full("nv", d, "bf16")
+
+
+NV_SHAPES = [(1, 1, 128), (17, 33, 256), (64, 64, 128), (130, 70, 384), (300, 257, 512), (1100, 1030, 256)]
+
+
+@pytest.mark.parametrize("g", [(1.0, 1.0), (2.0, 0.375), (3.0, -0.5)])
+@pytest.mark.parametrize("shape", NV_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in NV_SHAPES])
+def test_nvfp4_shapes(shape, g):
+    M, N, K = shape
+    rng = np.random.default_rng(M + N)
+    d = datagen.random_nv(M, N, K, rng, gA=g[0], gB=g[1])
+    d.update({"M": M, "N": N, "K": K})
+    check_full("nv", d, "f32")
+
+
+def test_nvfp4_full_scale_range_including_subnormals():
+    rng = np.random.default_rng(13)
+    d = datagen.random_nv(96, 80, 256, rng)
+    d["sfA"] = rng.integers(0, 0x7F, d["sfA"].shape, dtype=np.uint8)   # every finite positive code
+    d["sfB"] = (rng.integers(0, 0x7F, d["sfB"].shape, dtype=np.uint8) | (rng.integers(0, 2, d["sfB"].shape, dtype=np.uint8) << 7))
+    d.update({"M": 96, "N": 80, "K": 256})
+    check_full("nv", d, "f32")
+
+
+# ---- W4A8 --------------------------------------------------------------------------------
+
+W4_SHAPES = [(1, 1, 128), (5, 70, 256), (64, 64, 128), (130, 65, 384), (256, 300, 1024), (300, 1000, 512)]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", W4_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in W4_SHAPES])
+def test_w4a8_shapes(shape, out):
+    M, N, K = shape
+    d = datagen.make_shape("w4a8", M, N, K, seed=M + 2 * N + K)
+    check_full("w4a8", d, out)
+
+
+def test_w4a8_workload_sampled():
+    d = datagen.make("w4a8_256x8192x8192")
+    print("case w4a8 256x8192x8192 seed 0", flush=True)
+    rng = np.random.default_rng(3)
+    ms, ns = sample_pairs(256, 8192, rng, 4096, edges=(0, 127, 255))
+    check_sampled("w4a8", d, "bf16", ms, ns)
+
+
+def test_w4a8_int4_extremes():
+    """All-(-8) and all-7 weights exercise both conversion tables' ends."""
+    rng = np.random.default_rng(14)
+    d = datagen.make_shape("w4a8", 64, 64, 256, seed=14)
+    q = np.where(rng.integers(0, 2, (64, 256)) > 0, 7, 8).astype(np.uint8)
+    d["B"] = datagen.pack_nibbles(q)
+    check_full("w4a8", d, "f32")
+
+
+# ---- edge cases ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["mx", "gemv", "nv", "w4a8"])
+def test_empty_k_gives_zeros(kind):
+    M, N = 5, 37
+    if kind == "w4a8":
+        d = {"A": np.zeros((M, 0), np.uint8), "sa": np.ones(M, np.float32),
+             "B": np.zeros((N, 0), np.uint8), "sB": np.zeros((N, 0), np.uint16)}
+    else:
+        V = 16 if kind == "nv" else 32
+        d = {"A": np.zeros((M, 0), np.uint8), "sfA": np.zeros((M, 0), np.uint8),
+             "B": np.zeros((N, 0), np.uint8), "sfB": np.zeros((N, 0), np.uint8), "gA": 1.0, "gB": 1.0}
+    for out in ("f32", "bf16"):
+        D = run(kind, d, out)
+        assert D.shape == (M, N) and not as_np(D).any()
+
+
+@pytest.mark.parametrize("kind", ["mx", "nv", "w4a8"])
+def test_empty_m(kind):
+    d = datagen.make_shape(kind if kind != "w4a8" else "w4a8", 3, 20, 256, seed=1)
+    for k in ("A", "sfA", "sa"):
+        if k in d:
+            d[k] = d[k][:0]
+    D = run(kind, d, "bf16")
+    assert D.shape == (0, 20)
+
+
+def test_invalid_calls_raise():
+    d = datagen.make_shape("mx", 4, 4, 256, seed=1)
+    t = up(d)
+    with pytest.raises(fp4.Fp4GemmError):
+        fp4.fp4_gemv(torch.zeros((17, 128), dtype=torch.uint8, device=DEV),
+                     torch.zeros((17, 8), dtype=torch.uint8, device=DEV), t["B"], t["sfB"])
+    with pytest.raises(TypeError):
+        fp4.mx_fp4_gemm(t["A"].to(torch.int8), t["sfA"], t["B"], t["sfB"])
+    with pytest.raises(ValueError):
+        fp4.mx_fp4_gemm(t["A"], t["sfA"][:, :4], t["B"], t["sfB"])
+    K = 192
+    A = torch.zeros((4, K // 2), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((4, K // 32), dtype=torch.uint8, device=DEV)
+    with pytest.raises(fp4.Fp4GemmError, match="status 2"):
+        fp4.mx_fp4_gemm(A, s, A, s)
