@@ -1,0 +1,277 @@
+"""Benchmark of the block-scaled FP4 GEMM path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--no-cpu]
+
+A step is one call of the hot path on one batch of resident synthetic input:
+the headline is the MXFP4 GEMM M = N = K = 8192 (E2M1 operands quantized from
+N(0,1) with max-abs E8M0 block scales, fp32 accumulation, bf16 output).  The
+decode GEMV (M=8, N=14336, K=4096, cache-cold through rotating weight copies),
+the W4A8 GEMM (256x8192x8192), the NVFP4 GEMM (1024^3) and the MXFP4 256^3 case
+are timed after it and reported in "also".  Every duration is the average of
+per-launch HIP event pairs recorded on the stream the kernel runs on (torch's
+current stream, which the binding passes to the library).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_scaled_precision_e2m1_amd as fp4  # noqa: E402
+import datagen  # noqa: E402
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "block_scaled_precision_e2m1_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(d, dev):
+    out = {}
+    for k, v in d.items():
+        if isinstance(v, np.ndarray) and v.ndim > 0:
+            if k == "sB":
+                out[k] = torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
+            else:
+                out[k] = torch.from_numpy(v).to(dev)
+    return out
+
+
+def time_launches(fn, steps, warmup, dev, arg_sets=None):
+    """Average duration (ms) of `steps` launches, each bracketed by its own HIP event
+    pair on the current stream.  `arg_sets` rotates inputs between launches."""
+    arg_sets = arg_sets or [()]
+    for i in range(warmup):
+        fn(*arg_sets[i % len(arg_sets)])
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        a = arg_sets[i % len(arg_sets)]
+        ev[i][0].record(stream)
+        fn(*a)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in ev]
+    return float(np.mean(per)), float(np.median(per)), wall
+
+
+def src_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(name, kernel_src, launches_bytes):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"{name}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("kernel_src_sha") != src_digest(*kernel_src):
+        return None
+    return float(c["fetch_bytes_scaled"] + c["write_bytes_scaled"])
+
+
+# ---- workloads ------------------------------------------------------------------------
+
+def bench_mx8192(steps, warmup, dev):
+    d = datagen.make("mxfp4_8192")
+    t = to_dev(d, dev)
+    M = N = K = 8192
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fn = lambda: fp4.mx_fp4_gemm(t["A"], t["sfA"], t["B"], t["sfB"], out=D)
+    mean_ms, med_ms, wall = time_launches(fn, steps, warmup, dev)
+    flops = 2.0 * M * N * K
+    tf = flops / (mean_ms * 1e-3) / 1e12
+    bytes_alg = d["A"].nbytes + d["sfA"].nbytes + d["B"].nbytes + d["sfB"].nbytes + M * N * 2
+    return d, {"ms": mean_ms, "median_ms": med_ms, "wall_s": wall, "tflops": tf, "flops": flops,
+               "bytes": bytes_alg}
+
+
+def bench_gemv(steps, warmup, dev):
+    d = datagen.make("mxfp4_gemv_8x14336x4096")
+    M, N, K = 8, 14336, 4096
+    base = to_dev(d, dev)
+    wbytes = d["B"].nbytes + d["sfB"].nbytes
+    copies = int(np.ceil(320e6 / wbytes))          # > 256 MB infinity cache: cold reads
+    sets = []
+    for c in range(copies):
+        B = base["B"].clone() if c else base["B"]
+        sB = base["sfB"].clone() if c else base["sfB"]
+        sets.append((B, sB))
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fn = lambda B, sB: fp4.fp4_gemv(base["A"], base["sfA"], B, sB, out=D)
+    mean_ms, med_ms, wall = time_launches(fn, steps, warmup, dev, sets)
+    bytes_alg = d["A"].nbytes + d["sfA"].nbytes + wbytes + M * N * 2
+    gbs = bytes_alg / (mean_ms * 1e-3) / 1e9
+    return {"ms": mean_ms, "median_ms": med_ms, "gbs": gbs, "bytes": bytes_alg, "copies": copies,
+            "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12}
+
+
+def bench_w4a8(steps, warmup, dev):
+    d = datagen.make("w4a8_256x8192x8192")
+    M, N, K = 256, 8192, 8192
+    base = to_dev(d, dev)
+    wbytes = d["B"].nbytes + d["sB"].nbytes
+    copies = int(np.ceil(320e6 / wbytes))
+    sets = [((base["B"].clone(), base["sB"].clone()) if c else (base["B"], base["sB"])) for c in range(copies)]
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fn = lambda B, sB: fp4.w4a8_gemm(base["A"], base["sa"], B, sB, out=D)
+    mean_ms, med_ms, wall = time_launches(fn, steps, warmup, dev, sets)
+    flops = 2.0 * M * N * K
+    bytes_alg = d["A"].nbytes + d["sa"].nbytes + wbytes + M * N * 2
+    return {"ms": mean_ms, "median_ms": med_ms, "tflops": flops / (mean_ms * 1e-3) / 1e12,
+            "gbs": bytes_alg / (mean_ms * 1e-3) / 1e9, "bytes": bytes_alg, "copies": copies}
+
+
+def bench_nv1024(steps, warmup, dev):
+    d = datagen.make("nvfp4_1024")
+    t = to_dev(d, dev)
+    M = N = K = 1024
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fn = lambda: fp4.nv_fp4_gemm(t["A"], t["sfA"], 1.0, t["B"], t["sfB"], 1.0, out=D)
+    mean_ms, med_ms, _ = time_launches(fn, steps, warmup, dev)
+    return {"ms": mean_ms, "median_ms": med_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12}
+
+
+def bench_mx256(steps, warmup, dev):
+    d = datagen.make("mxfp4_256")
+    t = to_dev(d, dev)
+    D = torch.empty((256, 256), dtype=torch.float32, device=dev)
+    fn = lambda: fp4.mx_fp4_gemm(t["A"], t["sfA"], t["B"], t["sfB"], out=D)
+    mean_ms, med_ms, _ = time_launches(fn, steps, warmup, dev)
+    return {"ms": mean_ms, "median_ms": med_ms, "tflops": 2.0 * 256 ** 3 / (mean_ms * 1e-3) / 1e12}
+
+
+def cpu_threads():
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(d, budget_s=15.0):
+    """The oracle, untuned, on whole rows of the 8192^3 workload: a short calibration
+    run picks the row count that fills about `budget_s` seconds."""
+    import oracle
+    threads = cpu_threads()
+    oracle.set_threads(threads)
+    N, K = 8192, 8192
+    t0 = time.perf_counter()
+    oracle.mx_gemm(d["A"], d["sfA"], d["B"], d["sfB"], rows=(0, threads))
+    per_row = (time.perf_counter() - t0) / threads
+    rows = int(max(threads, min(8192, budget_s / max(per_row, 1e-6))))
+    rows = (rows // threads) * threads
+    t0 = time.perf_counter()
+    oracle.mx_gemm(d["A"], d["sfA"], d["B"], d["sfB"], rows=(0, rows))
+    secs = time.perf_counter() - t0
+    return {"value": 2.0 * rows * N * K / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the 8192^3 MXFP4 GEMM (all 8192 columns, full K), "
+                      f"{secs:.1f} s on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", nargs="*", default=None,
+                    help="subset of: mx8192 gemv w4a8 nv1024 mx256")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    fp4.load_library()
+    only = set(args.only) if args.only else {"mx8192", "gemv", "w4a8", "nv1024", "mx256"}
+    also = {}
+    head = None
+    d8192 = None
+    if "mx8192" in only:
+        log("bench: mxfp4 8192^3 ...")
+        d8192, head = bench_mx8192(args.steps, args.warmup, dev)
+        log(f"bench: mxfp4 8192^3 {head['ms'] * 1e3:.1f} us/launch, {head['tflops']:.0f} TFLOP/s")
+    if "gemv" in only:
+        log("bench: gemv 8x14336x4096 (cold) ...")
+        g = bench_gemv(max(args.steps, 100), args.warmup, dev)
+        log(f"bench: gemv {g['ms'] * 1e3:.2f} us/launch, {g['gbs']:.0f} GB/s")
+        traffic = traffic_from_profile("fp4_gemv_8x14336x4096", ["fp4_gemv.hip"], g["bytes"])
+        also["mxfp4_gemv_8x14336x4096"] = {
+            "metric": "HBM GB/s", "value": g["gbs"], "ms_per_launch": g["ms"], "median_ms": g["median_ms"],
+            "cache": f"cold ({g['copies']} rotating weight copies)",
+            "roofline": {"bound": "hbm", "achieved": g["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": g["gbs"] / PEAK_HBM_GBS, "traffic": traffic},
+            "algorithmic_bytes": g["bytes"], "tflops": g["tflops"]}
+    if "w4a8" in only:
+        log("bench: w4a8 256x8192x8192 ...")
+        w = bench_w4a8(args.steps, args.warmup, dev)
+        log(f"bench: w4a8 {w['ms'] * 1e3:.1f} us/launch, {w['tflops']:.0f} TFLOP/s, {w['gbs']:.0f} GB/s")
+        also["w4a8_256x8192x8192"] = {
+            "metric": "TFLOP/s", "value": w["tflops"], "ms_per_launch": w["ms"],
+            "cache": f"cold ({w['copies']} rotating weight copies)",
+            "roofline": {"bound": "mfma", "achieved": w["tflops"], "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                         "frac": w["tflops"] / PEAK_TFLOPS["fp8"], "traffic": None},
+            "hbm": {"achieved": w["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": w["gbs"] / PEAK_HBM_GBS}}
+    if "nv1024" in only:
+        n = bench_nv1024(args.steps, args.warmup, dev)
+        log(f"bench: nvfp4 1024^3 {n['ms'] * 1e3:.1f} us/launch, {n['tflops']:.0f} TFLOP/s")
+        also["nvfp4_1024"] = {"metric": "TFLOP/s", "value": n["tflops"], "ms_per_launch": n["ms"],
+                              "roofline": {"bound": "mfma", "achieved": n["tflops"], "peak": PEAK_TFLOPS["bf16"],
+                                           "unit": "TFLOP/s", "frac": n["tflops"] / PEAK_TFLOPS["bf16"],
+                                           "traffic": None}}
+    if "mx256" in only:
+        s = bench_mx256(args.steps, args.warmup, dev)
+        also["mxfp4_256_f32"] = {"metric": "TFLOP/s", "value": s["tflops"], "ms_per_launch": s["ms"]}
+
+    line = {"metric": "TFLOP/s MXFP4 GEMM 8192^3 (% MFMA peak); FP4 GEMV HBM GB/s (% of 8 TB/s)",
+            "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp4e2m1", "data": "synthetic",
+            "config": {"workload": "mxfp4_gemm_8192x8192x8192", "M": 8192, "N": 8192, "K": 8192,
+                       "scale": "e8m0 per 32", "out": "bf16", "inputs": "N(0,1) max-abs MX-quantized, seed 0"}}
+    if head is not None:
+        line["value"] = head["tflops"]
+        line["ms_per_step"] = head["ms"]
+        line["roofline"] = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_TFLOPS["fp4"],
+                            "unit": "TFLOP/s", "frac": head["tflops"] / PEAK_TFLOPS["fp4"],
+                            "traffic": traffic_from_profile("mxfp4_gemm_8192", ["mxfp4_gemm.hip", "common.hpp"],
+                                                            head["bytes"])}
+        if not args.no_cpu:
+            log("bench: cpu oracle baseline ...")
+            line["cpu_baseline"] = cpu_baseline(d8192)
+    line["also"] = also
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
