@@ -166,6 +166,16 @@ def bench_mx256(steps, warmup, dev):
     return {"ms": mean_ms, "median_ms": med_ms, "tflops": 2.0 * 256 ** 3 / (mean_ms * 1e-3) / 1e12}
 
 
+def bench_copy(dev, mib=512):
+    """A plain device copy of known size, the reference that scales the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) into bytes."""
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    ms, _, _ = time_launches(lambda: dst.copy_(src), 3, 1, dev)
+    return {"bytes_each_way": n, "ms": ms, "gbs": 2 * n / (ms * 1e-3) / 1e9}
+
+
 def cpu_threads():
     n = len(os.sched_getaffinity(0))
     env = os.environ.get("OMP_NUM_THREADS")
@@ -201,7 +211,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: mx8192 gemv w4a8 nv1024 mx256")
+                    help="subset of: mx8192 gemv w4a8 nv1024 mx256 copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -249,6 +259,10 @@ def main():
                               "roofline": {"bound": "mfma", "achieved": n["tflops"], "peak": PEAK_TFLOPS["bf16"],
                                            "unit": "TFLOP/s", "frac": n["tflops"] / PEAK_TFLOPS["bf16"],
                                            "traffic": None}}
+    if "copy" in only:
+        c = bench_copy(dev)
+        log(f"bench: copy 512 MiB {c['ms'] * 1e3:.1f} us, {c['gbs']:.0f} GB/s (read+write)")
+        also["copy_512MiB"] = c
     if "mx256" in only:
         s = bench_mx256(args.steps, args.warmup, dev)
         also["mxfp4_256_f32"] = {"metric": "TFLOP/s", "value": s["tflops"], "ms_per_launch": s["ms"]}

@@ -2,50 +2,50 @@
 //
 // The block-scaled product with E8M0 scales per 32 K elements is the one of
 // section 1 ("Block-Scaled MXFP4 GEMM in cute-rs (SM120a)") of the cuda-oxide
-// page "TMA Pipelines, Tensor Cores, and ctm-rs Interop": each 128-element K
-// stage of packed FP4 is consumed as two K=64 MMA steps, one E8M0 scale pair
-// per step, fed by a multi-stage ring of asynchronous copies.  The loop nest
-// (output tiles over the grid, a runtime K-tile loop, an unrolled inner loop
-// over instructions) follows the tiled-GEMM nest of the Hopper CUTLASS/CuTe DSL
-// post, section "Where each level sits in the GEMM loop nest"; accumulators
-// start at zero and D is never read (same section, the zero-fill form).  The
-// ring depth follows the rule of that post's section "The six choices of the
-// SS builder" (choice 5): as many stages as fit in the on-chip memory.
+// page "TMA Pipelines, Tensor Cores, and ctm-rs Interop": packed FP4 K stages
+// are consumed as K=64 MMA steps, one E8M0 scale pair per step, fed by a ring of
+// asynchronous copies.  The loop nest (output tiles over the grid, a runtime
+// K-tile loop, an unrolled inner loop over instructions) follows the tiled-GEMM
+// nest of the Hopper CUTLASS/CuTe DSL post, section "Where each level sits in the
+// GEMM loop nest"; accumulators start at zero and D is never read (same section,
+// the zero-fill form).  The ring depth follows the rule of that post's section
+// "The six choices of the SS builder" (choice 5): as many stages as fit on chip.
 //
 // gfx950 design:
 //   * one workgroup of 4 waves per BM x BN output tile, each wave owning a
 //     WM x WN sub-tile (128 x 128 at the large configuration: 16 32x32 blocks,
 //     256 fp32 accumulators per lane, held in AGPRs);
-//   * K advances 128 elements (64 bytes of packed FP4 per row) per step.  The
-//     A/B tiles and their E8M0 scale dwords of a step are copied HBM -> LDS by
-//     global_load_lds_dwordx4 / _dword (no VGPR round trip) into a STAGES-deep
-//     ring, issued STAGES-1 steps ahead; each wave waits for its own copies with
-//     s_waitcnt vmcnt and one s_barrier per step publishes them;
-//   * LDS rows are 64 bytes; the four 16-byte chunks of row r sit at chunk
-//     position c ^ swz(r), so 8 (or 16) lanes reading one logical chunk of
+//   * a K stage is BK elements (BK/2 bytes of packed FP4 per row): 256 when K
+//     allows, so every row segment a copy fetches is a whole 128-byte cache line
+//     (64-byte half lines cost twice the L1 traffic); 128 otherwise;
+//   * the A/B tiles of a stage and their E8M0 scale dwords are copied HBM -> LDS
+//     by global_load_lds_dwordx4 / _dword (no VGPR round trip) into a ring of
+//     STAGES slots; each wave waits for its own copies with s_waitcnt vmcnt and
+//     one s_barrier per stage publishes them;
+//   * LDS rows are BK/2 bytes; 16-byte chunk c of row r sits at chunk position
+//     c ^ swz(r), so the 8 (or 16) lanes that read one logical chunk of
 //     consecutive rows hit distinct banks with ds_read_b128.  A copy instruction
 //     writes 1 KB contiguously (lane i -> bytes 16i..16i+15), so lane i fetches
 //     the global chunk that belongs at that position;
-//   * v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands: lane l (slot h = l/32)
-//     holds chunks 2h and 2h+1 of its row, i.e. K blocks {2h, 2h+1}; the MFMA of
-//     half kk uses chunk 2h+kk with op_sel = kk on the row's scale dword shifted
-//     right by 16*h, so every lane's scale byte matches its 32 elements;
-//   * the fragments of the next half step are read from LDS while the MFMAs of
-//     the current one run (two register sets), and the barrier sits between the
-//     two halves, so the MFMA pipe is fed across it;
+//   * v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands: a stage is NQ = BK/64
+//     MFMA quarters; lane l (slot h = l/32) owns chunks NQ*h .. NQ*h+NQ-1 of its
+//     row, and quarter kq uses chunk NQ*h+kq with op_sel = kq on the scale dword
+//     that holds blocks NQ*h .. NQ*h+3 (shifted when NQ = 2), so every lane's
+//     scale byte matches its 32 elements;
+//   * inside a stage the fragments of the next quarter are read while the 16
+//     MFMAs of the current one run; the barrier sits before the last quarter,
+//     whose MFMAs hide the copies for stage s+STAGES (into the slot stage s just
+//     released) and the reads of stage s+1's first quarter and scales;
 //   * output tiles are numbered so that the tiles resident at once on one XCD
 //     (workgroups are dealt round-robin over the 8 XCDs) share A and B panels
 //     in that XCD's L2.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.h"
 
 namespace fp4g {
 namespace {
-
-constexpr int kBK = 128;            // K elements per step
-constexpr int kRowBytes = kBK / 2;  // 64 bytes of packed FP4 per row per step
-
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -88,6 +88,17 @@ __device__ __forceinline__ void barrier_lds() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Chunk swizzles: rows of 4 chunks (64 B) and of 8 chunks (128 B).  Consecutive
+// rows read at one logical chunk land in distinct 16-byte bank groups within any
+// 8 (mod 128 B) or 16 (mod 256 B) lane group.
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+template <int CHUNKS>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CHUNKS == 4) return swz4(r);
+  else return swz8(r);
+}
+
 // Map a linear workgroup id to an output tile (tm, tn).  Consecutive ids are dealt
 // to the 8 XCDs in turn; they are regrouped so each XCD owns a contiguous range of
 // a grouped (G tile rows at a time) tile order.
@@ -104,29 +115,40 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int* t
   *tn = in_group / gsize;
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES>
 struct Cfg {
   static constexpr int NW = (BM / WM) * (BN / WN);
   static constexpr int NT = NW * 64;
-  static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
-  static constexpr int SA_OFF = A_BYTES + B_BYTES, SB_OFF = SA_OFF + BM * 4;
-  static constexpr int STAGE = SB_OFF + BN * 4;
+  static constexpr int ROWB = BK / 2;              // bytes of one row per stage
+  static constexpr int CHUNKS = ROWB / 16;         // 16-byte chunks per row
+  static constexpr int NQ = BK / 64;               // MFMA quarters per stage
+  static constexpr int SDW = BK / 128;             // scale dwords per row per stage
+  static constexpr int RPC = 1024 / ROWB;          // rows per 1 KB copy
+  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  static constexpr int SA_OFF = A_BYTES + B_BYTES;            // scales: [SDW][rows] dwords
+  static constexpr int SB_OFF = SA_OFF + SDW * BM * 4;
+  static constexpr int STAGE = SB_OFF + SDW * BN * 4;
   static constexpr int LDS = STAGE * STAGES;
-  static constexpr int IA = BM / 16 / NW, IB = BN / 16 / NW;   // 1 KB copies per wave per step
-  static constexpr int SCA = BM / 64, SCB = BN / 64;           // 256 B scale copies per step
-  static constexpr int LOADS = IA + IB + 2;                    // copies per wave per step
-  static_assert(IA >= 1 && IB >= 1 && BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "tile/waves");
-  static_assert(SCA >= 1 && SCB >= 1 && NW % SCA == 0 && NW % SCB == 0, "scale copies");
+  static constexpr int IA = BM / RPC / NW, IB = BN / RPC / NW;   // 1 KB copies per wave per stage
+  static constexpr int TSA = SDW * BM / 64, TSB = SDW * BN / 64;  // 256 B scale copies per stage
+  static constexpr int SCA = (TSA + NW - 1) / NW, SCB = (TSB + NW - 1) / NW;   // per wave
+  static constexpr int LOADS = IA + IB + SCA + SCB;             // copies per wave per stage
+  static_assert(BK == 128 || BK == 256, "stage size");
+  static_assert(IA >= 1 && IB >= 1 && BM % (RPC * NW) == 0 && BN % (RPC * NW) == 0, "tile/waves");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "scale copies cover 64 rows");
+  static_assert(STAGE % 256 == 0, "stage alignment");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2 && (STAGES - 1) * LOADS < 64, "vmcnt range");
 };
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool BF16>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, bool BF16>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
                   const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, void* __restrict__ D) {
-  using C = Cfg<BM, BN, WM, WN, STAGES>;
+  using C = Cfg<BM, BN, WM, WN, BK, STAGES>;
   constexpr int NWN = BN / WN;
   constexpr int FI = WM / 32, FJ = WN / 32;
+  constexpr int NQ = C::NQ;
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
@@ -141,44 +163,65 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int64_t lda = K / 2, ldsf = K / 32;
-  const int KT = K / kBK;
+  const int KS = K / BK;
 
   // ---- copy sources: this lane's global rows / chunks for each of its copies ----
   const uint8_t* ga[C::IA];
   const uint8_t* gb[C::IB];
 #pragma unroll
   for (int i = 0; i < C::IA; ++i) {
-    const int row = 16 * (wave * C::IA + i) + (lane >> 2);
-    const int c = (lane & 3) ^ swz(row);
+    const int row = C::RPC * (wave * C::IA + i) + lane / C::CHUNKS;
+    const int c = (lane % C::CHUNKS) ^ swz<C::CHUNKS>(row);
     ga[i] = A + (int64_t)min(m0 + row, M - 1) * lda + c * 16;
   }
 #pragma unroll
   for (int i = 0; i < C::IB; ++i) {
-    const int row = 16 * (wave * C::IB + i) + (lane >> 2);
-    const int c = (lane & 3) ^ swz(row);
+    const int row = C::RPC * (wave * C::IB + i) + lane / C::CHUNKS;
+    const int c = (lane % C::CHUNKS) ^ swz<C::CHUNKS>(row);
     gb[i] = B + (int64_t)min(n0 + row, N - 1) * lda + c * 16;
   }
-  // scale copies: wave w copies 64 rows of sfA (block w % SCA) and of sfB (block w % SCB);
-  // waves beyond the block count repeat a block (identical bytes to identical places).
-  const int sca_blk = wave % C::SCA, scb_blk = wave % C::SCB;
-  const uint8_t* gsa = sfA + (int64_t)min(m0 + 64 * sca_blk + lane, M - 1) * ldsf;
-  const uint8_t* gsb = sfB + (int64_t)min(n0 + 64 * scb_blk + lane, N - 1) * ldsf;
+  // Scale copy z covers dword d = z / (rows/64) of 64 rows (block z % (rows/64)).  When
+  // there are fewer copies than waves, waves repeat one (identical bytes, same place).
+  const uint8_t* gsa[C::SCA];
+  const uint8_t* gsb[C::SCB];
+  int lsa[C::SCA], lsb[C::SCB];
+#pragma unroll
+  for (int j = 0; j < C::SCA; ++j) {
+    const int z = (wave * C::SCA + j) % C::TSA, d = z / (BM / 64), blk = z % (BM / 64);
+    gsa[j] = sfA + (int64_t)min(m0 + 64 * blk + lane, M - 1) * ldsf + 4 * d;
+    lsa[j] = C::SA_OFF + d * BM * 4 + 256 * blk;
+  }
+#pragma unroll
+  for (int j = 0; j < C::SCB; ++j) {
+    const int z = (wave * C::SCB + j) % C::TSB, d = z / (BN / 64), blk = z % (BN / 64);
+    gsb[j] = sfB + (int64_t)min(n0 + 64 * blk + lane, N - 1) * ldsf + 4 * d;
+    lsb[j] = C::SB_OFF + d * BN * 4 + 256 * blk;
+  }
 
-  // Copies of step kt into ring slot kt % STAGES.  Steps past the end re-read the last
-  // step (the copies land in slots nobody reads), which keeps the loop branch-free.
-  auto issue = [&](int kt) {
-    const int st = kt % STAGES;
-    const int ks = min(kt, KT - 1);
+  // Copy q (0 .. LOADS-1) of stage ks into ring slot ks % STAGES: A chunks, B chunks,
+  // then the scale blocks.  Stages past the end re-read the last stage (the copies land
+  // in slots nobody reads), which keeps the loop branch-free.
+  auto issue_one = [&](int ks, int q) {
+    const int st = ks % STAGES;
+    const int kc = min(ks, KS - 1);
     uint8_t* base = smem + st * C::STAGE;
-    const int64_t kb = (int64_t)ks * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < C::IA; ++i)
-      lds_copy16(ga[i] + kb, (lds_void*)(base + 1024 * (wave * C::IA + i)));
-#pragma unroll
-    for (int i = 0; i < C::IB; ++i)
+    const int64_t kb = (int64_t)kc * C::ROWB;
+    if (q < C::IA) {
+      lds_copy16(ga[q] + kb, (lds_void*)(base + 1024 * (wave * C::IA + q)));
+    } else if (q < C::IA + C::IB) {
+      const int i = q - C::IA;
       lds_copy16(gb[i] + kb, (lds_void*)(base + C::A_BYTES + 1024 * (wave * C::IB + i)));
-    lds_copy4(gsa + ks * 4, (lds_void*)(base + C::SA_OFF + 256 * sca_blk));
-    lds_copy4(gsb + ks * 4, (lds_void*)(base + C::SB_OFF + 256 * scb_blk));
+    } else if (q < C::IA + C::IB + C::SCA) {
+      const int j = q - C::IA - C::IB;
+      lds_copy4(gsa[j] + kc * 4 * C::SDW, (lds_void*)(base + lsa[j]));
+    } else {
+      const int j = q - C::IA - C::IB - C::SCA;
+      lds_copy4(gsb[j] + kc * 4 * C::SDW, (lds_void*)(base + lsb[j]));
+    }
+  };
+  auto issue = [&](int ks) {
+#pragma unroll
+    for (int q = 0; q < C::LOADS; ++q) issue_one(ks, q);
   };
 
   // ---- LDS read offsets of this lane's fragments ----
@@ -189,25 +232,41 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   for (int j = 0; j < FJ; ++j) rb[j] = wn * WN + j * 32 + r32;
 
   v4i fa[2][FI], fb[2][FJ];
-  int sa[FI], sb[FJ];
-  auto read_frags = [&](int kt, int kk, int set) {
-    const uint8_t* base = smem + (kt % STAGES) * C::STAGE;
-    const int c = 2 * hi + kk;
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-      fa[set][i] = *reinterpret_cast<const v4i*>(base + ra[i] * kRowBytes + ((c ^ swz(ra[i])) << 4));
-#pragma unroll
-    for (int j = 0; j < FJ; ++j)
-      fb[set][j] = *reinterpret_cast<const v4i*>(base + C::A_BYTES + rb[j] * kRowBytes + ((c ^ swz(rb[j])) << 4));
+  int sa[FI], sb[FJ];     // scales of the stage being computed
+  int na[FI], nb[FJ];     // scales of the next stage, read during the current one
+  // Fragment r (0 .. FI+FJ-1: A blocks, then B blocks) of quarter kq of stage ks.
+  auto read_frag = [&](int ks, int kq, int set, int r) {
+    const uint8_t* base = smem + (ks % STAGES) * C::STAGE;
+    const int c = NQ * hi + kq;
+    if (r < FI)
+      fa[set][r] = *reinterpret_cast<const v4i*>(base + ra[r] * C::ROWB + ((c ^ swz<C::CHUNKS>(ra[r])) << 4));
+    else
+      fb[set][r - FI] = *reinterpret_cast<const v4i*>(base + C::A_BYTES + rb[r - FI] * C::ROWB +
+                                                      ((c ^ swz<C::CHUNKS>(rb[r - FI])) << 4));
   };
-  auto read_scales = [&](int kt) {
-    const uint8_t* base = smem + (kt % STAGES) * C::STAGE;
+  auto read_frags = [&](int ks, int kq, int set) {
 #pragma unroll
-    for (int i = 0; i < FI; ++i)
-      sa[i] = (int)(*reinterpret_cast<const uint32_t*>(base + C::SA_OFF + 4 * ra[i]) >> (16 * hi));
+    for (int r = 0; r < FI + FJ; ++r) read_frag(ks, kq, set, r);
+  };
+  // Scale dword r (A blocks, then B blocks) of stage ks into the next-stage set: the dword
+  // holding blocks NQ*hi .., shifted so op_sel = kq picks block NQ*hi + kq.
+  auto read_scale = [&](int ks, int r) {
+    const uint8_t* base = smem + (ks % STAGES) * C::STAGE;
+    const int d = (NQ * hi) >> 2, sh = 8 * ((NQ * hi) & 3);
+    if (r < FI)
+      na[r] = (int)(*reinterpret_cast<const uint32_t*>(base + C::SA_OFF + d * BM * 4 + 4 * ra[r]) >> sh);
+    else
+      nb[r - FI] = (int)(*reinterpret_cast<const uint32_t*>(base + C::SB_OFF + d * BN * 4 + 4 * rb[r - FI]) >> sh);
+  };
+  auto read_scales = [&](int ks) {
 #pragma unroll
-    for (int j = 0; j < FJ; ++j)
-      sb[j] = (int)(*reinterpret_cast<const uint32_t*>(base + C::SB_OFF + 4 * rb[j]) >> (16 * hi));
+    for (int r = 0; r < FI + FJ; ++r) read_scale(ks, r);
+  };
+  auto take_scales = [&]() {
+#pragma unroll
+    for (int i = 0; i < FI; ++i) sa[i] = na[i];
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) sb[j] = nb[j];
   };
 
   v16f acc[FI][FJ];
@@ -216,47 +275,74 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 #pragma unroll
     for (int j = 0; j < FJ; ++j) acc[i][j] = v16f{};
 
-  // ---- prologue: copies for steps 0 .. STAGES-2, then step 0's first half ----
+  // The MFMAs of quarter KQ (register set SET); after MFMA q, `extra(q)` issues that
+  // slot's memory instructions, in a fixed order (sched_barrier pins it), so their issue
+  // hides under the MFMA pipe.
+  auto quarter = [&](auto kq_c, auto set_c, auto&& extra) {
+    constexpr int KQ = decltype(kq_c)::value, SET = decltype(set_c)::value;
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p) issue(p);
-  wait_vmcnt<(STAGES - 2) * C::LOADS>();
+    for (int q = 0; q < FI * FJ; ++q) {
+      const int i = q / FJ, j = q % FJ;
+      acc[i][j] = mfma_fp4_32x32<KQ>(fa[SET][i], fb[SET][j], acc[i][j], sa[i], sb[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      extra(q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Quarter KQ (not the last) while reading quarter KQ+1's fragments into the other set.
+  auto mid_quarter = [&](int ks, auto kq_c) {
+    constexpr int KQ = decltype(kq_c)::value;
+    quarter(kq_c, std::integral_constant<int, (KQ & 1)>{}, [&](int q) {
+      if (q < FI + FJ) read_frag(ks, KQ + 1, (KQ + 1) & 1, q);
+    });
+#pragma unroll
+    for (int q = FI * FJ; q < FI + FJ; ++q) read_frag(ks, KQ + 1, (KQ + 1) & 1, q);
+  };
+
+  // ---- prologue: copies for stages 0 .. STAGES-1, then stage 0's first quarter ----
+#pragma unroll
+  for (int p = 0; p < STAGES; ++p) issue(p);
+  wait_vmcnt<(STAGES - 1) * C::LOADS>();
   barrier_lds();
   read_scales(0);
+  take_scales();
   read_frags(0, 0, 0);
 
-  // One K step per iteration, in seven phases, with no branches in the body (so the
-  // compiler keeps the phase order):
-  //   (1) copies for step kt+STAGES-1 into the slot freed by step kt-1
-  //   (2) second-half fragments of step kt
-  //   (3) first-half MFMAs of step kt
-  //   (4) this wave's copies of step kt+1 complete; the barrier publishes everyone's
-  //   (5) first-half fragments of step kt+1
-  //   (6) second-half MFMAs of step kt
-  //   (7) scales of step kt+1 (the MFMAs of (6) have read the old ones at issue)
-  // The MFMAs of (3) and (6) drain in the MFMA pipe while the wave waits at the
-  // barrier and for its LDS reads.  On the last step, (5) and (7) read a slot that
-  // holds a re-read copy; the values are unused.
-  for (int kt = 0; kt < KT; ++kt) {
-    issue(kt + STAGES - 1);
-    read_frags(kt, 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < FJ; ++j)
-        acc[i][j] = mfma_fp4_32x32<0>(fa[0][i], fb[0][j], acc[i][j], sa[i], sb[j]);
-    __builtin_amdgcn_sched_barrier(0);
+  // One stage per iteration, no branches in the body (so the compiler keeps the order):
+  //   quarters 0 .. NQ-2: MFMAs of quarter kq, reading quarter kq+1's fragments;
+  //   this wave's copies of stage ks+1 complete; the barrier publishes everyone's and
+  //     certifies that every wave has finished reading slot ks % STAGES;
+  //   quarter NQ-1: MFMAs, while issuing the copies of stage ks+STAGES into that slot
+  //     and reading stage ks+1's first-quarter fragments and scales;
+  //   the next scales become current.
+  // On the last stages the reads of stage ks+1 hit a slot holding a re-read copy; the
+  // values are unused.
+  constexpr int LQ = NQ - 1;
+  static_assert((LQ & 1) == 1, "the last quarter uses register set 1");
+  for (int ks = 0; ks < KS; ++ks) {
+    mid_quarter(ks, std::integral_constant<int, 0>{});
+    if constexpr (NQ == 4) {
+      mid_quarter(ks, std::integral_constant<int, 1>{});
+      mid_quarter(ks, std::integral_constant<int, 2>{});
+    }
+    // Stage ks+1's copies were issued one stage ago; STAGES-2 newer stages may still fly.
     wait_vmcnt<(STAGES - 2) * C::LOADS>();
     barrier_lds();
-    read_frags(kt + 1, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    quarter(std::integral_constant<int, LQ>{}, std::integral_constant<int, 1>{}, [&](int q) {
+      if (q < C::LOADS) issue_one(ks + STAGES, q);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < FI + FJ) read_frag(ks + 1, 0, 0, q);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < FI + FJ) read_scale(ks + 1, q);
+    });
 #pragma unroll
-    for (int i = 0; i < FI; ++i)
+    for (int q = FI * FJ; q < C::LOADS; ++q) issue_one(ks + STAGES, q);
 #pragma unroll
-      for (int j = 0; j < FJ; ++j)
-        acc[i][j] = mfma_fp4_32x32<1>(fa[1][i], fb[1][j], acc[i][j], sa[i], sb[j]);
-    __builtin_amdgcn_sched_barrier(0);
-    read_scales(kt + 1);
+    for (int q = FI * FJ; q < FI + FJ; ++q) {
+      read_frag(ks + 1, 0, 0, q);
+      read_scale(ks + 1, q);
+    }
+    take_scales();
   }
   // No copy may still be landing in LDS when the workgroup exits.
   wait_vmcnt<0>();
@@ -275,17 +361,17 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
     }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES>
 hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
-  using C = Cfg<BM, BN, WM, WN, STAGES>;
+  using C = Cfg<BM, BN, WM, WN, BK, STAGES>;
   const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, BN);
   if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
   if (a.bf16_out)
-    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, STAGES, true>), dim3((unsigned)tiles), dim3(C::NT), 0,
-                       s, (int)a.M, (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
+    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, BK, STAGES, true>), dim3((unsigned)tiles), dim3(C::NT),
+                       0, s, (int)a.M, (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
   else
-    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, STAGES, false>), dim3((unsigned)tiles), dim3(C::NT), 0,
-                       s, (int)a.M, (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
+    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, BK, STAGES, false>), dim3((unsigned)tiles), dim3(C::NT),
+                       0, s, (int)a.M, (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
   return hipGetLastError();
 }
 
@@ -294,9 +380,16 @@ hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
 hipError_t launch_mxfp4_gemm(const FP4Args& a, hipStream_t s) {
   const int64_t t256 = ceil_div(a.M, 256) * ceil_div(a.N, 256);
   const int64_t t128 = ceil_div(a.M, 128) * ceil_div(a.N, 128);
-  if (t256 >= 256) return launch_cfg<256, 256, 128, 128, 4>(a, s);
-  if (t128 >= 128) return launch_cfg<128, 128, 64, 64, 4>(a, s);
-  return launch_cfg<64, 64, 32, 32, 4>(a, s);
+  const bool k256 = a.K % 256 == 0;
+  if (t256 >= 256) {
+    if (k256) return launch_cfg<256, 256, 128, 128, 256, 2>(a, s);
+    return launch_cfg<256, 256, 128, 128, 128, 4>(a, s);
+  }
+  if (t128 >= 128) {
+    if (k256) return launch_cfg<128, 128, 64, 64, 256, 2>(a, s);
+    return launch_cfg<128, 128, 64, 64, 128, 4>(a, s);
+  }
+  return launch_cfg<64, 64, 32, 32, 128, 4>(a, s);
 }
 
 }  // namespace fp4g
