@@ -29,12 +29,16 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kFmtFp8 = 0;   // OCP E4M3
 constexpr int kFmtFp4 = 4;   // E2M1
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays NaN (quiet).
+// fp32 -> bf16 bits with gfx950's v_cvt_pk_bf16_f32: round to nearest even, NaN stays
+// NaN (quiet).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two values -> packed bf16x2 (low half = a), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float v2f_ __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf_ __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_{a, b}), v2bf_));
 }
 
 // Store one output element of type OUT (float or bf16 bits) to D[idx].
@@ -44,6 +48,37 @@ __device__ __forceinline__ void store_out(void* D, int64_t idx, float v) {
     reinterpret_cast<uint16_t*>(D)[idx] = f32_to_bf16_rne(v);
   } else {
     reinterpret_cast<float*>(D)[idx] = v;
+  }
+}
+
+// Store four consecutive output elements D[idx .. idx+3] of type OUT; only the first
+// `avail` exist when the row ends inside the group.  A whole group goes out as one
+// 8-byte (bf16) or 16-byte (fp32) store when its address is aligned for it.
+template <bool BF16>
+__device__ __forceinline__ void store_out4(void* D, int64_t idx, int avail, float v0, float v1, float v2,
+                                           float v3) {
+  if constexpr (BF16) {
+    uint16_t* p = reinterpret_cast<uint16_t*>(D) + idx;
+    const uint32_t w01 = pack_bf16x2(v0, v1), w23 = pack_bf16x2(v2, v3);
+    if (avail >= 4 && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
+      typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<v2u*>(p) = v2u{w01, w23};
+    } else {
+      if (avail > 0) p[0] = (uint16_t)w01;
+      if (avail > 1) p[1] = (uint16_t)(w01 >> 16);
+      if (avail > 2) p[2] = (uint16_t)w23;
+      if (avail > 3) p[3] = (uint16_t)(w23 >> 16);
+    }
+  } else {
+    float* p = reinterpret_cast<float*>(D) + idx;
+    if (avail >= 4 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      *reinterpret_cast<v4f*>(p) = v4f{v0, v1, v2, v3};
+    } else {
+      if (avail > 0) p[0] = v0;
+      if (avail > 1) p[1] = v1;
+      if (avail > 2) p[2] = v2;
+      if (avail > 3) p[3] = v3;
+    }
   }
 }
 

@@ -29,6 +29,9 @@ struct W4A8Args {
   bool bf16_out;
 };
 
+// Compute units of the current device (queried once per device, then cached).
+int64_t device_cus();
+
 hipError_t launch_mxfp4_gemm(const FP4Args& a, hipStream_t s);
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s);
 hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s);

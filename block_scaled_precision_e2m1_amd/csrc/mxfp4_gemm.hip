@@ -158,8 +158,14 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   const int wm = wave / NWN, wn = wave % NWN;
   const int hi = lane >> 5, r32 = lane & 31;
 
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int T = tiles_m * tiles_n;
+  // Persistent: the grid is at most one workgroup per CU and each workgroup walks its
+  // tiles.  A tile's output stores drain while the next tile's copies and MFMAs run,
+  // instead of every CU writing its tile at the same moment.
+  for (int tile = blockIdx.x; tile < T; tile += gridDim.x) {
   int tm, tn;
-  tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, &tm, &tn);
+  tile_of(tile, tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int64_t lda = K / 2, ldsf = K / 32;
@@ -283,26 +289,41 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 #pragma unroll
     for (int q = 0; q < FI * FJ; ++q) {
       const int i = q / FJ, j = q % FJ;
-      acc[i][j] = mfma_fp4_32x32<KQ>(fa[SET][i], fb[SET][j], acc[i][j], sa[i], sb[j]);
+      // B first: the accumulator holds D^T, so a lane owns 4 consecutive columns of a row
+      acc[i][j] = mfma_fp4_32x32<KQ>(fb[SET][j], fa[SET][i], acc[i][j], sb[j], sa[i]);
       __builtin_amdgcn_sched_barrier(0);
       extra(q);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Quarter KQ (not the last) while reading quarter KQ+1's fragments into the other set.
+  // The copies of stage j are issued in two halves: copies 0 .. LH-1 under the last
+  // quarter of stage j-STAGES (right after the barrier that frees its slot), copies
+  // LH .. LOADS-1 under the first quarter of stage j-STAGES+1.
+  constexpr int LH = (C::LOADS + 1) / 2;
+  // Quarter KQ (not the last) while reading quarter KQ+1's fragments into the other set;
+  // quarter 0 also issues the second half of stage ks+STAGES-1's copies.
   auto mid_quarter = [&](int ks, auto kq_c) {
     constexpr int KQ = decltype(kq_c)::value;
     quarter(kq_c, std::integral_constant<int, (KQ & 1)>{}, [&](int q) {
       if (q < FI + FJ) read_frag(ks, KQ + 1, (KQ + 1) & 1, q);
+      __builtin_amdgcn_sched_barrier(0);
+      if (KQ == 0 && q < C::LOADS - LH) issue_one(ks + STAGES - 1, LH + q);
     });
 #pragma unroll
     for (int q = FI * FJ; q < FI + FJ; ++q) read_frag(ks, KQ + 1, (KQ + 1) & 1, q);
+    if constexpr (KQ == 0) {
+#pragma unroll
+      for (int q = FI * FJ; q < C::LOADS - LH; ++q) issue_one(ks + STAGES - 1, LH + q);
+    }
   };
 
-  // ---- prologue: copies for stages 0 .. STAGES-1, then stage 0's first quarter ----
+  // ---- prologue: copies for stages 0 .. STAGES-2 and the first half of stage
+  // STAGES-1, then stage 0's first quarter ----
 #pragma unroll
-  for (int p = 0; p < STAGES; ++p) issue(p);
-  wait_vmcnt<(STAGES - 1) * C::LOADS>();
+  for (int p = 0; p < STAGES - 1; ++p) issue(p);
+#pragma unroll
+  for (int q = 0; q < LH; ++q) issue_one(STAGES - 1, q);
+  wait_vmcnt<(STAGES - 2) * C::LOADS + LH>();
   barrier_lds();
   read_scales(0);
   take_scales();
@@ -325,18 +346,19 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
       mid_quarter(ks, std::integral_constant<int, 1>{});
       mid_quarter(ks, std::integral_constant<int, 2>{});
     }
-    // Stage ks+1's copies were issued one stage ago; STAGES-2 newer stages may still fly.
+    // Stage ks+1's copies are complete once at most the STAGES-2 stages issued after them
+    // (ks+2 .. ks+STAGES-1, both halves) are in flight.
     wait_vmcnt<(STAGES - 2) * C::LOADS>();
     barrier_lds();
     quarter(std::integral_constant<int, LQ>{}, std::integral_constant<int, 1>{}, [&](int q) {
-      if (q < C::LOADS) issue_one(ks + STAGES, q);
+      if (q < LH) issue_one(ks + STAGES, q);
       __builtin_amdgcn_sched_barrier(0);
       if (q < FI + FJ) read_frag(ks + 1, 0, 0, q);
       __builtin_amdgcn_sched_barrier(0);
       if (q < FI + FJ) read_scale(ks + 1, q);
     });
 #pragma unroll
-    for (int q = FI * FJ; q < C::LOADS; ++q) issue_one(ks + STAGES, q);
+    for (int q = FI * FJ; q < LH; ++q) issue_one(ks + STAGES, q);
 #pragma unroll
     for (int q = FI * FJ; q < FI + FJ; ++q) {
       read_frag(ks + 1, 0, 0, q);
@@ -344,21 +366,77 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
     }
     take_scales();
   }
-  // No copy may still be landing in LDS when the workgroup exits.
+  // No copy may still be landing in LDS when the ring is reused or the workgroup exits.
   wait_vmcnt<0>();
+  // Every wave's copies have landed and nobody reads the ring any more: its LDS is free.
+  barrier_lds();
 
-  // Epilogue: lane (hi, r32) of block (i, j) holds rows 8*(t/4) + 4*hi + t%4, column r32.
+  // Epilogue.  The accumulator of block (i, j) is D^T: lane (hi, r32) holds row
+  // m = i*32 + r32 of the wave tile and, for g = 0..3, the four consecutive columns
+  // j*32 + 8g + 4hi + 0..3.  When D's rows are whole 16-byte units the wave tile goes
+  // through its own LDS region (rows padded to PB+16 bytes) in panels of PB bytes per
+  // row, and is read back row-wise so each lane stores 16 contiguous bytes and a store
+  // instruction writes 64/(PB/16) whole row segments.  Otherwise each group of four
+  // goes out directly.
+  constexpr int ELEM = BF16 ? 2 : 4;
+  constexpr int PB = (WN * ELEM < 256) ? WN * ELEM : 256;   // panel bytes per row
+  constexpr int PW = PB / ELEM;                             // panel columns
+  constexpr int RS = PB + 16;                               // LDS row stride
+  constexpr int LPR = PB / 16, RPI = 64 / LPR;              // lanes per row, rows per read
+  static_assert(WN % PW == 0 && PW % 32 == 0, "panels hold whole 32-column blocks");
+  static_assert(WM * RS * C::NW <= C::LDS, "output panel fits the wave's LDS share");
+  const int mw = m0 + wm * WM, nw = n0 + wn * WN;
+  if ((N % (16 / ELEM)) == 0) {
+    uint8_t* region = smem + wave * (WM * RS);
 #pragma unroll
-  for (int i = 0; i < FI; ++i)
+    for (int p = 0; p < WN / PW; ++p) {
 #pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-      const int n = n0 + wn * WN + j * 32 + r32;
+      for (int i = 0; i < FI; ++i)
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int m = m0 + wm * WM + i * 32 + 8 * (t >> 2) + 4 * hi + (t & 3);
-        if (m < M && n < N) store_out<BF16>(D, (int64_t)m * N + n, acc[i][j][t]);
+        for (int jj = 0; jj < PW / 32; ++jj) {
+          const int j = p * (PW / 32) + jj;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint8_t* dst = region + (i * 32 + r32) * RS + (jj * 32 + 8 * g + 4 * hi) * ELEM;
+            const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+            const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+            if constexpr (BF16) {
+              typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+              *reinterpret_cast<v2u*>(dst) = v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            } else {
+              *reinterpret_cast<v4f*>(dst) = v4f{v0, v1, v2, v3};
+            }
+          }
+        }
+#pragma unroll
+      for (int it = 0; it < WM / RPI; ++it) {
+        const int r = it * RPI + lane / LPR, ch = lane % LPR;
+        const v4i val = *reinterpret_cast<const v4i*>(region + r * RS + ch * 16);
+        const int m = mw + r, n = nw + p * PW + ch * (16 / ELEM);
+        if (m < M && n < N)
+          *reinterpret_cast<v4i*>(static_cast<uint8_t*>(D) + ((int64_t)m * N + n) * ELEM) = val;
       }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const int m = mw + i * 32 + r32;
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = nw + j * 32 + 8 * g + 4 * hi;
+          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+          if (m < M) store_out4<BF16>(D, (int64_t)m * N + n, N - n, v0, v1, v2, v3);
+        }
+      }
+    }
+  }
+  // No wave may start the next tile's copies into LDS while another still reads its
+  // output panel.
+  barrier_lds();
+  }  // tile loop
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES>
@@ -366,11 +444,12 @@ hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
   using C = Cfg<BM, BN, WM, WN, BK, STAGES>;
   const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, BN);
   if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
+  const unsigned grid = (unsigned)(tiles < device_cus() ? tiles : device_cus());
   if (a.bf16_out)
-    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, BK, STAGES, true>), dim3((unsigned)tiles), dim3(C::NT),
+    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, BK, STAGES, true>), dim3(grid), dim3(C::NT),
                        0, s, (int)a.M, (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
   else
-    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, BK, STAGES, false>), dim3((unsigned)tiles), dim3(C::NT),
+    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, BK, STAGES, false>), dim3(grid), dim3(C::NT),
                        0, s, (int)a.M, (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
   return hipGetLastError();
 }

@@ -15,6 +15,18 @@ __global__ void zero_tail_kernel(uint16_t* __restrict__ p) { *p = 0; }
 
 }  // namespace
 
+int64_t device_cus() {
+  static int64_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_zero_fill(void* D, int64_t count, bool bf16_out, hipStream_t s) {
   const int64_t bytes = count * (bf16_out ? 2 : 4);
   const int64_t words = bytes / 4;
