@@ -7,9 +7,10 @@ the headline is the MXFP4 GEMM M = N = K = 8192 (E2M1 operands quantized from
 N(0,1) with max-abs E8M0 block scales, fp32 accumulation, bf16 output).  The
 decode GEMV (M=8, N=14336, K=4096, cache-cold through rotating weight copies),
 the W4A8 GEMM (256x8192x8192), the NVFP4 GEMM (1024^3) and the MXFP4 256^3 case
-are timed after it and reported in "also".  Every duration is the average of
-per-launch HIP event pairs recorded on the stream the kernel runs on (torch's
-current stream, which the binding passes to the library).
+are timed after it and reported in "also".  Every duration is the average over
+`steps` launches captured in one HIP graph and replayed between a HIP event pair
+on the stream the kernels run on (torch's current stream, which the binding
+passes to the library); the GEMV is also timed with eager launches.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -53,25 +54,39 @@ def to_dev(d, dev):
     return out
 
 
-def time_launches(fn, steps, warmup, dev, arg_sets=None):
-    """Average duration (ms) of `steps` launches, each bracketed by its own HIP event
-    pair on the current stream.  `arg_sets` rotates inputs between launches."""
+def time_launches(fn, steps, warmup, dev, arg_sets=None, graph=True):
+    """Average duration (ms) of one launch.  `steps` launches (rotating through
+    `arg_sets`) are captured into one HIP graph, which is replayed once untimed and
+    once between a HIP event pair on the current stream, so the host's per-call cost
+    (Python, ctypes) does not leave the GPU idle between short kernels.  With
+    graph=False the launches are enqueued eagerly between the event pair instead.
+    Returns (ms per launch, host wall seconds of the timed region)."""
     arg_sets = arg_sets or [()]
     for i in range(warmup):
         fn(*arg_sets[i % len(arg_sets)])
     torch.cuda.synchronize(dev)
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        a = arg_sets[i % len(arg_sets)]
-        ev[i][0].record(stream)
-        fn(*a)
-        ev[i][1].record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(*arg_sets[i % len(arg_sets)])
+        g.replay()
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    else:
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            fn(*arg_sets[i % len(arg_sets)])
+        e1.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in ev]
-    return float(np.mean(per)), float(np.median(per)), wall
+    return float(e0.elapsed_time(e1) / steps), wall
 
 
 def src_digest(*names):
@@ -103,11 +118,11 @@ def bench_mx8192(steps, warmup, dev):
     M = N = K = 8192
     D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     fn = lambda: fp4.mx_fp4_gemm(t["A"], t["sfA"], t["B"], t["sfB"], out=D)
-    mean_ms, med_ms, wall = time_launches(fn, steps, warmup, dev)
+    mean_ms, wall = time_launches(fn, steps, warmup, dev)
     flops = 2.0 * M * N * K
     tf = flops / (mean_ms * 1e-3) / 1e12
     bytes_alg = d["A"].nbytes + d["sfA"].nbytes + d["B"].nbytes + d["sfB"].nbytes + M * N * 2
-    return d, {"ms": mean_ms, "median_ms": med_ms, "wall_s": wall, "tflops": tf, "flops": flops,
+    return d, {"ms": mean_ms, "wall_s": wall, "tflops": tf, "flops": flops,
                "bytes": bytes_alg}
 
 
@@ -124,10 +139,16 @@ def bench_gemv(steps, warmup, dev):
         sets.append((B, sB))
     D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     fn = lambda B, sB: fp4.fp4_gemv(base["A"], base["sfA"], B, sB, out=D)
-    mean_ms, med_ms, wall = time_launches(fn, steps, warmup, dev, sets)
+    mean_ms, wall = time_launches(fn, steps, warmup, dev, sets)
+    replayed = D.clone()                           # output of the graph's last launch
+    fn(*sets[(steps - 1) % copies])
+    torch.cuda.synchronize(dev)
+    if not torch.equal(replayed, D):
+        raise RuntimeError("GEMV: graph replay and eager launch disagree")
+    eager_ms, _ = time_launches(fn, steps, 0, dev, sets, graph=False)
     bytes_alg = d["A"].nbytes + d["sfA"].nbytes + wbytes + M * N * 2
     gbs = bytes_alg / (mean_ms * 1e-3) / 1e9
-    return {"ms": mean_ms, "median_ms": med_ms, "gbs": gbs, "bytes": bytes_alg, "copies": copies,
+    return {"ms": mean_ms, "eager_ms": eager_ms, "gbs": gbs, "bytes": bytes_alg, "copies": copies,
             "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12}
 
 
@@ -140,10 +161,10 @@ def bench_w4a8(steps, warmup, dev):
     sets = [((base["B"].clone(), base["sB"].clone()) if c else (base["B"], base["sB"])) for c in range(copies)]
     D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     fn = lambda B, sB: fp4.w4a8_gemm(base["A"], base["sa"], B, sB, out=D)
-    mean_ms, med_ms, wall = time_launches(fn, steps, warmup, dev, sets)
+    mean_ms, wall = time_launches(fn, steps, warmup, dev, sets)
     flops = 2.0 * M * N * K
     bytes_alg = d["A"].nbytes + d["sa"].nbytes + wbytes + M * N * 2
-    return {"ms": mean_ms, "median_ms": med_ms, "tflops": flops / (mean_ms * 1e-3) / 1e12,
+    return {"ms": mean_ms, "tflops": flops / (mean_ms * 1e-3) / 1e12,
             "gbs": bytes_alg / (mean_ms * 1e-3) / 1e9, "bytes": bytes_alg, "copies": copies}
 
 
@@ -153,8 +174,8 @@ def bench_nv1024(steps, warmup, dev):
     M = N = K = 1024
     D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     fn = lambda: fp4.nv_fp4_gemm(t["A"], t["sfA"], 1.0, t["B"], t["sfB"], 1.0, out=D)
-    mean_ms, med_ms, _ = time_launches(fn, steps, warmup, dev)
-    return {"ms": mean_ms, "median_ms": med_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12}
+    mean_ms, _ = time_launches(fn, steps, warmup, dev)
+    return {"ms": mean_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12}
 
 
 def bench_mx256(steps, warmup, dev):
@@ -162,8 +183,8 @@ def bench_mx256(steps, warmup, dev):
     t = to_dev(d, dev)
     D = torch.empty((256, 256), dtype=torch.float32, device=dev)
     fn = lambda: fp4.mx_fp4_gemm(t["A"], t["sfA"], t["B"], t["sfB"], out=D)
-    mean_ms, med_ms, _ = time_launches(fn, steps, warmup, dev)
-    return {"ms": mean_ms, "median_ms": med_ms, "tflops": 2.0 * 256 ** 3 / (mean_ms * 1e-3) / 1e12}
+    mean_ms, _ = time_launches(fn, steps, warmup, dev)
+    return {"ms": mean_ms, "tflops": 2.0 * 256 ** 3 / (mean_ms * 1e-3) / 1e12}
 
 
 def bench_copy(dev, mib=512):
@@ -172,7 +193,7 @@ def bench_copy(dev, mib=512):
     n = mib * (1 << 20)
     src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
-    ms, _, _ = time_launches(lambda: dst.copy_(src), 3, 1, dev)
+    ms, _ = time_launches(lambda: dst.copy_(src), 3, 1, dev)
     return {"bytes_each_way": n, "ms": ms, "gbs": 2 * n / (ms * 1e-3) / 1e9}
 
 
@@ -234,10 +255,12 @@ def main():
     if "gemv" in only:
         log("bench: gemv 8x14336x4096 (cold) ...")
         g = bench_gemv(max(args.steps, 100), args.warmup, dev)
-        log(f"bench: gemv {g['ms'] * 1e3:.2f} us/launch, {g['gbs']:.0f} GB/s")
-        traffic = traffic_from_profile("fp4_gemv_8x14336x4096", ["fp4_gemv.hip"], g["bytes"])
+        log(f"bench: gemv {g['ms'] * 1e3:.2f} us/launch, {g['gbs']:.0f} GB/s "
+            f"(eager launches: {g['eager_ms'] * 1e3:.2f} us)")
+        traffic = traffic_from_profile("fp4_gemv_8x14336x4096", ["fp4_gemv.hip", "common.hpp"], g["bytes"])
         also["mxfp4_gemv_8x14336x4096"] = {
-            "metric": "HBM GB/s", "value": g["gbs"], "ms_per_launch": g["ms"], "median_ms": g["median_ms"],
+            "metric": "HBM GB/s", "value": g["gbs"], "ms_per_launch": g["ms"],
+            "ms_per_launch_eager": g["eager_ms"],
             "cache": f"cold ({g['copies']} rotating weight copies)",
             "roofline": {"bound": "hbm", "achieved": g["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": g["gbs"] / PEAK_HBM_GBS, "traffic": traffic},

@@ -29,6 +29,36 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kFmtFp8 = 0;   // OCP E4M3
 constexpr int kFmtFp4 = 4;   // E2M1
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous global -> LDS copies (global_load_lds_dwordx4 / _dword): lane i writes
+// 16 (or 4) bytes at offset 16*i (4*i) after the wave-uniform LDS address.  The
+// builtin is only spelled in the device pass: in the host pass its presence in a
+// kernel body suppresses the kernel's launch stub.
+__device__ __forceinline__ void lds_copy16(const void* g, lds_void* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+#else
+  (void)g;
+  (void)l;
+#endif
+}
+__device__ __forceinline__ void lds_copy4(const void* g, lds_void* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+#else
+  (void)g;
+  (void)l;
+#endif
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // fp32 -> bf16 bits with gfx950's v_cvt_pk_bf16_f32: round to nearest even, NaN stays
 // NaN (quiet).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

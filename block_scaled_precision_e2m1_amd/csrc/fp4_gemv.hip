@@ -7,28 +7,177 @@
 // the operands are swapped as in the W4A8 kernel of the Hopper CUTLASS/CuTe DSL
 // post (section "The W4A8 kernel: the same four definitions, with the operands
 // swapped"): 16 weight rows fill the 16-row slot of the MFMA and the tokens sit
-// in the other slot, padded with zero codes up to 16.  The product computed is
-// D^T = B * A^T; its accumulator lane l holds D^T rows 4*(l/16)+t, column l%16,
-// which is stored straight into row-major D.
+// in the other slot, zero past M.  The product computed is D^T = B * A^T; its
+// accumulator lane l holds D^T rows 4*(l/16)+t, column l%16.
 //
-// gfx950 mapping: one workgroup of KSPLIT waves per 16 weight rows; wave w owns
-// a contiguous range of 128-element K steps, issues its weight loads (16 bytes
-// per lane, the row's 64 bytes per step spread over 4 lanes) eight steps at a
-// time so many bytes are in flight, runs one v_mfma_scale_f32_16x16x128_f8f6f4
-// per step, and the KSPLIT partial tiles are summed through LDS.
+// gfx950 mapping (K <= 16384, the decode shapes):
+//   * one workgroup of 8 waves per RG groups of 16 weight rows; wave w owns the K
+//     segment of ST = 4*NJ consecutive 128-element steps starting at w*ST, for all
+//     of the workgroup's rows, so its token fragments are loaded once and reused
+//     for every row group;
+//   * the weights reach LDS through global->LDS copies (global_load_lds_dwordx4)
+//     that read whole 128-byte lines: each 1 KB copy covers RPI rows x ST*64 bytes.
+//     A row's 16-byte units are XOR-swizzled by the row index (the copy lane picks
+//     the global unit, the LDS slot stays linear), so the MFMA-layout
+//     ds_read_b128 of 16 rows at one K position hits 16 distinct bank groups;
+//   * every load is issued up front (tokens first, then the weight copies, then
+//     the scale words) and waited for once: a decode GEMV is one pass over a
+//     cold weight stream, and what matters is how many bytes are in flight;
+//   * the 8 partial 16-row tiles of a row group are summed through LDS (reusing
+//     the weight area) in a fixed order, so results are run-to-run identical.
+// Steps past K (the last segment of a ragged K) read clamped in-bounds addresses
+// and are given zero tokens and unit scales; rows past N read row N-1 and are
+// not stored.  Longer K uses the streaming kernel at the end of this file.
 #include "common.hpp"
 #include "internal.h"
 
 namespace fp4g {
 namespace {
 
+constexpr int WAVES = 8;
+
+template <int NJ, int RG, bool BF16>
+__global__ void __launch_bounds__(WAVES * 64)
+fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
+                const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, void* __restrict__ D) {
+  constexpr int ST = 4 * NJ;             // steps (128 K elements, 64 bytes) per wave
+  constexpr int SEG = ST * 64;           // bytes per row per wave
+  constexpr int UPR = SEG / 16;          // 16-byte units per row segment
+  constexpr int RPI = 64 / UPR;          // rows per 1 KB copy
+  constexpr int ROWS = 16 * RG;
+  constexpr int NI = ROWS / RPI;         // copies per wave
+  constexpr int WBYTES = ROWS * SEG;     // LDS bytes per wave
+  static_assert(UPR >= 16 && UPR <= 64 && 64 % UPR == 0, "segment shape");
+  static_assert(WAVES * WBYTES <= 160 * 1024, "LDS budget");
+  static_assert(WAVES * RG * 64 * 4 * 4 <= WAVES * WBYTES, "reduction fits in the weight area");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[WAVES * WBYTES];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, slot = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * ROWS;
+  const int64_t ld = K / 2, lsc = K / 32;
+  const int KT = K / 128;
+  const int ks0 = wave * ST;
+  uint8_t* wl = lds + wave * WBYTES;
+
+  // ---- tokens of this wave's segment (lanes r >= M and steps past K get zeros) ----
+  const bool tok = r < M;
+  const int64_t trow = tok ? r : 0;
+  // Scale words of 4 consecutive steps are one 16-byte load when the segment lies
+  // inside the row and rows of scales are 16-byte multiples (K % 512 == 0).
+  const bool vec_scales = (K & 511) == 0;
+  auto load_words = [&](const uint8_t* rowp, int q, int* dst) {
+    const int ks = ks0 + 4 * q;
+    if (vec_scales && ks + 4 <= KT) {
+      const v4i w4 = *reinterpret_cast<const v4i*>(rowp + ks * 4);
+      dst[0] = w4[0]; dst[1] = w4[1]; dst[2] = w4[2]; dst[3] = w4[3];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dst[u] = *reinterpret_cast<const int*>(rowp + min(ks + u, KT - 1) * 4);
+    }
+  };
+  v4i t[ST];
+  int ts[ST];
+  if (M <= 8) {
+    // Lanes r >= 8 would only hold zeros: let them fetch the next step of token r-8,
+    // then rotate each 16-lane row by 8 (DPP row_ror:8) to move it into lanes 0..7.
+    const int64_t prow = min(r & 7, M - 1);
+#pragma unroll
+    for (int s = 0; s < ST; s += 2) {
+      const int ks = min(ks0 + s + (r >> 3), KT - 1);
+      t[s] = *reinterpret_cast<const v4i*>(A + prow * ld + (int64_t)ks * 64 + slot * 16);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+      const int ks = min(ks0 + s, KT - 1);
+      t[s] = *reinterpret_cast<const v4i*>(A + trow * ld + (int64_t)ks * 64 + slot * 16);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < ST / 4; ++q) load_words(sfA + trow * lsc, q, ts + 4 * q);
+
+  // ---- weight copies: copy i covers rows i*RPI .. i*RPI+RPI-1 of the segment ----
+  {
+    const int u = lane % UPR, rr = lane / UPR;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = i * RPI + rr;
+      const int gu = u ^ (row & 15);                      // global unit held by LDS unit u
+      const int ks = min(ks0 + (gu >> 2), KT - 1);
+      const int64_t grow = min(n0 + row, (int64_t)N - 1);
+      lds_copy16(B + grow * ld + (int64_t)ks * 64 + (gu & 3) * 16, (lds_void*)(wl + i * 1024));
+    }
+  }
+
+  // ---- weight scale words: lane (r, slot) needs byte `slot` of word (row, step) ----
+  int ws[RG][ST];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    const int64_t grow = min(n0 + 16 * g + r, (int64_t)N - 1);
+#pragma unroll
+    for (int q = 0; q < ST / 4; ++q) load_words(sfB + grow * lsc, q, ws[g] + 4 * q);
+  }
+  __builtin_amdgcn_s_waitcnt(0);          // every load of this wave, copies included
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+  if (M <= 8) {
+#pragma unroll
+    for (int s = 0; s < ST; s += 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[s + 1][e] = __builtin_amdgcn_mov_dpp(t[s][e], 0x128, 0xF, 0xF, false);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < ST; ++s) {
+    const bool ok = tok && ks0 + s < KT;
+    ts[s] = ok ? (ts[s] >> (8 * slot)) & 255 : 127;
+    if (!ok) t[s] = v4i{0, 0, 0, 0};
+  }
+
+  v4f acc[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+    const int row = 16 * g + r;
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+      const v4i w = *reinterpret_cast<const v4i*>(wl + row * SEG + (((s * 4 + slot) ^ (row & 15)) * 16));
+      const int wsc = ks0 + s < KT ? (ws[g][s] >> (8 * slot)) & 255 : 127;
+      acc[g] = mfma_fp4_16x16<0>(w, t[s], acc[g], wsc, ts[s]);
+    }
+  }
+
+  // ---- sum the WAVES partial tiles in wave order, store D[m][n] ----
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);   // [WAVES][RG][64 lanes][4]
+#pragma unroll
+  for (int g = 0; g < RG; ++g) *reinterpret_cast<v4f*>(red + ((wave * RG + g) * 64 + lane) * 4) = acc[g];
+  __syncthreads();
+  if (threadIdx.x < RG * 64) {
+    const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int m = l & 15;
+    v4f v = *reinterpret_cast<const v4f*>(red + (g * 64 + l) * 4);
+#pragma unroll
+    for (int w2 = 1; w2 < WAVES; ++w2) v += *reinterpret_cast<const v4f*>(red + ((w2 * RG + g) * 64 + l) * 4);
+    const int64_t n = n0 + 16 * g + 4 * (l >> 4);
+    if (m < M && n < N) {
+      const int avail = (int)min((int64_t)4, (int64_t)N - n);
+      store_out4<BF16>(D, (int64_t)m * N + n, avail, v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// Long-K path (K > 16384): KSPLIT waves per 16 weight rows, each streaming a
+// contiguous range of K steps with eight 16-byte loads in flight per lane; the
+// partial tiles are summed through LDS.
 constexpr int KSPLIT = 4;
 constexpr int UNROLL = 8;
 
 template <bool BF16>
 __global__ void __launch_bounds__(KSPLIT * 64)
-fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
-                const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, void* __restrict__ D) {
+fp4_gemv_long_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
+                     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, void* __restrict__ D) {
   __shared__ float red[KSPLIT][64][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, slot = lane >> 4;
@@ -37,7 +186,6 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
   const int KT = K / 128;
   const int ks0 = (int)((int64_t)wave * KT / KSPLIT), ks1 = (int)((int64_t)(wave + 1) * KT / KSPLIT);
 
-  // Weight row of this lane (clamped for the ragged last group) and token column.
   const int wrow = min(n0 + r, N - 1);
   const uint8_t* wp = B + (int64_t)wrow * ld + slot * 16;
   const uint8_t* wsp = sfB + (int64_t)wrow * lds_ + slot;
@@ -74,7 +222,6 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
   for (int t = 0; t < 4; ++t) red[wave][lane][t] = acc[t];
   __syncthreads();
   if (wave == 0) {
-    // lane: token column m = lane % 16, weight rows n0 + 4*(lane/16) + t.
     const int m = r;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -87,17 +234,36 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
   }
 }
 
+template <int NJ, int RG>
+hipError_t launch_segmented(const FP4Args& a, hipStream_t s) {
+  const int64_t g64 = ceil_div(a.N, 16 * RG);
+  if (g64 > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)g64), block(WAVES * 64);
+  if (a.bf16_out)
+    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K, a.A,
+                       a.sfA, a.B, a.sfB, a.D);
+  else
+    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K, a.A,
+                       a.sfA, a.B, a.sfB, a.D);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s) {
+  const int64_t KT = a.K / 128;
+  // Segment of ST = 4*NJ steps per wave, WAVES segments per row: K <= WAVES*ST*128.
+  if (KT <= WAVES * 4) return launch_segmented<1, 2>(a, s);     // K <= 4096: 32 rows per workgroup
+  if (KT <= WAVES * 8) return launch_segmented<2, 1>(a, s);     // K <= 8192
+  if (KT <= WAVES * 16) return launch_segmented<4, 1>(a, s);    // K <= 16384
   const int64_t g64 = ceil_div(a.N, 16);
   if (g64 > INT32_MAX) return hipErrorInvalidConfiguration;
   const unsigned groups = (unsigned)g64;
   if (a.bf16_out)
-    hipLaunchKernelGGL(fp4_gemv_kernel<true>, dim3(groups), dim3(KSPLIT * 64), 0, s, (int)a.M, (int)a.N,
+    hipLaunchKernelGGL(fp4_gemv_long_kernel<true>, dim3(groups), dim3(KSPLIT * 64), 0, s, (int)a.M, (int)a.N,
                        (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
   else
-    hipLaunchKernelGGL(fp4_gemv_kernel<false>, dim3(groups), dim3(KSPLIT * 64), 0, s, (int)a.M, (int)a.N,
+    hipLaunchKernelGGL(fp4_gemv_long_kernel<false>, dim3(groups), dim3(KSPLIT * 64), 0, s, (int)a.M, (int)a.N,
                        (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
   return hipGetLastError();
 }

@@ -47,36 +47,6 @@
 namespace fp4g {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Asynchronous global -> LDS copies (global_load_lds_dwordx4 / _dword): lane i writes
-// 16 (or 4) bytes at offset 16*i (4*i) after the wave-uniform LDS address.  The
-// builtin is only spelled in the device pass: in the host pass its presence in a
-// kernel body suppresses the kernel's launch stub.
-__device__ __forceinline__ void lds_copy16(const void* g, lds_void* l) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-#else
-  (void)g;
-  (void)l;
-#endif
-}
-__device__ __forceinline__ void lds_copy4(const void* g, lds_void* l) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
-#else
-  (void)g;
-  (void)l;
-#endif
-}
-
-// Wait until at most n vector-memory operations of this wave are outstanding.
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Workgroup barrier that waits only for this wave's LDS operations (lgkmcnt), not
 // for its in-flight global->LDS copies: those are waited for explicitly with
 // wait_vmcnt, which keeps later ring stages in flight across the barrier.  The

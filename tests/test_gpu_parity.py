@@ -188,6 +188,17 @@ def test_gemv_shapes(M, NK):
     check_full("gemv", d, "f32")
 
 
+@pytest.mark.parametrize("MNK", [(8, 300, 5120), (16, 257, 8192), (5, 130, 14336), (3, 70, 16384),
+                                 (8, 40, 16512), (16, 1000, 4096), (1, 33, 12800)])
+def test_gemv_long_k(MNK):
+    # K past one 4096-element pass: segments of 8 and 16 steps per wave, a ragged last
+    # segment, and K beyond 16384 (the streaming kernel).
+    M, N, K = MNK
+    d = datagen.make_shape("gemv", M, N, K, seed=M + N + K)
+    print(f"case gemv {M}x{N}x{K}", flush=True)
+    check_full("gemv", d, "bf16" if N % 2 == 0 else "f32")
+
+
 def test_gemv_matches_gemm():
     d = datagen.make_shape("mx", 16, 700, 512, seed=12, dist="gaussian")
     a = as_np(run("gemv", d, "f32"))
