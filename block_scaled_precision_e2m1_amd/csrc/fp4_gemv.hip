@@ -36,7 +36,7 @@ namespace {
 
 constexpr int WAVES = 8;
 
-template <int NJ, int RG, bool BF16>
+template <int NJ, int RG, bool COOP, bool BF16>
 __global__ void __launch_bounds__(WAVES * 64)
 fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
                 const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, void* __restrict__ D) {
@@ -50,7 +50,10 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
   static_assert(UPR >= 16 && UPR <= 64 && 64 % UPR == 0, "segment shape");
   static_assert(WAVES * WBYTES <= 160 * 1024, "LDS budget");
   static_assert(WAVES * RG * 64 * 4 * 4 <= WAVES * WBYTES, "reduction fits in the weight area");
+  constexpr int SCL = COOP ? ROWS * ST * WAVES * 4 : 16;   // the workgroup's scale rows (K / 32 bytes each)
+  static_assert(WAVES * WBYTES + SCL <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[WAVES * WBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t scl[SCL];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, slot = lane >> 4;
@@ -112,14 +115,39 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
 
   // ---- weight scale words: lane (r, slot) needs byte `slot` of word (row, step) ----
   int ws[RG][ST];
+  if constexpr (COOP) {
+    // The workgroup's rows of scales are one contiguous run of ROWS * K/32 bytes
+    // (16-byte aligned: the launcher checks K % 512 == 0 and the base address).
+    // Waves copy it in whole-line 1 KB pieces, so every line is requested once.
+    const int64_t total = (int64_t)N * lsc;
+    const int64_t first = n0 * lsc;
+    const int pieces = (int)((min((int64_t)ROWS * lsc, total - first) + 1023) / 1024);
+    if (wave < pieces) {
+      const int64_t off = min(first + wave * 1024 + lane * 16, total - 16);
+      lds_copy16(sfB + off, (lds_void*)(scl + wave * 1024));
+    }
+  } else {
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    const int64_t grow = min(n0 + 16 * g + r, (int64_t)N - 1);
+    for (int g = 0; g < RG; ++g) {
+      const int64_t grow = min(n0 + 16 * g + r, (int64_t)N - 1);
 #pragma unroll
-    for (int q = 0; q < ST / 4; ++q) load_words(sfB + grow * lsc, q, ws[g] + 4 * q);
+      for (int q = 0; q < ST / 4; ++q) load_words(sfB + grow * lsc, q, ws[g] + 4 * q);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);          // every load of this wave, copies included
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if constexpr (COOP) {
+    __syncthreads();                      // every wave's piece of the scale rows has landed
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+#pragma unroll
+      for (int q = 0; q < ST / 4; ++q) {
+        const int ks = min(ks0 + 4 * q, KT - 4);   // KT % 4 == 0 here; steps past K are masked below
+        const v4i w4 = *reinterpret_cast<const v4i*>(scl + (16 * g + r) * lsc + ks * 4);
+        ws[g][4 * q] = w4[0]; ws[g][4 * q + 1] = w4[1]; ws[g][4 * q + 2] = w4[2]; ws[g][4 * q + 3] = w4[3];
+      }
+    }
+  }
 
   if (M <= 8) {
 #pragma unroll
@@ -234,18 +262,25 @@ fp4_gemv_long_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const u
   }
 }
 
-template <int NJ, int RG>
+template <int NJ, int RG, bool COOP>
 hipError_t launch_segmented(const FP4Args& a, hipStream_t s) {
   const int64_t g64 = ceil_div(a.N, 16 * RG);
   if (g64 > INT32_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)g64), block(WAVES * 64);
   if (a.bf16_out)
-    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K, a.A,
-                       a.sfA, a.B, a.sfB, a.D);
+    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, COOP, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
+                       a.A, a.sfA, a.B, a.sfB, a.D);
   else
-    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K, a.A,
-                       a.sfA, a.B, a.sfB, a.D);
+    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, COOP, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
+                       a.A, a.sfA, a.B, a.sfB, a.D);
   return hipGetLastError();
+}
+
+template <int NJ, int RG>
+hipError_t launch_segmented(const FP4Args& a, hipStream_t s) {
+  // Cooperative scale copies need 16-byte aligned scale rows and whole segments.
+  const bool coop = a.K % (WAVES * 4 * NJ * 128) == 0 && (reinterpret_cast<uintptr_t>(a.sfB) & 15) == 0;
+  return coop ? launch_segmented<NJ, RG, true>(a, s) : launch_segmented<NJ, RG, false>(a, s);
 }
 
 }  // namespace

@@ -199,6 +199,21 @@ def test_gemv_long_k(MNK):
     check_full("gemv", d, "bf16" if N % 2 == 0 else "f32")
 
 
+def test_gemv_scale_rows_not_16_byte_aligned():
+    # Scale pointers need only 4-byte alignment: a view 4 bytes into a buffer takes the
+    # per-wave scale loads instead of the whole-line cooperative copy.
+    M, N, K = 8, 200, 4096
+    d = datagen.make_shape("gemv", M, N, K, seed=77)
+    t = up(d)
+    buf = torch.zeros(d["sfB"].size + 16, dtype=torch.uint8, device=DEV)
+    sfB = buf[4:4 + d["sfB"].size].view(N, K // 32)
+    sfB.copy_(t["sfB"])
+    assert sfB.data_ptr() % 16 == 4
+    D = as_np(fp4.fp4_gemv(t["A"], t["sfA"], t["B"], sfB, out_dtype=torch.float32))
+    ref, S = oracle.run("mx", d)
+    assert oracle.parity_ratio(D, ref, S, "f32") <= 1.0
+
+
 def test_gemv_matches_gemm():
     d = datagen.make_shape("mx", 16, 700, 512, seed=12, dist="gaussian")
     a = as_np(run("gemv", d, "f32"))
