@@ -54,7 +54,10 @@ def to_dev(d, dev):
     return out
 
 
-def time_launches(fn, steps, warmup, dev, arg_sets=None, graph=True):
+USE_GRAPH = True
+
+
+def time_launches(fn, steps, warmup, dev, arg_sets=None, graph=None):
     """Average duration (ms) of one launch.  `steps` launches (rotating through
     `arg_sets`) are captured into one HIP graph, which is replayed once untimed and
     once between a HIP event pair on the current stream, so the host's per-call cost
@@ -62,6 +65,7 @@ def time_launches(fn, steps, warmup, dev, arg_sets=None, graph=True):
     graph=False the launches are enqueued eagerly between the event pair instead.
     Returns (ms per launch, host wall seconds of the timed region)."""
     arg_sets = arg_sets or [()]
+    graph = USE_GRAPH if graph is None else graph
     for i in range(warmup):
         fn(*arg_sets[i % len(arg_sets)])
     torch.cuda.synchronize(dev)
@@ -97,10 +101,16 @@ def src_digest(*names):
     return h.hexdigest()[:16]
 
 
+# Counter summaries: (profile name, kernel-name prefix in the trace, sources of the kernel).
+COUNTED = [("mxfp4_gemm_8192", "fp4g::(anonymous namespace)::mxfp4_gemm_kernel", ["mxfp4_gemm.hip", "common.hpp"]),
+           ("fp4_gemv_8x14336x4096", "fp4g::(anonymous namespace)::fp4_gemv_kernel", ["fp4_gemv.hip", "common.hpp"])]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
 def traffic_from_profile(name, kernel_src, launches_bytes):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
     current kernel source; otherwise None."""
-    path = os.path.join(PROFILES, f"{name}_counters.json")
+    path = os.path.join(PROFILES, f"{name}_counters.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -108,6 +118,60 @@ def traffic_from_profile(name, kernel_src, launches_bytes):
     if c.get("kernel_src_sha") != src_digest(*kernel_src):
         return None
     return float(c["fetch_bytes_scaled"] + c["write_bytes_scaled"])
+
+
+def summarize_counters(fetch_dir, write_dir, command):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
+    `bench.py --only mx8192 gemv copy --no-graph` into profiles/<name>_counters.txt.
+    The counters are scaled by what they read for the 512 MiB device copy (which
+    reads and writes exactly 512 MiB): bytes = counter * (copy bytes / copy counter)."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        per = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return per
+
+    os.makedirs(PROFILES, exist_ok=True)
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+
+    def pick(per, prefix):
+        vals = [v for k, vs in per.items() if prefix in k for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatches of {prefix} in the counter runs")
+        return float(np.median(vals)), len(vals)
+
+    def pick_copy(per):
+        # The 512 MiB copy is the largest blit in the run (input uploads and the GEMV's
+        # weight clones are blits too): take the dispatches within 1% of the largest.
+        vals = [v for k, vs in per.items() if COPY_KERNEL in k for v in vs]
+        if not vals:
+            raise SystemExit("no copy dispatches in the counter runs")
+        top = max(vals)
+        return float(np.median([v for v in vals if v >= 0.99 * top]))
+
+    copy_bytes = 512 * (1 << 20)
+    cf, cw = pick_copy(fetch), pick_copy(write)
+    f_scale, w_scale = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    for name, prefix, src in COUNTED:
+        fk, nf = pick(fetch, prefix)
+        wk, nw = pick(write, prefix)
+        out = {"kernel": prefix, "kernel_src_sha": src_digest(*src), "dispatches": [nf, nw],
+               "fetch_kib_median": fk, "write_kib_median": wk,
+               "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes_each_way": copy_bytes,
+               "fetch_scale": f_scale, "write_scale": w_scale,
+               "fetch_bytes_scaled": fk * 1024 * f_scale, "write_bytes_scaled": wk * 1024 * w_scale,
+               "command": command}
+        with open(os.path.join(PROFILES, f"{name}_counters.txt"), "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
+        log(f"{name}: fetch {out['fetch_bytes_scaled'] / 1e6:.1f} MB, write {out['write_bytes_scaled'] / 1e6:.1f} MB "
+            f"per launch (scales {f_scale:.3f} / {w_scale:.3f})")
 
 
 # ---- workloads ------------------------------------------------------------------------
@@ -193,7 +257,7 @@ def bench_copy(dev, mib=512):
     n = mib * (1 << 20)
     src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
-    ms, _ = time_launches(lambda: dst.copy_(src), 3, 1, dev)
+    ms, _ = time_launches(lambda: dst.copy_(src), 3, 1, dev, graph=False)   # eager: a blit kernel
     return {"bytes_each_way": n, "ms": ms, "gbs": 2 * n / (ms * 1e-3) / 1e9}
 
 
@@ -234,7 +298,17 @@ def main():
     ap.add_argument("--only", nargs="*", default=None,
                     help="subset of: mx8192 gemv w4a8 nv1024 mx256 copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="enqueue launches eagerly instead of replaying a HIP graph (for counter runs)")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/*_counters.txt from two rocprofv3 --pmc runs, then exit")
+    ap.add_argument("--counters-command", default="", help="the profiling command, recorded with --counters")
     args = ap.parse_args()
+    if args.counters:
+        summarize_counters(args.counters[0], args.counters[1], args.counters_command)
+        return
+    global USE_GRAPH
+    USE_GRAPH = not args.no_graph
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)

@@ -37,6 +37,11 @@
  * caller's next synchronisation.  The library allocates no memory, keeps no
  * per-call state, and may be called from several threads at once.
  * Validation failures return a status code and launch nothing.
+ *
+ * Sizes (all entry points): M, N, K >= 0 and below 2^31; K a multiple of 128
+ * (FP4G_EUNSUPPORTED otherwise).  M == 0 or N == 0 is an empty output: nothing
+ * is read, written or launched, and the call returns FP4G_OK.  K == 0 is an
+ * empty sum: D is set to zero and the inputs are not read (they may be NULL).
  */
 #ifndef FP4GEMM_H
 #define FP4GEMM_H
@@ -49,7 +54,7 @@ extern "C" {
 
 typedef enum {
     FP4G_OK = 0,
-    FP4G_EINVAL = 1,       /* null pointer, size <= 0, bad enum, D overlaps an input */
+    FP4G_EINVAL = 1,       /* null pointer, negative or too large size, bad enum, D overlaps an input */
     FP4G_EUNSUPPORTED = 2, /* K not a multiple of 128, or GEMV with M > 16 */
     FP4G_EALIGN = 3,       /* operand / output not 16-byte aligned, scales not 4-byte aligned */
     FP4G_EHIP = 4          /* the HIP runtime rejected the launch */
@@ -61,16 +66,14 @@ typedef enum {
 } fp4g_out;
 
 /* MXFP4 GEMM: V = 32, E8M0 scales.
- *   A [M][K/2], sfA [M][K/32], B [N][K/2], sfB [N][K/32], D [M][N] of d_type.
- *   Requires M, N >= 1 and K a positive multiple of 128. */
+ *   A [M][K/2], sfA [M][K/32], B [N][K/2], sfB [N][K/32], D [M][N] of d_type. */
 fp4g_status mx_fp4_gemm(int64_t M, int64_t N, int64_t K,
                         const void *A, const void *sfA,
                         const void *B, const void *sfB,
                         void *D, int d_type, void *stream);
 
 /* NVFP4 GEMM: V = 16, E4M3 scales, then D *= global_a * global_b.
- *   A [M][K/2], sfA [M][K/16], B [N][K/2], sfB [N][K/16], D [M][N].
- *   Requires K a positive multiple of 128. */
+ *   A [M][K/2], sfA [M][K/16], B [N][K/2], sfB [N][K/16], D [M][N]. */
 fp4g_status nv_fp4_gemm(int64_t M, int64_t N, int64_t K,
                         const void *A, const void *sfA, float global_a,
                         const void *B, const void *sfB, float global_b,
@@ -80,7 +83,7 @@ fp4g_status nv_fp4_gemm(int64_t M, int64_t N, int64_t K,
  *   D[m][n] = sa[m] * sum_g bf16(sB[n][g]) * sum_{k in group g} e4m3(A[m][k]) * int4(B[n][k])
  *   with groups of 128 consecutive K elements.
  *   A [M][K] bytes, sa [M] fp32, B [N][K/2] bytes, sB [N][K/128] bf16 (raw
- *   16-bit patterns), D [M][N].  Requires K a positive multiple of 128. */
+ *   16-bit patterns), D [M][N]. */
 fp4g_status w4a8_gemm(int64_t M, int64_t N, int64_t K,
                       const void *A, const float *sa,
                       const void *B, const void *sB,
@@ -88,7 +91,7 @@ fp4g_status w4a8_gemm(int64_t M, int64_t N, int64_t K,
 
 /* MXFP4 GEMV for decode (few tokens): the MXFP4 GEMM with 1 <= M <= 16 and the
  * same layouts, tuned for streaming the weight operand B once from HBM.
- * Requires K a positive multiple of 128; M > 16 returns FP4G_EUNSUPPORTED. */
+ * M > 16 returns FP4G_EUNSUPPORTED. */
 fp4g_status fp4_gemv(int64_t M, int64_t N, int64_t K,
                      const void *A, const void *sfA,
                      const void *B, const void *sfB,
