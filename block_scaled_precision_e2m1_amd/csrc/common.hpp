@@ -43,6 +43,15 @@ __device__ __forceinline__ void lds_copy16(const void* g, lds_void* l) {
   (void)l;
 #endif
 }
+// The same copy with the nontemporal cache policy, for data read exactly once.
+__device__ __forceinline__ void lds_copy16_nt(const void* g, lds_void* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 2);
+#else
+  (void)g;
+  (void)l;
+#endif
+}
 __device__ __forceinline__ void lds_copy4(const void* g, lds_void* l) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
@@ -57,6 +66,17 @@ template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations (lgkmcnt), not
+// for its in-flight global->LDS copies: those are waited for explicitly with
+// wait_vmcnt, which keeps later ring stages in flight across the barrier.  The
+// signal fences stop the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // fp32 -> bf16 bits with gfx950's v_cvt_pk_bf16_f32: round to nearest even, NaN stays

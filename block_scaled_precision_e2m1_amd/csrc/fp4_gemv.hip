@@ -109,7 +109,7 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
       const int gu = u ^ (row & 15);                      // global unit held by LDS unit u
       const int ks = min(ks0 + (gu >> 2), KT - 1);
       const int64_t grow = min(n0 + row, (int64_t)N - 1);
-      lds_copy16(B + grow * ld + (int64_t)ks * 64 + (gu & 3) * 16, (lds_void*)(wl + i * 1024));
+      lds_copy16_nt(B + grow * ld + (int64_t)ks * 64 + (gu & 3) * 16, (lds_void*)(wl + i * 1024));
     }
   }
 

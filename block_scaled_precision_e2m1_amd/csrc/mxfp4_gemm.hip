@@ -47,17 +47,6 @@
 namespace fp4g {
 namespace {
 
-// Workgroup barrier that waits only for this wave's LDS operations (lgkmcnt), not
-// for its in-flight global->LDS copies: those are waited for explicitly with
-// wait_vmcnt, which keeps later ring stages in flight across the barrier.  The
-// signal fences stop the compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_lds() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // Chunk swizzles: rows of 4 chunks (64 B) and of 8 chunks (128 B).  Consecutive
 // rows read at one logical chunk land in distinct 16-byte bank groups within any
 // 8 (mod 128 B) or 16 (mod 256 B) lane group.

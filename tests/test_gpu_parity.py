@@ -254,7 +254,8 @@ def test_nvfp4_full_scale_range_including_subnormals():
 
 # ---- W4A8 --------------------------------------------------------------------------------
 
-W4_SHAPES = [(1, 1, 128), (5, 70, 256), (64, 64, 128), (130, 65, 384), (256, 300, 1024), (300, 1000, 512)]
+W4_SHAPES = [(1, 1, 128), (5, 70, 256), (64, 64, 128), (130, 65, 384), (256, 300, 1024), (300, 1000, 512),
+             (64, 128, 256), (70, 130, 768), (100, 300, 2048), (256, 512, 4096)]
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
