@@ -77,6 +77,8 @@ def bind(lib):
     lib.oracle_w4a8_gemm_rows.argtypes = [i64, i64, i64, p, p, p, p, i64, i64, p, p]
     lib.oracle_sampled.restype = ctypes.c_int
     lib.oracle_sampled.argtypes = [ctypes.c_int, i64, i64, i64, p, p, d, p, p, d, p, p, i64, p, p]
+    lib.oracle_mx_quantize.argtypes = [i64, i64, p, p, p]
+    lib.oracle_mx_quantize.restype = ctypes.c_int
     return lib
 
 
@@ -215,6 +217,23 @@ def run(kind, inputs, rows=None):
     if kind == "w4a8":
         return w4a8_gemm(inputs["A"], inputs["sa"], inputs["B"], inputs["sB"], rows)
     raise ValueError(kind)
+
+
+# ---- MX quantizer ------------------------------------------------------------------------
+
+def mx_quantize(x):
+    """fp32 [rows][K] (K % 32 == 0) -> (codes [rows][K/2] u8, E8M0 scales [rows][K/32] u8) by
+    the max-abs rule written out in oracle.c.  bf16 inputs are passed widened to fp32
+    (exact)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 2 or x.shape[1] % 32:
+        raise ValueError("x must be [rows][K] with K a multiple of 32")
+    rows, K = x.shape
+    codes = np.empty((rows, K // 2), np.uint8)
+    scales = np.empty((rows, K // 32), np.uint8)
+    if rows and K and _load().oracle_mx_quantize(rows, K, _ptr(x), _ptr(codes), _ptr(scales)):
+        raise ValueError("oracle_mx_quantize: bad arguments")
+    return codes, scales
 
 
 # ---- the comparison rule ---------------------------------------------------------------

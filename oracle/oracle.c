@@ -271,3 +271,78 @@ int oracle_sampled(int kind, int64_t M, int64_t N, int64_t K,
     }
     return bad ? -1 : 0;
 }
+
+/* ---- MX quantizer: fp32 -> E2M1 codes + E8M0 block scales ---------------
+ *
+ * The step before the GEMM for activations: the issue page's "Impact" section
+ * places FP4 GEMMs in inference, and the cute-rs page's "Where to Go Next"
+ * table lists the MXFP4 GEMV, whose activations must arrive as E2M1 codes
+ * with E8M0 scales.  The pages fix no rounding rule; the reading taken is the
+ * max-abs rule, per block of 32 consecutive K elements with amax = max |x|:
+ *   e = clamp(floor(log2 amax) - 2 + 127, 0, 254)     (e = 127 for amax = 0)
+ * so the block's largest magnitude lands in [4, 8) once scaled by 2^(127-e);
+ * each element becomes x * 2^(127-e) rounded to the NEAREST E2M1 value, a
+ * tie going to the code whose mantissa bit is 0, so magnitudes past 6
+ * saturate to 6.  A result of magnitude 0 is encoded +0 (code 0).  A block
+ * holding an infinity or a NaN gets the NaN scale 0xFF and all-zero codes.
+ * The nearest value is found by trying all eight magnitudes through
+ * oracle_e2m1, the decoder written from the format's bit fields.
+ *
+ * x [rows][K] fp32, codes [rows][K/2] (low nibble = even k), scales
+ * [rows][K/32].  Returns 0, or -1 on bad arguments (K not a multiple of 32). */
+static unsigned e2m1_nearest_magnitude(double y) {
+    unsigned best = 0;
+    double best_d = INFINITY;
+    for (unsigned c = 0; c < 8; ++c) {
+        const double d = fabs(y - oracle_e2m1(c));
+        if (d < best_d || (d == best_d && (c & 1u) == 0 && (best & 1u) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return best;
+}
+
+int oracle_mx_quantize(int64_t rows, int64_t K, const float *x, uint8_t *codes, uint8_t *scales) {
+    if (rows < 0 || K < 0 || K % 32) return -1;
+    if (rows && K && (!x || !codes || !scales)) return -1;
+    const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *blk = x + r * K + 32 * b;
+            uint8_t *out = codes + r * (K / 2) + 16 * b;
+            int finite = 1;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                if (!isfinite(blk[i])) finite = 0;
+                else if (fabs((double)blk[i]) > amax) amax = fabs((double)blk[i]);
+            }
+            if (!finite) {
+                scales[r * nb + b] = 0xFF;
+                memset(out, 0, 16);
+                continue;
+            }
+            int e = 127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);          /* amax = f * 2^ex, f in [0.5, 1): floor(log2) = ex - 1 */
+                e = ex - 1 - 2 + 127;
+                if (e < 0) e = 0;
+                if (e > 254) e = 254;
+            }
+            scales[r * nb + b] = (uint8_t)e;
+            for (int i = 0; i < 32; i += 2) {
+                unsigned nib[2];
+                for (int h = 0; h < 2; ++h) {
+                    const double y = ldexp((double)blk[i + h], 127 - e);
+                    unsigned c = e2m1_nearest_magnitude(fabs(y));
+                    if (c != 0 && y < 0.0) c |= 8u;
+                    nib[h] = c;
+                }
+                out[i / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
+            }
+        }
+    }
+    return 0;
+}

@@ -17,6 +17,7 @@ import pytest
 import oracle
 from tests import test_oracle_codecs as codecs
 from tests import test_oracle_pins as pins
+from tests import test_oracle_quant as quant
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -51,13 +52,18 @@ MUTANTS = {
         "fp4_dot(K, V, dec, A + m * a_ld, sfA + m * s_ld, B + n * a_ld, sfB + n * s_ld, &d, &s);",
         "fp4_dot(K, V, dec, A + m * a_ld, sfA + m * s_ld, B + n * a_ld, sfB + m * s_ld, &d, &s);"),
     "abs-sum-signed": ("mag += fabs(p);\n    }\n    *d = acc;", "mag += p;\n    }\n    *d = acc;"),
+    "quant-exponent-offset": ("e = ex - 1 - 2 + 127;", "e = ex - 2 + 127;"),
+    "quant-ties-to-odd": ("(c & 1u) == 0 && (best & 1u) == 1", "(c & 1u) == 1 && (best & 1u) == 0"),
+    "quant-negative-zero": ("if (c != 0 && y < 0.0) c |= 8u;", "if (y < 0.0) c |= 8u;"),
+    "quant-nibble-order": ("out[i / 2] = (uint8_t)(nib[0] | (nib[1] << 4));", "out[i / 2] = (uint8_t)(nib[1] | (nib[0] << 4));"),
+    "quant-no-nonfinite-check": ("if (!isfinite(blk[i])) finite = 0;", "if (0) finite = 0;"),
 }
 
 
 def _quick_pins():
     """(callable, kwargs) for every quick pin, over all of its parametrisations."""
     out = []
-    for mod in (codecs, pins):
+    for mod in (codecs, pins, quant):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue
