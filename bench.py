@@ -251,6 +251,21 @@ def bench_mx256(steps, warmup, dev):
     return {"ms": mean_ms, "tflops": 2.0 * 256 ** 3 / (mean_ms * 1e-3) / 1e12}
 
 
+def bench_quant(steps, warmup, dev):
+    """MX quantizer on an 8192 x 8192 fp32 activation (the GEMM's operand size): two
+    input copies alternate (512 MB, past the 256 MB last-level cache)."""
+    rows, K = 8192, 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    xs = [torch.randn((rows, K), generator=g, device=dev, dtype=torch.float32) for _ in range(2)]
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=dev)
+    fn = lambda X: fp4.mx_fp4_quantize(X, codes, scales)
+    mean_ms, _ = time_launches(fn, steps, warmup, dev, [(x,) for x in xs])
+    bytes_alg = rows * K * 4 + codes.numel() + scales.numel()
+    return {"ms": mean_ms, "bytes": bytes_alg, "gbs": bytes_alg / (mean_ms * 1e-3) / 1e9}
+
+
 def bench_copy(dev, mib=512):
     """A plain device copy of known size, the reference that scales the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) into bytes."""
@@ -296,7 +311,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: mx8192 gemv w4a8 nv1024 mx256 copy")
+                    help="subset of: mx8192 gemv w4a8 nv1024 mx256 quant copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue launches eagerly instead of replaying a HIP graph (for counter runs)")
@@ -318,7 +333,7 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     fp4.load_library()
-    only = set(args.only) if args.only else {"mx8192", "gemv", "w4a8", "nv1024", "mx256"}
+    only = set(args.only) if args.only else {"mx8192", "gemv", "w4a8", "nv1024", "mx256", "quant"}
     also = {}
     head = None
     d8192 = None
@@ -356,6 +371,15 @@ def main():
                               "roofline": {"bound": "mfma", "achieved": n["tflops"], "peak": PEAK_TFLOPS["bf16"],
                                            "unit": "TFLOP/s", "frac": n["tflops"] / PEAK_TFLOPS["bf16"],
                                            "traffic": None}}
+    if "quant" in only:
+        log("bench: mx quantize 8192x8192 fp32 ...")
+        q = bench_quant(args.steps, args.warmup, dev)
+        log(f"bench: mx quantize {q['ms'] * 1e3:.1f} us/launch, {q['gbs']:.0f} GB/s")
+        also["mx_quantize_8192x8192_f32"] = {
+            "metric": "HBM GB/s", "value": q["gbs"], "ms_per_launch": q["ms"],
+            "roofline": {"bound": "hbm", "achieved": q["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": q["gbs"] / PEAK_HBM_GBS, "traffic": None},
+            "algorithmic_bytes": q["bytes"]}
     if "copy" in only:
         c = bench_copy(dev)
         log(f"bench: copy 512 MiB {c['ms'] * 1e3:.1f} us, {c['gbs']:.0f} GB/s (read+write)")

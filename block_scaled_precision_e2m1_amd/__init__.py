@@ -23,14 +23,15 @@ import os
 
 import torch
 
-__all__ = ["mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "fp4g_status_string",
+__all__ = ["mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp4g_status_string",
            "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfp4gemm.so")
-SYMBOLS = ("mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "fp4g_status_string")
+SYMBOLS = ("mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp4g_status_string")
 
 OUT_F32, OUT_BF16 = 0, 1
+IN_F32, IN_BF16 = 0, 1
 _lib = None
 
 
@@ -64,6 +65,8 @@ def load_library():
     lib.nv_fp4_gemm.restype = c_int
     lib.w4a8_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.w4a8_gemm.restype = c_int
+    lib.mx_fp4_quantize.argtypes = [i64, i64, p, c_int, p, p, p]
+    lib.mx_fp4_quantize.restype = c_int
     lib.fp4g_status_string.argtypes = [c_int]
     lib.fp4g_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -182,3 +185,29 @@ def w4a8_gemm(A, sa, B, sB, out=None, out_dtype=torch.bfloat16):
     st = lib.w4a8_gemm(M, N, K, _ptr(A), _ptr(sa), _ptr(B), _ptr(sB), _ptr(D), dt, _stream(device))
     _raise_on("w4a8_gemm", st)
     return D
+
+
+def mx_fp4_quantize(X, codes=None, scales=None):
+    """MX quantizer: X [rows, K] float32 or bfloat16 (K % 32 == 0) -> (codes [rows, K/2]
+    uint8 packed E2M1, scales [rows, K/32] uint8 E8M0), the operand layout of
+    mx_fp4_gemm / fp4_gemv, by the max-abs rule of include/fp4gemm.h."""
+    lib = load_library()
+    device = _device_of(X)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    if X.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"X must be float32 or bfloat16, got {X.dtype}")
+    rows, K = X.shape
+    if K % 32:
+        raise ValueError(f"K={K} must be a multiple of 32")
+    _check(X, "X", X.dtype, (rows, K), device)
+    if codes is None:
+        codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=device)
+    if scales is None:
+        scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=device)
+    _check(codes, "codes", torch.uint8, (rows, K // 2), device)
+    _check(scales, "scales", torch.uint8, (rows, K // 32), device)
+    xt = IN_BF16 if X.dtype == torch.bfloat16 else IN_F32
+    st = lib.mx_fp4_quantize(rows, K, _ptr(X), xt, _ptr(codes), _ptr(scales), _stream(device))
+    _raise_on("mx_fp4_quantize", st)
+    return codes, scales

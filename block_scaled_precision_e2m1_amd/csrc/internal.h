@@ -38,5 +38,8 @@ hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s);
 hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t s);
 // D[M][N] = 0 (the empty-K product); never uses hipMemset so it can be captured.
 hipError_t launch_zero_fill(void* D, int64_t count, bool bf16_out, hipStream_t s);
+// E2M1 codes + E8M0 scales of X[rows][K] (K % 32 == 0), max-abs rule.
+hipError_t launch_mx_quantize(int64_t rows, int64_t K, const void* X, bool bf16_in, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
 
 }  // namespace fp4g

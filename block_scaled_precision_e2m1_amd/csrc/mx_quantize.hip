@@ -1,0 +1,118 @@
+// MX quantizer for gfx950: fp32 or bf16 X[rows][K] -> E2M1 codes [rows][K/2] and
+// E8M0 block scales [rows][K/32], the step that turns activations into the MXFP4
+// operand of the GEMM and the decode GEMV (the issue page's "Impact" section puts
+// FP4 GEMMs in inference; the cute-rs page's "Where to Go Next" table lists the
+// MXFP4 GEMV).  The rounding rule is the max-abs rule, per 32-element block:
+//   e = clamp(floor(log2 amax) - 2 + 127, 0, 254)   (127 for an all-zero block),
+//   code = nearest E2M1 value of x * 2^(127-e), ties to the even mantissa bit,
+//          saturating at 6; a zero result is +0;
+// a block holding an infinity or NaN gets scale 0xFF and zero codes.
+//
+// HBM-bound: X is read once, the codes and scales written once.  8 lanes share a
+// block (4 elements each), so one wave-wide load is 1 KB (fp32) or 512 B (bf16) of
+// consecutive blocks and one 2-byte store per lane writes 128 contiguous code
+// bytes.  The block maximum and the non-finite flag are reduced over the 8 lanes
+// with DPP row shifts inside each 16-lane row.  floor(log2 amax) comes from the
+// fp32 exponent field; x * 2^(127-e) is an exact v_ldexp_f32, and the rounding is
+// the count of grid midpoints passed (">" below a midpoint whose upper neighbour
+// has an odd code, ">=" where it is even).
+#include "common.hpp"
+#include "internal.h"
+
+namespace fp4g {
+namespace {
+
+constexpr int kUnroll = 4;   // blocks-of-8 per wave per iteration, for loads in flight
+
+// Maximum over the 8-lane group (lanes 8g .. 8g+7) of non-negative integers, via DPP
+// row_shr within 16-lane rows: groups never straddle a row.
+__device__ __forceinline__ uint32_t group8_max(uint32_t v) {
+  // xor-style butterfly with quad_perm and row_ror inside each 8-lane half-row
+  uint32_t t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  v = v > t ? v : t;
+  // swap the two quads of each 8-lane group: lane i <- lane i ^ 4
+  t = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);               // xor mask 4 within 32
+  v = v > t ? v : t;
+  return v;
+}
+
+template <bool BF16_IN>
+__global__ void __launch_bounds__(256)
+mx_quantize_kernel(int64_t nblocks, const void* __restrict__ X, uint8_t* __restrict__ codes,
+                   uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 7;                 // position of this lane's 4 elements in the block
+  const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  // block handled by this lane in unit u of an iteration: 8 blocks per wave-unit
+  for (int64_t base = wave_id * 8 * kUnroll; base < nblocks; base += nwaves * 8 * kUnroll) {
+    uint32_t bits[kUnroll][4];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t blk = min(base + u * 8 + (lane >> 3), nblocks - 1);   // clamped: in bounds
+      if constexpr (BF16_IN) {
+        typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+        const v2u w = *reinterpret_cast<const v2u*>(static_cast<const uint16_t*>(X) + blk * 32 + sub * 4);
+        bits[u][0] = w[0] << 16;
+        bits[u][1] = w[0] & 0xFFFF0000u;
+        bits[u][2] = w[1] << 16;
+        bits[u][3] = w[1] & 0xFFFF0000u;
+      } else {
+        const v4i w = *reinterpret_cast<const v4i*>(static_cast<const float*>(X) + blk * 32 + sub * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bits[u][i] = (uint32_t)w[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t blk = base + u * 8 + (lane >> 3);
+      // |x| as ordered integers; any exponent field of all ones marks the block non-finite
+      uint32_t amax = 0, bad = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a = bits[u][i] & 0x7FFFFFFFu;
+        bad |= (a >= 0x7F800000u) ? 1u : 0u;
+        amax = a > amax ? a : amax;
+      }
+      amax = group8_max(amax);
+      bad = group8_max(bad);
+      const int E = (int)(amax >> 23);                  // biased exponent of the block maximum
+      const int e = amax == 0 ? 127 : (E - 2 > 0 ? E - 2 : 0);
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = __builtin_bit_cast(float, bits[u][i]);
+        const float y = __builtin_fabsf(__builtin_amdgcn_ldexpf(x, 127 - e));
+        uint32_t c = (y > 0.25f) + (y >= 0.75f) + (y > 1.25f) + (y >= 1.75f) + (y > 2.5f) + (y >= 3.5f) +
+                     (y > 5.0f);
+        if (c != 0 && (bits[u][i] >> 31)) c |= 8u;
+        packed |= c << (4 * i);
+      }
+      if (bad) packed = 0;
+      if (blk < nblocks) {
+        *reinterpret_cast<uint16_t*>(codes + blk * 16 + sub * 2) = (uint16_t)packed;
+        if (sub == 0) scales[blk] = bad ? (uint8_t)0xFF : (uint8_t)e;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mx_quantize(int64_t rows, int64_t K, const void* X, bool bf16_in, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s) {
+  const int64_t nblocks = rows * (K / 32);
+  const int64_t units = ceil_div(nblocks, 8 * kUnroll);          // wave-iterations of work
+  const int64_t wgs = ceil_div(units, 4);                          // 4 waves per workgroup
+  const unsigned grid = (unsigned)(wgs < device_cus() * 8 ? wgs : device_cus() * 8);
+  if (bf16_in)
+    hipLaunchKernelGGL(mx_quantize_kernel<true>, dim3(grid), dim3(256), 0, s, nblocks, X, codes, scales);
+  else
+    hipLaunchKernelGGL(mx_quantize_kernel<false>, dim3(grid), dim3(256), 0, s, nblocks, X, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace fp4g

@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
     FP4G_OK = 0,
     FP4G_EINVAL = 1,       /* null pointer, negative or too large size, bad enum, D overlaps an input */
-    FP4G_EUNSUPPORTED = 2, /* K not a multiple of 128, or GEMV with M > 16 */
+    FP4G_EUNSUPPORTED = 2, /* K not a multiple of 128 (of 32 for the quantizer), or GEMV with M > 16 */
     FP4G_EALIGN = 3,       /* operand / output not 16-byte aligned, scales not 4-byte aligned */
     FP4G_EHIP = 4          /* the HIP runtime rejected the launch */
 } fp4g_status;
@@ -64,6 +64,11 @@ typedef enum {
     FP4G_OUT_F32 = 0,
     FP4G_OUT_BF16 = 1
 } fp4g_out;
+
+typedef enum {
+    FP4G_IN_F32 = 0,
+    FP4G_IN_BF16 = 1
+} fp4g_in;
 
 /* MXFP4 GEMM: V = 32, E8M0 scales.
  *   A [M][K/2], sfA [M][K/32], B [N][K/2], sfB [N][K/32], D [M][N] of d_type. */
@@ -96,6 +101,21 @@ fp4g_status fp4_gemv(int64_t M, int64_t N, int64_t K,
                      const void *A, const void *sfA,
                      const void *B, const void *sfB,
                      void *D, int d_type, void *stream);
+
+/* MX quantizer: X[rows][K] (fp32 or bf16 by x_type) -> E2M1 codes [rows][K/2] (low
+ * nibble = even k, the operand layout above) and E8M0 scales [rows][K/32].  It makes
+ * the activation operand of mx_fp4_gemm and fp4_gemv from activations, the
+ * inference setting of the issue page ("Impact") and of the cute-rs page's MXFP4
+ * GEMV ("Where to Go Next").  The pages fix no rounding rule; the rule is max-abs
+ * per 32-element block:
+ *   e = clamp(floor(log2 max|x|) - 2 + 127, 0, 254)   (127 for an all-zero block),
+ *   code = the E2M1 value nearest to x * 2^(127 - e), ties to the even mantissa bit,
+ *          magnitudes past 6 saturating to 6; a zero result is +0;
+ *   a block holding an infinity or NaN gets scale 0xFF (NaN) and zero codes.
+ * Requires K a multiple of 32 (FP4G_EUNSUPPORTED otherwise); X and codes 16-byte
+ * aligned; the three buffers must not overlap.  rows == 0 or K == 0 is a no-op. */
+fp4g_status mx_fp4_quantize(int64_t rows, int64_t K, const void *X, int x_type,
+                            void *codes, void *scales, void *stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *fp4g_status_string(int status);

@@ -28,9 +28,9 @@ def lib():
     return fp4.load_library()
 
 
-def test_header_declares_the_four_operations():
+def test_header_declares_the_operations():
     assert declared_functions() == sorted(["mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv",
-                                            "fp4g_status_string"])
+                                            "mx_fp4_quantize", "fp4g_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -115,6 +115,20 @@ def test_nv_and_w4a8_validation(lib):
     assert lib.w4a8_gemm(4, 4, 128, A_, None, B_, SB_, D_, 0, None) == EINVAL
     assert lib.w4a8_gemm(4, 4, 128, A_, SA_ + 2, B_, SB_, D_, 0, None) == EALIGN
     assert lib.w4a8_gemm(4, 4, 128, A_, SA_, B_, SB_, A_ + 64, 0, None) == EINVAL
+
+
+def test_quantizer_validation(lib):
+    q = lib.mx_fp4_quantize
+    assert q(0, 64, None, 0, None, None, None) == OK                 # empty: nothing read
+    assert q(4, 0, None, 1, None, None, None) == OK
+    assert q(-1, 64, A_, 0, B_, SB_, None) == EINVAL
+    assert q(4, 64, A_, 2, B_, SB_, None) == EINVAL                  # bad input type
+    assert q(4, 48, A_, 0, B_, SB_, None) == EUNSUP                  # K % 32
+    assert q(4, 64, None, 0, B_, SB_, None) == EINVAL
+    assert q(4, 64, A_ + 4, 0, B_, SB_, None) == EALIGN
+    assert q(4, 64, A_, 0, B_ + 2, SB_, None) == EALIGN
+    assert q(4, 64, A_, 0, A_ + 512, SB_, None) == EINVAL            # codes inside X (1 KB of fp32)
+    assert q(4, 64, A_, 1, B_, B_ + 64, None) == EINVAL              # scales inside codes
 
 
 def test_binding_rejects_host_tensors():
