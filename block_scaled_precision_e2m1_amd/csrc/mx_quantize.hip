@@ -12,7 +12,7 @@
 // block (4 elements each), so one wave-wide load is 1 KB (fp32) or 512 B (bf16) of
 // consecutive blocks and one 2-byte store per lane writes 128 contiguous code
 // bytes.  The block maximum and the non-finite flag are reduced over the 8 lanes
-// with DPP row shifts inside each 16-lane row.  floor(log2 amax) comes from the
+// with lane permutations (no LDS storage).  floor(log2 amax) comes from the
 // fp32 exponent field; x * 2^(127-e) is an exact v_ldexp_f32, and the rounding is
 // the count of grid midpoints passed (">" below a midpoint whose upper neighbour
 // has an odd code, ">=" where it is even).
@@ -22,12 +22,12 @@
 namespace fp4g {
 namespace {
 
-constexpr int kUnroll = 4;   // blocks-of-8 per wave per iteration, for loads in flight
+constexpr int kUnroll = 8;   // blocks-of-8 per wave per iteration, for loads in flight
 
-// Maximum over the 8-lane group (lanes 8g .. 8g+7) of non-negative integers, via DPP
-// row_shr within 16-lane rows: groups never straddle a row.
+// Maximum over the 8-lane group (lanes 8g .. 8g+7) of unsigned integers: a butterfly
+// of two DPP quad permutations (partners 1 and 2 apart) and one ds_swizzle that
+// exchanges the two quads of the group (partner 4 apart).
 __device__ __forceinline__ uint32_t group8_max(uint32_t v) {
-  // xor-style butterfly with quad_perm and row_ror inside each 8-lane half-row
   uint32_t t;
   t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
   v = v > t ? v : t;
@@ -55,13 +55,13 @@ mx_quantize_kernel(int64_t nblocks, const void* __restrict__ X, uint8_t* __restr
       const int64_t blk = min(base + u * 8 + (lane >> 3), nblocks - 1);   // clamped: in bounds
       if constexpr (BF16_IN) {
         typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-        const v2u w = *reinterpret_cast<const v2u*>(static_cast<const uint16_t*>(X) + blk * 32 + sub * 4);
+        const v2u w = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(static_cast<const uint16_t*>(X) + blk * 32 + sub * 4));
         bits[u][0] = w[0] << 16;
         bits[u][1] = w[0] & 0xFFFF0000u;
         bits[u][2] = w[1] << 16;
         bits[u][3] = w[1] & 0xFFFF0000u;
       } else {
-        const v4i w = *reinterpret_cast<const v4i*>(static_cast<const float*>(X) + blk * 32 + sub * 4);
+        const v4i w = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(static_cast<const float*>(X) + blk * 32 + sub * 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) bits[u][i] = (uint32_t)w[i];
       }
