@@ -146,6 +146,30 @@ def random_w4a8(M, N, K, rng):
     return {"A": A, "sa": sa, "B": B, "sB": sB}
 
 
+FP8_BLOCK = 128
+
+
+def quantize_e4m3_blocks(x: np.ndarray):
+    """fp32 [rows][K] -> (E4M3 codes [rows][K], fp32 scales [rows][K/128]): per row and
+    128-element block, s = amax / 448 (1 for an all-zero block), code = E4M3(x / s)."""
+    x = np.asarray(x, dtype=np.float32)
+    rows, K = x.shape
+    xb = x.reshape(rows, K // FP8_BLOCK, FP8_BLOCK)
+    amax = np.max(np.abs(xb), axis=2)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return e4m3_codes((xb / s[:, :, None]).reshape(rows, K)), s
+
+
+def random_fp8b(M, N, K, rng):
+    """FP8 blockwise operands: A and B from N(0,1), each quantized to E4M3 with one fp32
+    scale per row per 128-element K block."""
+    if K % FP8_BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    A, sA = quantize_e4m3_blocks(rng.standard_normal((M, K), dtype=np.float32))
+    B, sB = quantize_e4m3_blocks(rng.standard_normal((N, K), dtype=np.float32))
+    return {"A": A, "sA": sA, "B": B, "sB": sB}
+
+
 # ---- the named workloads ------------------------------------------------------------------
 
 # name -> (kind, M, N, K, output dtype, generator)
@@ -155,6 +179,7 @@ CONFIGS = {
     "mxfp4_gemv_8x14336x4096": ("gemv", 8, 14336, 4096, "bf16", "gaussian"),
     "w4a8_256x8192x8192": ("w4a8", 256, 8192, 8192, "bf16", "gaussian"),
     "mxfp4_8192": ("mx", 8192, 8192, 8192, "bf16", "gaussian"),
+    "fp8_block_4096": ("fp8b", 4096, 4096, 4096, "bf16", "gaussian"),
 }
 
 
@@ -168,6 +193,8 @@ def make(name: str, seed: int = 0):
         d = random_nv(M, N, K, rng)
     elif kind == "w4a8":
         d = random_w4a8(M, N, K, rng)
+    elif kind == "fp8b":
+        d = random_fp8b(M, N, K, rng)
     else:
         raise ValueError(kind)
     d.update({"kind": kind, "M": M, "N": N, "K": K, "out": out, "name": name})
@@ -183,6 +210,8 @@ def make_shape(kind: str, M: int, N: int, K: int, seed: int = 0, dist: str = "un
         d = random_nv(M, N, K, rng)
     elif kind == "w4a8":
         d = random_w4a8(M, N, K, rng)
+    elif kind == "fp8b":
+        d = random_fp8b(M, N, K, rng)
     else:
         raise ValueError(kind)
     d.update({"kind": kind, "M": M, "N": N, "K": K})

@@ -77,6 +77,8 @@ def bind(lib):
     lib.oracle_w4a8_gemm_rows.argtypes = [i64, i64, i64, p, p, p, p, i64, i64, p, p]
     lib.oracle_sampled.restype = ctypes.c_int
     lib.oracle_sampled.argtypes = [ctypes.c_int, i64, i64, i64, p, p, d, p, p, d, p, p, i64, p, p]
+    lib.oracle_fp8b_gemm_rows.restype = ctypes.c_int
+    lib.oracle_fp8b_gemm_rows.argtypes = [i64, i64, i64, p, p, p, p, i64, i64, p, p]
     lib.oracle_mx_quantize.argtypes = [i64, i64, p, p, p]
     lib.oracle_mx_quantize.restype = ctypes.c_int
     return lib
@@ -177,7 +179,23 @@ def w4a8_gemm(A, sa, B, sB, rows=None):
     return D, S
 
 
-_KIND = {"mx": 0, "nv": 1, "w4a8": 2}
+def fp8b_gemm(A, sA, B, sB, rows=None):
+    """FP8 blockwise: A [M][K] u8 E4M3, sA [M][K/128] fp32, B [N][K] u8 E4M3, sB [N][K/128] fp32."""
+    A, B = _u8(A), _u8(B)
+    sA = np.ascontiguousarray(sA, dtype=np.float32)
+    sB = np.ascontiguousarray(sB, dtype=np.float32)
+    M, N, K = A.shape[0], B.shape[0], A.shape[1]
+    r0, r1 = rows if rows is not None else (0, M)
+    D = np.empty((r1 - r0, N), np.float64)
+    S = np.empty((r1 - r0, N), np.float64)
+    rc = _load().oracle_fp8b_gemm_rows(M, N, K, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), r0, r1,
+                                       _ptr(D), _ptr(S))
+    if rc:
+        raise ValueError("oracle_fp8b_gemm_rows: bad arguments")
+    return D, S
+
+
+_KIND = {"mx": 0, "nv": 1, "w4a8": 2, "fp8b": 3}
 
 
 def sampled(kind, inputs, ms, ns):
@@ -192,6 +210,12 @@ def sampled(kind, inputs, ms, ns):
         A, B = _u8(inputs["A"]), _u8(inputs["B"])
         sfa = np.ascontiguousarray(inputs["sa"], dtype=np.float32)
         sfb = np.ascontiguousarray(inputs["sB"], dtype=np.uint16)
+        M, N, K = A.shape[0], B.shape[0], A.shape[1]
+        gA = gB = 1.0
+    elif kind == "fp8b":
+        A, B = _u8(inputs["A"]), _u8(inputs["B"])
+        sfa = np.ascontiguousarray(inputs["sA"], dtype=np.float32)
+        sfb = np.ascontiguousarray(inputs["sB"], dtype=np.float32)
         M, N, K = A.shape[0], B.shape[0], A.shape[1]
         gA = gB = 1.0
     else:
@@ -216,6 +240,8 @@ def run(kind, inputs, rows=None):
                        inputs["sfB"], inputs.get("gB", 1.0), rows)
     if kind == "w4a8":
         return w4a8_gemm(inputs["A"], inputs["sa"], inputs["B"], inputs["sB"], rows)
+    if kind == "fp8b":
+        return fp8b_gemm(inputs["A"], inputs["sA"], inputs["B"], inputs["sB"], rows)
     raise ValueError(kind)
 
 

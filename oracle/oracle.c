@@ -212,10 +212,52 @@ int oracle_w4a8_gemm(int64_t M, int64_t N, int64_t K,
     return oracle_w4a8_gemm_rows(M, N, K, A, sa, B, sB, 0, M, D, S);
 }
 
+/* FP8 blockwise-scaled GEMM.  The issue page ("What Works", "Background" and
+ * "Scale Factor Granularity") names the FP8 blockwise GEMM as the existing
+ * Blackwell example that the FP4 kernels extend, with a scale granularity of 128
+ * along K.  The plainest reading of that granularity: each row of each operand
+ * carries one fp32 scale per 128 consecutive K elements, and
+ *   D[m][n] = sum_g sA[m][g] * sB[n][g] * sum_{k in group g} e4m3(A[m][k]) * e4m3(B[n][k]).
+ * A [M][K] and B [N][K] are E4M3 codes (K-major), sA [M][K/128], sB [N][K/128]. */
+#define FP8_BLOCK 128
+int oracle_fp8b_gemm_rows(int64_t M, int64_t N, int64_t K,
+                          const uint8_t *A, const float *sA,
+                          const uint8_t *B, const float *sB,
+                          int64_t row0, int64_t row1, double *D, double *S) {
+    if (M < 0 || N < 0 || K < 0 || (K % FP8_BLOCK) != 0) return -1;
+    if (row0 < 0 || row1 > M || row0 > row1) return -1;
+    if ((M && N && K) && (!A || !sA || !B || !sB)) return -1;
+    if ((row1 > row0 && N) && (!D || !S)) return -1;
+    const int64_t G = K / FP8_BLOCK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = row0; m < row1; ++m) {
+        const uint8_t *arow = A + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *brow = B + n * K;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                double part = 0.0, part_mag = 0.0;
+                for (int64_t k = g * FP8_BLOCK; k < (g + 1) * FP8_BLOCK; ++k) {
+                    double p = oracle_e4m3fn(arow[k]) * oracle_e4m3fn(brow[k]);
+                    part += p;
+                    part_mag += fabs(p);
+                }
+                const double sc = (double)sA[m * G + g] * (double)sB[n * G + g];
+                acc += sc * part;
+                mag += fabs(sc) * part_mag;
+            }
+            D[(m - row0) * N + n] = acc;
+            S[(m - row0) * N + n] = mag;
+        }
+    }
+    return 0;
+}
+
 /* Sampled outputs: the same definitions evaluated only at the listed (m, n)
  * pairs, for shapes whose full product is too slow on the CPU.  kind selects
  * the operation: 0 = MXFP4, 1 = NVFP4 (gA, gB used), 2 = W4A8 (A is FP8,
- * sfA is the fp32 row-scale array, sfB the bf16 group scales). */
+ * sfA is the fp32 row-scale array, sfB the bf16 group scales), 3 = FP8 blockwise
+ * (A and B are FP8, sfA and sfB their fp32 group scales). */
 int oracle_sampled(int kind, int64_t M, int64_t N, int64_t K,
                    const void *A, const void *sfA, double gA,
                    const void *B, const void *sfB, double gB,
@@ -262,6 +304,22 @@ int oracle_sampled(int kind, int64_t M, int64_t N, int64_t K,
             double rs = (double)((const float *)sfA)[m];
             d = rs * acc;
             s = fabs(rs) * mag;
+        } else if (kind == 3) {
+            if (K % FP8_BLOCK) { bad = 1; continue; }
+            const uint8_t *arow = (const uint8_t *)A + m * K;
+            const uint8_t *brow = (const uint8_t *)B + n * K;
+            const int64_t G = K / FP8_BLOCK;
+            for (int64_t g = 0; g < G; ++g) {
+                double part = 0.0, part_mag = 0.0;
+                for (int64_t k = g * FP8_BLOCK; k < (g + 1) * FP8_BLOCK; ++k) {
+                    double p = oracle_e4m3fn(arow[k]) * oracle_e4m3fn(brow[k]);
+                    part += p;
+                    part_mag += fabs(p);
+                }
+                const double sc = (double)((const float *)sfA)[m * G + g] * (double)((const float *)sfB)[n * G + g];
+                d += sc * part;
+                s += fabs(sc) * part_mag;
+            }
         } else {
             bad = 1;
             continue;

@@ -18,6 +18,7 @@ import oracle
 from tests import test_oracle_codecs as codecs
 from tests import test_oracle_pins as pins
 from tests import test_oracle_quant as quant
+from tests import test_oracle_fp8b as fp8b
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -57,13 +58,20 @@ MUTANTS = {
     "quant-negative-zero": ("if (c != 0 && y < 0.0) c |= 8u;", "if (y < 0.0) c |= 8u;"),
     "quant-nibble-order": ("out[i / 2] = (uint8_t)(nib[0] | (nib[1] << 4));", "out[i / 2] = (uint8_t)(nib[1] | (nib[0] << 4));"),
     "quant-no-nonfinite-check": ("if (!isfinite(blk[i])) finite = 0;", "if (0) finite = 0;"),
+    "fp8b-group-size": ("#define FP8_BLOCK 128", "#define FP8_BLOCK 64"),
+    "fp8b-b-scale-row": ("const double sc = (double)sA[m * G + g] * (double)sB[n * G + g];",
+                         "const double sc = (double)sA[m * G + g] * (double)sB[m * G + g];"),
+    "fp8b-scale-group-shift": ("const double sc = (double)sA[m * G + g] * (double)sB[n * G + g];",
+                               "const double sc = (double)sA[m * G + g] * (double)sB[n * G + (g + 1) % G];"),
+    "fp8b-b-row-stride": ("const uint8_t *brow = B + n * K;\n            double acc = 0.0, mag = 0.0;",
+                          "const uint8_t *brow = B + n * (K / 2);\n            double acc = 0.0, mag = 0.0;"),
 }
 
 
 def _quick_pins():
     """(callable, kwargs) for every quick pin, over all of its parametrisations."""
     out = []
-    for mod in (codecs, pins, quant):
+    for mod in (codecs, pins, quant, fp8b):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue
