@@ -47,7 +47,7 @@ def to_dev(d, dev):
     out = {}
     for k, v in d.items():
         if isinstance(v, np.ndarray) and v.ndim > 0:
-            if k == "sB":
+            if k == "sB" and v.dtype == np.uint16:      # W4A8 group scales: raw bf16 bits
                 out[k] = torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
             else:
                 out[k] = torch.from_numpy(v).to(dev)
@@ -251,6 +251,16 @@ def bench_mx256(steps, warmup, dev):
     return {"ms": mean_ms, "tflops": 2.0 * 256 ** 3 / (mean_ms * 1e-3) / 1e12}
 
 
+def bench_fp8b(steps, warmup, dev):
+    d = datagen.make("fp8_block_4096")
+    M = N = K = 4096
+    t = to_dev(d, dev)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fn = lambda: fp4.fp8_blockwise_gemm(t["A"], t["sA"], t["B"], t["sB"], out=D)
+    mean_ms, _ = time_launches(fn, steps, warmup, dev)
+    return {"ms": mean_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12}
+
+
 def bench_quant(steps, warmup, dev):
     """MX quantizer on an 8192 x 8192 fp32 activation (the GEMM's operand size): two
     input copies alternate (512 MB, past the 256 MB last-level cache)."""
@@ -311,7 +321,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: mx8192 gemv w4a8 nv1024 mx256 quant copy")
+                    help="subset of: mx8192 gemv w4a8 nv1024 mx256 quant fp8b copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue launches eagerly instead of replaying a HIP graph (for counter runs)")
@@ -333,7 +343,7 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     fp4.load_library()
-    only = set(args.only) if args.only else {"mx8192", "gemv", "w4a8", "nv1024", "mx256", "quant"}
+    only = set(args.only) if args.only else {"mx8192", "gemv", "w4a8", "nv1024", "mx256", "quant", "fp8b"}
     also = {}
     head = None
     d8192 = None
@@ -371,6 +381,14 @@ def main():
                               "roofline": {"bound": "mfma", "achieved": n["tflops"], "peak": PEAK_TFLOPS["bf16"],
                                            "unit": "TFLOP/s", "frac": n["tflops"] / PEAK_TFLOPS["bf16"],
                                            "traffic": None}}
+    if "fp8b" in only:
+        log("bench: fp8 blockwise 4096^3 ...")
+        f = bench_fp8b(args.steps, args.warmup, dev)
+        log(f"bench: fp8 blockwise 4096^3 {f['ms'] * 1e3:.1f} us/launch, {f['tflops']:.0f} TFLOP/s")
+        also["fp8_blockwise_4096"] = {
+            "metric": "TFLOP/s", "value": f["tflops"], "ms_per_launch": f["ms"],
+            "roofline": {"bound": "mfma", "achieved": f["tflops"], "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                         "frac": f["tflops"] / PEAK_TFLOPS["fp8"], "traffic": None}}
     if "quant" in only:
         log("bench: mx quantize 8192x8192 fp32 ...")
         q = bench_quant(args.steps, args.warmup, dev)

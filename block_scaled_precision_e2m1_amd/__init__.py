@@ -23,12 +23,14 @@ import os
 
 import torch
 
-__all__ = ["mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp4g_status_string",
+__all__ = ["mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
+           "fp4g_status_string",
            "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfp4gemm.so")
-SYMBOLS = ("mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp4g_status_string")
+SYMBOLS = ("mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
+           "fp4g_status_string")
 
 OUT_F32, OUT_BF16 = 0, 1
 IN_F32, IN_BF16 = 0, 1
@@ -65,6 +67,8 @@ def load_library():
     lib.nv_fp4_gemm.restype = c_int
     lib.w4a8_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.w4a8_gemm.restype = c_int
+    lib.fp8_blockwise_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
+    lib.fp8_blockwise_gemm.restype = c_int
     lib.mx_fp4_quantize.argtypes = [i64, i64, p, c_int, p, p, p]
     lib.mx_fp4_quantize.restype = c_int
     lib.fp4g_status_string.argtypes = [c_int]
@@ -211,3 +215,25 @@ def mx_fp4_quantize(X, codes=None, scales=None):
     st = lib.mx_fp4_quantize(rows, K, _ptr(X), xt, _ptr(codes), _ptr(scales), _stream(device))
     _raise_on("mx_fp4_quantize", st)
     return codes, scales
+
+
+def fp8_blockwise_gemm(A, sA, B, sB, out=None, out_dtype=torch.bfloat16):
+    """FP8 blockwise-scaled GEMM: A [M, K] and B [N, K] E4M3 codes (uint8), sA [M, K/128]
+    and sB [N, K/128] float32 scales; returns D [M, N]."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    N = B.shape[0]
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(A, "A", torch.uint8, (M, K), device)
+    _check(sA, "sA", torch.float32, (M, K // 128), device)
+    _check(B, "B", torch.uint8, (N, K), device)
+    _check(sB, "sB", torch.float32, (N, K // 128), device)
+    D = _out(out, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    st = lib.fp8_blockwise_gemm(M, N, K, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(D), dt, _stream(device))
+    _raise_on("fp8_blockwise_gemm", st)
+    return D

@@ -10,6 +10,7 @@ namespace {
 
 using fp4g::FP4Args;
 using fp4g::W4A8Args;
+using fp4g::Fp8bArgs;
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // each of M, N, K below 2^31
 
@@ -112,6 +113,26 @@ fp4g_status w4a8_gemm(int64_t M, int64_t N, int64_t K, const void* A, const floa
   W4A8Args a{M, N, K, static_cast<const uint8_t*>(A), sa, static_cast<const uint8_t*>(B),
              static_cast<const uint16_t*>(sB), D, bf16};
   return finish(fp4g::launch_w4a8_gemm(a, s));
+}
+
+fp4g_status fp8_blockwise_gemm(int64_t M, int64_t N, int64_t K, const void* A, const float* sA, const void* B,
+                               const float* sB, void* D, int d_type, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_common(M, N, K, d_type, D, &empty);
+  if (st != FP4G_OK || empty) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, M * N, bf16, s));
+  if (!A || !sA || !B || !sB) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16)) return FP4G_EALIGN;
+  if (!aligned(sA, 4) || !aligned(sB, 4)) return FP4G_EALIGN;
+  const Range d = range_of(D, M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, M * K), range_of(sA, M * (K / 128) * 4), range_of(B, N * K),
+                        range_of(sB, N * (K / 128) * 4)};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  Fp8bArgs a{M, N, K, static_cast<const uint8_t*>(A), sA, static_cast<const uint8_t*>(B), sB, D, bf16};
+  return finish(fp4g::launch_fp8b_gemm(a, s));
 }
 
 fp4g_status mx_fp4_quantize(int64_t rows, int64_t K, const void* X, int x_type, void* codes, void* scales,

@@ -1,0 +1,182 @@
+// FP8 blockwise-scaled GEMM for gfx950: E4M3 operands with one fp32 scale per row
+// per 128-element K group,
+//   D[m][n] = sum_g sA[m][g] * sB[n][g] * sum_{k in group g} e4m3(A[m][k]) * e4m3(B[n][k]).
+// This is the FP8 blockwise GEMM that the NVIDIA/cutlass issue "Add FP4 TMA kernel
+// example for Blackwell in CuTe Python DSL" takes as its starting point ("What
+// Works", and "Scale Factor Granularity": FP8 uses a granularity of 128 along K).
+//
+// gfx950 design:
+//   * workgroup tile 128 x 128, 4 waves in a 2 x 2 grid of 64 x 64; a stage is one
+//     128-element group: 128 FP8 bytes (one cache line) per row of A and of B, and
+//     the group's 128 + 128 fp32 scales;
+//   * stages reach LDS through global->LDS copies (global_load_lds_dwordx4 for the
+//     operands, _dword for the scales) into a 4-slot ring, waited for with counted
+//     vmcnt and one barrier per stage; 16-byte chunks are XOR-swizzled by row so the
+//     MFMA-layout ds_read_b128 is free of bank conflicts;
+//   * a group's product is two v_mfma_scale_f32_32x32x64_f8f6f4 (FP8 x FP8, unit
+//     E8M0 scales) per 32 x 32 block into fresh registers; the fp32 accumulator then
+//     takes it times sA[m][g] * sB[n][g] (no FP8 value can absorb an fp32 scale
+//     exactly, so the scaling is a VALU multiply-add per element and group);
+//   * B is the first MFMA operand, so the accumulator holds D^T: a lane owns one m
+//     and four consecutive n per register quad, stored as one 8- or 16-byte write.
+#include "common.hpp"
+#include "internal.h"
+
+namespace fp4g {
+namespace {
+
+constexpr int FBM = 128, FBN = 128;
+constexpr int FSTAGES = 4;
+constexpr int F_A = FBM * 128;              // FP8 bytes of A per stage (16 KB)
+constexpr int F_B = FBN * 128;              // FP8 bytes of B per stage (16 KB)
+constexpr int F_SA = F_A + F_B;             // sA: 128 fp32
+constexpr int F_SB = F_SA + FBM * 4;        // sB: 128 fp32
+constexpr int F_STAGE = F_SB + FBN * 4;
+constexpr int F_LOADS = 4 + 4 + 1;          // copies per wave per stage: A, B, one scale copy
+static_assert(FSTAGES * F_STAGE <= 160 * 1024, "LDS budget");
+static_assert((FSTAGES - 2) * F_LOADS < 64, "vmcnt range");
+
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
+                 const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FSTAGES * F_STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int hi = lane >> 5, r32 = lane & 31;
+
+  // Tile order: consecutive ids go to the 8 XCDs in turn; regroup so each XCD owns a
+  // contiguous band of tiles (shared A and B panels in its L2).
+  const int tiles_m = (M + FBM - 1) / FBM, tiles_n = (N + FBN - 1) / FBN;
+  const int T = tiles_m * tiles_n;
+  int lin = blockIdx.x;
+  if ((T & 7) == 0) lin = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  const int m0 = (lin / tiles_n) * FBM, n0 = (lin % tiles_n) * FBN;
+  const int G = K / 128;
+
+  // ---- copy sources: copy c (0..15) of an operand covers rows 8c .. 8c+7 ----
+  const uint8_t* ga[4];
+  const uint8_t* gb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = wave * 4 + i;
+    const int row = 8 * c + (lane >> 3), u = lane & 7;
+    ga[i] = A + (int64_t)min(m0 + row, M - 1) * K + ((u ^ swz8(row)) << 4);
+    gb[i] = B + (int64_t)min(n0 + row, N - 1) * K + ((u ^ swz8(row)) << 4);
+  }
+  // Scale copy: wave w fetches 64 scales -- sA rows 0..63 / 64..127, sB rows 0..63 / 64..127.
+  const int srow = 64 * (wave & 1) + lane;
+  const float* gs = (wave < 2) ? sA + (int64_t)min(m0 + srow, M - 1) * G : sB + (int64_t)min(n0 + srow, N - 1) * G;
+  const int ls = ((wave < 2) ? F_SA : F_SB) + 256 * (wave & 1);
+
+  auto issue = [&](int g) {
+    const int gc = min(g, G - 1);                  // past the end: re-read the last group
+    uint8_t* base = smem + (g % FSTAGES) * F_STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_copy16(ga[i] + (int64_t)gc * 128, (lds_void*)(base + (wave * 4 + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_copy16(gb[i] + (int64_t)gc * 128, (lds_void*)(base + F_A + (wave * 4 + i) * 1024));
+    lds_copy4(gs + gc, (lds_void*)(base + ls));
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+  const int unit = 0x7F7F7F7F;
+
+#pragma unroll
+  for (int p = 0; p < FSTAGES - 1; ++p) issue(p);
+
+  for (int g = 0; g < G; ++g) {
+    // Group g is complete once only groups g+1 .. g+FSTAGES-2 are in flight; the barrier
+    // publishes every wave's copies and frees slot (g-1) % FSTAGES.
+    wait_vmcnt<(FSTAGES - 2) * F_LOADS>();
+    barrier_lds();
+    issue(g + FSTAGES - 1);
+    const uint8_t* base = smem + (g % FSTAGES) * F_STAGE;
+    v16f part[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c0 = 4 * kk + 2 * hi;              // this lane's 32 bytes: chunks c0, c0+1
+      v8i af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + i * 32 + r32;
+        const v4i x0 = *reinterpret_cast<const v4i*>(base + row * 128 + ((c0 ^ swz8(row)) << 4));
+        const v4i x1 = *reinterpret_cast<const v4i*>(base + row * 128 + (((c0 + 1) ^ swz8(row)) << 4));
+        af[i] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = wn * 64 + j * 32 + r32;
+        const v4i x0 = *reinterpret_cast<const v4i*>(base + F_A + row * 128 + ((c0 ^ swz8(row)) << 4));
+        const v4i x1 = *reinterpret_cast<const v4i*>(base + F_A + row * 128 + (((c0 + 1) ^ swz8(row)) << 4));
+        bf[j] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], kk == 0 ? v16f{} : part[i][j],
+                                                                       kFmtFp8, kFmtFp8, 0, unit, 0, unit);
+    }
+    // part[i][j] holds D^T: element t of lane (hi, r32) is n = 32j + 8(t/4) + 4hi + t%4,
+    // m = 32i + r32 of the wave tile.
+    const float* ssa = reinterpret_cast<const float*>(base + F_SA);
+    const float* ssb = reinterpret_cast<const float*>(base + F_SB);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float sa_m = ssa[wm * 64 + i * 32 + r32];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4f sb4 = *reinterpret_cast<const v4f*>(ssb + wn * 64 + j * 32 + 8 * q + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][j][4 * q + e] = __builtin_fmaf(part[i][j][4 * q + e], sa_m * sb4[e], acc[i][j][4 * q + e]);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+
+  // Epilogue: lane (hi, r32) of block (i, j) owns row m = 32i + r32 and, for q = 0..3,
+  // the four consecutive columns n = 32j + 8q + 4hi + 0..3.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + wm * 64 + i * 32 + r32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 64 + j * 32 + 8 * q + 4 * hi;
+        if (n < N)
+          store_out4<BF16>(D, (int64_t)m * N + n, N - n, acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                           acc[i][j][4 * q + 3]);
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fp8b_gemm(const Fp8bArgs& a, hipStream_t s) {
+  const int64_t tiles = ceil_div(a.M, FBM) * ceil_div(a.N, FBN);
+  if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (a.bf16_out)
+    hipLaunchKernelGGL(fp8b_gemm_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M, (int)a.N, (int)a.K,
+                       a.A, a.sA, a.B, a.sB, a.D);
+  else
+    hipLaunchKernelGGL(fp8b_gemm_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M, (int)a.N, (int)a.K,
+                       a.A, a.sA, a.B, a.sB, a.D);
+  return hipGetLastError();
+}
+
+}  // namespace fp4g

@@ -29,6 +29,16 @@ struct W4A8Args {
   bool bf16_out;
 };
 
+struct Fp8bArgs {            // FP8 blockwise-scaled GEMM
+  int64_t M, N, K;
+  const uint8_t* A;         // [M][K] E4M3
+  const float* sA;          // [M][K/128]
+  const uint8_t* B;         // [N][K] E4M3
+  const float* sB;          // [N][K/128]
+  void* D;
+  bool bf16_out;
+};
+
 // Compute units of the current device (queried once per device, then cached).
 int64_t device_cus();
 
@@ -36,6 +46,7 @@ hipError_t launch_mxfp4_gemm(const FP4Args& a, hipStream_t s);
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s);
 hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s);
 hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t s);
+hipError_t launch_fp8b_gemm(const Fp8bArgs& a, hipStream_t s);
 // D[M][N] = 0 (the empty-K product); never uses hipMemset so it can be captured.
 hipError_t launch_zero_fill(void* D, int64_t count, bool bf16_out, hipStream_t s);
 // E2M1 codes + E8M0 scales of X[rows][K] (K % 32 == 0), max-abs rule.

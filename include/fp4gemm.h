@@ -94,6 +94,17 @@ fp4g_status w4a8_gemm(int64_t M, int64_t N, int64_t K,
                       const void *B, const void *sB,
                       void *D, int d_type, void *stream);
 
+/* FP8 blockwise-scaled GEMM, the FP8 starting point of the issue page ("What
+ * Works"; "Scale Factor Granularity": FP8 scales cover 128 elements of K):
+ *   D[m][n] = sum_g sA[m][g] * sB[n][g] * sum_{k in group g} e4m3(A[m][k]) * e4m3(B[n][k])
+ *   with groups of 128 consecutive K elements and one fp32 scale per row per group.
+ *   A [M][K] bytes and B [N][K] bytes of E4M3 codes (K-major), sA [M][K/128] and
+ *   sB [N][K/128] fp32, D [M][N].  Scales need 4-byte alignment. */
+fp4g_status fp8_blockwise_gemm(int64_t M, int64_t N, int64_t K,
+                               const void *A, const float *sA,
+                               const void *B, const float *sB,
+                               void *D, int d_type, void *stream);
+
 /* MXFP4 GEMV for decode (few tokens): the MXFP4 GEMM with 1 <= M <= 16 and the
  * same layouts, tuned for streaming the weight operand B once from HBM.
  * M > 16 returns FP4G_EUNSUPPORTED. */

@@ -30,7 +30,7 @@ def lib():
 
 def test_header_declares_the_operations():
     assert declared_functions() == sorted(["mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv",
-                                            "mx_fp4_quantize", "fp4g_status_string"])
+                                            "mx_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -115,6 +115,16 @@ def test_nv_and_w4a8_validation(lib):
     assert lib.w4a8_gemm(4, 4, 128, A_, None, B_, SB_, D_, 0, None) == EINVAL
     assert lib.w4a8_gemm(4, 4, 128, A_, SA_ + 2, B_, SB_, D_, 0, None) == EALIGN
     assert lib.w4a8_gemm(4, 4, 128, A_, SA_, B_, SB_, A_ + 64, 0, None) == EINVAL
+
+
+def test_fp8_blockwise_validation(lib):
+    f = lib.fp8_blockwise_gemm
+    assert f(0, 4, 128, None, None, None, None, None, 1, None) == OK
+    assert f(4, 4, 192, A_, SA_, B_, SB_, D_, 0, None) == EUNSUP
+    assert f(4, 4, 128, A_, None, B_, SB_, D_, 0, None) == EINVAL
+    assert f(4, 4, 128, A_ + 8, SA_, B_, SB_, D_, 0, None) == EALIGN
+    assert f(4, 4, 128, A_, SA_ + 2, B_, SB_, D_, 0, None) == EALIGN
+    assert f(4, 4, 128, A_, SA_, B_, SB_, A_ + 256, 0, None) == EINVAL   # D inside A
 
 
 def test_quantizer_validation(lib):

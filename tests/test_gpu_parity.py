@@ -25,7 +25,7 @@ def up(d):
     for k, v in d.items():
         if not isinstance(v, np.ndarray) or v.ndim == 0:
             continue
-        if k == "sB":
+        if k == "sB" and v.dtype == np.uint16:       # W4A8 group scales: raw bf16 bits
             t[k] = torch.from_numpy(v.view(np.int16)).to(DEV).view(torch.bfloat16)
         else:
             t[k] = torch.from_numpy(v).to(DEV)
@@ -43,6 +43,8 @@ def run(kind, d, out_dtype, t=None):
         D = fp4.nv_fp4_gemm(t["A"], t["sfA"], float(d["gA"]), t["B"], t["sfB"], float(d["gB"]), out_dtype=od)
     elif kind == "w4a8":
         D = fp4.w4a8_gemm(t["A"], t["sa"], t["B"], t["sB"], out_dtype=od)
+    elif kind == "fp8b":
+        D = fp4.fp8_blockwise_gemm(t["A"], t["sA"], t["B"], t["sB"], out_dtype=od)
     else:
         raise ValueError(kind)
     torch.cuda.synchronize(DEV)
@@ -57,10 +59,20 @@ def okind(kind):
     return "mx" if kind == "gemv" else kind
 
 
+# FP8 x FP8 (the blockwise GEMM, not one of the five workloads, whose bar is 1e-5):
+# v_mfma_scale_f32_32x32x64_f8f6f4 does not sum the 64 products of one instruction
+# exactly (low bits of products far below the chunk's largest are dropped).  Over
+# random groups its error reaches 1.4e-5 of sum |a b| at K = 128 and falls with K
+# (cancellation across groups); FP8 x INT4 products, with 3 fewer significant bits,
+# stay far inside 1e-5.  The bar for FP8 x FP8 keeps a factor of about 3 over the
+# worst measured case.
+REL_TOL_BY_KIND = {"fp8b": 4e-5}
+
+
 def check_full(kind, d, out_dtype):
     D = as_np(run(kind, d, out_dtype))
     ref, S = oracle.run(okind(kind), d)
-    r = oracle.parity_ratio(D, ref, S, out_dtype)
+    r = oracle.parity_ratio(D, ref, S, out_dtype, REL_TOL_BY_KIND.get(kind, oracle.REL_TOL))
     assert r <= 1.0, f"{kind} {d['M']}x{d['N']}x{d['K']} {out_dtype}: max |err|/tol = {r}"
     return r
 
@@ -80,7 +92,7 @@ def check_sampled(kind, d, out_dtype, ms, ns, D=None):
         D = run(kind, d, out_dtype)
     Dn = as_np(D[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)])
     ref, S = oracle.sampled(okind(kind), d, ms, ns)
-    r = oracle.parity_ratio(Dn, ref, S, out_dtype)
+    r = oracle.parity_ratio(Dn, ref, S, out_dtype, REL_TOL_BY_KIND.get(kind, oracle.REL_TOL))
     assert r <= 1.0, f"{kind} sampled: max |err|/tol = {r}"
     return r
 
@@ -281,6 +293,38 @@ def test_w4a8_int4_extremes():
     q = np.where(rng.integers(0, 2, (64, 256)) > 0, 7, 8).astype(np.uint8)
     d["B"] = datagen.pack_nibbles(q)
     check_full("w4a8", d, "f32")
+
+
+# ---- FP8 blockwise ----------------------------------------------------------------------
+
+F8_SHAPES = [(1, 1, 128), (5, 70, 256), (64, 128, 128), (130, 200, 384), (256, 256, 1024), (300, 257, 512)]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", F8_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in F8_SHAPES])
+def test_fp8b_shapes(shape, out):
+    M, N, K = shape
+    d = datagen.make_shape("fp8b", M, N, K, seed=M + 3 * N + K)
+    print(f"case fp8b {M}x{N}x{K} {out}", flush=True)
+    check_full("fp8b", d, out)
+
+
+def test_fp8b_workload_sampled():
+    d = datagen.make("fp8_block_4096")
+    print("case fp8b 4096^3 seed 0", flush=True)
+    rng = np.random.default_rng(5)
+    ms, ns = sample_pairs(4096, 4096, rng, 4096, edges=(0, 127, 4095))
+    check_sampled("fp8b", d, "bf16", ms, ns)
+
+
+def test_fp8b_scale_extremes():
+    # Scales spanning many octaves and a negative scale: the per-group fp32 multiply
+    # must keep each group's weight.
+    d = datagen.make_shape("fp8b", 64, 96, 512, seed=9)
+    rng = np.random.default_rng(9)
+    d["sA"] = (d["sA"] * np.ldexp(1.0, rng.integers(-20, 20, d["sA"].shape))).astype(np.float32)
+    d["sB"][3, 1] = -d["sB"][3, 1]
+    check_full("fp8b", d, "f32")
 
 
 # ---- edge cases ----------------------------------------------------------------------------
