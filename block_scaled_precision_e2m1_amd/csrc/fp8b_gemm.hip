@@ -19,6 +19,8 @@
 //     exactly, so the scaling is a VALU multiply-add per element and group);
 //   * B is the first MFMA operand, so the accumulator holds D^T: a lane owns one m
 //     and four consecutive n per register quad, stored as one 8- or 16-byte write.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.h"
 
@@ -93,14 +95,45 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
 #pragma unroll
   for (int p = 0; p < FSTAGES - 1; ++p) issue(p);
 
-  for (int g = 0; g < G; ++g) {
+  // Software pipeline: the MFMAs of group g run while the VALU folds group g-1's
+  // partial sums (and their scales, read from LDS during iteration g-1) into the
+  // accumulator, so the matrix pipe and the vector ALU overlap.
+  v16f part[2][2][2];                               // [buffer][i][j]
+  float sa_r[2][2];                                 // [buffer][i]: sA of the lane's row
+  v4f sb_r[2][2][4];                                // [buffer][j][q]: sB of the lane's 16 columns
+  auto read_scales = [&](const uint8_t* base, int buf) {
+    const float* ssa = reinterpret_cast<const float*>(base + F_SA);
+    const float* ssb = reinterpret_cast<const float*>(base + F_SB);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sa_r[buf][i] = ssa[wm * 64 + i * 32 + r32];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sb_r[buf][j][q] = *reinterpret_cast<const v4f*>(ssb + wn * 64 + j * 32 + 8 * q + 4 * hi);
+  };
+  // part[buf][i][j] holds D^T: element t of lane (hi, r32) is n = 32j + 8(t/4) + 4hi + t%4,
+  // m = 32i + r32 of the wave tile.
+  auto fold = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][j][4 * q + e] =
+                __builtin_fmaf(part[buf][i][j][4 * q + e], sa_r[buf][i] * sb_r[buf][j][q][e], acc[i][j][4 * q + e]);
+  };
+  auto group = [&](int g, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
     // Group g is complete once only groups g+1 .. g+FSTAGES-2 are in flight; the barrier
     // publishes every wave's copies and frees slot (g-1) % FSTAGES.
     wait_vmcnt<(FSTAGES - 2) * F_LOADS>();
     barrier_lds();
     issue(g + FSTAGES - 1);
     const uint8_t* base = smem + (g % FSTAGES) * F_STAGE;
-    v16f part[2][2];
+    read_scales(base, BUF);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int c0 = 4 * kk + 2 * hi;              // this lane's 32 bytes: chunks c0, c0+1
@@ -123,27 +156,22 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], kk == 0 ? v16f{} : part[i][j],
-                                                                       kFmtFp8, kFmtFp8, 0, unit, 0, unit);
+          part[BUF][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              bf[j], af[i], kk == 0 ? v16f{} : part[BUF][i][j], kFmtFp8, kFmtFp8, 0, unit, 0, unit);
     }
-    // part[i][j] holds D^T: element t of lane (hi, r32) is n = 32j + 8(t/4) + 4hi + t%4,
-    // m = 32i + r32 of the wave tile.
-    const float* ssa = reinterpret_cast<const float*>(base + F_SA);
-    const float* ssb = reinterpret_cast<const float*>(base + F_SB);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float sa_m = ssa[wm * 64 + i * 32 + r32];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v4f sb4 = *reinterpret_cast<const v4f*>(ssb + wn * 64 + j * 32 + 8 * q + 4 * hi);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[i][j][4 * q + e] = __builtin_fmaf(part[i][j][4 * q + e], sa_m * sb4[e], acc[i][j][4 * q + e]);
-        }
-      }
-    }
+    if (g > 0) fold(BUF ^ 1);
+  };
+
+  int g = 0;
+  for (; g + 2 <= G; g += 2) {
+    group(g, std::integral_constant<int, 0>{});
+    group(g + 1, std::integral_constant<int, 1>{});
+  }
+  if (g < G) {
+    group(g, std::integral_constant<int, 0>{});
+    fold(0);
+  } else {
+    fold(1);
   }
   wait_vmcnt<0>();
 
