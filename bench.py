@@ -261,6 +261,31 @@ def bench_fp8b(steps, warmup, dev):
     return {"ms": mean_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12}
 
 
+def bench_skinny(steps, warmup, dev, L=1, M=128, N=8192, K=8192):
+    """Batched MXFP4 GEMM on a skinny problem whose 128 x 128 tiles cannot fill the
+    CUs, timed with the library's own K split and without one.  Weight copies rotate
+    (past the 256 MB last-level cache) as in a decode/prefill step."""
+    rng = np.random.default_rng(0)
+    d = datagen.random_mx_gaussian(L * M, N, K, rng)
+    A = torch.from_numpy(d["A"]).to(dev).view(L, M, K // 2)
+    sA = torch.from_numpy(d["sfA"]).to(dev).view(L, M, K // 32)
+    B0 = torch.from_numpy(d["B"]).to(dev)[None].expand(L, N, K // 2).contiguous()
+    sB0 = torch.from_numpy(d["sfB"]).to(dev)[None].expand(L, N, K // 32).contiguous()
+    wbytes = B0.numel() + sB0.numel()
+    copies = int(np.ceil(320e6 / wbytes))
+    sets = [((B0.clone(), sB0.clone()) if c else (B0, sB0)) for c in range(copies)]
+    D = torch.empty((L, M, N), dtype=torch.bfloat16, device=dev)
+    out = {"copies": copies}
+    for label, splits in (("auto", 0), ("none", 1)):
+        nbytes = fp4.mx_fp4_gemm_workspace_size(L, M, N, K, splits)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        fn = lambda B, sB: fp4.mx_fp4_gemm_batched(A, sA, B, sB, out=D, splits=splits, workspace=ws)
+        ms, _ = time_launches(fn, steps, warmup, dev, sets)
+        out[label] = {"ms": ms, "tflops": 2.0 * L * M * N * K / (ms * 1e-3) / 1e12,
+                      "splits": nbytes // (L * M * N * 4) if nbytes else 1}
+    return out
+
+
 def bench_quant(steps, warmup, dev):
     """MX quantizer on an 8192 x 8192 fp32 activation (the GEMM's operand size): two
     input copies alternate (512 MB, past the 256 MB last-level cache)."""
@@ -321,7 +346,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: mx8192 gemv w4a8 nv1024 mx256 quant fp8b copy")
+                    help="subset of: mx8192 gemv w4a8 nv1024 mx256 quant fp8b skinny copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue launches eagerly instead of replaying a HIP graph (for counter runs)")
@@ -343,7 +368,8 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     fp4.load_library()
-    only = set(args.only) if args.only else {"mx8192", "gemv", "w4a8", "nv1024", "mx256", "quant", "fp8b"}
+    only = set(args.only) if args.only else {"mx8192", "gemv", "w4a8", "nv1024", "mx256", "quant", "fp8b",
+                                             "skinny"}
     also = {}
     head = None
     d8192 = None
@@ -398,6 +424,17 @@ def main():
             "roofline": {"bound": "hbm", "achieved": q["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": q["gbs"] / PEAK_HBM_GBS, "traffic": None},
             "algorithmic_bytes": q["bytes"]}
+    if "skinny" in only:
+        log("bench: mxfp4 batched/split-K 128x8192x8192 (cold weights) ...")
+        k = bench_skinny(args.steps, args.warmup, dev)
+        log(f"bench: mxfp4 128x8192x8192 split {k['auto']['splits']}: {k['auto']['ms'] * 1e3:.1f} us "
+            f"({k['auto']['tflops']:.0f} TFLOP/s); unsplit {k['none']['ms'] * 1e3:.1f} us")
+        also["mxfp4_split_k_128x8192x8192"] = {
+            "metric": "TFLOP/s", "value": k["auto"]["tflops"], "ms_per_launch": k["auto"]["ms"],
+            "splits": k["auto"]["splits"], "unsplit_ms_per_launch": k["none"]["ms"],
+            "cache": f"cold ({k['copies']} rotating weight copies)",
+            "roofline": {"bound": "mfma", "achieved": k["auto"]["tflops"], "peak": PEAK_TFLOPS["fp4"],
+                         "unit": "TFLOP/s", "frac": k["auto"]["tflops"] / PEAK_TFLOPS["fp4"], "traffic": None}}
     if "copy" in only:
         c = bench_copy(dev)
         log(f"bench: copy 512 MiB {c['ms'] * 1e3:.1f} us, {c['gbs']:.0f} GB/s (read+write)")

@@ -23,13 +23,13 @@ import os
 
 import torch
 
-__all__ = ["mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
+__all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
            "fp4g_status_string",
            "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfp4gemm.so")
-SYMBOLS = ("mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
+SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
            "fp4g_status_string")
 
 OUT_F32, OUT_BF16 = 0, 1
@@ -61,6 +61,10 @@ def load_library():
     i64, p, c_int, f = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.mx_fp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.mx_fp4_gemm.restype = c_int
+    lib.mx_fp4_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, p, p, p, c_int, i64, p, ctypes.c_size_t, p]
+    lib.mx_fp4_gemm_batched.restype = c_int
+    lib.mx_fp4_gemm_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mx_fp4_gemm_workspace_size.restype = c_int
     lib.fp4_gemv.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.fp4_gemv.restype = c_int
     lib.nv_fp4_gemm.argtypes = [i64, i64, i64, p, p, f, p, p, f, p, c_int, p]
@@ -149,6 +153,49 @@ def mx_fp4_gemm(A, sfA, B, sfB, out=None, out_dtype=torch.bfloat16):
     lib, dev, M, N, K, D, dt = _fp4_common("mx_fp4_gemm", 32, A, sfA, B, sfB, out, out_dtype)
     st = lib.mx_fp4_gemm(M, N, K, _ptr(A), _ptr(sfA), _ptr(B), _ptr(sfB), _ptr(D), dt, _stream(dev))
     _raise_on("mx_fp4_gemm", st)
+    return D
+
+
+def mx_fp4_gemm_workspace_size(L, M, N, K, splits=0) -> int:
+    """Bytes of workspace mx_fp4_gemm_batched uses for these sizes on the current device."""
+    n = ctypes.c_size_t(0)
+    st = load_library().mx_fp4_gemm_workspace_size(L, M, N, K, splits, ctypes.byref(n))
+    _raise_on("mx_fp4_gemm_workspace_size", st)
+    return int(n.value)
+
+
+def mx_fp4_gemm_batched(A, sfA, B, sfB, out=None, out_dtype=torch.bfloat16, splits=0, workspace=None):
+    """Batched MXFP4 GEMM: A [L, M, K/2], sfA [L, M, K/32], B [L, N, K/2], sfB [L, N, K/32]
+    -> D [L, M, N].  `splits` = 0 lets the library split K when the tiles are too few
+    to fill the GPU, 1 never splits, s > 1 asks for s slices.  `workspace` is a uint8
+    device tensor for the partial sums; None allocates the size the library asks for."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 3 or B.dim() != 3:
+        raise ValueError("A and B must be 3-D [L, rows, K/2]")
+    L, M, K = A.shape[0], A.shape[1], A.shape[2] * 2
+    N = B.shape[1]
+    if K % 32:
+        raise ValueError(f"K={K} must be a multiple of 32")
+    _check(A, "A", torch.uint8, (L, M, K // 2), device)
+    _check(sfA, "sfA", torch.uint8, (L, M, K // 32), device)
+    _check(B, "B", torch.uint8, (L, N, K // 2), device)
+    _check(sfB, "sfB", torch.uint8, (L, N, K // 32), device)
+    if out is None:
+        D = torch.empty((L, M, N), dtype=out_dtype, device=device)
+    else:
+        if out.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("out must be float32 or bfloat16")
+        _check(out, "out", out.dtype, (L, M, N), device)
+        D = out
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    if workspace is None:
+        nbytes = mx_fp4_gemm_workspace_size(L, M, N, K, splits) if K % 128 == 0 else 0
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _check(workspace, "workspace", torch.uint8, (workspace.numel(),), device)
+    st = lib.mx_fp4_gemm_batched(L, M, N, K, _ptr(A), _ptr(sfA), _ptr(B), _ptr(sfB), _ptr(D), dt, splits,
+                                 _ptr(workspace), workspace.numel(), _stream(device))
+    _raise_on("mx_fp4_gemm_batched", st)
     return D
 
 

@@ -74,9 +74,70 @@ fp4g_status run_fp4(int which, int64_t M, int64_t N, int64_t K, const void* A, c
   return finish(fp4g::launch_fp4_gemv(a, s));
 }
 
+// Sizes of the batched MXFP4 GEMM; *empty when there is no output element.
+fp4g_status check_batched_sizes(int64_t L, int64_t M, int64_t N, int64_t K, int64_t splits, bool* empty) {
+  if (L < 0 || L >= kMaxDim || splits < 0) return FP4G_EINVAL;
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP4G_EINVAL;
+  if (L * M >= kMaxDim || L * N >= kMaxDim) return FP4G_EINVAL;
+  if (K % 128 != 0) return FP4G_EUNSUPPORTED;
+  *empty = (L == 0 || M == 0 || N == 0);
+  return FP4G_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+fp4g_status mx_fp4_gemm_workspace_size(int64_t L, int64_t M, int64_t N, int64_t K, int64_t splits, size_t* bytes) {
+  bool empty = false;
+  const fp4g_status st = check_batched_sizes(L, M, N, K, splits, &empty);
+  if (st != FP4G_OK) return st;
+  if (!bytes) return FP4G_EINVAL;
+  *bytes = 0;
+  if (empty || K == 0 || splits == 1) return FP4G_OK;
+  const int64_t S = fp4g::mxfp4_gemm_splits(L, M, N, K, splits, fp4g::kMaxSplits);
+  if (S > 1) *bytes = (size_t)(L * S * M * N * 4);
+  return FP4G_OK;
+}
+
+fp4g_status mx_fp4_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
+                                const void* B, const void* sfB, void* D, int d_type, int64_t splits,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_batched_sizes(L, M, N, K, splits, &empty);
+  if (st != FP4G_OK) return st;
+  if (d_type != FP4G_OUT_F32 && d_type != FP4G_OUT_BF16) return FP4G_EINVAL;
+  if (!workspace && workspace_bytes > 0) return FP4G_EINVAL;
+  if (empty) return FP4G_OK;
+  if (!D) return FP4G_EINVAL;
+  if (!aligned(D, 16)) return FP4G_EALIGN;
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, L * M * N, bf16, s));
+  if (!A || !sfA || !B || !sfB) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16)) return FP4G_EALIGN;
+  if (!aligned(sfA, 4) || !aligned(sfB, 4)) return FP4G_EALIGN;
+  const Range d = range_of(D, L * M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, L * M * (K / 2)), range_of(sfA, L * M * (K / 32)),
+                        range_of(B, L * N * (K / 2)), range_of(sfB, L * N * (K / 32))};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  // The split: what was asked (or chosen), limited to what the workspace holds.
+  int64_t S = 1;
+  if (splits != 1 && workspace_bytes > 0) {
+    if (!aligned(workspace, 16)) return FP4G_EALIGN;
+    const Range w = range_of(workspace, (int64_t)workspace_bytes);
+    if (overlaps(w, d)) return FP4G_EINVAL;
+    for (const Range& r : ins)
+      if (overlaps(w, r)) return FP4G_EINVAL;
+    const int64_t per_split = L * M * N * 4;
+    const int64_t fits = (int64_t)(workspace_bytes / (size_t)per_split);
+    S = fp4g::mxfp4_gemm_splits(L, M, N, K, splits, fits);
+  }
+  FP4Args a{M, N, K, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(sfA),
+            static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(sfB), 1.0f, D, bf16};
+  return finish(fp4g::launch_mxfp4_gemm_batched(a, L, S, static_cast<float*>(workspace), s));
+}
 
 fp4g_status mx_fp4_gemm(int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
                         const void* B, const void* sfB, void* D, int d_type, void* stream) {

@@ -43,6 +43,14 @@ struct Fp8bArgs {            // FP8 blockwise-scaled GEMM
 int64_t device_cus();
 
 hipError_t launch_mxfp4_gemm(const FP4Args& a, hipStream_t s);
+// Batched MXFP4 GEMM: L problems of a.M x a.N x a.K stored back to back.  With S > 1
+// the K stages are split S ways into the fp32 buffer P [L][S][M][N], then reduced
+// into a.D in slice order; S must come from mxfp4_gemm_splits.
+constexpr int64_t kMaxSplits = 16;
+hipError_t launch_mxfp4_gemm_batched(const FP4Args& a, int64_t L, int64_t S, float* P, hipStream_t s);
+// The K split the batched launcher uses: `requested` slices if > 0, else its own
+// choice for the current device; at most `cap`, kMaxSplits and the K stage count.
+int64_t mxfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t requested, int64_t cap);
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s);
 hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s);
 hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t s);

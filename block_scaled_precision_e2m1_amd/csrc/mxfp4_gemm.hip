@@ -39,6 +39,16 @@
 //   * output tiles are numbered so that the tiles resident at once on one XCD
 //     (workgroups are dealt round-robin over the 8 XCDs) share A and B panels
 //     in that XCD's L2.
+//
+// Batch and K split.  The problem shape is (M, N, K, L) with L a batch count, all
+// runtime values (the Hopper post, section "How a kernel is assembled"); the L
+// problems sit back to back in memory and share one persistent grid.  When the
+// output tiles cannot fill the CUs (skinny or small problems: the post's
+// introduction names a stream-K scheduler as the load-balancing variant of the
+// persistent one), the K loop of every tile is cut into S slices that run as
+// separate work items and write fp32 partial sums; a second kernel adds the S
+// partials of each element in slice order and converts.  No workgroup waits on
+// another, and the sum order is fixed, so results are reproducible bit for bit.
 #include <type_traits>
 
 #include "common.hpp"
@@ -58,20 +68,31 @@ __device__ __forceinline__ int swz(int r) {
   else return swz8(r);
 }
 
-// Map a linear workgroup id to an output tile (tm, tn).  Consecutive ids are dealt
-// to the 8 XCDs in turn; they are regrouped so each XCD owns a contiguous range of
-// a grouped (G tile rows at a time) tile order.
-__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int* tm, int* tn) {
-  const int T = tiles_m * tiles_n;
+// One work item: output tile (tm, tn) of problem b of the batch, K slice s.
+struct Item { int b, s, tm, tn; };
+
+// Map a linear work id to an item.  Consecutive ids are dealt to the 8 XCDs in turn;
+// they are regrouped so each XCD owns a contiguous range of the item order, in which
+// the K slices of one tile are adjacent and the tiles of one problem follow a grouped
+// (G tile rows at a time) order, so the tiles resident at once on an XCD share A and
+// B panels in its L2.
+__device__ __forceinline__ Item item_of(int wg, int total, int S, int tiles_m, int tiles_n) {
   int lin = wg;
-  if ((T & 7) == 0) lin = (wg & 7) * (T >> 3) + (wg >> 3);
+  if ((total & 7) == 0) lin = (wg & 7) * (total >> 3) + (wg >> 3);
+  Item it;
+  const int T = tiles_m * tiles_n;
+  it.s = lin % S;
+  const int r = lin / S;
+  it.b = r / T;
+  const int t = r - it.b * T;
   constexpr int G = 8;
-  const int group = lin / (G * tiles_n);
+  const int group = t / (G * tiles_n);
   const int first_m = group * G;
   const int gsize = min(G, tiles_m - first_m);
-  const int in_group = lin - group * G * tiles_n;
-  *tm = first_m + in_group % gsize;
-  *tn = in_group / gsize;
+  const int in_group = t - group * G * tiles_n;
+  it.tm = first_m + in_group % gsize;
+  it.tn = in_group / gsize;
+  return it;
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES>
@@ -100,10 +121,16 @@ struct Cfg {
   static_assert(STAGES >= 2 && (STAGES - 1) * LOADS < 64, "vmcnt range");
 };
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, bool BF16>
+// L problems of one shape stored back to back: A [L][M][K/2], sfA [L][M][K/32], B
+// [L][N][K/2], sfB [L][N][K/32].  Without SPLIT, D is [L][M][N] of the output type.
+// With SPLIT, the K stages are cut into S slices of (near) equal length, every
+// (problem, tile, slice) is one work item, and D is the fp32 partial-sum buffer
+// [L][S][M][N] that splitk_reduce_kernel folds into the output.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, bool BF16, bool SPLIT>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
-                  const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, void* __restrict__ D) {
+mxfp4_gemm_kernel(int M, int N, int K, int L, int S, const uint8_t* __restrict__ A,
+                  const uint8_t* __restrict__ sfA, const uint8_t* __restrict__ B,
+                  const uint8_t* __restrict__ sfB, void* __restrict__ D) {
   using C = Cfg<BM, BN, WM, WN, BK, STAGES>;
   constexpr int NWN = BN / WN;
   constexpr int FI = WM / 32, FJ = WN / 32;
@@ -118,17 +145,23 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   const int hi = lane >> 5, r32 = lane & 31;
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int T = tiles_m * tiles_n;
+  const int total = L * tiles_m * tiles_n * S;
   // Persistent: the grid is at most one workgroup per CU and each workgroup walks its
-  // tiles.  A tile's output stores drain while the next tile's copies and MFMAs run,
-  // instead of every CU writing its tile at the same moment.
-  for (int tile = blockIdx.x; tile < T; tile += gridDim.x) {
-  int tm, tn;
-  tile_of(tile, tiles_m, tiles_n, &tm, &tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  // work items.  A tile's output stores drain while the next tile's copies and MFMAs
+  // run, instead of every CU writing its tile at the same moment.
+  for (int work = blockIdx.x; work < total; work += gridDim.x) {
+  const Item it = item_of(work, total, S, tiles_m, tiles_n);
+  const int m0 = it.tm * BM, n0 = it.tn * BN;
 
   const int64_t lda = K / 2, ldsf = K / 32;
-  const int KS = K / BK;
+  // This item's K stages: ks0 .. ks0+KS-1 of the KT stages (KS >= 1: S <= KT).
+  const int KT = K / BK;
+  const int ks0 = (int)((int64_t)it.s * KT / S);
+  const int KS = (int)((int64_t)(it.s + 1) * KT / S) - ks0;
+  const uint8_t* Ab = A + (int64_t)it.b * M * lda + (int64_t)ks0 * C::ROWB;
+  const uint8_t* Bb = B + (int64_t)it.b * N * lda + (int64_t)ks0 * C::ROWB;
+  const uint8_t* sfAb = sfA + (int64_t)it.b * M * ldsf + (int64_t)ks0 * 4 * C::SDW;
+  const uint8_t* sfBb = sfB + (int64_t)it.b * N * ldsf + (int64_t)ks0 * 4 * C::SDW;
 
   // ---- copy sources: this lane's global rows / chunks for each of its copies ----
   const uint8_t* ga[C::IA];
@@ -137,13 +170,13 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   for (int i = 0; i < C::IA; ++i) {
     const int row = C::RPC * (wave * C::IA + i) + lane / C::CHUNKS;
     const int c = (lane % C::CHUNKS) ^ swz<C::CHUNKS>(row);
-    ga[i] = A + (int64_t)min(m0 + row, M - 1) * lda + c * 16;
+    ga[i] = Ab + (int64_t)min(m0 + row, M - 1) * lda + c * 16;
   }
 #pragma unroll
   for (int i = 0; i < C::IB; ++i) {
     const int row = C::RPC * (wave * C::IB + i) + lane / C::CHUNKS;
     const int c = (lane % C::CHUNKS) ^ swz<C::CHUNKS>(row);
-    gb[i] = B + (int64_t)min(n0 + row, N - 1) * lda + c * 16;
+    gb[i] = Bb + (int64_t)min(n0 + row, N - 1) * lda + c * 16;
   }
   // Scale copy z covers dword d = z / (rows/64) of 64 rows (block z % (rows/64)).  When
   // there are fewer copies than waves, waves repeat one (identical bytes, same place).
@@ -153,13 +186,13 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 #pragma unroll
   for (int j = 0; j < C::SCA; ++j) {
     const int z = (wave * C::SCA + j) % C::TSA, d = z / (BM / 64), blk = z % (BM / 64);
-    gsa[j] = sfA + (int64_t)min(m0 + 64 * blk + lane, M - 1) * ldsf + 4 * d;
+    gsa[j] = sfAb + (int64_t)min(m0 + 64 * blk + lane, M - 1) * ldsf + 4 * d;
     lsa[j] = C::SA_OFF + d * BM * 4 + 256 * blk;
   }
 #pragma unroll
   for (int j = 0; j < C::SCB; ++j) {
     const int z = (wave * C::SCB + j) % C::TSB, d = z / (BN / 64), blk = z % (BN / 64);
-    gsb[j] = sfB + (int64_t)min(n0 + 64 * blk + lane, N - 1) * ldsf + 4 * d;
+    gsb[j] = sfBb + (int64_t)min(n0 + 64 * blk + lane, N - 1) * ldsf + 4 * d;
     lsb[j] = C::SB_OFF + d * BN * 4 + 256 * blk;
   }
 
@@ -337,7 +370,9 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   // row, and is read back row-wise so each lane stores 16 contiguous bytes and a store
   // instruction writes 64/(PB/16) whole row segments.  Otherwise each group of four
   // goes out directly.
-  constexpr int ELEM = BF16 ? 2 : 4;
+  constexpr bool OUT_BF16 = BF16 && !SPLIT;
+  constexpr int ELEM = OUT_BF16 ? 2 : 4;
+  uint8_t* const Dt = static_cast<uint8_t*>(D) + (SPLIT ? (int64_t)it.b * S + it.s : (int64_t)it.b) * M * N * ELEM;
   constexpr int PB = (WN * ELEM < 256) ? WN * ELEM : 256;   // panel bytes per row
   constexpr int PW = PB / ELEM;                             // panel columns
   constexpr int RS = PB + 16;                               // LDS row stride
@@ -359,7 +394,7 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
             uint8_t* dst = region + (i * 32 + r32) * RS + (jj * 32 + 8 * g + 4 * hi) * ELEM;
             const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
             const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-            if constexpr (BF16) {
+            if constexpr (OUT_BF16) {
               typedef unsigned int v2u __attribute__((ext_vector_type(2)));
               *reinterpret_cast<v2u*>(dst) = v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
             } else {
@@ -373,7 +408,7 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
         const v4i val = *reinterpret_cast<const v4i*>(region + r * RS + ch * 16);
         const int m = mw + r, n = nw + p * PW + ch * (16 / ELEM);
         if (m < M && n < N)
-          *reinterpret_cast<v4i*>(static_cast<uint8_t*>(D) + ((int64_t)m * N + n) * ELEM) = val;
+          *reinterpret_cast<v4i*>(Dt + ((int64_t)m * N + n) * ELEM) = val;
       }
     }
   } else {
@@ -387,7 +422,7 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
           const int n = nw + j * 32 + 8 * g + 4 * hi;
           const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
           const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          if (m < M) store_out4<BF16>(D, (int64_t)m * N + n, N - n, v0, v1, v2, v3);
+          if (m < M) store_out4<OUT_BF16>(Dt, (int64_t)m * N + n, N - n, v0, v1, v2, v3);
         }
       }
     }
@@ -395,39 +430,114 @@ mxfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   // No wave may start the next tile's copies into LDS while another still reads its
   // output panel.
   barrier_lds();
-  }  // tile loop
+  }  // work-item loop
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES>
-hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
+// D[b][i] = sum over s = 0, 1, .., S-1 (in that order) of P[b][s][i], i < MN, converted
+// to the output type.  VEC: four consecutive elements per lane (MN % 4 == 0).
+template <bool BF16, bool VEC>
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(int64_t MN, int L, int S, const float* __restrict__ P, void* __restrict__ D) {
+  constexpr int W = VEC ? 4 : 1;
+  const int64_t per = MN / W, total = per * L;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (int64_t)gridDim.x * 256) {
+    const int64_t b = u / per, i = (u - b * per) * W;
+    const float* p = P + b * S * MN + i;
+    if constexpr (VEC) {
+      v4f acc = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+      for (int s = 1; s < S; ++s) acc += __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + s * MN));
+      store_out4<BF16>(D, b * MN + i, 4, acc[0], acc[1], acc[2], acc[3]);
+    } else {
+      float acc = p[0];
+      for (int s = 1; s < S; ++s) acc += p[s * MN];
+      store_out<BF16>(D, b * MN + i, acc);
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPLIT>
+hipError_t launch_cfg(const FP4Args& a, int64_t L, int S, void* out, hipStream_t s) {
   using C = Cfg<BM, BN, WM, WN, BK, STAGES>;
-  const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, BN);
-  if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
-  const unsigned grid = (unsigned)(tiles < device_cus() ? tiles : device_cus());
-  if (a.bf16_out)
-    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, BK, STAGES, true>), dim3(grid), dim3(C::NT),
-                       0, s, (int)a.M, (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
+  const int64_t items = L * ceil_div(a.M, BM) * ceil_div(a.N, BN) * S;
+  if (items > INT32_MAX) return hipErrorInvalidConfiguration;
+  const unsigned grid = (unsigned)(items < device_cus() ? items : device_cus());
+  if (SPLIT || !a.bf16_out)
+    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, BK, STAGES, false, SPLIT>), dim3(grid), dim3(C::NT),
+                       0, s, (int)a.M, (int)a.N, (int)a.K, (int)L, S, a.A, a.sfA, a.B, a.sfB, out);
   else
-    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, BK, STAGES, false>), dim3(grid), dim3(C::NT),
-                       0, s, (int)a.M, (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
+    hipLaunchKernelGGL((mxfp4_gemm_kernel<BM, BN, WM, WN, BK, STAGES, true, false>), dim3(grid), dim3(C::NT),
+                       0, s, (int)a.M, (int)a.N, (int)a.K, (int)L, S, a.A, a.sfA, a.B, a.sfB, out);
   return hipGetLastError();
 }
 
+hipError_t launch_reduce(const FP4Args& a, int64_t L, int S, const float* P, hipStream_t s) {
+  const int64_t MN = a.M * a.N;
+  const bool vec = MN % 4 == 0;
+  const int64_t units = L * (vec ? MN / 4 : MN);
+  const int64_t cap = device_cus() * 8;
+  const unsigned grid = (unsigned)(ceil_div(units, 256) < cap ? ceil_div(units, 256) : cap);
+  if (a.bf16_out) {
+    if (vec) hipLaunchKernelGGL((splitk_reduce_kernel<true, true>), dim3(grid), dim3(256), 0, s, MN, (int)L, S, P, a.D);
+    else hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), dim3(grid), dim3(256), 0, s, MN, (int)L, S, P, a.D);
+  } else {
+    if (vec) hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), dim3(grid), dim3(256), 0, s, MN, (int)L, S, P, a.D);
+    else hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), dim3(grid), dim3(256), 0, s, MN, (int)L, S, P, a.D);
+  }
+  return hipGetLastError();
+}
+
+// K stages of the 128 x 128 configuration that the split path uses.
+int64_t split_stages(int64_t K) { return K % 256 == 0 ? K / 256 : K / 128; }
+
 }  // namespace
 
-hipError_t launch_mxfp4_gemm(const FP4Args& a, hipStream_t s) {
-  const int64_t t256 = ceil_div(a.M, 256) * ceil_div(a.N, 256);
-  const int64_t t128 = ceil_div(a.M, 128) * ceil_div(a.N, 128);
+int64_t mxfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t requested, int64_t cap) {
+  const int64_t KT = split_stages(K);
+  int64_t smax = KT < kMaxSplits ? KT : kMaxSplits;
+  if (cap < smax) smax = cap;
+  if (smax < 2 || L * M * N == 0) return 1;
+  if (requested > 0) return requested < smax ? requested : smax;
+  // Automatic choice.  Problems that already fill the chip with 256 x 256 tiles are not
+  // split.  Otherwise model the time of the 128 x 128 path as (rounds of work items over
+  // the CUs) x (stages per item + a fixed cost per item) plus the reduction's HBM
+  // traffic, and take the cheapest S; one slice needs at least 4 stages.
+  const int64_t cus = device_cus();
+  if (L * ceil_div(M, 256) * ceil_div(N, 256) >= cus) return 1;
+  const int64_t items = L * ceil_div(M, 128) * ceil_div(N, 128);
+  const double stage_us = 0.6 * (K % 256 == 0 ? 1.0 : 0.5), item_us = 2.0 * stage_us;
+  const double bytes_per_us = 4.0e6;
+  int64_t best = 1;
+  double best_t = 0;
+  for (int64_t S = 1; S <= smax && (S == 1 || KT / S >= 4); ++S) {
+    const double rounds = (double)ceil_div(items * S, cus);
+    double t = rounds * ((double)KT / S * stage_us + item_us);
+    if (S > 1) t += (double)(L * M * N) * 4.0 * (S + 1) / bytes_per_us;
+    if (S == 1 || t < best_t) { best = S; best_t = t; }
+  }
+  return best;
+}
+
+hipError_t launch_mxfp4_gemm_batched(const FP4Args& a, int64_t L, int64_t S, float* P, hipStream_t s) {
   const bool k256 = a.K % 256 == 0;
+  if (S > 1) {
+    hipError_t e = k256 ? launch_cfg<128, 128, 64, 64, 256, 2, true>(a, L, (int)S, P, s)
+                        : launch_cfg<128, 128, 64, 64, 128, 4, true>(a, L, (int)S, P, s);
+    if (e != hipSuccess) return e;
+    return launch_reduce(a, L, (int)S, P, s);
+  }
+  const int64_t t256 = L * ceil_div(a.M, 256) * ceil_div(a.N, 256);
+  const int64_t t128 = L * ceil_div(a.M, 128) * ceil_div(a.N, 128);
   if (t256 >= 256) {
-    if (k256) return launch_cfg<256, 256, 128, 128, 256, 2>(a, s);
-    return launch_cfg<256, 256, 128, 128, 128, 4>(a, s);
+    if (k256) return launch_cfg<256, 256, 128, 128, 256, 2, false>(a, L, 1, a.D, s);
+    return launch_cfg<256, 256, 128, 128, 128, 4, false>(a, L, 1, a.D, s);
   }
   if (t128 >= 128) {
-    if (k256) return launch_cfg<128, 128, 64, 64, 256, 2>(a, s);
-    return launch_cfg<128, 128, 64, 64, 128, 4>(a, s);
+    if (k256) return launch_cfg<128, 128, 64, 64, 256, 2, false>(a, L, 1, a.D, s);
+    return launch_cfg<128, 128, 64, 64, 128, 4, false>(a, L, 1, a.D, s);
   }
-  return launch_cfg<64, 64, 32, 32, 128, 4>(a, s);
+  return launch_cfg<64, 64, 32, 32, 128, 4, false>(a, L, 1, a.D, s);
 }
+
+hipError_t launch_mxfp4_gemm(const FP4Args& a, hipStream_t s) { return launch_mxfp4_gemm_batched(a, 1, 1, nullptr, s); }
 
 }  // namespace fp4g

@@ -46,6 +46,7 @@
 #ifndef FP4GEMM_H
 #define FP4GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -76,6 +77,42 @@ fp4g_status mx_fp4_gemm(int64_t M, int64_t N, int64_t K,
                         const void *A, const void *sfA,
                         const void *B, const void *sfB,
                         void *D, int d_type, void *stream);
+
+/* Batched MXFP4 GEMM with an optional split of K.  The problem shape is
+ * (M, N, K, L), L the batch count, all four runtime values (the Hopper
+ * CUTLASS/CuTe DSL blog post, section "How a kernel is assembled"): L
+ * independent MXFP4 products of one shape, stored back to back:
+ *   A [L][M][K/2], sfA [L][M][K/32], B [L][N][K/2], sfB [L][N][K/32],
+ *   D [L][M][N] of d_type.
+ * When the output tiles are too few to fill the GPU (skinny or small problems;
+ * the post's introduction names a stream-K scheduler as the load-balancing
+ * variant of the persistent one), the K loop is cut into s slices whose fp32
+ * partial sums go to `workspace` and are then added in slice order.
+ *   splits     0: the library chooses s for the current device; 1: no split;
+ *              s > 1: s slices.  s is clamped to 16, to the number of K stages
+ *              (K/256 when K % 256 == 0, else K/128) and to what the workspace
+ *              holds; below 2 nothing is split.
+ *   workspace  caller-owned device memory of workspace_bytes (16-byte aligned,
+ *              not overlapping any input or D), or NULL with 0 bytes.  A split
+ *              into s slices uses L*s*M*N*4 bytes.  Its contents on entry are
+ *              ignored and on return undefined; calls in flight at the same time
+ *              must not share a workspace.
+ * For a given s the result is reproducible bit for bit; different s round
+ * differently, each within fp32 accumulation error.  L == 0 behaves like
+ * M == 0; L < 0 or L*M, L*N >= 2^31 is FP4G_EINVAL.  With L == 1 and no split
+ * this is mx_fp4_gemm. */
+fp4g_status mx_fp4_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K,
+                                const void *A, const void *sfA,
+                                const void *B, const void *sfB,
+                                void *D, int d_type, int64_t splits,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace that mx_fp4_gemm_batched with these sizes and `splits` uses on the
+ * current device when given as much as it wants: L*s*M*N*4 bytes for the split s
+ * it would pick, 0 when it would not split.  Writes *bytes; sizes are checked as
+ * in mx_fp4_gemm_batched (FP4G_EINVAL, FP4G_EUNSUPPORTED; bytes may not be NULL). */
+fp4g_status mx_fp4_gemm_workspace_size(int64_t L, int64_t M, int64_t N, int64_t K,
+                                       int64_t splits, size_t *bytes);
 
 /* NVFP4 GEMM: V = 16, E4M3 scales, then D *= global_a * global_b.
  *   A [M][K/2], sfA [M][K/16], B [N][K/2], sfB [N][K/16], D [M][N]. */

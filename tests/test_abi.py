@@ -29,7 +29,8 @@ def lib():
 
 
 def test_header_declares_the_operations():
-    assert declared_functions() == sorted(["mx_fp4_gemm", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv",
+    assert declared_functions() == sorted(["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size",
+                                            "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv",
                                             "mx_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string"])
 
 
@@ -139,6 +140,48 @@ def test_quantizer_validation(lib):
     assert q(4, 64, A_, 0, B_ + 2, SB_, None) == EALIGN
     assert q(4, 64, A_, 0, A_ + 512, SB_, None) == EINVAL            # codes inside X (1 KB of fp32)
     assert q(4, 64, A_, 1, B_, B_ + 64, None) == EINVAL              # scales inside codes
+
+
+W_ = 0x10000000     # fake workspace address, far from the operands
+
+
+def mxb(lib, L, M, N, K, A=A_, sA=SA_, B=B_, sB=SB_, D=D_, dt=1, splits=0, ws=None, wsb=0):
+    return lib.mx_fp4_gemm_batched(L, M, N, K, A, sA, B, sB, D, dt, splits, ws, wsb, None)
+
+
+def test_batched_validation(lib):
+    assert mxb(lib, -1, 4, 4, 128) == EINVAL
+    assert mxb(lib, 2, 4, 4, 128, splits=-1) == EINVAL
+    assert mxb(lib, 1 << 20, 1 << 11, 4, 128) == EINVAL               # L*M = 2^31
+    assert mxb(lib, 2, 4, 4, 192) == EUNSUP
+    assert mxb(lib, 2, 4, 4, 128, dt=3) == EINVAL
+    assert mxb(lib, 0, 4, 4, 128, A=None, sA=None, B=None, sB=None, D=None) == OK
+    assert mxb(lib, 2, 4, 4, 128, ws=None, wsb=64) == EINVAL          # bytes without memory
+    assert mxb(lib, 2, 4, 4, 128, A=None) == EINVAL
+    assert mxb(lib, 2, 4, 4, 128, sB=SB_ + 2) == EALIGN
+    # D inside the second problem of A: A spans L*M*K/2 = 2*4*512 bytes
+    assert mxb(lib, 2, 4, 4, 1024, D=A_ + 2048) == EINVAL
+    # workspace checks apply only when a split may run (splits != 1, bytes > 0)
+    assert mxb(lib, 2, 4, 4, 1024, splits=2, ws=W_ + 8, wsb=4096) == EALIGN
+    assert mxb(lib, 2, 4, 4, 1024, splits=2, ws=D_, wsb=4096) == EINVAL   # overlaps D
+    assert mxb(lib, 2, 4, 4, 1024, splits=2, ws=B_, wsb=4096) == EINVAL   # overlaps B
+
+
+def test_workspace_size(lib):
+    n = ctypes.c_size_t(123)
+    f = lib.mx_fp4_gemm_workspace_size
+    assert f(2, 4, 4, 128, 0, None) == EINVAL
+    assert f(-1, 4, 4, 128, 0, ctypes.byref(n)) == EINVAL
+    assert f(1, 4, 4, 96, 0, ctypes.byref(n)) == EUNSUP
+    assert f(3, 128, 128, 4096, 1, ctypes.byref(n)) == OK and n.value == 0        # no split
+    assert f(3, 128, 128, 0, 4, ctypes.byref(n)) == OK and n.value == 0          # empty sum
+    assert f(3, 128, 128, 256, 4, ctypes.byref(n)) == OK and n.value == 0        # one K stage
+    assert f(3, 128, 128, 4096, 4, ctypes.byref(n)) == OK and n.value == 3 * 4 * 128 * 128 * 4
+    assert f(1, 64, 64, 8192, 100, ctypes.byref(n)) == OK and n.value == 16 * 64 * 64 * 4   # clamped
+    assert f(1, 64, 64, 640, 100, ctypes.byref(n)) == OK and n.value == 5 * 64 * 64 * 4     # K/128 stages
+    assert f(1, 8192, 8192, 8192, 0, ctypes.byref(n)) == OK and n.value == 0     # fills the GPU
+    assert f(1, 64, 8192, 8192, 0, ctypes.byref(n)) == OK
+    assert n.value > 0 and n.value % (64 * 8192 * 4) == 0 and n.value <= 16 * 64 * 8192 * 4
 
 
 def test_binding_rejects_host_tensors():
