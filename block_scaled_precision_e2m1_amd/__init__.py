@@ -23,13 +23,15 @@ import os
 
 import torch
 
-__all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
+__all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm",
+           "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
            "fp4g_status_string",
            "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfp4gemm.so")
-SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
+SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm",
+           "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
            "fp4g_status_string")
 
 OUT_F32, OUT_BF16 = 0, 1
@@ -65,6 +67,12 @@ def load_library():
     lib.mx_fp4_gemm_batched.restype = c_int
     lib.mx_fp4_gemm_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.mx_fp4_gemm_workspace_size.restype = c_int
+    lib.fp4_gemv_prepack_size.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+    lib.fp4_gemv_prepack_size.restype = c_int
+    lib.fp4_gemv_prepack.argtypes = [i64, i64, p, p, p, p, p]
+    lib.fp4_gemv_prepack.restype = c_int
+    lib.fp4_gemv_prepacked.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
+    lib.fp4_gemv_prepacked.restype = c_int
     lib.fp4_gemv.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.fp4_gemv.restype = c_int
     lib.nv_fp4_gemm.argtypes = [i64, i64, i64, p, p, f, p, p, f, p, c_int, p]
@@ -204,6 +212,55 @@ def fp4_gemv(A, sfA, B, sfB, out=None, out_dtype=torch.bfloat16):
     lib, dev, M, N, K, D, dt = _fp4_common("fp4_gemv", 32, A, sfA, B, sfB, out, out_dtype)
     st = lib.fp4_gemv(M, N, K, _ptr(A), _ptr(sfA), _ptr(B), _ptr(sfB), _ptr(D), dt, _stream(dev))
     _raise_on("fp4_gemv", st)
+    return D
+
+
+def fp4_gemv_prepack_size(N, K):
+    """(weight bytes, scale bytes) of the pre-packed layout of an N x K MXFP4 weight."""
+    wb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = load_library().fp4_gemv_prepack_size(N, K, ctypes.byref(wb), ctypes.byref(sb))
+    _raise_on("fp4_gemv_prepack_size", st)
+    return int(wb.value), int(sb.value)
+
+
+def fp4_gemv_prepack(B, sfB):
+    """Re-pack MXFP4 weights B [N, K/2] / sfB [N, K/32] into the GEMV's MFMA-register
+    order; returns (Bp, Sp) as flat uint8 device tensors."""
+    lib = load_library()
+    device = _device_of(B)
+    if B.dim() != 2:
+        raise ValueError("B must be 2-D")
+    N, K = B.shape[0], B.shape[1] * 2
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(B, "B", torch.uint8, (N, K // 2), device)
+    _check(sfB, "sfB", torch.uint8, (N, K // 32), device)
+    wb, sb = fp4_gemv_prepack_size(N, K)
+    Bp = torch.empty(wb, dtype=torch.uint8, device=device)
+    Sp = torch.empty(sb, dtype=torch.uint8, device=device)
+    st = lib.fp4_gemv_prepack(N, K, _ptr(B), _ptr(sfB), _ptr(Bp), _ptr(Sp), _stream(device))
+    _raise_on("fp4_gemv_prepack", st)
+    return Bp, Sp
+
+
+def fp4_gemv_prepacked(A, sfA, Bp, Sp, N, out=None, out_dtype=torch.bfloat16):
+    """fp4_gemv with weights from fp4_gemv_prepack (N weight rows); returns D [M, N]."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 2:
+        raise ValueError("A must be 2-D")
+    M, K = A.shape[0], A.shape[1] * 2
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(A, "A", torch.uint8, (M, K // 2), device)
+    _check(sfA, "sfA", torch.uint8, (M, K // 32), device)
+    wb, sb = fp4_gemv_prepack_size(N, K)
+    _check(Bp, "Bp", torch.uint8, (wb,), device)
+    _check(Sp, "Sp", torch.uint8, (sb,), device)
+    D = _out(out, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    st = lib.fp4_gemv_prepacked(M, N, K, _ptr(A), _ptr(sfA), _ptr(Bp), _ptr(Sp), _ptr(D), dt, _stream(device))
+    _raise_on("fp4_gemv_prepacked", st)
     return D
 
 

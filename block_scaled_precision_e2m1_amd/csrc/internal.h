@@ -53,6 +53,12 @@ hipError_t launch_mxfp4_gemm_batched(const FP4Args& a, int64_t L, int64_t S, flo
 int64_t mxfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t requested, int64_t cap);
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s);
 hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s);
+// Pre-packed decode weights: sizes, the load-time re-pack, and the GEMV over them
+// (a.B is the packed weight buffer; Sp the packed scale dwords).
+void gemv_prepack_sizes(int64_t N, int64_t K, int64_t* weight_bytes, int64_t* scale_bytes);
+hipError_t launch_gemv_prepack(int64_t N, int64_t K, const uint8_t* B, const uint8_t* sfB, uint8_t* Bp,
+                               uint32_t* Sp, hipStream_t s);
+hipError_t launch_fp4_gemv_prepacked(const FP4Args& a, const uint32_t* Sp, hipStream_t s);
 hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t s);
 hipError_t launch_fp8b_gemm(const Fp8bArgs& a, hipStream_t s);
 // D[M][N] = 0 (the empty-K product); never uses hipMemset so it can be captured.

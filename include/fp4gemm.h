@@ -150,6 +150,35 @@ fp4g_status fp4_gemv(int64_t M, int64_t N, int64_t K,
                      const void *B, const void *sfB,
                      void *D, int d_type, void *stream);
 
+/* Pre-packed decode weights (a load-time step, like the weight re-encoding and
+ * re-ordering that the Hopper CUTLASS/CuTe DSL blog post describes for W4A8 in
+ * section "The W4A8 kernel: the same four definitions, with the operands
+ * swapped").  The MXFP4 weight operand of fp4_gemv, B [N][K/2] and sfB [N][K/32],
+ * is re-ordered into the register layout of the 16x16x128 FP4 matrix
+ * instruction, with G = ceil(N/16) groups of 16 rows, KT = K/128 steps,
+ * KC = ceil(KT/4), and lane l = 16*slot + r (slot 0..3, r 0..15):
+ *   Bp bytes [G][KT][64 lanes][16]:  Bp[g][s][l][b] = B[16g+r][64s + 16*slot + b]
+ *   Sp dwords [G][KC][64 lanes]:     byte i of Sp[g][c][l] = sfB[16g+r][4(4c+i) + slot]
+ * Rows past N are zero codes with scale 127; steps past KT in the last chunk have
+ * scale 127.
+ *
+ * fp4_gemv_prepack_size: bytes of Bp (G*KT*1024) and Sp (G*KC*256); neither
+ *   pointer may be NULL.  Sizes as for fp4_gemv (K % 128 == 0).
+ * fp4_gemv_prepack: writes Bp and Sp from B and sfB on `stream`.  B 16-byte
+ *   aligned, sfB any alignment; Bp 16-byte and Sp 4-byte aligned, of the sizes
+ *   above; outputs must not overlap each other or the inputs.  N == 0 or K == 0
+ *   is a no-op.
+ * fp4_gemv_prepacked: fp4_gemv (1 <= M <= 16 tokens, same A, sfA and D layouts
+ *   and result) with the weights given as Bp and Sp.  Bp 16-byte and Sp 4-byte
+ *   aligned; D must not overlap any input.  M > 16 returns FP4G_EUNSUPPORTED. */
+fp4g_status fp4_gemv_prepack_size(int64_t N, int64_t K, size_t *weight_bytes, size_t *scale_bytes);
+fp4g_status fp4_gemv_prepack(int64_t N, int64_t K, const void *B, const void *sfB,
+                             void *Bp, void *Sp, void *stream);
+fp4g_status fp4_gemv_prepacked(int64_t M, int64_t N, int64_t K,
+                               const void *A, const void *sfA,
+                               const void *Bp, const void *Sp,
+                               void *D, int d_type, void *stream);
+
 /* MX quantizer: X[rows][K] (fp32 or bf16 by x_type) -> E2M1 codes [rows][K/2] (low
  * nibble = even k, the operand layout above) and E8M0 scales [rows][K/32].  It makes
  * the activation operand of mx_fp4_gemm and fp4_gemv from activations, the

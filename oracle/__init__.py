@@ -262,6 +262,34 @@ def mx_quantize(x):
     return codes, scales
 
 
+# ---- pre-packed decode weights ------------------------------------------------------------
+
+def gemv_prepack(B, sfB):
+    """The pre-packed layout of MXFP4 decode weights, from its definition: 16-row groups g,
+    128-element K steps s, 4-step scale chunks c, lanes l = 16*slot + r:
+      Bp[g][s][l][b] = B[16g + r][64s + 16*slot + b]
+      byte i of Sp[g][c][l] = sfB[16g + r][4(4c + i) + slot]
+    with rows past N given zero codes and scale 127, and steps past K/128 scale 127.
+    Returns (Bp, Sp) as flat uint8 arrays.  A byte permutation: no arithmetic."""
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    sfB = np.ascontiguousarray(sfB, dtype=np.uint8)
+    N, half = B.shape
+    K = half * 2
+    if K % 128 or sfB.shape != (N, K // 32):
+        raise ValueError("B must be [N][K/2] with K % 128 == 0 and sfB [N][K/32]")
+    G, KT = -(-N // 16), K // 128
+    KC = -(-KT // 4)
+    Bpad = np.zeros((16 * G, half), np.uint8)
+    Bpad[:N] = B
+    spad = np.full((16 * G, 4 * KC * 4), 127, np.uint8)     # [row][step*4 + slot], steps padded to 4*KC
+    spad[:N, :K // 32] = sfB
+    # B row 16g+r, bytes 64s + 16 slot + b  ->  [g][s][slot][r][b]
+    Bp = Bpad.reshape(G, 16, KT, 4, 16).transpose(0, 2, 3, 1, 4)
+    # sfB row 16g+r, byte 4(4c+i) + slot  ->  [g][c][slot][r][i]
+    Sp = spad.reshape(G, 16, KC, 4, 4).transpose(0, 2, 4, 1, 3)
+    return np.ascontiguousarray(Bp).reshape(-1), np.ascontiguousarray(Sp).reshape(-1)
+
+
 # ---- the comparison rule ---------------------------------------------------------------
 
 def ulp_bf16(x):

@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_operations():
     assert declared_functions() == sorted(["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size",
-                                            "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv",
+                                            "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "fp4_gemv_prepack_size",
+                                            "fp4_gemv_prepack", "fp4_gemv_prepacked",
                                             "mx_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string"])
 
 
@@ -182,6 +183,30 @@ def test_workspace_size(lib):
     assert f(1, 8192, 8192, 8192, 0, ctypes.byref(n)) == OK and n.value == 0     # fills the GPU
     assert f(1, 64, 8192, 8192, 0, ctypes.byref(n)) == OK
     assert n.value > 0 and n.value % (64 * 8192 * 4) == 0 and n.value <= 16 * 64 * 8192 * 4
+
+
+def test_prepack_validation(lib):
+    wb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    f = lib.fp4_gemv_prepack_size
+    assert f(37, 640, ctypes.byref(wb), ctypes.byref(sb)) == OK
+    assert wb.value == 3 * 5 * 1024 and sb.value == 3 * 2 * 256     # G = 3, KT = 5, KC = 2
+    assert f(37, 640, None, ctypes.byref(sb)) == EINVAL
+    assert f(-1, 640, ctypes.byref(wb), ctypes.byref(sb)) == EINVAL
+    assert f(4, 96, ctypes.byref(wb), ctypes.byref(sb)) == EUNSUP
+    p = lib.fp4_gemv_prepack
+    assert p(0, 128, None, None, None, None, None) == OK
+    assert p(4, 128, B_, SB_, None, D_, None) == EINVAL
+    assert p(4, 128, B_ + 4, SB_, A_, D_, None) == EALIGN
+    assert p(4, 128, B_, SB_, A_, D_ + 2, None) == EALIGN
+    assert p(4, 128, B_, SB_, B_, D_, None) == EINVAL                  # packed weights over B
+    assert p(4, 128, B_, SB_, A_, A_ + 512, None) == EINVAL            # Sp inside Bp (1 KB)
+    g = lib.fp4_gemv_prepacked
+    assert g(0, 16, 128, None, None, None, None, None, 1, None) == OK
+    assert g(17, 16, 128, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
+    assert g(4, 16, 128, A_, SA_, None, SB_, D_, 1, None) == EINVAL
+    assert g(4, 16, 128, A_, SA_, B_ + 8, SB_, D_, 1, None) == EALIGN
+    assert g(4, 16, 128, A_, SA_, B_, SB_ + 2, D_, 1, None) == EALIGN
+    assert g(4, 16, 128, A_, SA_, B_, SB_, B_ + 256, 1, None) == EINVAL   # D inside Bp
 
 
 def test_binding_rejects_host_tensors():
