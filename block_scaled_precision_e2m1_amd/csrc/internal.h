@@ -60,6 +60,12 @@ hipError_t launch_gemv_prepack(int64_t N, int64_t K, const uint8_t* B, const uin
                                uint32_t* Sp, hipStream_t s);
 hipError_t launch_fp4_gemv_prepacked(const FP4Args& a, const uint32_t* Sp, hipStream_t s);
 hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t s);
+// Pre-packed W4A8 weights: sizes, the load-time re-pack, and the GEMM over them
+// (a.B is the packed weight buffer, a.sB unused; Sp the packed fp32 scales).
+void w4a8_prepack_sizes(int64_t N, int64_t K, int64_t* weight_bytes, int64_t* scale_bytes);
+hipError_t launch_w4a8_prepack(int64_t N, int64_t K, const uint8_t* B, const uint16_t* sB, uint8_t* Bp, float* Sp,
+                               hipStream_t s);
+hipError_t launch_w4a8_gemm_prepacked(const W4A8Args& a, const float* Sp, hipStream_t s);
 hipError_t launch_fp8b_gemm(const Fp8bArgs& a, hipStream_t s);
 // D[M][N] = 0 (the empty-K product); never uses hipMemset so it can be captured.
 hipError_t launch_zero_fill(void* D, int64_t count, bool bf16_out, hipStream_t s);

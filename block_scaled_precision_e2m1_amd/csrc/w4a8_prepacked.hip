@@ -1,0 +1,264 @@
+// Pre-packed W4A8 weights and the GEMM that consumes them (gfx950).
+//
+// The W4A8 product is that of w4a8_gemm,
+//   D[m][n] = sa[m] * sum_g sB[n][g] * sum_{k in g} e4m3(A[m][k]) * int4(B[n][k]),
+// groups of 128 K elements.  The Hopper CUTLASS/CuTe DSL post (section "The W4A8
+// kernel: the same four definitions, with the operands swapped") reports that the
+// INT4 -> FP8 conversion method decides the kernel's speed, and that the fast
+// method needs the weights re-encoded and re-ordered, and the scales re-packed, once
+// when they are loaded.  This file is that load-time step and its kernel, designed
+// for gfx950:
+//
+// Re-pack.  A two's-complement nibble q = v - 8s (v = its low 3 bits, s = bit 3).
+// Within every run of 8 consecutive K elements the nibbles are re-ordered so that
+// byte j holds element j in its low nibble and element j+4 in its high nibble, and
+// the 16-row x 128-K operand of one 16x16x128 instruction is stored lane by lane:
+//   Bp[g16][kg][lane][16 B], lane = 16*slot + r, row 16*g16 + r,
+//   K = 128*kg + 32*slot + 8*w + (j or j+4) in byte 4*w + j;
+//   Sp[kg][n] = the group scale as fp32 (exact from bf16), n < 16*ceil(N/16).
+// Rows past N are zero with scale 0.
+//
+// Conversion.  With that order, eight nibbles in one dword x give two FP8 operands
+// exactly, with seven VALU instructions and no select between tables:
+//   E4M3(v): one v_perm_b32 table lookup of (x & 0x07070707), and of x >> 4;
+//   -s * 2^-6: (x & 0x08080808) | 0x80808080 (byte 0x88 = -2^-6, 0x80 = -0),
+//              taken by the MFMA with an E8M0 scale of 2^9, i.e. as -8s;
+// and v + (-8s) = q, so two chained FP8 MFMAs over the same activations compute
+// the group's exact INT4 product: the matrix pipe does twice the work and the
+// vector ALU a third of a two-table conversion.  (Splitting instead into 8 + v and
+// -8 - 8s, two bit-ORs, makes both halves about three times larger than q; the
+// instruction's inexact internal summation then came within 6% of the 1e-5 bar.)
+//
+// Kernel.  Workgroup tile BM = 64 tokens x 64 weight rows, 4 waves, wave w owning
+// weight rows 16w .. 16w+15 and all BM tokens (each weight converted once per
+// workgroup).
+// A stage is one K group: BM x 128 B of activations (16-byte chunks XOR-swizzled by
+// row), 4 x 1 KB of packed weights, 64 fp32 scales, copied HBM -> LDS by
+// global_load_lds into a 4-slot ring with counted waits and one barrier per group.
+// Weights are the first MFMA operand (v_mfma_scale_f32_16x16x128_f8f6f4, unit E8M0
+// scales), so a lane's four accumulators are four consecutive n of one token m; a
+// group's product goes to fresh registers and is folded into the fp32 accumulator
+// times sB[n][g] while the next group's MFMAs run.  The epilogue multiplies by sa[m].
+#include <type_traits>
+
+#include "common.hpp"
+#include "internal.h"
+
+namespace fp4g {
+namespace {
+
+constexpr int QBN = 64;          // weight rows per tile
+constexpr int QSTAGES = 4;
+
+template <int BM>
+struct QCfg {
+  static constexpr int FI = BM / 16;                // token blocks per wave
+  static constexpr int B_OFF = BM * 128;            // packed weights of the stage
+  static constexpr int S_OFF = B_OFF + QBN * 64;    // fp32 group scales
+  static constexpr int STAGE = S_OFF + 1024;
+  static constexpr int IA = BM * 128 / 1024 / 4;    // 1 KB activation copies per wave
+  static constexpr int LOADS = IA + 2;              // + one weight copy + the scale copy
+  static_assert(IA >= 1 && BM % 32 == 0, "tile");
+  static_assert(QSTAGES * STAGE <= 160 * 1024, "LDS budget");
+  static_assert((QSTAGES - 2) * LOADS < 64, "vmcnt range");
+};
+
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// E4M3 codes of 0..7 as a v_perm_b32 table: selector k picks byte k of {hi:lo}.
+constexpr uint32_t kE4M3Lo = 0x44403800u;   // 0, 1, 2, 3
+constexpr uint32_t kE4M3Hi = 0x4E4C4A48u;   // 4, 5, 6, 7
+constexpr int kScale2p9 = 0x88888888;       // E8M0 136 = 2^9 in every byte
+
+__global__ void __launch_bounds__(256)
+w4a8_prepack_weights_kernel(int64_t units, int N, int G, int64_t ld, const uint8_t* __restrict__ B,
+                            uint8_t* __restrict__ Bp) {
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256) {
+    const int l = (int)(u & 63);
+    const int64_t gk = u >> 6;
+    const int kg = (int)(gk % G);
+    const int64_t row = 16 * (gk / G) + (l & 15);
+    v4i out = v4i{0, 0, 0, 0};
+    if (row < N) {
+      const v4i in = *reinterpret_cast<const v4i*>(B + row * ld + (int64_t)kg * 64 + (l >> 4) * 16);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // nibble i of the dword is element 8w+i; byte j of the result = (elem j) | (elem j+4) << 4
+        const uint32_t x = (uint32_t)in[w];
+        uint32_t y = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y |= (((x >> (4 * j)) & 15u) | (((x >> (4 * j + 16)) & 15u) << 4)) << (8 * j);
+        out[w] = (int)y;
+      }
+    }
+    *reinterpret_cast<v4i*>(Bp + u * 16) = out;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+w4a8_prepack_scales_kernel(int64_t units, int N, int G, int64_t Np, const uint16_t* __restrict__ sB,
+                           float* __restrict__ Sp) {
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256) {
+    const int64_t n = u % Np, kg = u / Np;
+    Sp[u] = n < N ? __builtin_bit_cast(float, (uint32_t)sB[n * G + kg] << 16) : 0.0f;
+  }
+}
+
+template <int BM, bool BF16>
+__global__ void __launch_bounds__(256)
+w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sa,
+                  const uint8_t* __restrict__ Bp, const float* __restrict__ Sp, void* __restrict__ D) {
+  using C = QCfg<BM>;
+  constexpr int FI = C::FI;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[QSTAGES * C::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, slot = lane >> 4;
+
+  // Tile order: the token tiles of one weight panel are adjacent (they share it in
+  // L2); consecutive ids go to the 8 XCDs in turn and are regrouped per XCD.
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + QBN - 1) / QBN;
+  const int T = tiles_m * tiles_n;
+  int lin = blockIdx.x;
+  if ((T & 7) == 0) lin = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  const int m0 = (lin % tiles_m) * BM, n0 = (lin / tiles_m) * QBN;
+  const int G = K / 128;
+  const int G16 = (N + 15) / 16;
+  const int64_t Np = 16 * (int64_t)G16;
+
+  // ---- copy sources ----
+  const uint8_t* ga[C::IA];
+#pragma unroll
+  for (int i = 0; i < C::IA; ++i) {
+    const int row = 8 * (wave * C::IA + i) + (lane >> 3), u = lane & 7;
+    ga[i] = A + (int64_t)min(m0 + row, M - 1) * K + ((u ^ swz8(row)) << 4);
+  }
+  const uint8_t* gb = Bp + (int64_t)min(n0 / 16 + wave, G16 - 1) * G * 1024 + lane * 16;
+  const float* gs = Sp + min((int64_t)n0 + lane, Np - 1);
+
+  auto issue = [&](int g) {
+    const int gc = min(g, G - 1);                  // past the end: re-read the last group
+    uint8_t* base = smem + (g % QSTAGES) * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::IA; ++i) lds_copy16(ga[i] + (int64_t)gc * 128, (lds_void*)(base + (wave * C::IA + i) * 1024));
+    lds_copy16(gb + (int64_t)gc * 1024, (lds_void*)(base + C::B_OFF + wave * 1024));
+    lds_copy4(gs + (int64_t)gc * Np, (lds_void*)(base + C::S_OFF));   // every wave: identical bytes
+  };
+
+  v4f acc[FI];
+#pragma unroll
+  for (int i = 0; i < FI; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int unit = 0x7F7F7F7F;
+
+#pragma unroll
+  for (int p = 0; p < QSTAGES - 1; ++p) issue(p);
+
+  v4f part[2][FI];
+  v4f sc[2];
+  auto fold = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[i][t] = __builtin_fmaf(part[buf][i][t], sc[buf][t], acc[i][t]);
+  };
+  auto group = [&](int g, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
+    wait_vmcnt<(QSTAGES - 2) * C::LOADS>();
+    barrier_lds();
+    issue(g + QSTAGES - 1);
+    const uint8_t* base = smem + (g % QSTAGES) * C::STAGE;
+    // weight operand of this wave's 16 rows, and their scales (n = 16w + 4slot + t)
+    const v4i x = *reinterpret_cast<const v4i*>(base + C::B_OFF + wave * 1024 + lane * 16);
+    sc[BUF] = *reinterpret_cast<const v4f*>(base + C::S_OFF + (wave * 16 + 4 * slot) * 4);
+    v8i bv, bs;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = (uint32_t)x[w], hi = lo >> 4;
+      bv[2 * w] = (int)__builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, lo & 0x07070707u);
+      bv[2 * w + 1] = (int)__builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, hi & 0x07070707u);
+      bs[2 * w] = (int)((lo & 0x08080808u) | 0x80808080u);
+      bs[2 * w + 1] = (int)((hi & 0x08080808u) | 0x80808080u);
+    }
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const int row = 16 * i + r;
+      const v4i a0 = *reinterpret_cast<const v4i*>(base + row * 128 + (((2 * slot) ^ swz8(row)) << 4));
+      const v4i a1 = *reinterpret_cast<const v4i*>(base + row * 128 + (((2 * slot + 1) ^ swz8(row)) << 4));
+      const v8i af = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      part[BUF][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, af, v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
+                                                                      kFmtFp8, 0, unit, 0, unit);
+      part[BUF][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bs, af, part[BUF][i], kFmtFp8, kFmtFp8, 0,
+                                                                      kScale2p9, 0, unit);
+    }
+    if (g > 0) fold(BUF ^ 1);
+  };
+
+  int g = 0;
+  for (; g + 2 <= G; g += 2) {
+    group(g, std::integral_constant<int, 0>{});
+    group(g + 1, std::integral_constant<int, 1>{});
+  }
+  if (g < G) {
+    group(g, std::integral_constant<int, 0>{});
+    fold(0);
+  } else {
+    fold(1);
+  }
+  wait_vmcnt<0>();
+
+  // Epilogue: lane (slot, r) of token block i holds m = 16i + r and the four
+  // consecutive n = 16w + 4slot + 0..3.
+  const int n = n0 + wave * 16 + 4 * slot;
+#pragma unroll
+  for (int i = 0; i < FI; ++i) {
+    const int m = m0 + 16 * i + r;
+    if (m < M && n < N) {
+      const float s = sa[m];
+      store_out4<BF16>(D, (int64_t)m * N + n, N - n, acc[i][0] * s, acc[i][1] * s, acc[i][2] * s, acc[i][3] * s);
+    }
+  }
+}
+
+template <int BM>
+hipError_t launch_bm(const W4A8Args& a, const float* Sp, hipStream_t s) {
+  const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, QBN);
+  if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (a.bf16_out)
+    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, true>), dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, a.A, a.sa, a.B, Sp, a.D);
+  else
+    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, false>), dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, a.A, a.sa, a.B, Sp, a.D);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void w4a8_prepack_sizes(int64_t N, int64_t K, int64_t* weight_bytes, int64_t* scale_bytes) {
+  const int64_t G16 = ceil_div(N, 16), G = K / 128;
+  *weight_bytes = G16 * G * 1024;
+  *scale_bytes = G * 16 * G16 * 4;
+}
+
+hipError_t launch_w4a8_prepack(int64_t N, int64_t K, const uint8_t* B, const uint16_t* sB, uint8_t* Bp, float* Sp,
+                               hipStream_t s) {
+  const int64_t G16 = ceil_div(N, 16), G = K / 128, Np = 16 * G16;
+  const int64_t cap = device_cus() * 8;
+  const int64_t wu = G16 * G * 64, su = G * Np;
+  const unsigned gw = (unsigned)(ceil_div(wu, 256) < cap ? ceil_div(wu, 256) : cap);
+  const unsigned gs = (unsigned)(ceil_div(su, 256) < cap ? ceil_div(su, 256) : cap);
+  hipLaunchKernelGGL(w4a8_prepack_weights_kernel, dim3(gw), dim3(256), 0, s, wu, (int)N, (int)G, K / 2, B, Bp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(w4a8_prepack_scales_kernel, dim3(gs), dim3(256), 0, s, su, (int)N, (int)G, Np, sB, Sp);
+  return hipGetLastError();
+}
+
+// a.B is the packed weight buffer; Sp the packed fp32 scales.
+hipError_t launch_w4a8_gemm_prepacked(const W4A8Args& a, const float* Sp, hipStream_t s) {
+  // 64-token tiles: two or three workgroups share a CU (52 KB of LDS, 152 registers),
+  // which measured faster than 128-token tiles at every size tried (M = 128 .. 1024).
+  return launch_bm<64>(a, Sp, s);
+}
+
+}  // namespace fp4g

@@ -131,6 +131,35 @@ fp4g_status w4a8_gemm(int64_t M, int64_t N, int64_t K,
                       const void *B, const void *sB,
                       void *D, int d_type, void *stream);
 
+/* Pre-packed W4A8 weights (the load-time re-encoding and re-ordering of the
+ * weights and re-packing of the scales that the Hopper CUTLASS/CuTe DSL blog post
+ * describes for its fast INT4 -> FP8 conversion, section "The W4A8 kernel: the
+ * same four definitions, with the operands swapped").  With G16 = ceil(N/16)
+ * groups of 16 weight rows, KG = K/128 scale groups, lane = 16*slot + r:
+ *   Bp bytes [G16][KG][64 lanes][16]: the 32 INT4 nibbles of row 16*g16 + r,
+ *      K = 128*kg + 32*slot + 0..31, re-ordered so that byte 4*w + j holds element
+ *      8*w + j in its low nibble and element 8*w + j + 4 in its high nibble
+ *      (same two's-complement values);
+ *   Sp fp32 [KG][16*G16]: Sp[kg][n] = sB[n][kg] widened from bf16 (exact).
+ * Rows past N are zero with scale 0.
+ *
+ * w4a8_prepack_size: bytes of Bp (G16*KG*1024) and Sp (KG*16*G16*4); sizes as
+ *   for w4a8_gemm; neither pointer may be NULL.
+ * w4a8_prepack: writes Bp and Sp from B [N][K/2] and sB [N][K/128] (bf16 bits)
+ *   on `stream`.  B and Bp 16-byte aligned, sB 2-byte and Sp 4-byte aligned;
+ *   outputs must not overlap each other or the inputs.  N == 0 or K == 0 is a
+ *   no-op.
+ * w4a8_gemm_prepacked: w4a8_gemm (same A, sa and D layouts and result) with the
+ *   weights given as Bp and Sp.  A 16-byte aligned, sa, Bp and Sp as above; D
+ *   must not overlap any input. */
+fp4g_status w4a8_prepack_size(int64_t N, int64_t K, size_t *weight_bytes, size_t *scale_bytes);
+fp4g_status w4a8_prepack(int64_t N, int64_t K, const void *B, const void *sB,
+                         void *Bp, void *Sp, void *stream);
+fp4g_status w4a8_gemm_prepacked(int64_t M, int64_t N, int64_t K,
+                                const void *A, const float *sa,
+                                const void *Bp, const void *Sp,
+                                void *D, int d_type, void *stream);
+
 /* FP8 blockwise-scaled GEMM, the FP8 starting point of the issue page ("What
  * Works"; "Scale Factor Granularity": FP8 scales cover 128 elements of K):
  *   D[m][n] = sum_g sA[m][g] * sB[n][g] * sum_{k in group g} e4m3(A[m][k]) * e4m3(B[n][k])

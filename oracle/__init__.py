@@ -290,6 +290,33 @@ def gemv_prepack(B, sfB):
     return np.ascontiguousarray(Bp).reshape(-1), np.ascontiguousarray(Sp).reshape(-1)
 
 
+def w4a8_prepack(B, sB):
+    """The pre-packed W4A8 weight layout, from its definition: 16-row groups g16, K
+    groups kg of 128, lanes l = 16*slot + r; the 32 nibbles of row 16*g16 + r at
+    K = 128*kg + 32*slot + 0..31 stored with byte 4*w + j holding element 8*w + j (low
+    nibble) and element 8*w + j + 4 (high nibble); scales Sp[kg][n] = sB[n][kg] as fp32.
+    Rows past N are zero codes with scale 0.  Returns (Bp uint8 flat, Sp float32 flat)."""
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    sB = np.ascontiguousarray(sB)
+    if sB.dtype != np.uint16:
+        raise TypeError("sB must hold raw bf16 bits as uint16")
+    N, half = B.shape
+    K = 2 * half
+    if K % 128 or sB.shape != (N, K // 128):
+        raise ValueError("B must be [N][K/2] with K % 128 == 0 and sB [N][K/128]")
+    G16, KG = -(-N // 16), K // 128
+    nib = np.zeros((16 * G16, K), np.uint8)
+    nib[:N, 0::2] = B & 0xF            # element 2j: low nibble of byte j
+    nib[:N, 1::2] = B >> 4
+    # row 16g+r, K = 128kg + 32slot + 8w + 4h + j  ->  [g][r][kg][slot][w][h][j]
+    v = nib.reshape(G16, 16, KG, 4, 4, 2, 4)
+    byte = v[..., 0, :] | (v[..., 1, :] << 4)           # [g][r][kg][slot][w][j]
+    Bp = byte.transpose(0, 2, 3, 1, 4, 5)                 # [g][kg][slot][r][w][j]
+    sf = np.zeros((16 * G16, KG), np.float32)
+    sf[:N] = (sB.astype(np.uint32) << 16).view(np.float32)
+    return np.ascontiguousarray(Bp).reshape(-1), np.ascontiguousarray(sf.T).reshape(-1)
+
+
 # ---- the comparison rule ---------------------------------------------------------------
 
 def ulp_bf16(x):

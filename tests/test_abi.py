@@ -32,6 +32,7 @@ def test_header_declares_the_operations():
     assert declared_functions() == sorted(["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size",
                                             "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "fp4_gemv_prepack_size",
                                             "fp4_gemv_prepack", "fp4_gemv_prepacked",
+                                            "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
                                             "mx_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string"])
 
 
@@ -207,6 +208,28 @@ def test_prepack_validation(lib):
     assert g(4, 16, 128, A_, SA_, B_ + 8, SB_, D_, 1, None) == EALIGN
     assert g(4, 16, 128, A_, SA_, B_, SB_ + 2, D_, 1, None) == EALIGN
     assert g(4, 16, 128, A_, SA_, B_, SB_, B_ + 256, 1, None) == EINVAL   # D inside Bp
+
+
+def test_w4a8_prepack_validation(lib):
+    wb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    f = lib.w4a8_prepack_size
+    assert f(20, 384, ctypes.byref(wb), ctypes.byref(sb)) == OK
+    assert wb.value == 2 * 3 * 1024 and sb.value == 3 * 32 * 4          # G16 = 2, KG = 3
+    assert f(20, 384, ctypes.byref(wb), None) == EINVAL
+    assert f(20, 200, ctypes.byref(wb), ctypes.byref(sb)) == EUNSUP
+    p = lib.w4a8_prepack
+    assert p(0, 128, None, None, None, None, None) == OK
+    assert p(4, 128, B_, None, A_, D_, None) == EINVAL
+    assert p(4, 128, B_, SB_ + 1, A_, D_, None) == EALIGN
+    assert p(4, 128, B_, SB_, A_ + 8, D_, None) == EALIGN
+    assert p(4, 128, B_, SB_, A_, B_, None) == EINVAL                   # Sp over B
+    g = lib.w4a8_gemm_prepacked
+    assert g(0, 16, 128, None, None, None, None, None, 1, None) == OK
+    assert g(4, 16, 192, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
+    assert g(4, 16, 128, A_, None, B_, SB_, D_, 1, None) == EINVAL
+    assert g(4, 16, 128, A_ + 4, SA_, B_, SB_, D_, 1, None) == EALIGN
+    assert g(4, 16, 128, A_, SA_, B_, SB_ + 2, D_, 1, None) == EALIGN
+    assert g(4, 16, 128, A_, SA_, B_, SB_, SB_ + 32, 1, None) == EINVAL   # D inside Sp (64 B)
 
 
 def test_binding_rejects_host_tensors():
