@@ -8,16 +8,18 @@
 //
 // gfx950 has no hardware E4M3-per-16 block scale (its scaled MFMA takes E8M0 per
 // 32), and e2m1 * e4m3 needs up to 6 significant bits, more than any 8-bit
-// float holds.  The exact fold is into bf16 (8 significant bits): each element
-// is widened with v_cvt_scalef32_pk_f32_fp4, multiplied by its decoded fp32
-// scale (exact), and truncated to bf16 (exact, the low 16 bits are zero).  The
-// folded tiles are written to LDS and consumed by v_mfma_f32_16x16x32_bf16 with
-// fp32 accumulation; gA*gB multiplies the accumulator in the epilogue.
+// float holds.  The exact fold is into fp16 (11 significant bits; every product
+// e2m1 * e4m3 lies in [2^-10, 2880], inside fp16's normal range): the scale
+// s = 2^e * m (1 <= m < 2, 3 fraction bits) is applied in two exact steps,
+// v_cvt_scalef32_pk_f16_fp4 (which widens two codes and multiplies them by the
+// power of two of its fp32 scale operand: 2^e) and one v_pk_mul_f16 by (m, m).
+// The folded tiles are written to LDS and consumed by v_mfma_f32_16x16x32_f16
+// with fp32 accumulation; gA*gB multiplies the accumulator in the epilogue.
 //
 // Structure: one workgroup per BM x BN tile, 4 waves of WM x WN; 64 K elements
 // (32 packed bytes, one scale dword) per row per step; the packed tile for the
 // next step is prefetched into registers while the MFMAs of the current one run;
-// LDS rows are 128 bytes (64 bf16) with 16-byte chunks XOR-swizzled by row.
+// LDS rows are 128 bytes (64 fp16) with 16-byte chunks XOR-swizzled by row.
 #include "common.hpp"
 #include "internal.h"
 
@@ -27,33 +29,31 @@ namespace {
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 64;             // K elements per step
-constexpr int kRowBf = kBK * 2;     // 128 bytes of bf16 per LDS row
+constexpr int kRowH = kBK * 2;     // 128 bytes of fp16 per LDS row
 
 __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
-// Exact E4M3 (OCP, bias 7) decode to fp32.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t s = (b >> 7) & 1u, E = (b >> 3) & 15u, Mt = b & 7u;
-  if (E == 15u && Mt == 7u) return __builtin_nanf("");
-  float mag;
-  if (E == 0u) mag = (float)Mt * 0x1p-9f;
-  else mag = __builtin_bit_cast(float, ((E + 120u) << 23) | (Mt << 20));
-  return s ? -mag : mag;
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// An E4M3 scale byte as the two factors of the fold: `pow2` (fp32; only its power
+// of two is used by the conversion) and `mant` = (m, m) in fp16 with the scale's
+// sign.  A NaN code (0x7F / 0xFF) gives mant = NaN, so the block's products are NaN.
+__device__ __forceinline__ void e4m3_split(uint32_t b, float* pow2, h2* mant) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+  const uint32_t u = __builtin_bit_cast(uint32_t, s);
+  uint32_t m16 = 0x3C00u | ((u >> 13) & 0x3FFu) | ((u >> 16) & 0x8000u);
+  if ((b & 0x7Fu) == 0x7Fu) m16 = 0x7E00u;
+  *pow2 = s;
+  *mant = __builtin_bit_cast(h2, m16 | (m16 << 16));
 }
 
-// 4 packed bytes (8 E2M1 codes) times one fp32 scale -> 8 bf16 in 4 dwords.
-__device__ __forceinline__ void fold8(uint32_t w, float sc, uint32_t* out) {
-#pragma unroll
-  for (int byte = 0; byte < 4; ++byte) {
-    v2f f;
-    if (byte == 0) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-    else if (byte == 1) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-    else if (byte == 2) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-    else f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-    const uint32_t lo = __builtin_bit_cast(uint32_t, f[0] * sc);
-    const uint32_t hi = __builtin_bit_cast(uint32_t, f[1] * sc);
-    out[byte] = (hi & 0xFFFF0000u) | (lo >> 16);
-  }
+// 4 packed bytes (8 E2M1 codes) times one E4M3 scale -> 8 fp16 in 4 dwords.
+__device__ __forceinline__ void fold8(uint32_t w, float pow2, h2 mant, uint32_t* out) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 0) * mant);
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 1) * mant);
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 2) * mant);
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 3) * mant);
 }
 
 template <int BM, int BN, int WM, int WN, bool BF16>
@@ -66,7 +66,7 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   constexpr int CH = (BM + BN) * 2 / NT;   // 16-byte packed chunks per thread per step
   constexpr int FI = WM / 16, FJ = WN / 16;
   static_assert(CH >= 1 && (BM + BN) * 2 % NT == 0, "tile/threads mismatch");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * kRowBf];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * kRowH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / NWN, wn = wave % NWN;
@@ -87,7 +87,7 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
     const int grow = isA ? min(m0 + row, M - 1) : min(n0 + row - BM, N - 1);
     gsrc[i] = (isA ? A : B) + (int64_t)grow * ld + c * 16;
     gscl[i] = (isA ? sfA : sfB) + (int64_t)grow * lds_ + c * 2;
-    ldst[i] = row * kRowBf + c * 64;   // 32 bf16 = 4 logical 16-byte chunks 4c..4c+3
+    ldst[i] = row * kRowH + c * 64;   // 32 fp16 = 4 logical 16-byte chunks 4c..4c+3
   }
 
   v4i pk[CH];
@@ -103,13 +103,16 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int row = (tid + i * NT) >> 1, c = (tid + i * NT) & 1;
-      const float s0 = e4m3_to_f32(ps[i] & 0xFFu), s1 = e4m3_to_f32(ps[i] >> 8);
+      float p0, p1;
+      h2 m0, m1;
+      e4m3_split(ps[i] & 0xFFu, &p0, &m0);
+      e4m3_split(ps[i] >> 8, &p1, &m1);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {   // dword d: elements 8d..8d+7 of the 32
         uint32_t out[4];
-        fold8((uint32_t)pk[i][d], d < 2 ? s0 : s1, out);
+        fold8((uint32_t)pk[i][d], d < 2 ? p0 : p1, d < 2 ? m0 : m1, out);
         const int chunk = 4 * c + d;
-        *reinterpret_cast<v4i*>(&lds[st][row * kRowBf + ((chunk ^ swz8(row)) << 4)]) =
+        *reinterpret_cast<v4i*>(&lds[st][row * kRowH + ((chunk ^ swz8(row)) << 4)]) =
             v4i{(int)out[0], (int)out[1], (int)out[2], (int)out[3]};
       }
     }
@@ -130,22 +133,22 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int chunk = 4 * sub + slot;
-      v8bf af[FI], bf[FJ];
+      v8h af[FI], bf[FJ];
 #pragma unroll
       for (int i = 0; i < FI; ++i) {
         const int row = wm * WM + i * 16 + r16;
-        af[i] = *reinterpret_cast<const v8bf*>(&lds[st][row * kRowBf + ((chunk ^ swz8(row)) << 4)]);
+        af[i] = *reinterpret_cast<const v8h*>(&lds[st][row * kRowH + ((chunk ^ swz8(row)) << 4)]);
       }
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
         const int row = BM + wn * WN + j * 16 + r16;
-        bf[j] = *reinterpret_cast<const v8bf*>(&lds[st][row * kRowBf + ((chunk ^ swz8(row)) << 4)]);
+        bf[j] = *reinterpret_cast<const v8h*>(&lds[st][row * kRowH + ((chunk ^ swz8(row)) << 4)]);
       }
 #pragma unroll
       for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < FJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < KT) {
       store_lds(st ^ 1);

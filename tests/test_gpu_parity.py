@@ -264,6 +264,20 @@ def test_nvfp4_full_scale_range_including_subnormals():
     check_full("nv", d, "f32")
 
 
+def test_nvfp4_nan_scale_codes():
+    """A NaN scale code (0x7F or 0xFF) makes every product of its block NaN: the
+    rows and columns that meet it come out NaN, the rest stay finite."""
+    rng = np.random.default_rng(17)
+    d = datagen.random_nv(48, 40, 256, rng)
+    d["sfA"][3, 2] = 0x7F
+    d["sfB"][7, 5] = 0xFF
+    d.update({"M": 48, "N": 40, "K": 256})
+    D = as_np(run("nv", d, "f32"))
+    assert np.isnan(D[3]).all() and np.isnan(D[:, 7]).all()
+    assert np.isfinite(np.delete(np.delete(D, 3, axis=0), 7, axis=1)).all()
+    check_full("nv", d, "f32")
+
+
 # ---- W4A8 --------------------------------------------------------------------------------
 
 W4_SHAPES = [(1, 1, 128), (5, 70, 256), (64, 64, 128), (130, 65, 384), (256, 300, 1024), (300, 1000, 512),
