@@ -16,10 +16,12 @@
 // The folded tiles are written to LDS and consumed by v_mfma_f32_16x16x32_f16
 // with fp32 accumulation; gA*gB multiplies the accumulator in the epilogue.
 //
-// Structure: one workgroup per BM x BN tile, 4 waves of WM x WN; 64 K elements
-// (32 packed bytes, one scale dword) per row per step; the packed tile for the
-// next step is prefetched into registers while the MFMAs of the current one run;
+// Structure: one workgroup per BM x BN tile, 4 or 8 waves of WM x WN; 64 K elements
+// (32 packed bytes, one scale dword) per row per step; packed tiles are prefetched
+// into registers two steps ahead while the MFMAs of the current step run;
 // LDS rows are 128 bytes (64 fp16) with 16-byte chunks XOR-swizzled by row.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.h"
 
@@ -63,9 +65,10 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
                   void* __restrict__ D) {
   constexpr int NWN = BN / WN;
   constexpr int NT = (BM / WM) * NWN * 64;
-  constexpr int CH = (BM + BN) * 2 / NT;   // 16-byte packed chunks per thread per step
+  constexpr int CHUNKS = (BM + BN) * 2;     // 16-byte packed chunks per step
+  constexpr int CH = (CHUNKS + NT - 1) / NT; // per thread (the last round may leave threads idle)
   constexpr int FI = WM / 16, FJ = WN / 16;
-  static_assert(CH >= 1 && (BM + BN) * 2 % NT == 0, "tile/threads mismatch");
+  static_assert(CHUNKS % NT == 0 || CH == 1, "tile/threads mismatch");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * kRowH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -82,7 +85,7 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   int ldst[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int q = tid + i * NT, row = q >> 1, c = q & 1;
+    const int q = min(tid + i * NT, CHUNKS - 1), row = q >> 1, c = q & 1;
     const bool isA = row < BM;
     const int grow = isA ? min(m0 + row, M - 1) : min(n0 + row - BM, N - 1);
     gsrc[i] = (isA ? A : B) + (int64_t)grow * ld + c * 16;
@@ -90,27 +93,34 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
     ldst[i] = row * kRowH + c * 64;   // 32 fp16 = 4 logical 16-byte chunks 4c..4c+3
   }
 
-  v4i pk[CH];
-  uint32_t ps[CH];
-  auto load_global = [&](int kt) {
+  // Packed tiles are prefetched two steps ahead into two register buffers (RB = the
+  // buffer index, a compile-time constant so the arrays stay in registers); loads
+  // past the last step re-read it (in bounds, never used).
+  v4i pk[2][CH];
+  uint32_t ps[2][CH];
+  auto load_global = [&](int kt, auto rb_c) {
+    constexpr int RB = decltype(rb_c)::value;
+    const int kc = min(kt, KT - 1);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      pk[i] = *reinterpret_cast<const v4i*>(gsrc[i] + (int64_t)kt * 32);
-      ps[i] = *reinterpret_cast<const uint16_t*>(gscl[i] + kt * 4);
+      pk[RB][i] = *reinterpret_cast<const v4i*>(gsrc[i] + (int64_t)kc * 32);
+      ps[RB][i] = *reinterpret_cast<const uint16_t*>(gscl[i] + kc * 4);
     }
   };
-  auto store_lds = [&](int st) {
+  auto store_lds = [&](int st, auto rb_c) {
+    constexpr int RB = decltype(rb_c)::value;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
+      if (CHUNKS % NT != 0 && tid + i * NT >= CHUNKS) break;   // idle thread in a partial round
       const int row = (tid + i * NT) >> 1, c = (tid + i * NT) & 1;
       float p0, p1;
       h2 m0, m1;
-      e4m3_split(ps[i] & 0xFFu, &p0, &m0);
-      e4m3_split(ps[i] >> 8, &p1, &m1);
+      e4m3_split(ps[RB][i] & 0xFFu, &p0, &m0);
+      e4m3_split(ps[RB][i] >> 8, &p1, &m1);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {   // dword d: elements 8d..8d+7 of the 32
         uint32_t out[4];
-        fold8((uint32_t)pk[i][d], d < 2 ? p0 : p1, d < 2 ? m0 : m1, out);
+        fold8((uint32_t)pk[RB][i][d], d < 2 ? p0 : p1, d < 2 ? m0 : m1, out);
         const int chunk = 4 * c + d;
         *reinterpret_cast<v4i*>(&lds[st][row * kRowH + ((chunk ^ swz8(row)) << 4)]) =
             v4i{(int)out[0], (int)out[1], (int)out[2], (int)out[3]};
@@ -124,12 +134,7 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 #pragma unroll
     for (int j = 0; j < FJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  load_global(0);
-  store_lds(0);
-  if (KT > 1) load_global(1);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    __syncthreads();
+  auto compute = [&](int st) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int chunk = 4 * sub + slot;
@@ -150,11 +155,29 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
         for (int j = 0; j < FJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
+  };
+  // Step kt: the MFMAs of LDS buffer kt&1; then step kt+1 is folded from register
+  // buffer (kt+1)&1 into the other LDS buffer, and step kt+3 is fetched into it.
+  auto step = [&](int kt, auto rb_c) {
+    __syncthreads();
+    compute(kt & 1);
     if (kt + 1 < KT) {
-      store_lds(st ^ 1);
-      if (kt + 2 < KT) load_global(kt + 2);
+      store_lds((kt + 1) & 1, rb_c);
+      load_global(kt + 3, rb_c);
     }
+  };
+  const std::integral_constant<int, 0> R0{};
+  const std::integral_constant<int, 1> R1{};
+  load_global(0, R0);
+  load_global(1, R1);
+  store_lds(0, R0);
+  load_global(2, R0);
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    step(kt, R1);
+    step(kt + 1, R0);
   }
+  if (kt < KT) step(kt, R1);
 
 #pragma unroll
   for (int i = 0; i < FI; ++i)
@@ -188,7 +211,9 @@ hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
 
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s) {
   if (ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256) return launch_cfg<128, 128, 64, 64>(a, s);
-  return launch_cfg<64, 64, 32, 32>(a, s);
+  // Small problems: 64 x 64 tiles with 8 waves of 16 x 32, so each SIMD interleaves two
+  // waves' folds, LDS traffic and MFMAs (1024^3: 8.6 us, against 9.6 us with 4 waves).
+  return launch_cfg<64, 64, 16, 32>(a, s);
 }
 
 }  // namespace fp4g
