@@ -179,18 +179,25 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
       bs[2 * w] = (int)((lo & 0x08080808u) | 0x80808080u);
       bs[2 * w + 1] = (int)((hi & 0x08080808u) | 0x80808080u);
     }
+    v8i af[FI];
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
       const int row = 16 * i + r;
       const v4i a0 = *reinterpret_cast<const v4i*>(base + row * 128 + (((2 * slot) ^ swz8(row)) << 4));
       const v4i a1 = *reinterpret_cast<const v4i*>(base + row * 128 + (((2 * slot + 1) ^ swz8(row)) << 4));
-      const v8i af = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      part[BUF][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, af, v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
-                                                                      kFmtFp8, 0, unit, 0, unit);
-      part[BUF][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bs, af, part[BUF][i], kFmtFp8, kFmtFp8, 0,
-                                                                      kScale2p9, 0, unit);
+      af[i] = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     }
+    // All E4M3(v) products first, then the sign products that accumulate onto them, so
+    // no MFMA waits for the one just issued; the previous group's fold fills the gap.
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+      part[BUF][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, af[i], v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
+                                                                      kFmtFp8, 0, unit, 0, unit);
     if (g > 0) fold(BUF ^ 1);
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+      part[BUF][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bs, af[i], part[BUF][i], kFmtFp8, kFmtFp8, 0,
+                                                                      kScale2p9, 0, unit);
   };
 
   int g = 0;
