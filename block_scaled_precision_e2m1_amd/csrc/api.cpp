@@ -13,6 +13,9 @@ using fp4g::W4A8Args;
 using fp4g::Fp8bArgs;
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // each of M, N, K below 2^31
+// Output elements (L*M*N) at most 2^50: far past any device memory, and small enough
+// that every byte count below (times 4 bytes, times up to 16 split slices) fits int64.
+constexpr int64_t kMaxOut = (int64_t)1 << 50;
 
 struct Range { uintptr_t lo, hi; };
 
@@ -29,6 +32,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 fp4g_status check_common(int64_t M, int64_t N, int64_t K, int d_type, const void* D, bool* empty) {
   if (M < 0 || N < 0 || K < 0) return FP4G_EINVAL;
   if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP4G_EINVAL;
+  if (N > 0 && M > kMaxOut / N) return FP4G_EINVAL;
   if (d_type != FP4G_OUT_F32 && d_type != FP4G_OUT_BF16) return FP4G_EINVAL;
   if (K % 128 != 0) return FP4G_EUNSUPPORTED;
   *empty = (M == 0 || N == 0);
@@ -79,6 +83,7 @@ fp4g_status check_batched_sizes(int64_t L, int64_t M, int64_t N, int64_t K, int6
   if (L < 0 || L >= kMaxDim || splits < 0) return FP4G_EINVAL;
   if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP4G_EINVAL;
   if (L * M >= kMaxDim || L * N >= kMaxDim) return FP4G_EINVAL;
+  if (N > 0 && L * M > kMaxOut / N) return FP4G_EINVAL;
   if (K % 128 != 0) return FP4G_EUNSUPPORTED;
   *empty = (L == 0 || M == 0 || N == 0);
   return FP4G_OK;

@@ -38,7 +38,8 @@
  * per-call state, and may be called from several threads at once.
  * Validation failures return a status code and launch nothing.
  *
- * Sizes (all entry points): M, N, K >= 0 and below 2^31; K a multiple of 128
+ * Sizes (all entry points): M, N, K >= 0 and below 2^31, and M*N (L*M*N for
+ * the batched GEMM) at most 2^50 (FP4G_EINVAL otherwise); K a multiple of 128
  * (FP4G_EUNSUPPORTED otherwise).  M == 0 or N == 0 is an empty output: nothing
  * is read, written or launched, and the call returns FP4G_OK.  K == 0 is an
  * empty sum: D is set to zero and the inputs are not read (they may be NULL).

@@ -73,6 +73,12 @@ def test_invalid_sizes(lib):
     assert mx(lib, 4, 4, 100) == EUNSUP
 
 
+def test_output_size_limit(lib):
+    # 2^30 x 2^30 outputs would overflow the byte counts of the range checks: rejected
+    assert mx(lib, 1 << 30, 1 << 30, 128) == EINVAL
+    assert lib.mx_fp4_gemm_batched(4, 1 << 27, 1 << 27, 128, A_, SA_, B_, SB_, D_, 1, 0, None, 0, None) == EINVAL
+
+
 def test_bad_output_type(lib):
     assert mx(lib, 4, 4, 128, dt=2) == EINVAL
     assert mx(lib, 4, 4, 128, dt=-1) == EINVAL
