@@ -306,6 +306,7 @@ fp4g_status w4a8_gemm_prepacked(int64_t M, int64_t N, int64_t K, const void* A, 
 fp4g_status mx_fp4_quantize(int64_t rows, int64_t K, const void* X, int x_type, void* codes, void* scales,
                             void* stream) {
   if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim) return FP4G_EINVAL;
+  if (K > 0 && rows > kMaxOut / K) return FP4G_EINVAL;
   if (x_type != FP4G_IN_F32 && x_type != FP4G_IN_BF16) return FP4G_EINVAL;
   if (K % 32 != 0) return FP4G_EUNSUPPORTED;
   if (rows == 0 || K == 0) return FP4G_OK;

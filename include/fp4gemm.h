@@ -219,7 +219,8 @@ fp4g_status fp4_gemv_prepacked(int64_t M, int64_t N, int64_t K,
  *   code = the E2M1 value nearest to x * 2^(127 - e), ties to the even mantissa bit,
  *          magnitudes past 6 saturating to 6; a zero result is +0;
  *   a block holding an infinity or NaN gets scale 0xFF (NaN) and zero codes.
- * Requires K a multiple of 32 (FP4G_EUNSUPPORTED otherwise); X and codes 16-byte
+ * Requires rows*K <= 2^50 (FP4G_EINVAL otherwise) and K a multiple of 32
+ * (FP4G_EUNSUPPORTED otherwise); X and codes 16-byte
  * aligned; the three buffers must not overlap.  rows == 0 or K == 0 is a no-op. */
 fp4g_status mx_fp4_quantize(int64_t rows, int64_t K, const void *X, int x_type,
                             void *codes, void *scales, void *stream);

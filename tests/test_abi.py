@@ -148,6 +148,7 @@ def test_quantizer_validation(lib):
     assert q(4, 64, A_, 0, B_ + 2, SB_, None) == EALIGN
     assert q(4, 64, A_, 0, A_ + 512, SB_, None) == EINVAL            # codes inside X (1 KB of fp32)
     assert q(4, 64, A_, 1, B_, B_ + 64, None) == EINVAL              # scales inside codes
+    assert q(1 << 30, 1 << 30, A_, 0, B_, SB_, None) == EINVAL       # rows*K above 2^50
 
 
 W_ = 0x10000000     # fake workspace address, far from the operands
