@@ -174,6 +174,60 @@ def summarize_counters(fetch_dir, write_dir, command):
             f"per launch (scales {f_scale:.3f} / {w_scale:.3f})")
 
 
+# Utilisation counters: (workload key, kernel-name prefix, sources of the kernel).
+UTIL_KERNELS = [("mxfp4_gemm_8192x8192x8192", "mxfp4_gemm_kernel<256, 256, 128, 128, 256, 2, true, false>",
+                 ["mxfp4_gemm.hip", "common.hpp"]),
+                ("mxfp4_gemv_8x14336x4096", "fp4_gemv_kernel<1, 2, true, true>", ["fp4_gemv.hip", "common.hpp"]),
+                ("w4a8_256x8192x8192", "w4a8_gemm_kernel<", ["w4a8_gemm.hip", "common.hpp"]),
+                ("w4a8_256x8192x8192_prepacked", "w4a8p_gemm_kernel<", ["w4a8_prepacked.hip", "common.hpp"]),
+                ("fp8_blockwise_4096", "fp8b_gemm_kernel<", ["fp8b_gemm.hip", "common.hpp"]),
+                ("nvfp4_1024", "nvfp4_gemm_kernel<", ["nvfp4_gemm.hip", "common.hpp"]),
+                ("mx_quantize_8192x8192_f32", "mx_quantize_kernel<", ["mx_quantize.hip", "common.hpp"])]
+UTIL_METRICS = ("MfmaUtil", "LdsUtil", "VALUBusy", "LdsBankConflict")
+UTIL_FILE = os.path.join(PROFILES, "utilisation_counters.txt")
+
+
+def summarize_util(util_dir, command):
+    """Turn one rocprofv3 --pmc run of the derived metrics MfmaUtil, LdsUtil, VALUBusy and
+    LdsBankConflict (percent of the busy GPU's cycles; conflicts per LDS cycle) over
+    `bench.py --no-graph` into profiles/utilisation_counters.txt."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(util_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+            per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = {"command": command, "kernels": {}}
+    for key, prefix, src in UTIL_KERNELS:
+        hits = [c for n, c in per.items() if prefix in n]
+        if not hits:
+            continue
+        vals = {m: float(np.median([v for c in hits for v in c.get(m, [])])) for m in UTIL_METRICS
+                if any(m in c for c in hits)}
+        out["kernels"][key] = {"kernel": prefix, "kernel_src_sha": src_digest(*src), **vals}
+        log(f"{key}: " + ", ".join(f"{m} {v:.1f}" for m, v in vals.items()))
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(UTIL_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+
+def util_from_profile(key):
+    """MFMA/LDS/VALU utilisation of a workload's kernel from the committed counter
+    summary, if it was taken on the current kernel source; otherwise None."""
+    if not os.path.exists(UTIL_FILE):
+        return None
+    k = json.load(open(UTIL_FILE)).get("kernels", {}).get(key)
+    if k is None:
+        return None
+    src = next(src for kk, _, src in UTIL_KERNELS if kk == key)
+    if k["kernel_src_sha"] != src_digest(*src):
+        return None
+    return {"mfma_util_pct": k.get("MfmaUtil"), "lds_util_pct": k.get("LdsUtil"),
+            "valu_busy_pct": k.get("VALUBusy")}
+
+
 # ---- workloads ------------------------------------------------------------------------
 
 def bench_mx8192(steps, warmup, dev):
@@ -389,9 +443,15 @@ def main():
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/*_counters.txt from two rocprofv3 --pmc runs, then exit")
     ap.add_argument("--counters-command", default="", help="the profiling command, recorded with --counters")
+    ap.add_argument("--util", metavar="UTIL_DIR",
+                    help="write profiles/utilisation_counters.txt from a rocprofv3 --pmc run of "
+                         "MfmaUtil LdsUtil LdsBankConflict VALUBusy, then exit")
     args = ap.parse_args()
     if args.counters:
         summarize_counters(args.counters[0], args.counters[1], args.counters_command)
+        return
+    if args.util:
+        summarize_util(args.util, args.counters_command)
         return
     global USE_GRAPH
     USE_GRAPH = not args.no_graph
@@ -517,6 +577,13 @@ def main():
         if not args.no_cpu:
             log("bench: cpu oracle baseline ...")
             line["cpu_baseline"] = cpu_baseline(d8192)
+    # MFMA / LDS / VALU utilisation of each kernel from the committed counter run
+    # (null when the kernel changed since the counters were taken).
+    if "roofline" in line:
+        line["roofline"]["utilisation"] = util_from_profile("mxfp4_gemm_8192x8192x8192")
+    for key, entry in also.items():
+        if isinstance(entry, dict) and "roofline" in entry and any(key == k for k, _, _ in UTIL_KERNELS):
+            entry["roofline"]["utilisation"] = util_from_profile(key)
     line["also"] = also
     print(json.dumps(line), flush=True)
 
