@@ -13,9 +13,10 @@
 // consecutive blocks and one 2-byte store per lane writes 128 contiguous code
 // bytes.  The block maximum and the non-finite flag are reduced over the 8 lanes
 // with lane permutations (no LDS storage).  floor(log2 amax) comes from the
-// fp32 exponent field; x * 2^(127-e) is an exact v_ldexp_f32, and the rounding is
-// the count of grid midpoints passed (">" below a midpoint whose upper neighbour
-// has an odd code, ">=" where it is even).
+// fp32 exponent field, and the scaling and rounding of two elements are one
+// hardware conversion (v_cvt_scalef32_pk_fp4_f32) whose results were checked
+// against the rule on a sweep of values, ties and saturation included, and are
+// checked bit for bit against the oracle by the tests.
 #include "common.hpp"
 #include "internal.h"
 
@@ -81,16 +82,18 @@ mx_quantize_kernel(int64_t nblocks, const void* __restrict__ X, uint8_t* __restr
       bad = group8_max(bad);
       const int E = (int)(amax >> 23);                  // biased exponent of the block maximum
       const int e = amax == 0 ? 127 : (E - 2 > 0 ? E - 2 : 0);
-      uint32_t packed = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = __builtin_bit_cast(float, bits[u][i]);
-        const float y = __builtin_fabsf(__builtin_amdgcn_ldexpf(x, 127 - e));
-        uint32_t c = (y > 0.25f) + (y >= 0.75f) + (y > 1.25f) + (y >= 1.75f) + (y > 2.5f) + (y >= 3.5f) +
-                     (y > 5.0f);
-        if (c != 0 && (bits[u][i] >> 31)) c |= 8u;
-        packed |= c << (4 * i);
-      }
+      // v_cvt_scalef32_pk_fp4_f32 divides two values by the power of two of its scale
+      // operand (here 2^(e-127), whose exponent field is e) and rounds each to the
+      // nearest E2M1 value, ties to the even code, saturating at 6: the rule above.  It
+      // writes -0 (code 8) for a negative value that rounds to zero; the rule's zero
+      // is +0, so the sign bit of every zero magnitude is cleared.
+      const float scale = __builtin_bit_cast(float, (uint32_t)e << 23);
+      uint32_t packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, __builtin_bit_cast(float, bits[u][0]),
+                                                                __builtin_bit_cast(float, bits[u][1]), scale, 0);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, __builtin_bit_cast(float, bits[u][2]),
+                                                        __builtin_bit_cast(float, bits[u][3]), scale, 1);
+      const uint32_t nonzero = ((packed & 0x7777u) + 0x7777u) & 0x8888u;   // bit 3 of a nibble: magnitude != 0
+      packed &= nonzero | 0x7777u;
       if (bad) packed = 0;
       if (blk < nblocks) {
         *reinterpret_cast<uint16_t*>(codes + blk * 16 + sub * 2) = (uint16_t)packed;
