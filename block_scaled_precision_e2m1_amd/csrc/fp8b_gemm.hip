@@ -6,7 +6,7 @@
 // Works", and "Scale Factor Granularity": FP8 uses a granularity of 128 along K).
 //
 // gfx950 design:
-//   * workgroup tile 128 x 128, 4 waves in a 2 x 2 grid of 64 x 64; a stage is one
+//   * workgroup tile 128 x 128, 8 waves in a 2 x 4 grid of 64 x 32; a stage is one
 //     128-element group: 128 FP8 bytes (one cache line) per row of A and of B, and
 //     the group's 128 + 128 fp32 scales;
 //   * stages reach LDS through global->LDS copies (global_load_lds_dwordx4 for the
@@ -34,20 +34,25 @@ constexpr int F_B = FBN * 128;              // FP8 bytes of B per stage (16 KB)
 constexpr int F_SA = F_A + F_B;             // sA: 128 fp32
 constexpr int F_SB = F_SA + FBM * 4;        // sB: 128 fp32
 constexpr int F_STAGE = F_SB + FBN * 4;
-constexpr int F_LOADS = 4 + 4 + 1;          // copies per wave per stage: A, B, one scale copy
 static_assert(FSTAGES * F_STAGE <= 160 * 1024, "LDS budget");
-static_assert((FSTAGES - 2) * F_LOADS < 64, "vmcnt range");
+// Copies per wave per stage with W waves: 16/W of A and of B (1 KB each), one scale copy.
+template <int W>
+constexpr int f_loads() { return 2 * (16 / W) + 1; }
+static_assert((FSTAGES - 2) * f_loads<4>() < 64, "vmcnt range");
 
 __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
-template <bool BF16>
-__global__ void __launch_bounds__(256)
+// NWN waves along N (2 or 4): 2*NWN waves of 64 x (128/NWN).
+template <int NWN, bool BF16>
+__global__ void __launch_bounds__(2 * NWN * 64)
 fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
                  const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D) {
+  constexpr int W = 2 * NWN, CPW = 16 / W, WN = FBN / NWN, FJ = WN / 32;
+  constexpr int F_LOADS = f_loads<W>();
   __shared__ __attribute__((aligned(1024))) uint8_t smem[FSTAGES * F_STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int hi = lane >> 5, r32 = lane & 31;
 
   // Tile order: consecutive ids go to the 8 XCDs in turn; regroup so each XCD owns a
@@ -60,36 +65,38 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
   const int G = K / 128;
 
   // ---- copy sources: copy c (0..15) of an operand covers rows 8c .. 8c+7 ----
-  const uint8_t* ga[4];
-  const uint8_t* gb[4];
+  const uint8_t* ga[CPW];
+  const uint8_t* gb[CPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = wave * 4 + i;
+  for (int i = 0; i < CPW; ++i) {
+    const int c = wave * CPW + i;
     const int row = 8 * c + (lane >> 3), u = lane & 7;
     ga[i] = A + (int64_t)min(m0 + row, M - 1) * K + ((u ^ swz8(row)) << 4);
     gb[i] = B + (int64_t)min(n0 + row, N - 1) * K + ((u ^ swz8(row)) << 4);
   }
-  // Scale copy: wave w fetches 64 scales -- sA rows 0..63 / 64..127, sB rows 0..63 / 64..127.
-  const int srow = 64 * (wave & 1) + lane;
-  const float* gs = (wave < 2) ? sA + (int64_t)min(m0 + srow, M - 1) * G : sB + (int64_t)min(n0 + srow, N - 1) * G;
-  const int ls = ((wave < 2) ? F_SA : F_SB) + 256 * (wave & 1);
+  // Scale copy z = wave % 4 fetches 64 scales -- sA rows 0..63 / 64..127, sB rows 0..63 /
+  // 64..127; with 8 waves, waves z and z+4 write the same bytes to the same place.
+  const int sz = wave & 3;
+  const int srow = 64 * (sz & 1) + lane;
+  const float* gs = (sz < 2) ? sA + (int64_t)min(m0 + srow, M - 1) * G : sB + (int64_t)min(n0 + srow, N - 1) * G;
+  const int ls = ((sz < 2) ? F_SA : F_SB) + 256 * (sz & 1);
 
   auto issue = [&](int g) {
     const int gc = min(g, G - 1);                  // past the end: re-read the last group
     uint8_t* base = smem + (g % FSTAGES) * F_STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_copy16(ga[i] + (int64_t)gc * 128, (lds_void*)(base + (wave * 4 + i) * 1024));
+    for (int i = 0; i < CPW; ++i) lds_copy16(ga[i] + (int64_t)gc * 128, (lds_void*)(base + (wave * CPW + i) * 1024));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      lds_copy16(gb[i] + (int64_t)gc * 128, (lds_void*)(base + F_A + (wave * 4 + i) * 1024));
+    for (int i = 0; i < CPW; ++i)
+      lds_copy16(gb[i] + (int64_t)gc * 128, (lds_void*)(base + F_A + (wave * CPW + i) * 1024));
     lds_copy4(gs + gc, (lds_void*)(base + ls));
   };
 
-  v16f acc[2][2];
+  v16f acc[2][FJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < FJ; ++j) acc[i][j] = v16f{};
   const int unit = 0x7F7F7F7F;
 
 #pragma unroll
@@ -98,18 +105,18 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
   // Software pipeline: the MFMAs of group g run while the VALU folds group g-1's
   // partial sums (and their scales, read from LDS during iteration g-1) into the
   // accumulator, so the matrix pipe and the vector ALU overlap.
-  v16f part[2][2][2];                               // [buffer][i][j]
+  v16f part[2][2][FJ];                              // [buffer][i][j]
   float sa_r[2][2];                                 // [buffer][i]: sA of the lane's row
-  v4f sb_r[2][2][4];                                // [buffer][j][q]: sB of the lane's 16 columns
+  v4f sb_r[2][FJ][4];                               // [buffer][j][q]: sB of the lane's 16 columns
   auto read_scales = [&](const uint8_t* base, int buf) {
     const float* ssa = reinterpret_cast<const float*>(base + F_SA);
     const float* ssb = reinterpret_cast<const float*>(base + F_SB);
 #pragma unroll
     for (int i = 0; i < 2; ++i) sa_r[buf][i] = ssa[wm * 64 + i * 32 + r32];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FJ; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sb_r[buf][j][q] = *reinterpret_cast<const v4f*>(ssb + wn * 64 + j * 32 + 8 * q + 4 * hi);
+      for (int q = 0; q < 4; ++q) sb_r[buf][j][q] = *reinterpret_cast<const v4f*>(ssb + wn * WN + j * 32 + 8 * q + 4 * hi);
   };
   // part[buf][i][j] holds D^T: element t of lane (hi, r32) is n = 32j + 8(t/4) + 4hi + t%4,
   // m = 32i + r32 of the wave tile.
@@ -117,7 +124,7 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < FJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -137,7 +144,7 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int c0 = 4 * kk + 2 * hi;              // this lane's 32 bytes: chunks c0, c0+1
-      v8i af[2], bf[2];
+      v8i af[2], bf[FJ];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = wm * 64 + i * 32 + r32;
@@ -146,8 +153,8 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
         af[i] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = wn * 64 + j * 32 + r32;
+      for (int j = 0; j < FJ; ++j) {
+        const int row = wn * WN + j * 32 + r32;
         const v4i x0 = *reinterpret_cast<const v4i*>(base + F_A + row * 128 + ((c0 ^ swz8(row)) << 4));
         const v4i x1 = *reinterpret_cast<const v4i*>(base + F_A + row * 128 + (((c0 + 1) ^ swz8(row)) << 4));
         bf[j] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
@@ -155,7 +162,7 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FJ; ++j)
           part[BUF][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               bf[j], af[i], kk == 0 ? v16f{} : part[BUF][i][j], kFmtFp8, kFmtFp8, 0, unit, 0, unit);
     }
@@ -182,10 +189,10 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
     const int m = m0 + wm * 64 + i * 32 + r32;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 64 + j * 32 + 8 * q + 4 * hi;
+        const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * hi;
         if (n < N)
           store_out4<BF16>(D, (int64_t)m * N + n, N - n, acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                            acc[i][j][4 * q + 3]);
@@ -193,18 +200,23 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
   }
 }
 
-}  // namespace
-
-hipError_t launch_fp8b_gemm(const Fp8bArgs& a, hipStream_t s) {
+template <int NWN>
+hipError_t launch_nwn(const Fp8bArgs& a, hipStream_t s) {
   const int64_t tiles = ceil_div(a.M, FBM) * ceil_div(a.N, FBN);
   if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
   if (a.bf16_out)
-    hipLaunchKernelGGL(fp8b_gemm_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M, (int)a.N, (int)a.K,
-                       a.A, a.sA, a.B, a.sB, a.D);
+    hipLaunchKernelGGL((fp8b_gemm_kernel<NWN, true>), dim3((unsigned)tiles), dim3(2 * NWN * 64), 0, s, (int)a.M,
+                       (int)a.N, (int)a.K, a.A, a.sA, a.B, a.sB, a.D);
   else
-    hipLaunchKernelGGL(fp8b_gemm_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M, (int)a.N, (int)a.K,
-                       a.A, a.sA, a.B, a.sB, a.D);
+    hipLaunchKernelGGL((fp8b_gemm_kernel<NWN, false>), dim3((unsigned)tiles), dim3(2 * NWN * 64), 0, s, (int)a.M,
+                       (int)a.N, (int)a.K, a.A, a.sA, a.B, a.sB, a.D);
   return hipGetLastError();
 }
+
+}  // namespace
+
+// 8 waves of 64 x 32: about 200 registers, so two waves share a SIMD and one wave's fold runs
+// beside another's MFMAs (4096^3: 145 us against 150 us with 4 waves of 64 x 64; same bits).
+hipError_t launch_fp8b_gemm(const Fp8bArgs& a, hipStream_t s) { return launch_nwn<4>(a, s); }
 
 }  // namespace fp4g
