@@ -1,5 +1,7 @@
 // D = 0 for a product with an empty K range.  A plain store kernel rather than
 // hipMemsetAsync, so a caller may capture the call in a HIP graph.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.h"
 
@@ -15,16 +17,20 @@ __global__ void zero_tail_kernel(uint16_t* __restrict__ p) { *p = 0; }
 
 }  // namespace
 
+// The count is cached per device in atomics: host threads may call the library at
+// once, and a first query racing another only stores the same value twice.
 int64_t device_cus() {
-  static int64_t cached[64] = {0};
+  static std::atomic<int64_t> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+  int64_t n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int q = 0;
+    if (hipDeviceGetAttribute(&q, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || q <= 0) q = 256;
+    n = q;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 hipError_t launch_zero_fill(void* D, int64_t count, bool bf16_out, hipStream_t s) {
