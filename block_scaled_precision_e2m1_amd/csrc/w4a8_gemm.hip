@@ -202,6 +202,10 @@ hipError_t launch_cfg(const W4A8Args& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t s) {
+  // The ring kernel of the pre-packed path also takes plain weights when the bf16 group
+  // scales of a row pair up into aligned dwords: K % 256 == 0 (the C ABI already
+  // requires sB to be 4-byte aligned; the check keeps the kernel's assumption local).
+  if (a.K % 256 == 0 && (reinterpret_cast<uintptr_t>(a.sB) & 3) == 0) return launch_w4a8_ring(a, s);
   return launch_cfg<128, 64, 64, 32>(a, s);
 }
 

@@ -104,10 +104,16 @@ w4a8_prepack_scales_kernel(int64_t units, int N, int G, int64_t Np, const uint16
   }
 }
 
-template <int BM, bool BF16>
+// PACKED: Bw is Bp and Sw is Sp as laid out above.  Otherwise Bw is the plain
+// w4a8_gemm weight B [N][K/2] and Sw its bf16 group scales sB [N][K/128] (K % 256 == 0,
+// sB 4-byte aligned): a wave copies its 16 rows x 64 bytes of the group with the
+// 16-byte units XOR-swizzled by row (conflict-free reads), the conversion puts the
+// two nibble halves back into K order with byte permutes, and the scale copy fetches
+// the aligned dword holding groups g & ~1 and (g & ~1) + 1 of each row.
+template <int BM, bool PACKED, bool BF16>
 __global__ void __launch_bounds__(256)
 w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sa,
-                  const uint8_t* __restrict__ Bp, const float* __restrict__ Sp, void* __restrict__ D) {
+                  const uint8_t* __restrict__ Bw, const void* __restrict__ Sw, void* __restrict__ D) {
   using C = QCfg<BM>;
   constexpr int FI = C::FI;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[QSTAGES * C::STAGE];
@@ -133,16 +139,31 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
     const int row = 8 * (wave * C::IA + i) + (lane >> 3), u = lane & 7;
     ga[i] = A + (int64_t)min(m0 + row, M - 1) * K + ((u ^ swz8(row)) << 4);
   }
-  const uint8_t* gb = Bp + (int64_t)min(n0 / 16 + wave, G16 - 1) * G * 1024 + lane * 16;
-  const float* gs = Sp + min((int64_t)n0 + lane, Np - 1);
+  const uint8_t* gb;
+  const uint8_t* gs;                               // scale copy source (4 bytes per lane)
+  int64_t gstep_b, gstep_s;                        // bytes per K group
+  if constexpr (PACKED) {
+    gb = Bw + (int64_t)min(n0 / 16 + wave, G16 - 1) * G * 1024 + lane * 16;
+    gs = static_cast<const uint8_t*>(Sw) + min((int64_t)n0 + lane, Np - 1) * 4;
+    gstep_b = 1024;
+    gstep_s = Np * 4;
+  } else {
+    const int rr = lane >> 2, u = lane & 3;        // LDS unit u of row rr holds global unit u ^ f(rr)
+    gb = Bw + (int64_t)min(n0 + 16 * wave + rr, N - 1) * (K / 2) + ((u ^ ((rr >> 2) & 3)) << 4);
+    gs = static_cast<const uint8_t*>(Sw) + (int64_t)min(n0 + lane, N - 1) * G * 2;
+    gstep_b = 64;
+    gstep_s = 0;                                   // the group offset is added per copy
+  }
 
   auto issue = [&](int g) {
     const int gc = min(g, G - 1);                  // past the end: re-read the last group
     uint8_t* base = smem + (g % QSTAGES) * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::IA; ++i) lds_copy16(ga[i] + (int64_t)gc * 128, (lds_void*)(base + (wave * C::IA + i) * 1024));
-    lds_copy16(gb + (int64_t)gc * 1024, (lds_void*)(base + C::B_OFF + wave * 1024));
-    lds_copy4(gs + (int64_t)gc * Np, (lds_void*)(base + C::S_OFF));   // every wave: identical bytes
+    lds_copy16(gb + (int64_t)gc * gstep_b, (lds_void*)(base + C::B_OFF + wave * 1024));
+    // every wave copies the same bytes to the same place
+    if constexpr (PACKED) lds_copy4(gs + (int64_t)gc * gstep_s, (lds_void*)(base + C::S_OFF));
+    else lds_copy4(gs + (int64_t)(gc & ~1) * 2, (lds_void*)(base + C::S_OFF));
   };
 
   v4f acc[FI];
@@ -168,16 +189,35 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
     issue(g + QSTAGES - 1);
     const uint8_t* base = smem + (g % QSTAGES) * C::STAGE;
     // weight operand of this wave's 16 rows, and their scales (n = 16w + 4slot + t)
-    const v4i x = *reinterpret_cast<const v4i*>(base + C::B_OFF + wave * 1024 + lane * 16);
-    sc[BUF] = *reinterpret_cast<const v4f*>(base + C::S_OFF + (wave * 16 + 4 * slot) * 4);
+    v4i x;
+    if constexpr (PACKED) {
+      x = *reinterpret_cast<const v4i*>(base + C::B_OFF + wave * 1024 + lane * 16);
+      sc[BUF] = *reinterpret_cast<const v4f*>(base + C::S_OFF + (wave * 16 + 4 * slot) * 4);
+    } else {
+      x = *reinterpret_cast<const v4i*>(base + C::B_OFF + wave * 1024 + r * 64 + ((slot ^ ((r >> 2) & 3)) << 4));
+      // g is even in buffer 0 and odd in buffer 1: the low or high bf16 of each dword
+      const v4i d = *reinterpret_cast<const v4i*>(base + C::S_OFF + (wave * 16 + 4 * slot) * 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        sc[BUF][t] = __builtin_bit_cast(float, BUF == 0 ? (uint32_t)d[t] << 16 : (uint32_t)d[t] & 0xFFFF0000u);
+    }
     v8i bv, bs;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t lo = (uint32_t)x[w], hi = lo >> 4;
-      bv[2 * w] = (int)__builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, lo & 0x07070707u);
-      bv[2 * w + 1] = (int)__builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, hi & 0x07070707u);
-      bs[2 * w] = (int)((lo & 0x08080808u) | 0x80808080u);
-      bs[2 * w + 1] = (int)((hi & 0x08080808u) | 0x80808080u);
+      const uint32_t vl = __builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, lo & 0x07070707u);
+      const uint32_t vh = __builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, hi & 0x07070707u);
+      const uint32_t sl = (lo & 0x08080808u) | 0x80808080u;
+      const uint32_t sh = (hi & 0x08080808u) | 0x80808080u;
+      if constexpr (PACKED) {                      // already in K order: 4 low nibbles, then 4 high
+        bv[2 * w] = (int)vl; bv[2 * w + 1] = (int)vh;
+        bs[2 * w] = (int)sl; bs[2 * w + 1] = (int)sh;
+      } else {                                     // natural order: interleave even and odd elements
+        bv[2 * w] = (int)__builtin_amdgcn_perm(vh, vl, 0x05010400u);
+        bv[2 * w + 1] = (int)__builtin_amdgcn_perm(vh, vl, 0x07030602u);
+        bs[2 * w] = (int)__builtin_amdgcn_perm(sh, sl, 0x05010400u);
+        bs[2 * w + 1] = (int)__builtin_amdgcn_perm(sh, sl, 0x07030602u);
+      }
     }
     v8i af[FI];
 #pragma unroll
@@ -226,16 +266,16 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
   }
 }
 
-template <int BM>
-hipError_t launch_bm(const W4A8Args& a, const float* Sp, hipStream_t s) {
+template <int BM, bool PACKED>
+hipError_t launch_bm(const W4A8Args& a, const void* S, hipStream_t s) {
   const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, QBN);
   if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
   if (a.bf16_out)
-    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, true>), dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M, (int)a.N,
-                       (int)a.K, a.A, a.sa, a.B, Sp, a.D);
+    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, true>), dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M,
+                       (int)a.N, (int)a.K, a.A, a.sa, a.B, S, a.D);
   else
-    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, false>), dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M, (int)a.N,
-                       (int)a.K, a.A, a.sa, a.B, Sp, a.D);
+    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, false>), dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M,
+                       (int)a.N, (int)a.K, a.A, a.sa, a.B, S, a.D);
   return hipGetLastError();
 }
 
@@ -265,7 +305,10 @@ hipError_t launch_w4a8_prepack(int64_t N, int64_t K, const uint8_t* B, const uin
 hipError_t launch_w4a8_gemm_prepacked(const W4A8Args& a, const float* Sp, hipStream_t s) {
   // 64-token tiles: two or three workgroups share a CU (52 KB of LDS, 152 registers),
   // which measured faster than 128-token tiles at every size tried (M = 128 .. 1024).
-  return launch_bm<64>(a, Sp, s);
+  return launch_bm<64, true>(a, Sp, s);
 }
+
+// Plain weights and bf16 scales (K % 256 == 0, sB 4-byte aligned).
+hipError_t launch_w4a8_ring(const W4A8Args& a, hipStream_t s) { return launch_bm<64, false>(a, a.sB, s); }
 
 }  // namespace fp4g

@@ -148,10 +148,10 @@ def w4a8_host(t, ms, ns):
     return d, ir, ic
 
 
-@pytest.mark.parametrize("packed", [False, True], ids=["unpacked", "prepacked"])
-def test_w4a8_output_past_2_to_31_elements(packed):
+@pytest.mark.parametrize("packed,K", [(False, 128), (False, 256), (True, 128)],
+                         ids=["unpacked-k128", "unpacked-k256", "prepacked"])
+def test_w4a8_output_past_2_to_31_elements(packed, K):
     M = N = 46400
-    K = 128
     print(f"case large w4a8 {M}x{N}x{K} packed={packed}", flush=True)
     t = w4a8_inputs(M, N, K, 30)
     if packed:
