@@ -184,6 +184,28 @@ def test_mxfp4_nan_scale_propagates():
     assert oracle.parity_ratio(D, ref, S, "f32") <= 1.0
 
 
+def test_nan_scale_on_every_mxfp4_path():
+    """E8M0 0xFF (NaN) in a weight row's block and in a token row's block: the GEMV, the
+    GEMV over pre-packed weights and the split-K batched GEMM put NaN exactly where the
+    oracle does (the whole token row, the whole weight column) and stay finite elsewhere."""
+    M, N, K = 8, 96, 1024
+    d = datagen.make_shape("gemv", M, N, K, seed=23)
+    d["sfA"][2, 5] = 0xFF
+    d["sfB"][17, 30] = 0xFF
+    ref, S = oracle.run("mx", d)
+    assert np.isnan(ref[2]).all() and np.isnan(ref[:, 17]).all()
+    t = up(d)
+    outs = {"gemv": fp4.fp4_gemv(t["A"], t["sfA"], t["B"], t["sfB"], out_dtype=torch.float32)}
+    Bp, Sp = fp4.fp4_gemv_prepack(t["B"], t["sfB"])
+    outs["gemv_prepacked"] = fp4.fp4_gemv_prepacked(t["A"], t["sfA"], Bp, Sp, N, out_dtype=torch.float32)
+    outs["batched_split"] = fp4.mx_fp4_gemm_batched(*(t[k][None] for k in ("A", "sfA", "B", "sfB")),
+                                                    out_dtype=torch.float32, splits=4)[0]
+    torch.cuda.synchronize(DEV)
+    for name, D in outs.items():
+        r = oracle.parity_ratio(as_np(D), ref, S, "f32")
+        assert r <= 1.0, f"{name}: {r}"
+
+
 # ---- GEMV --------------------------------------------------------------------------------
 
 def test_gemv_decode_workload_full():
