@@ -206,6 +206,28 @@ def test_nan_scale_on_every_mxfp4_path():
         assert r <= 1.0, f"{name}: {r}"
 
 
+def test_nan_activation_code_on_fp8_paths():
+    """An E4M3 NaN code (0x7F) in one activation row: W4A8 (plain and pre-packed weights)
+    and the FP8 blockwise GEMM make that output row NaN, as the oracle does."""
+    M, N, K = 40, 72, 512
+    d = datagen.make_shape("w4a8", M, N, K, seed=29)
+    d["A"][6, 300] = 0x7F
+    ref, S = oracle.run("w4a8", d)
+    assert np.isnan(ref[6]).all() and np.isfinite(np.delete(ref, 6, axis=0)).all()
+    t = up(d)
+    Bp, Sp = fp4.w4a8_prepack(t["B"], t["sB"])
+    for name, D in (("w4a8", fp4.w4a8_gemm(t["A"], t["sa"], t["B"], t["sB"], out_dtype=torch.float32)),
+                    ("w4a8_prepacked", fp4.w4a8_gemm_prepacked(t["A"], t["sa"], Bp, Sp, N, out_dtype=torch.float32))):
+        torch.cuda.synchronize(DEV)
+        assert oracle.parity_ratio(as_np(D), ref, S, "f32") <= 1.0, name
+    f = datagen.make_shape("fp8b", M, N, K, seed=31)
+    f["B"][9, 17] = 0xFF                         # negative NaN code, in a weight row this time
+    ref, S = oracle.run("fp8b", f)
+    assert np.isnan(ref[:, 9]).all()
+    D = as_np(run("fp8b", f, "f32"))
+    assert oracle.parity_ratio(D, ref, S, "f32", REL_TOL_BY_KIND["fp8b"]) <= 1.0
+
+
 # ---- GEMV --------------------------------------------------------------------------------
 
 def test_gemv_decode_workload_full():
