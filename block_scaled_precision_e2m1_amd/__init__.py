@@ -25,7 +25,8 @@ import torch
 
 __all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm",
            "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked",
-           "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
+           "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
+           "nv_fp4_gemm_batched", "w4a8_gemm_batched", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
            "fp4g_status_string",
            "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
 
@@ -34,7 +35,10 @@ _LIB_PATH = os.path.join(_HERE, "libfp4gemm.so")
 SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm",
            "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked",
            "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
-           "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
+           "nv_fp4_gemm_batched", "w4a8_gemm_batched",
+           "nv_fp4_gemm_batched", "w4a8_gemm_batched",
+           "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
+           "nv_fp4_gemm_batched", "w4a8_gemm_batched", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
            "fp4g_status_string")
 
 OUT_F32, OUT_BF16 = 0, 1
@@ -82,6 +86,10 @@ def load_library():
     lib.w4a8_prepack.restype = c_int
     lib.w4a8_gemm_prepacked.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.w4a8_gemm_prepacked.restype = c_int
+    lib.nv_fp4_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, f, p, p, f, p, c_int, p]
+    lib.nv_fp4_gemm_batched.restype = c_int
+    lib.w4a8_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, p, p, p, c_int, p]
+    lib.w4a8_gemm_batched.restype = c_int
     lib.fp4_gemv.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.fp4_gemv.restype = c_int
     lib.nv_fp4_gemm.argtypes = [i64, i64, i64, p, p, f, p, p, f, p, c_int, p]
@@ -350,6 +358,60 @@ def w4a8_gemm_prepacked(A, sa, Bp, Sp, N, out=None, out_dtype=torch.bfloat16):
     dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
     st = lib.w4a8_gemm_prepacked(M, N, K, _ptr(A), _ptr(sa), _ptr(Bp), _ptr(Sp), _ptr(D), dt, _stream(device))
     _raise_on("w4a8_gemm_prepacked", st)
+    return D
+
+
+def _batched_out(out, L, M, N, out_dtype, device):
+    if out is None:
+        return torch.empty((L, M, N), dtype=out_dtype, device=device)
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    _check(out, "out", out.dtype, (L, M, N), device)
+    return out
+
+
+def nv_fp4_gemm_batched(A, sfA, global_a, B, sfB, global_b, out=None, out_dtype=torch.bfloat16):
+    """Batched NVFP4 GEMM: A [L, M, K/2], sfA [L, M, K/16], B [L, N, K/2], sfB [L, N, K/16]
+    -> D [L, M, N]; the global scales apply to every problem."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 3 or B.dim() != 3:
+        raise ValueError("A and B must be 3-D [L, rows, K/2]")
+    L, M, K = A.shape[0], A.shape[1], A.shape[2] * 2
+    N = B.shape[1]
+    if K % 16:
+        raise ValueError(f"K={K} must be a multiple of 16")
+    _check(A, "A", torch.uint8, (L, M, K // 2), device)
+    _check(sfA, "sfA", torch.uint8, (L, M, K // 16), device)
+    _check(B, "B", torch.uint8, (L, N, K // 2), device)
+    _check(sfB, "sfB", torch.uint8, (L, N, K // 16), device)
+    D = _batched_out(out, L, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    st = lib.nv_fp4_gemm_batched(L, M, N, K, _ptr(A), _ptr(sfA), float(global_a), _ptr(B), _ptr(sfB),
+                                 float(global_b), _ptr(D), dt, _stream(device))
+    _raise_on("nv_fp4_gemm_batched", st)
+    return D
+
+
+def w4a8_gemm_batched(A, sa, B, sB, out=None, out_dtype=torch.bfloat16):
+    """Batched W4A8 GEMM: A [L, M, K] uint8 E4M3, sa [L, M] float32, B [L, N, K/2] uint8 INT4,
+    sB [L, N, K/128] bfloat16 -> D [L, M, N]."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 3 or B.dim() != 3:
+        raise ValueError("A and B must be 3-D")
+    L, M, K = A.shape
+    N = B.shape[1]
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(A, "A", torch.uint8, (L, M, K), device)
+    _check(sa, "sa", torch.float32, (L, M), device)
+    _check(B, "B", torch.uint8, (L, N, K // 2), device)
+    _check(sB, "sB", torch.bfloat16, (L, N, K // 128), device)
+    D = _batched_out(out, L, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    st = lib.w4a8_gemm_batched(L, M, N, K, _ptr(A), _ptr(sa), _ptr(B), _ptr(sB), _ptr(D), dt, _stream(device))
+    _raise_on("w4a8_gemm_batched", st)
     return D
 
 

@@ -16,6 +16,8 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;   // each of M, N, K below 2^31
 // Output elements (L*M*N) at most 2^50: far past any device memory, and small enough
 // that every byte count below (times 4 bytes, times up to 16 split slices) fits int64.
 constexpr int64_t kMaxOut = (int64_t)1 << 50;
+// Batches of the NVFP4 and W4A8 GEMMs are a grid dimension of at most 65535.
+constexpr int64_t kMaxGridY = 65535;
 
 struct Range { uintptr_t lo, hi; };
 
@@ -92,6 +94,59 @@ fp4g_status check_batched_sizes(int64_t L, int64_t M, int64_t N, int64_t K, int6
 }  // namespace
 
 extern "C" {
+
+fp4g_status nv_fp4_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
+                                float global_a, const void* B, const void* sfB, float global_b, void* D,
+                                int d_type, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_batched_sizes(L, M, N, K, 0, &empty);
+  if (st != FP4G_OK) return st;
+  if (d_type != FP4G_OUT_F32 && d_type != FP4G_OUT_BF16) return FP4G_EINVAL;
+  if (L > kMaxGridY) return FP4G_EUNSUPPORTED;
+  if (empty) return FP4G_OK;
+  if (!D) return FP4G_EINVAL;
+  if (!aligned(D, 16)) return FP4G_EALIGN;
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, L * M * N, bf16, s));
+  if (!A || !sfA || !B || !sfB) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16)) return FP4G_EALIGN;
+  if (!aligned(sfA, 4) || !aligned(sfB, 4)) return FP4G_EALIGN;
+  const Range d = range_of(D, L * M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, L * M * (K / 2)), range_of(sfA, L * M * (K / 16)),
+                        range_of(B, L * N * (K / 2)), range_of(sfB, L * N * (K / 16))};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  FP4Args a{M, N, K, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(sfA),
+            static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(sfB), global_a * global_b, D, bf16, L};
+  return finish(fp4g::launch_nvfp4_gemm(a, s));
+}
+
+fp4g_status w4a8_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K, const void* A, const float* sa,
+                              const void* B, const void* sB, void* D, int d_type, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_batched_sizes(L, M, N, K, 0, &empty);
+  if (st != FP4G_OK) return st;
+  if (d_type != FP4G_OUT_F32 && d_type != FP4G_OUT_BF16) return FP4G_EINVAL;
+  if (L > kMaxGridY) return FP4G_EUNSUPPORTED;
+  if (empty) return FP4G_OK;
+  if (!D) return FP4G_EINVAL;
+  if (!aligned(D, 16)) return FP4G_EALIGN;
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, L * M * N, bf16, s));
+  if (!A || !sa || !B || !sB) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16)) return FP4G_EALIGN;
+  if (!aligned(sa, 4) || !aligned(sB, 4)) return FP4G_EALIGN;
+  const Range d = range_of(D, L * M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, L * M * K), range_of(sa, L * M * 4), range_of(B, L * N * (K / 2)),
+                        range_of(sB, L * N * (K / 128) * 2)};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  W4A8Args a{M, N, K, static_cast<const uint8_t*>(A), sa, static_cast<const uint8_t*>(B),
+             static_cast<const uint16_t*>(sB), D, bf16, L};
+  return finish(fp4g::launch_w4a8_gemm(a, s));
+}
 
 fp4g_status mx_fp4_gemm_workspace_size(int64_t L, int64_t M, int64_t N, int64_t K, int64_t splits, size_t* bytes) {
   bool empty = false;

@@ -17,6 +17,7 @@ struct FP4Args {            // MXFP4 / NVFP4 / GEMV
   float gscale;             // NVFP4: global_a * global_b; unused otherwise
   void* D;                  // [M][N]
   bool bf16_out;
+  int64_t L = 1;            // NVFP4: problems stored back to back (grid dimension y)
 };
 
 struct W4A8Args {
@@ -27,6 +28,7 @@ struct W4A8Args {
   const uint16_t* sB;       // [N][K/128] bf16
   void* D;
   bool bf16_out;
+  int64_t L = 1;            // problems stored back to back (grid dimension y)
 };
 
 struct Fp8bArgs {            // FP8 blockwise-scaled GEMM

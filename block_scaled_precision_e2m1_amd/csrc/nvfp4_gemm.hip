@@ -74,6 +74,14 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / NWN, wn = wave % NWN;
   const int r16 = lane & 15, slot = lane >> 4;
+  {  // problem blockIdx.y of a batch stored back to back
+    const int64_t b = blockIdx.y;
+    A += b * M * (K / 2);
+    sfA += b * M * (K / 16);
+    B += b * N * (K / 2);
+    sfB += b * N * (K / 16);
+    D = static_cast<uint8_t*>(D) + b * M * N * (BF16 ? 2 : 4);
+  }
   const int tiles_n = (N + BN - 1) / BN;
   const int m0 = (int)(blockIdx.x / tiles_n) * BM, n0 = (int)(blockIdx.x % tiles_n) * BN;
   const int64_t ld = K / 2, lds_ = K / 16;
@@ -197,7 +205,7 @@ hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
   const int64_t tiles = ceil_div(a.N, BN) * ceil_div(a.M, BM);
   if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)tiles);
+  const dim3 grid((unsigned)tiles, (unsigned)a.L);
   if (a.bf16_out)
     hipLaunchKernelGGL((nvfp4_gemm_kernel<BM, BN, WM, WN, true>), grid, dim3(NT), 0, s, (int)a.M,
                        (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.gscale, a.D);
@@ -210,7 +218,7 @@ hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s) {
-  if (ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256) return launch_cfg<128, 128, 64, 64>(a, s);
+  if (a.L * ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256) return launch_cfg<128, 128, 64, 64>(a, s);
   // Small problems: 64 x 64 tiles with 8 waves of 16 x 32, so each SIMD interleaves two
   // waves' folds, LDS traffic and MFMAs (1024^3: 8.6 us, against 9.6 us with 4 waves).
   return launch_cfg<64, 64, 16, 32>(a, s);

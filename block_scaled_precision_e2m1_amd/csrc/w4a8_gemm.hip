@@ -68,6 +68,14 @@ w4a8_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / NWN, wn = wave % NWN;
   const int hi = lane >> 5, r32 = lane & 31;
+  {  // problem blockIdx.y of a batch stored back to back
+    const int64_t b = blockIdx.y;
+    A += b * M * K;
+    sa += b * M;
+    B += b * N * (K / 2);
+    sB += b * N * (K / 128);
+    D = static_cast<uint8_t*>(D) + b * M * N * (BF16 ? 2 : 4);
+  }
   const int tiles_n = (N + BN - 1) / BN;
   const int m0 = (int)(blockIdx.x / tiles_n) * BM, n0 = (int)(blockIdx.x % tiles_n) * BN;
   const int G = K / kBK;
@@ -189,7 +197,7 @@ hipError_t launch_cfg(const W4A8Args& a, hipStream_t s) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
   const int64_t tiles = ceil_div(a.N, BN) * ceil_div(a.M, BM);
   if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)tiles);
+  const dim3 grid((unsigned)tiles, (unsigned)a.L);
   if (a.bf16_out)
     hipLaunchKernelGGL((w4a8_gemm_kernel<BM, BN, WM, WN, true>), grid, dim3(NT), 0, s, (int)a.M, (int)a.N,
                        (int)a.K, a.A, a.sa, a.B, a.sB, a.D);

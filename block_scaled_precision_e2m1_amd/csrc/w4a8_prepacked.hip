@@ -120,6 +120,14 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, slot = lane >> 4;
+  if constexpr (!PACKED) {  // plain operands: problem blockIdx.y of a batch stored back to back
+    const int64_t b = blockIdx.y;
+    A += b * M * K;
+    sa += b * M;
+    Bw += b * N * (K / 2);
+    Sw = static_cast<const uint8_t*>(Sw) + b * N * (K / 128) * 2;
+    D = static_cast<uint8_t*>(D) + b * M * N * (BF16 ? 2 : 4);
+  }
 
   // Tile order: the token tiles of one weight panel are adjacent (they share it in
   // L2); consecutive ids go to the 8 XCDs in turn and are regrouped per XCD.
@@ -270,12 +278,13 @@ template <int BM, bool PACKED>
 hipError_t launch_bm(const W4A8Args& a, const void* S, hipStream_t s) {
   const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, QBN);
   if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)tiles, PACKED ? 1u : (unsigned)a.L);
   if (a.bf16_out)
-    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, true>), dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M,
-                       (int)a.N, (int)a.K, a.A, a.sa, a.B, S, a.D);
+    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, true>), grid, dim3(256), 0, s, (int)a.M, (int)a.N, (int)a.K,
+                       a.A, a.sa, a.B, S, a.D);
   else
-    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, false>), dim3((unsigned)tiles), dim3(256), 0, s, (int)a.M,
-                       (int)a.N, (int)a.K, a.A, a.sa, a.B, S, a.D);
+    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, false>), grid, dim3(256), 0, s, (int)a.M, (int)a.N, (int)a.K,
+                       a.A, a.sa, a.B, S, a.D);
   return hipGetLastError();
 }
 

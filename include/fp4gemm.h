@@ -180,6 +180,22 @@ fp4g_status fp4_gemv(int64_t M, int64_t N, int64_t K,
                      const void *B, const void *sfB,
                      void *D, int d_type, void *stream);
 
+/* Batched NVFP4 and W4A8 GEMMs: L independent problems of one shape stored back
+ * to back, the same (M, N, K, L) problem shape as mx_fp4_gemm_batched (the Hopper
+ * CUTLASS/CuTe DSL blog post, section "How a kernel is assembled"):
+ *   NVFP4: A [L][M][K/2], sfA [L][M][K/16], B [L][N][K/2], sfB [L][N][K/16],
+ *          D [L][M][N]; global_a and global_b apply to every problem.
+ *   W4A8:  A [L][M][K], sa [L][M], B [L][N][K/2], sB [L][N][K/128], D [L][M][N].
+ * Sizes as for mx_fp4_gemm_batched, and L <= 65535 (FP4G_EUNSUPPORTED above). */
+fp4g_status nv_fp4_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K,
+                                const void *A, const void *sfA, float global_a,
+                                const void *B, const void *sfB, float global_b,
+                                void *D, int d_type, void *stream);
+fp4g_status w4a8_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K,
+                              const void *A, const float *sa,
+                              const void *B, const void *sB,
+                              void *D, int d_type, void *stream);
+
 /* Pre-packed decode weights (a load-time step, like the weight re-encoding and
  * re-ordering that the Hopper CUTLASS/CuTe DSL blog post describes for W4A8 in
  * section "The W4A8 kernel: the same four definitions, with the operands

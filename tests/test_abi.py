@@ -33,6 +33,7 @@ def test_header_declares_the_operations():
                                             "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "fp4_gemv_prepack_size",
                                             "fp4_gemv_prepack", "fp4_gemv_prepacked",
                                             "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
+                                            "nv_fp4_gemm_batched", "w4a8_gemm_batched",
                                             "mx_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string"])
 
 
@@ -174,6 +175,21 @@ def test_batched_validation(lib):
     assert mxb(lib, 2, 4, 4, 1024, splits=2, ws=W_ + 8, wsb=4096) == EALIGN
     assert mxb(lib, 2, 4, 4, 1024, splits=2, ws=D_, wsb=4096) == EINVAL   # overlaps D
     assert mxb(lib, 2, 4, 4, 1024, splits=2, ws=B_, wsb=4096) == EINVAL   # overlaps B
+
+
+def test_nv_and_w4a8_batched_validation(lib):
+    nb, wb = lib.nv_fp4_gemm_batched, lib.w4a8_gemm_batched
+    assert nb(-1, 4, 4, 128, A_, SA_, 1.0, B_, SB_, 1.0, D_, 1, None) == EINVAL
+    assert nb(0, 4, 4, 128, None, None, 1.0, None, None, 1.0, None, 1, None) == OK
+    assert nb(65536, 4, 4, 128, A_, SA_, 1.0, B_, SB_, 1.0, D_, 1, None) == EUNSUP   # grid y
+    assert nb(2, 4, 4, 192, A_, SA_, 1.0, B_, SB_, 1.0, D_, 1, None) == EUNSUP
+    assert nb(2, 4, 4, 1024, A_, SA_, 1.0, B_, SB_, 1.0, A_ + 2048, 1, None) == EINVAL  # D in 2nd A
+    assert wb(-1, 4, 4, 128, A_, SA_, B_, SB_, D_, 1, None) == EINVAL
+    assert wb(0, 4, 4, 128, None, None, None, None, None, 1, None) == OK
+    assert wb(65536, 4, 4, 128, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
+    assert wb(2, 4, 4, 128, A_, None, B_, SB_, D_, 1, None) == EINVAL
+    assert wb(2, 4, 4, 128, A_, SA_ + 2, B_, SB_, D_, 1, None) == EALIGN
+    assert wb(3, 4, 4, 128, A_, SA_, B_, SB_, SA_ + 32, 1, None) == EINVAL           # D in sa (48 B)
 
 
 def test_workspace_size(lib):
