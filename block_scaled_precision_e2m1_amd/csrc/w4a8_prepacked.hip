@@ -9,8 +9,7 @@
 // when they are loaded.  This file is that load-time step and its kernel, designed
 // for gfx950:
 //
-// Re-pack.  A two's-complement nibble q = v - 8s (v = its low 3 bits, s = bit 3).
-// Within every run of 8 consecutive K elements the nibbles are re-ordered so that
+// Re-pack.  Within every run of 8 consecutive K elements the nibbles are re-ordered so that
 // byte j holds element j in its low nibble and element j+4 in its high nibble, and
 // the 16-row x 128-K operand of one 16x16x128 instruction is stored lane by lane:
 //   Bp[g16][kg][lane][16 B], lane = 16*slot + r, row 16*g16 + r,
@@ -18,27 +17,31 @@
 //   Sp[kg][n] = the group scale as fp32 (exact from bf16), n < 16*ceil(N/16).
 // Rows past N are zero with scale 0.
 //
-// Conversion.  With that order, eight nibbles in one dword x give two FP8 operands
-// exactly, with seven VALU instructions and no select between tables:
+// Conversion.  A two's-complement nibble q = v - 8s (v = its low 3 bits, s = bit 3).
+// With the order above, eight nibbles in one dword x give two FP8 operands exactly,
+// with seven VALU instructions and no select between tables:
 //   E4M3(v): one v_perm_b32 table lookup of (x & 0x07070707), and of x >> 4;
 //   -s * 2^-6: (x & 0x08080808) | 0x80808080 (byte 0x88 = -2^-6, 0x80 = -0),
 //              taken by the MFMA with an E8M0 scale of 2^9, i.e. as -8s;
 // and v + (-8s) = q, so two chained FP8 MFMAs over the same activations compute
-// the group's exact INT4 product: the matrix pipe does twice the work and the
-// vector ALU a third of a two-table conversion.  (Splitting instead into 8 + v and
-// -8 - 8s, two bit-ORs, makes both halves about three times larger than q; the
-// instruction's inexact internal summation then came within 6% of the 1e-5 bar.)
+// the group's exact INT4 product.  (Splitting instead into 8 + v and -8 - 8s, two
+// bit-ORs, makes both halves about three times larger than q; the instruction's
+// inexact internal summation then came within 6% of the 1e-5 bar.  An offset-binary
+// operand u = q + 8, one MFMA plus a shared activation sum, measured no faster and
+// reached 0.63 of the bar against 0.39.)
 //
 // Kernel.  Workgroup tile BM = 64 tokens x 64 weight rows, 4 waves, wave w owning
 // weight rows 16w .. 16w+15 and all BM tokens (each weight converted once per
 // workgroup).
 // A stage is one K group: BM x 128 B of activations (16-byte chunks XOR-swizzled by
 // row), 4 x 1 KB of packed weights, 64 fp32 scales, copied HBM -> LDS by
-// global_load_lds into a 4-slot ring with counted waits and one barrier per group.
-// Weights are the first MFMA operand (v_mfma_scale_f32_16x16x128_f8f6f4, unit E8M0
-// scales), so a lane's four accumulators are four consecutive n of one token m; a
-// group's product goes to fresh registers and is folded into the fp32 accumulator
-// times sB[n][g] while the next group's MFMAs run.  The epilogue multiplies by sa[m].
+// global_load_lds into a 6-slot ring with counted waits and one barrier per group.
+// The barrier of group g certifies stage g+1, whose fragments are read into a second
+// register set while group g is converted and multiplied.
+// Weights are the first MFMA operand (v_mfma_scale_f32_16x16x128_f8f6f4), so a lane's
+// four accumulators are four consecutive n of one token m; a group's product goes to
+// fresh registers and is folded into the fp32 accumulator times sB[n][g] while the
+// next group's MFMAs run.  The epilogue multiplies by sa[m].
 #include <type_traits>
 
 #include "common.hpp"
@@ -48,7 +51,7 @@ namespace fp4g {
 namespace {
 
 constexpr int QBN = 64;          // weight rows per tile
-constexpr int QSTAGES = 4;
+constexpr int QSTAGES = 6;
 
 template <int BM>
 struct QCfg {
@@ -60,7 +63,7 @@ struct QCfg {
   static constexpr int LOADS = IA + 2;              // + one weight copy + the scale copy
   static_assert(IA >= 1 && BM % 32 == 0, "tile");
   static_assert(QSTAGES * STAGE <= 160 * 1024, "LDS budget");
-  static_assert((QSTAGES - 2) * LOADS < 64, "vmcnt range");
+  static_assert(QSTAGES >= 3 && (QSTAGES - 2) * LOADS < 64, "vmcnt range");
 };
 
 __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
@@ -111,7 +114,7 @@ w4a8_prepack_scales_kernel(int64_t units, int N, int G, int64_t Np, const uint16
 // two nibble halves back into K order with byte permutes, and the scale copy fetches
 // the aligned dword holding groups g & ~1 and (g & ~1) + 1 of each row.
 template <int BM, bool PACKED, bool BF16>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sa,
                   const uint8_t* __restrict__ Bw, const void* __restrict__ Sw, void* __restrict__ D) {
   using C = QCfg<BM>;
@@ -190,29 +193,50 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[i][t] = __builtin_fmaf(part[buf][i][t], sc[buf][t], acc[i][t]);
   };
-  auto group = [&](int g, auto buf_c) {
-    constexpr int BUF = decltype(buf_c)::value;
-    wait_vmcnt<(QSTAGES - 2) * C::LOADS>();
-    barrier_lds();
-    issue(g + QSTAGES - 1);
+
+  // One group's LDS fragments: the wave's weight dwords and scales, and all BM tokens.
+  // Two register sets: the next group's are read while this group's are converted
+  // and multiplied.
+  struct Frag { v4i x; v4f s; v8i af[FI]; };
+  Frag fr[2];
+  auto load = [&](int g, auto set_c) {
+    constexpr int SET = decltype(set_c)::value;    // = g & 1
     const uint8_t* base = smem + (g % QSTAGES) * C::STAGE;
+    Frag& f = fr[SET];
     // weight operand of this wave's 16 rows, and their scales (n = 16w + 4slot + t)
-    v4i x;
     if constexpr (PACKED) {
-      x = *reinterpret_cast<const v4i*>(base + C::B_OFF + wave * 1024 + lane * 16);
-      sc[BUF] = *reinterpret_cast<const v4f*>(base + C::S_OFF + (wave * 16 + 4 * slot) * 4);
+      f.x = *reinterpret_cast<const v4i*>(base + C::B_OFF + wave * 1024 + lane * 16);
+      f.s = *reinterpret_cast<const v4f*>(base + C::S_OFF + (wave * 16 + 4 * slot) * 4);
     } else {
-      x = *reinterpret_cast<const v4i*>(base + C::B_OFF + wave * 1024 + r * 64 + ((slot ^ ((r >> 2) & 3)) << 4));
-      // g is even in buffer 0 and odd in buffer 1: the low or high bf16 of each dword
+      f.x = *reinterpret_cast<const v4i*>(base + C::B_OFF + wave * 1024 + r * 64 + ((slot ^ ((r >> 2) & 3)) << 4));
+      // g is even in set 0 and odd in set 1: the low or high bf16 of each dword
       const v4i d = *reinterpret_cast<const v4i*>(base + C::S_OFF + (wave * 16 + 4 * slot) * 4);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        sc[BUF][t] = __builtin_bit_cast(float, BUF == 0 ? (uint32_t)d[t] << 16 : (uint32_t)d[t] & 0xFFFF0000u);
+        f.s[t] = __builtin_bit_cast(float, SET == 0 ? (uint32_t)d[t] << 16 : (uint32_t)d[t] & 0xFFFF0000u);
     }
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const int row = 16 * i + r;
+      const v4i a0 = *reinterpret_cast<const v4i*>(base + row * 128 + (((2 * slot) ^ swz8(row)) << 4));
+      const v4i a1 = *reinterpret_cast<const v4i*>(base + row * 128 + (((2 * slot + 1) ^ swz8(row)) << 4));
+      f.af[i] = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    }
+  };
+
+  // Group g (BUF = g & 1): stage g+1 has landed and stage g's fragments are in set BUF.
+  auto group = [&](int g, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
+    wait_vmcnt<(QSTAGES - 3) * C::LOADS>();
+    barrier_lds();
+    issue(g + QSTAGES - 1);
+    load(g + 1, std::integral_constant<int, BUF ^ 1>{});
+    const Frag& f = fr[BUF];
+    sc[BUF] = f.s;
     v8i bv, bs;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = (uint32_t)x[w], hi = lo >> 4;
+      const uint32_t lo = (uint32_t)f.x[w], hi = lo >> 4;
       const uint32_t vl = __builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, lo & 0x07070707u);
       const uint32_t vh = __builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, hi & 0x07070707u);
       const uint32_t sl = (lo & 0x08080808u) | 0x80808080u;
@@ -227,27 +251,23 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
         bs[2 * w + 1] = (int)__builtin_amdgcn_perm(sh, sl, 0x07030602u);
       }
     }
-    v8i af[FI];
-#pragma unroll
-    for (int i = 0; i < FI; ++i) {
-      const int row = 16 * i + r;
-      const v4i a0 = *reinterpret_cast<const v4i*>(base + row * 128 + (((2 * slot) ^ swz8(row)) << 4));
-      const v4i a1 = *reinterpret_cast<const v4i*>(base + row * 128 + (((2 * slot + 1) ^ swz8(row)) << 4));
-      af[i] = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    }
     // All E4M3(v) products first, then the sign products that accumulate onto them, so
     // no MFMA waits for the one just issued; the previous group's fold fills the gap.
 #pragma unroll
     for (int i = 0; i < FI; ++i)
-      part[BUF][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, af[i], v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
+      part[BUF][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, f.af[i], v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
                                                                       kFmtFp8, 0, unit, 0, unit);
     if (g > 0) fold(BUF ^ 1);
 #pragma unroll
     for (int i = 0; i < FI; ++i)
-      part[BUF][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bs, af[i], part[BUF][i], kFmtFp8, kFmtFp8, 0,
+      part[BUF][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bs, f.af[i], part[BUF][i], kFmtFp8, kFmtFp8, 0,
                                                                       kScale2p9, 0, unit);
   };
 
+  // stage 0 landed: its fragments into set 0
+  wait_vmcnt<(QSTAGES - 2) * C::LOADS>();
+  barrier_lds();
+  load(0, std::integral_constant<int, 0>{});
   int g = 0;
   for (; g + 2 <= G; g += 2) {
     group(g, std::integral_constant<int, 0>{});
@@ -312,8 +332,7 @@ hipError_t launch_w4a8_prepack(int64_t N, int64_t K, const uint8_t* B, const uin
 
 // a.B is the packed weight buffer; Sp the packed fp32 scales.
 hipError_t launch_w4a8_gemm_prepacked(const W4A8Args& a, const float* Sp, hipStream_t s) {
-  // 64-token tiles: two or three workgroups share a CU (52 KB of LDS, 152 registers),
-  // which measured faster than 128-token tiles at every size tried (M = 128 .. 1024).
+  // 64-token tiles: two workgroups share a CU (79 KB of LDS, at most 256 registers).
   return launch_bm<64, true>(a, Sp, s);
 }
 
