@@ -16,10 +16,10 @@
 // The folded tiles are written to LDS and consumed by v_mfma_f32_16x16x32_f16
 // with fp32 accumulation; gA*gB multiplies the accumulator in the epilogue.
 //
-// Structure: one workgroup per BM x BN tile, 4 or 8 waves of WM x WN; 64 K elements
-// (32 packed bytes, one scale dword) per row per step; packed tiles are prefetched
+// Structure: one workgroup per BM x BN tile, 4 or 8 waves of WM x WN; 128 K elements
+// (64 packed bytes, two scale dwords) per row per step; packed tiles are prefetched
 // into registers two steps ahead while the MFMAs of the current step run;
-// LDS rows are 128 bytes (64 fp16) with 16-byte chunks XOR-swizzled by row.
+// LDS rows are 256 bytes (128 fp16) with 16-byte chunks XOR-swizzled by row.
 #include <type_traits>
 
 #include "common.hpp"
@@ -30,10 +30,13 @@ namespace {
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 64;             // K elements per step
-constexpr int kRowH = kBK * 2;     // 128 bytes of fp16 per LDS row
+constexpr int kBK = 128;            // K elements per step
+constexpr int kRowH = kBK * 2;     // 256 bytes of fp16 per LDS row: 16 chunks of 16 bytes
 
-__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+// 16-byte chunk c of LDS row r sits at position c ^ (r & 15): the 16 consecutive rows
+// that one MFMA fragment read touches at one logical chunk, and the 4 rows x 4 chunks
+// that 16 consecutive threads of the fold write, all land in distinct bank groups.
+__device__ __forceinline__ int swz16(int r) { return r & 15; }
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -65,7 +68,7 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
                   void* __restrict__ D) {
   constexpr int NWN = BN / WN;
   constexpr int NT = (BM / WM) * NWN * 64;
-  constexpr int CHUNKS = (BM + BN) * 2;     // 16-byte packed chunks per step
+  constexpr int CHUNKS = (BM + BN) * 4;     // 16-byte packed chunks per step
   constexpr int CH = (CHUNKS + NT - 1) / NT; // per thread (the last round may leave threads idle)
   constexpr int FI = WM / 16, FJ = WN / 16;
   static_assert(CHUNKS % NT == 0 || CH == 1, "tile/threads mismatch");
@@ -87,18 +90,17 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   const int64_t ld = K / 2, lds_ = K / 16;
   const int KT = K / kBK;
 
-  // Thread chunk q: packed row (A rows first, then B rows), half c of its 32 bytes.
+  // Thread chunk q: packed row (A rows first, then B rows), quarter c of its 64 bytes
+  // (32 elements, two scales).
   const uint8_t* gsrc[CH];
   const uint8_t* gscl[CH];
-  int ldst[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int q = min(tid + i * NT, CHUNKS - 1), row = q >> 1, c = q & 1;
+    const int q = min(tid + i * NT, CHUNKS - 1), row = q >> 2, c = q & 3;
     const bool isA = row < BM;
     const int grow = isA ? min(m0 + row, M - 1) : min(n0 + row - BM, N - 1);
     gsrc[i] = (isA ? A : B) + (int64_t)grow * ld + c * 16;
     gscl[i] = (isA ? sfA : sfB) + (int64_t)grow * lds_ + c * 2;
-    ldst[i] = row * kRowH + c * 64;   // 32 fp16 = 4 logical 16-byte chunks 4c..4c+3
   }
 
   // Packed tiles are prefetched two steps ahead into two register buffers (RB = the
@@ -111,8 +113,8 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
     const int kc = min(kt, KT - 1);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      pk[RB][i] = *reinterpret_cast<const v4i*>(gsrc[i] + (int64_t)kc * 32);
-      ps[RB][i] = *reinterpret_cast<const uint16_t*>(gscl[i] + kc * 4);
+      pk[RB][i] = *reinterpret_cast<const v4i*>(gsrc[i] + (int64_t)kc * 64);
+      ps[RB][i] = *reinterpret_cast<const uint16_t*>(gscl[i] + kc * 8);
     }
   };
   auto store_lds = [&](int st, auto rb_c) {
@@ -120,7 +122,7 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       if (CHUNKS % NT != 0 && tid + i * NT >= CHUNKS) break;   // idle thread in a partial round
-      const int row = (tid + i * NT) >> 1, c = (tid + i * NT) & 1;
+      const int row = (tid + i * NT) >> 2, c = (tid + i * NT) & 3;
       float p0, p1;
       h2 m0, m1;
       e4m3_split(ps[RB][i] & 0xFFu, &p0, &m0);
@@ -130,7 +132,7 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
         uint32_t out[4];
         fold8((uint32_t)pk[RB][i][d], d < 2 ? p0 : p1, d < 2 ? m0 : m1, out);
         const int chunk = 4 * c + d;
-        *reinterpret_cast<v4i*>(&lds[st][row * kRowH + ((chunk ^ swz8(row)) << 4)]) =
+        *reinterpret_cast<v4i*>(&lds[st][row * kRowH + ((chunk ^ swz16(row)) << 4)]) =
             v4i{(int)out[0], (int)out[1], (int)out[2], (int)out[3]};
       }
     }
@@ -144,18 +146,18 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 
   auto compute = [&](int st) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < 4; ++sub) {
       const int chunk = 4 * sub + slot;
       v8h af[FI], bf[FJ];
 #pragma unroll
       for (int i = 0; i < FI; ++i) {
         const int row = wm * WM + i * 16 + r16;
-        af[i] = *reinterpret_cast<const v8h*>(&lds[st][row * kRowH + ((chunk ^ swz8(row)) << 4)]);
+        af[i] = *reinterpret_cast<const v8h*>(&lds[st][row * kRowH + ((chunk ^ swz16(row)) << 4)]);
       }
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
         const int row = BM + wn * WN + j * 16 + r16;
-        bf[j] = *reinterpret_cast<const v8h*>(&lds[st][row * kRowH + ((chunk ^ swz8(row)) << 4)]);
+        bf[j] = *reinterpret_cast<const v8h*>(&lds[st][row * kRowH + ((chunk ^ swz16(row)) << 4)]);
       }
 #pragma unroll
       for (int i = 0; i < FI; ++i)
@@ -220,7 +222,8 @@ hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s) {
   if (a.L * ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256) return launch_cfg<128, 128, 64, 64>(a, s);
   // Small problems: 64 x 64 tiles with 8 waves of 16 x 32, so each SIMD interleaves two
-  // waves' folds, LDS traffic and MFMAs (1024^3: 8.6 us, against 9.6 us with 4 waves).
+  // waves' folds, LDS traffic and MFMAs (1024^3: 7.1 us, against 8.3 us with 4 waves of
+  // 32 x 32, which read a third less from LDS but fold with half as many threads).
   return launch_cfg<64, 64, 16, 32>(a, s);
 }
 
