@@ -136,7 +136,27 @@ mxfp4_gemm_kernel(int M, int N, int K, int L, int S, const uint8_t* __restrict__
   constexpr int FI = WM / 32, FJ = WN / 32;
   constexpr int NQ = C::NQ;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+  // Output panels.  The epilogue stages the wave tile through LDS in panels of PB bytes
+  // per row.  With 256 x 256 tiles (one workgroup per CU) the panels sit past the ring,
+  // in the LDS the ring leaves free, so the next tile's first copies can land while
+  // this tile's output is written; otherwise they reuse the ring.
+  constexpr bool OUT_BF16 = BF16 && !SPLIT;
+  constexpr int ELEM = OUT_BF16 ? 2 : 4;
+  constexpr bool EPI_SPARE = BM == 256 && BN == 256;
+  constexpr int EPI_AVAIL = EPI_SPARE ? 160 * 1024 - C::LDS : C::LDS;
+  constexpr int PR = EPI_SPARE ? 32 : WM;                   // panel rows
+  constexpr int PFIT = EPI_AVAIL / (C::NW * PR) - 16;
+  constexpr int PB0 = (WN * ELEM < 256) ? WN * ELEM : 256;
+  constexpr int PB = PB0 <= PFIT ? PB0 : PB0 / 2 <= PFIT ? PB0 / 2 : PB0 / 4;   // panel bytes per row
+  constexpr int PW = PB / ELEM;                             // panel columns
+  constexpr int RS = PB + 16;                               // LDS row stride
+  constexpr int LPR = PB / 16, RPI = 64 / LPR;              // lanes per row, rows per read
+  static_assert(PB >= 8 * ELEM && WN % PW == 0 && PW % 8 == 0, "panels hold whole 8-column groups");
+  static_assert(C::NW * PR * RS <= EPI_AVAIL && PR % RPI == 0, "output panels fit");
+  constexpr int EPI_OFF = EPI_SPARE ? C::LDS : 0;
+  constexpr int SMEM = EPI_SPARE ? C::LDS + C::NW * PR * RS : C::LDS;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,52 +169,56 @@ mxfp4_gemm_kernel(int M, int N, int K, int L, int S, const uint8_t* __restrict__
   // Persistent: the grid is at most one workgroup per CU and each workgroup walks its
   // work items.  A tile's output stores drain while the next tile's copies and MFMAs
   // run, instead of every CU writing its tile at the same moment.
-  for (int work = blockIdx.x; work < total; work += gridDim.x) {
-  const Item it = item_of(work, total, S, tiles_m, tiles_n);
-  const int m0 = it.tm * BM, n0 = it.tn * BN;
-
+  if ((int)blockIdx.x >= total) return;
   const int64_t lda = K / 2, ldsf = K / 32;
-  // This item's K stages: ks0 .. ks0+KS-1 of the KT stages (KS >= 1: S <= KT).
   const int KT = K / BK;
-  const int ks0 = (int)((int64_t)it.s * KT / S);
-  const int KS = (int)((int64_t)(it.s + 1) * KT / S) - ks0;
-  const uint8_t* Ab = A + (int64_t)it.b * M * lda + (int64_t)ks0 * C::ROWB;
-  const uint8_t* Bb = B + (int64_t)it.b * N * lda + (int64_t)ks0 * C::ROWB;
-  const uint8_t* sfAb = sfA + (int64_t)it.b * M * ldsf + (int64_t)ks0 * 4 * C::SDW;
-  const uint8_t* sfBb = sfB + (int64_t)it.b * N * ldsf + (int64_t)ks0 * 4 * C::SDW;
 
-  // ---- copy sources: this lane's global rows / chunks for each of its copies ----
+  // The current work item: its tile, its K stages ks0 .. ks0+KS-1 of the KT stages
+  // (KS >= 1: S <= KT), and this lane's copy sources.
+  Item it;
+  int m0 = 0, n0 = 0, KS = 1;
   const uint8_t* ga[C::IA];
   const uint8_t* gb[C::IB];
-#pragma unroll
-  for (int i = 0; i < C::IA; ++i) {
-    const int row = C::RPC * (wave * C::IA + i) + lane / C::CHUNKS;
-    const int c = (lane % C::CHUNKS) ^ swz<C::CHUNKS>(row);
-    ga[i] = Ab + (int64_t)min(m0 + row, M - 1) * lda + c * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < C::IB; ++i) {
-    const int row = C::RPC * (wave * C::IB + i) + lane / C::CHUNKS;
-    const int c = (lane % C::CHUNKS) ^ swz<C::CHUNKS>(row);
-    gb[i] = Bb + (int64_t)min(n0 + row, N - 1) * lda + c * 16;
-  }
-  // Scale copy z covers dword d = z / (rows/64) of 64 rows (block z % (rows/64)).  When
-  // there are fewer copies than waves, waves repeat one (identical bytes, same place).
   const uint8_t* gsa[C::SCA];
   const uint8_t* gsb[C::SCB];
   int lsa[C::SCA], lsb[C::SCB];
+  auto setup = [&](int work) {
+    it = item_of(work, total, S, tiles_m, tiles_n);
+    m0 = it.tm * BM;
+    n0 = it.tn * BN;
+    const int ks0 = (int)((int64_t)it.s * KT / S);
+    KS = (int)((int64_t)(it.s + 1) * KT / S) - ks0;
+    const uint8_t* Ab = A + (int64_t)it.b * M * lda + (int64_t)ks0 * C::ROWB;
+    const uint8_t* Bb = B + (int64_t)it.b * N * lda + (int64_t)ks0 * C::ROWB;
+    const uint8_t* sfAb = sfA + (int64_t)it.b * M * ldsf + (int64_t)ks0 * 4 * C::SDW;
+    const uint8_t* sfBb = sfB + (int64_t)it.b * N * ldsf + (int64_t)ks0 * 4 * C::SDW;
 #pragma unroll
-  for (int j = 0; j < C::SCA; ++j) {
-    const int z = (wave * C::SCA + j) % C::TSA, d = z / (BM / 64), blk = z % (BM / 64);
-    gsa[j] = sfAb + (int64_t)min(m0 + 64 * blk + lane, M - 1) * ldsf + 4 * d;
-    lsa[j] = C::SA_OFF + d * BM * 4 + 256 * blk;
-  }
+    for (int i = 0; i < C::IA; ++i) {
+      const int row = C::RPC * (wave * C::IA + i) + lane / C::CHUNKS;
+      const int c = (lane % C::CHUNKS) ^ swz<C::CHUNKS>(row);
+      ga[i] = Ab + (int64_t)min(m0 + row, M - 1) * lda + c * 16;
+    }
 #pragma unroll
-  for (int j = 0; j < C::SCB; ++j) {
-    const int z = (wave * C::SCB + j) % C::TSB, d = z / (BN / 64), blk = z % (BN / 64);
-    gsb[j] = sfBb + (int64_t)min(n0 + 64 * blk + lane, N - 1) * ldsf + 4 * d;
-    lsb[j] = C::SB_OFF + d * BN * 4 + 256 * blk;
-  }
+    for (int i = 0; i < C::IB; ++i) {
+      const int row = C::RPC * (wave * C::IB + i) + lane / C::CHUNKS;
+      const int c = (lane % C::CHUNKS) ^ swz<C::CHUNKS>(row);
+      gb[i] = Bb + (int64_t)min(n0 + row, N - 1) * lda + c * 16;
+    }
+    // Scale copy z covers dword d = z / (rows/64) of 64 rows (block z % (rows/64)).  When
+    // there are fewer copies than waves, waves repeat one (identical bytes, same place).
+#pragma unroll
+    for (int j = 0; j < C::SCA; ++j) {
+      const int z = (wave * C::SCA + j) % C::TSA, d = z / (BM / 64), blk = z % (BM / 64);
+      gsa[j] = sfAb + (int64_t)min(m0 + 64 * blk + lane, M - 1) * ldsf + 4 * d;
+      lsa[j] = C::SA_OFF + d * BM * 4 + 256 * blk;
+    }
+#pragma unroll
+    for (int j = 0; j < C::SCB; ++j) {
+      const int z = (wave * C::SCB + j) % C::TSB, d = z / (BN / 64), blk = z % (BN / 64);
+      gsb[j] = sfBb + (int64_t)min(n0 + 64 * blk + lane, N - 1) * ldsf + 4 * d;
+      lsb[j] = C::SB_OFF + d * BN * 4 + 256 * blk;
+    }
+  };
 
   // Copy q (0 .. LOADS-1) of stage ks into ring slot ks % STAGES: A chunks, B chunks,
   // then the scale blocks.  Stages past the end re-read the last stage (the copies land
@@ -268,10 +292,6 @@ mxfp4_gemm_kernel(int M, int N, int K, int L, int S, const uint8_t* __restrict__
   };
 
   v16f acc[FI][FJ];
-#pragma unroll
-  for (int i = 0; i < FI; ++i)
-#pragma unroll
-    for (int j = 0; j < FJ; ++j) acc[i][j] = v16f{};
 
   // The MFMAs of quarter KQ (register set SET); after MFMA q, `extra(q)` issues that
   // slot's memory instructions, in a fixed order (sched_barrier pins it), so their issue
@@ -309,17 +329,32 @@ mxfp4_gemm_kernel(int M, int N, int K, int L, int S, const uint8_t* __restrict__
     }
   };
 
-  // ---- prologue: copies for stages 0 .. STAGES-2 and the first half of stage
-  // STAGES-1, then stage 0's first quarter ----
+  // ---- prologue copies of the current item: stages 0 .. STAGES-2 and the first half
+  // of stage STAGES-1 ----
+  auto prologue = [&]() {
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p) issue(p);
+    for (int p = 0; p < STAGES - 1; ++p) issue(p);
 #pragma unroll
-  for (int q = 0; q < LH; ++q) issue_one(STAGES - 1, q);
+    for (int q = 0; q < LH; ++q) issue_one(STAGES - 1, q);
+  };
+
+  int work = blockIdx.x;
+  setup(work);
+  prologue();
+  while (true) {
+  // Stage 0 has landed once at most the first half of stage STAGES-1 (and the STAGES-2
+  // stages before it) is in flight.  Output stores of the previous tile issued after
+  // these copies only make the wait longer: copies complete in order, so while any
+  // copy of stage 0 is pending, every later copy is too.
   wait_vmcnt<(STAGES - 2) * C::LOADS + LH>();
   barrier_lds();
   read_scales(0);
   take_scales();
   read_frags(0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[i][j] = v16f{};
 
   // One stage per iteration, no branches in the body (so the compiler keeps the order):
   //   quarters 0 .. NQ-2: MFMAs of quarter kq, reading quarter kq+1's fragments;
@@ -363,50 +398,54 @@ mxfp4_gemm_kernel(int M, int N, int K, int L, int S, const uint8_t* __restrict__
   // Every wave's copies have landed and nobody reads the ring any more: its LDS is free.
   barrier_lds();
 
+  // The output coordinates of this item; with the panels past the ring, the next item's
+  // first copies go out now and land while this tile's output is written.
+  const int eb = it.b, es = it.s, em0 = m0, en0 = n0;
+  const int next = work + (int)gridDim.x;
+  if constexpr (EPI_SPARE) {
+    if (next < total) {
+      setup(next);
+      prologue();
+    }
+  }
+
   // Epilogue.  The accumulator of block (i, j) is D^T: lane (hi, r32) holds row
   // m = i*32 + r32 of the wave tile and, for g = 0..3, the four consecutive columns
   // j*32 + 8g + 4hi + 0..3.  When D's rows are whole 16-byte units the wave tile goes
-  // through its own LDS region (rows padded to PB+16 bytes) in panels of PB bytes per
-  // row, and is read back row-wise so each lane stores 16 contiguous bytes and a store
+  // through its own LDS region (rows padded to PB+16 bytes) in panels of PR rows x PW
+  // columns, and is read back row-wise so each lane stores 16 contiguous bytes and a store
   // instruction writes 64/(PB/16) whole row segments.  Otherwise each group of four
   // goes out directly.
-  constexpr bool OUT_BF16 = BF16 && !SPLIT;
-  constexpr int ELEM = OUT_BF16 ? 2 : 4;
-  uint8_t* const Dt = static_cast<uint8_t*>(D) + (SPLIT ? (int64_t)it.b * S + it.s : (int64_t)it.b) * M * N * ELEM;
-  constexpr int PB = (WN * ELEM < 256) ? WN * ELEM : 256;   // panel bytes per row
-  constexpr int PW = PB / ELEM;                             // panel columns
-  constexpr int RS = PB + 16;                               // LDS row stride
-  constexpr int LPR = PB / 16, RPI = 64 / LPR;              // lanes per row, rows per read
-  static_assert(WN % PW == 0 && PW % 32 == 0, "panels hold whole 32-column blocks");
-  static_assert(WM * RS * C::NW <= C::LDS, "output panel fits the wave's LDS share");
-  const int mw = m0 + wm * WM, nw = n0 + wn * WN;
+  uint8_t* const Dt = static_cast<uint8_t*>(D) + (SPLIT ? (int64_t)eb * S + es : (int64_t)eb) * M * N * ELEM;
+  const int mw = em0 + wm * WM, nw = en0 + wn * WN;
   if ((N % (16 / ELEM)) == 0) {
-    uint8_t* region = smem + wave * (WM * RS);
+    uint8_t* region = smem + EPI_OFF + wave * (PR * RS);
+#pragma unroll
+    for (int ib = 0; ib < WM / PR; ++ib)
 #pragma unroll
     for (int p = 0; p < WN / PW; ++p) {
 #pragma unroll
-      for (int i = 0; i < FI; ++i)
+      for (int ii = 0; ii < PR / 32; ++ii)
 #pragma unroll
-        for (int jj = 0; jj < PW / 32; ++jj) {
-          const int j = p * (PW / 32) + jj;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            uint8_t* dst = region + (i * 32 + r32) * RS + (jj * 32 + 8 * g + 4 * hi) * ELEM;
-            const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-            const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-            if constexpr (OUT_BF16) {
-              typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-              *reinterpret_cast<v2u*>(dst) = v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            } else {
-              *reinterpret_cast<v4f*>(dst) = v4f{v0, v1, v2, v3};
-            }
+        for (int c8 = 0; c8 < PW / 8; ++c8) {
+          const int i = ib * (PR / 32) + ii;
+          const int col = p * PW + 8 * c8;              // first column of the 8-column group
+          const int j = col / 32, g = (col % 32) / 8;
+          uint8_t* dst = region + (ii * 32 + r32) * RS + (8 * c8 + 4 * hi) * ELEM;
+          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+          if constexpr (OUT_BF16) {
+            typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<v2u*>(dst) = v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          } else {
+            *reinterpret_cast<v4f*>(dst) = v4f{v0, v1, v2, v3};
           }
         }
 #pragma unroll
-      for (int it = 0; it < WM / RPI; ++it) {
-        const int r = it * RPI + lane / LPR, ch = lane % LPR;
+      for (int rd = 0; rd < PR / RPI; ++rd) {
+        const int r = rd * RPI + lane / LPR, ch = lane % LPR;
         const v4i val = *reinterpret_cast<const v4i*>(region + r * RS + ch * 16);
-        const int m = mw + r, n = nw + p * PW + ch * (16 / ELEM);
+        const int m = mw + ib * PR + r, n = nw + p * PW + ch * (16 / ELEM);
         if (m < M && n < N)
           *reinterpret_cast<v4i*>(Dt + ((int64_t)m * N + n) * ELEM) = val;
       }
@@ -427,9 +466,17 @@ mxfp4_gemm_kernel(int M, int N, int K, int L, int S, const uint8_t* __restrict__
       }
     }
   }
-  // No wave may start the next tile's copies into LDS while another still reads its
-  // output panel.
-  barrier_lds();
+  if constexpr (!EPI_SPARE) {
+    // No wave may start the next tile's copies into LDS while another still reads its
+    // output panel.
+    barrier_lds();
+    if (next < total) {
+      setup(next);
+      prologue();
+    }
+  }
+  if (next >= total) break;
+  work = next;
   }  // work-item loop
 }
 
