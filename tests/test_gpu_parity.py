@@ -135,6 +135,22 @@ def test_mxfp4_big_tile_config_sampled(shape):
     check_sampled("mx", d, "bf16", nt, mt)
 
 
+# 256 x 256 tiles with several tiles per workgroup (the next tile's copies go out before
+# the epilogue), fp32 panels of 32 columns, and a ragged last column of tiles.
+@pytest.mark.parametrize("shape,out", [((4096, 4096, 256), "f32"), ((4352, 8192, 256), "f32"),
+                                       ((4352, 8200, 512), "bf16")])
+def test_mxfp4_big_tile_multi_item_sampled(shape, out):
+    M, N, K = shape
+    print(f"case mx {M}x{N}x{K} {out} seed 11", flush=True)
+    d = datagen.make_shape("mx", M, N, K, seed=11, dist="gaussian")
+    D = run("mx", d, out)
+    rng = np.random.default_rng(4)
+    ms, ns = sample_pairs(M, N, rng, 20000, edges=(0, 255, 256, M - 1))
+    check_sampled("mx", d, out, ms, ns, D=D)
+    nt, mt = sample_pairs(N, M, rng, 0, edges=(0, 4095, N - 1))    # whole columns
+    check_sampled("mx", d, out, mt, nt, D=D)
+
+
 def test_mxfp4_8192_sampled_and_repeatable():
     d = datagen.make("mxfp4_8192")
     print("case mxfp4_8192 seed 0", flush=True)
