@@ -110,8 +110,8 @@ w4a8_prepack_scales_kernel(int64_t units, int N, int G, int64_t Np, const uint16
 // PACKED: Bw is Bp and Sw is Sp as laid out above.  Otherwise Bw is the plain
 // w4a8_gemm weight B [N][K/2] and Sw its bf16 group scales sB [N][K/128] (K % 256 == 0,
 // sB 4-byte aligned): a wave copies its 16 rows x 64 bytes of the group with the
-// 16-byte units XOR-swizzled by row (conflict-free reads), the conversion puts the
-// two nibble halves back into K order with byte permutes, and the scale copy fetches
+// 16-byte units XOR-swizzled by row (conflict-free reads), the conversion first puts
+// the nibbles into K order with two byte permutes per 8 weights, and the scale copy fetches
 // the aligned dword holding groups g & ~1 and (g & ~1) + 1 of each row.
 template <int BM, bool PACKED, bool BF16>
 __global__ void __launch_bounds__(256, 2)
@@ -236,20 +236,16 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
     v8i bv, bs;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = (uint32_t)f.x[w], hi = lo >> 4;
-      const uint32_t vl = __builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, lo & 0x07070707u);
-      const uint32_t vh = __builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, hi & 0x07070707u);
-      const uint32_t sl = (lo & 0x08080808u) | 0x80808080u;
-      const uint32_t sh = (hi & 0x08080808u) | 0x80808080u;
-      if constexpr (PACKED) {                      // already in K order: 4 low nibbles, then 4 high
-        bv[2 * w] = (int)vl; bv[2 * w + 1] = (int)vh;
-        bs[2 * w] = (int)sl; bs[2 * w + 1] = (int)sh;
-      } else {                                     // natural order: interleave even and odd elements
-        bv[2 * w] = (int)__builtin_amdgcn_perm(vh, vl, 0x05010400u);
-        bv[2 * w + 1] = (int)__builtin_amdgcn_perm(vh, vl, 0x07030602u);
-        bs[2 * w] = (int)__builtin_amdgcn_perm(sh, sl, 0x05010400u);
-        bs[2 * w + 1] = (int)__builtin_amdgcn_perm(sh, sl, 0x07030602u);
-      }
+      const uint32_t x = (uint32_t)f.x[w], xs = x >> 4;
+      // Elements 0..3 and 4..7 in the low nibbles of the bytes of a and b.  Pre-packed
+      // weights are already in that order; plain ones (byte j holds elements 2j, 2j+1)
+      // take one byte permute each of x and x >> 4.
+      const uint32_t a = PACKED ? x : __builtin_amdgcn_perm(xs, x, 0x05010400u);
+      const uint32_t b = PACKED ? xs : __builtin_amdgcn_perm(xs, x, 0x07030602u);
+      bv[2 * w] = (int)__builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, a & 0x07070707u);
+      bv[2 * w + 1] = (int)__builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, b & 0x07070707u);
+      bs[2 * w] = (int)((a & 0x08080808u) | 0x80808080u);
+      bs[2 * w + 1] = (int)((b & 0x08080808u) | 0x80808080u);
     }
     // All E4M3(v) products first, then the sign products that accumulate onto them, so
     // no MFMA waits for the one just issued; the previous group's fold fills the gap.
