@@ -315,6 +315,15 @@ def test_nvfp4_shapes(shape, g):
     check_full("nv", d, "f32")
 
 
+def test_nvfp4_big_tile_config_full():
+    """At least 256 tiles of 128 x 128 select the 4-wave 128 x 128 kernel; K = 384 is an
+    odd number of 128-element steps (the register prefetch ends on its second buffer)."""
+    M, N, K = 2048, 2112, 384
+    print(f"case nv {M}x{N}x{K} seed 21", flush=True)
+    d = datagen.random_nv(M, N, K, np.random.default_rng(21), gA=2.0, gB=0.375)
+    check_full("nv", d, "bf16")
+
+
 def test_nvfp4_full_scale_range_including_subnormals():
     rng = np.random.default_rng(13)
     d = datagen.random_nv(96, 80, 256, rng)
