@@ -159,6 +159,10 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
         const v4i x1 = *reinterpret_cast<const v4i*>(base + F_A + row * 128 + (((c0 + 1) ^ swz8(row)) << 4));
         bf[j] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
+      // The group's MFMAs at raised wave priority, the fold at normal priority: the two
+      // waves sharing a SIMD then tend to run opposite phases (one multiplying, one
+      // folding) between barriers (4096^3: 149 against 152 us on the same box).
+      if (kk == 0) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -166,6 +170,7 @@ fp8b_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
           part[BUF][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               bf[j], af[i], kk == 0 ? v16f{} : part[BUF][i][j], kFmtFp8, kFmtFp8, 0, unit, 0, unit);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (g > 0) fold(BUF ^ 1);
   };
 
