@@ -52,6 +52,8 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
   static_assert(WAVES * RG * 64 * 4 * 4 <= WAVES * WBYTES, "reduction fits in the weight area");
   constexpr int SCL = COOP ? ROWS * ST * WAVES * 4 : 16;   // the workgroup's scale rows (K / 32 bytes each)
   static_assert(WAVES * WBYTES + SCL <= 160 * 1024, "LDS budget");
+  // The cooperative copy gives each wave at most one 1 KB piece of the scale rows.
+  static_assert(!COOP || (SCL + 1023) / 1024 <= WAVES, "one scale piece per wave at most");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[WAVES * WBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t scl[SCL];
 
