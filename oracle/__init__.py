@@ -81,6 +81,8 @@ def bind(lib):
     lib.oracle_fp8b_gemm_rows.argtypes = [i64, i64, i64, p, p, p, p, i64, i64, p, p]
     lib.oracle_mx_quantize.argtypes = [i64, i64, p, p, p]
     lib.oracle_mx_quantize.restype = ctypes.c_int
+    lib.oracle_nv_quantize.argtypes = [i64, i64, p, ctypes.c_float, p, p]
+    lib.oracle_nv_quantize.restype = ctypes.c_int
     return lib
 
 
@@ -259,6 +261,21 @@ def mx_quantize(x):
     scales = np.empty((rows, K // 32), np.uint8)
     if rows and K and _load().oracle_mx_quantize(rows, K, _ptr(x), _ptr(codes), _ptr(scales)):
         raise ValueError("oracle_mx_quantize: bad arguments")
+    return codes, scales
+
+
+def nv_quantize(x, g):
+    """fp32 [rows][K] (K % 16 == 0) and an fp32 global scale g > 0 -> (codes [rows][K/2] u8,
+    E4M3 scales [rows][K/16] u8) by the max-abs rule written out in oracle.c.  bf16 inputs
+    are passed widened to fp32 (exact)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 2 or x.shape[1] % 16:
+        raise ValueError("x must be [rows][K] with K a multiple of 16")
+    rows, K = x.shape
+    codes = np.empty((rows, K // 2), np.uint8)
+    scales = np.empty((rows, K // 16), np.uint8)
+    if rows and K and _load().oracle_nv_quantize(rows, K, _ptr(x), float(np.float32(g)), _ptr(codes), _ptr(scales)):
+        raise ValueError("oracle_nv_quantize: bad arguments")
     return codes, scales
 
 

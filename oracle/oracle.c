@@ -404,3 +404,83 @@ int oracle_mx_quantize(int64_t rows, int64_t K, const float *x, uint8_t *codes, 
     }
     return 0;
 }
+
+/* ---- NV quantizer (NVFP4 operand from activations) ---------------------
+ *
+ * The NVFP4 counterpart of oracle_mx_quantize: E2M1 codes with one E4M3 scale
+ * per 16 consecutive K elements (the issue page's "Scale Factor Granularity":
+ * sf_vec_size 16 with Float8E4M3FN scales) and one fp32 global scale g per
+ * tensor, supplied by the caller.  The pages fix no rounding rule; the reading
+ * taken is max-abs, with every decision taken in fp32 (the precision of the
+ * device kernel), per block with amax = max |x|:
+ *   sv = amax / (6 * g)                 (two fp32 operations: 6 * g, then amax / it)
+ *   s  = the E4M3 code nearest to sv, a tie going to the even code, values past
+ *        448 saturating to 448 (code 0x7E); found by trying every finite
+ *        non-negative code through oracle_e4m3fn;
+ *   if s decodes to 0 every code is +0; otherwise, with d = e4m3(s) * g (fp32),
+ *   each element becomes y = x / d (fp32), rounded to the nearest E2M1 value as
+ *   in oracle_mx_quantize (ties to the even mantissa bit, saturating at 6, zero
+ *   encoded +0).
+ * A block holding an infinity or NaN gets the NaN scale 0x7F and zero codes.
+ *
+ * x [rows][K] fp32, codes [rows][K/2], scales [rows][K/16].  Returns 0, or -1 on
+ * bad arguments (K not a multiple of 16, g not finite and positive). */
+static unsigned e4m3_nearest_code(float sv) {
+    /* saturation first: far above 448 every distance rounds to the same double */
+    if (sv >= 448.0f) return 0x7E;
+    unsigned best = 0;
+    double best_d = INFINITY;
+    for (unsigned c = 0; c <= 0x7E; ++c) {
+        const double d = fabs((double)sv - oracle_e4m3fn(c));
+        if (d < best_d || (d == best_d && (c & 1u) == 0 && (best & 1u) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return best;
+}
+
+int oracle_nv_quantize(int64_t rows, int64_t K, const float *x, float g, uint8_t *codes, uint8_t *scales) {
+    if (rows < 0 || K < 0 || K % 16 || !(g > 0.0f) || !isfinite(g)) return -1;
+    if (rows && K && (!x || !codes || !scales)) return -1;
+    const int64_t nb = K / 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *blk = x + r * K + 16 * b;
+            uint8_t *out = codes + r * (K / 2) + 8 * b;
+            int finite = 1;
+            float amax = 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                if (!isfinite(blk[i])) finite = 0;
+                else if (fabsf(blk[i]) > amax) amax = fabsf(blk[i]);
+            }
+            if (!finite) {
+                scales[r * nb + b] = 0x7F;
+                memset(out, 0, 8);
+                continue;
+            }
+            const float six_g = 6.0f * g;
+            const float sv = amax / six_g;
+            const unsigned s = e4m3_nearest_code(sv);
+            scales[r * nb + b] = (uint8_t)s;
+            const float sdec = (float)oracle_e4m3fn(s);
+            if (sdec == 0.0f) {
+                memset(out, 0, 8);
+                continue;
+            }
+            const float d = sdec * g;
+            for (int i = 0; i < 16; i += 2) {
+                unsigned nib[2];
+                for (int h = 0; h < 2; ++h) {
+                    const float y = blk[i + h] / d;
+                    unsigned c = e2m1_nearest_magnitude(fabs((double)y));
+                    if (c != 0 && y < 0.0f) c |= 8u;
+                    nib[h] = c;
+                }
+                out[i / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
+            }
+        }
+    }
+    return 0;
+}
