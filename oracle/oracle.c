@@ -349,6 +349,8 @@ int oracle_sampled(int kind, int64_t M, int64_t N, int64_t K,
  * x [rows][K] fp32, codes [rows][K/2] (low nibble = even k), scales
  * [rows][K/32].  Returns 0, or -1 on bad arguments (K not a multiple of 32). */
 static unsigned e2m1_nearest_magnitude(double y) {
+    /* saturation first: far above 6 every distance rounds to the same double */
+    if (y >= 6.0) return 7;
     unsigned best = 0;
     double best_d = INFINITY;
     for (unsigned c = 0; c < 8; ++c) {

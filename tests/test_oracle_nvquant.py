@@ -86,6 +86,19 @@ def test_scale_is_nearest_and_saturates(oracle_lib):
     assert list(s2[:, 0]) == [0x7E, 0x7E]
 
 
+def test_elements_saturate_however_large(oracle_lib):
+    # with the scale saturated at 448, x / d can be far above 6: the code is still 6
+    x = np.zeros((3, 16), np.float32)
+    x[0, 2] = np.float32(3e38)
+    x[1, 0], x[1, 1] = 6 * 500.0, -6 * 500.0
+    x[2, 5] = -np.float32(1e30)
+    codes, s = oracle_lib.nv_quantize(x, 1.0)
+    assert np.all(s[:, 0] == 0x7E)
+    c = datagen.unpack_nibbles(codes)[:, :16]
+    assert c[0, 2] == 7 and c[1, 0] == 7 and c[1, 1] == 15 and c[2, 5] == 15
+    assert c[0, [0, 1, 3]].tolist() == [0, 0, 0]
+
+
 def test_grid_values_round_trip(oracle_lib):
     # scale code 0x38 (1.0) with g = 1/4: d = 0.25 exactly, and x = 0.25 * grid value
     rng = np.random.default_rng(5)
