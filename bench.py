@@ -392,6 +392,22 @@ def bench_quant(steps, warmup, dev):
     return {"ms": mean_ms, "bytes": bytes_alg, "gbs": bytes_alg / (mean_ms * 1e-3) / 1e9}
 
 
+def bench_nvquant(steps, warmup, dev):
+    """NV quantizer on the same 8192 x 8192 fp32 activations (two alternating copies),
+    with the tensor's global scale max|x| / (448 * 6) computed once, outside the timing."""
+    rows, K = 8192, 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    xs = [torch.randn((rows, K), generator=g, device=dev, dtype=torch.float32) for _ in range(2)]
+    gs = [float(x.abs().max()) / (448.0 * 6.0) for x in xs]
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
+    fn = lambda X, gsc: fp4.nv_fp4_quantize(X, gsc, codes, scales)
+    mean_ms, _ = time_launches(fn, steps, warmup, dev, list(zip(xs, gs)))
+    bytes_alg = rows * K * 4 + codes.numel() + scales.numel()
+    return {"ms": mean_ms, "bytes": bytes_alg, "gbs": bytes_alg / (mean_ms * 1e-3) / 1e9}
+
+
 def bench_copy(dev, mib=512):
     """A plain device copy of known size, the reference that scales the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) into bytes."""
@@ -437,7 +453,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: mx8192 gemv gemvp w4a8 w4a8p nv1024 mx256 quant fp8b skinny copy")
+                    help="subset of: mx8192 gemv gemvp w4a8 w4a8p nv1024 mx256 quant nvquant fp8b skinny copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue launches eagerly instead of replaying a HIP graph (for counter runs)")
@@ -466,7 +482,7 @@ def main():
     dev = torch.device("cuda:0")
     fp4.load_library()
     only = set(args.only) if args.only else {"mx8192", "gemv", "gemvp", "w4a8", "w4a8p", "nv1024", "mx256",
-                                             "quant", "fp8b", "skinny"}
+                                             "quant", "nvquant", "fp8b", "skinny"}
     also = {}
     head = None
     d8192 = None
@@ -539,6 +555,15 @@ def main():
         q = bench_quant(args.steps, args.warmup, dev)
         log(f"bench: mx quantize {q['ms'] * 1e3:.1f} us/launch, {q['gbs']:.0f} GB/s")
         also["mx_quantize_8192x8192_f32"] = {
+            "metric": "HBM GB/s", "value": q["gbs"], "ms_per_launch": q["ms"],
+            "roofline": {"bound": "hbm", "achieved": q["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": q["gbs"] / PEAK_HBM_GBS, "traffic": None},
+            "algorithmic_bytes": q["bytes"]}
+    if "nvquant" in only:
+        log("bench: nv quantize 8192x8192 fp32 ...")
+        q = bench_nvquant(args.steps, args.warmup, dev)
+        log(f"bench: nv quantize {q['ms'] * 1e3:.1f} us/launch, {q['gbs']:.0f} GB/s")
+        also["nv_quantize_8192x8192_f32"] = {
             "metric": "HBM GB/s", "value": q["gbs"], "ms_per_launch": q["ms"],
             "roofline": {"bound": "hbm", "achieved": q["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": q["gbs"] / PEAK_HBM_GBS, "traffic": None},

@@ -26,20 +26,17 @@ import torch
 __all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm",
            "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked",
            "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
-           "nv_fp4_gemm_batched", "w4a8_gemm_batched", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
-           "fp4g_status_string",
+           "nv_fp4_gemm_batched", "w4a8_gemm_batched", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "nv_fp4_quantize",
+           "fp8_blockwise_gemm", "fp4g_status_string",
            "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfp4gemm.so")
 SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm",
+           "nv_fp4_gemm_batched", "w4a8_gemm", "w4a8_gemm_batched", "fp4_gemv",
            "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked",
            "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
-           "nv_fp4_gemm_batched", "w4a8_gemm_batched",
-           "nv_fp4_gemm_batched", "w4a8_gemm_batched",
-           "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
-           "nv_fp4_gemm_batched", "w4a8_gemm_batched", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "fp8_blockwise_gemm",
-           "fp4g_status_string")
+           "mx_fp4_quantize", "nv_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string")
 
 OUT_F32, OUT_BF16 = 0, 1
 IN_F32, IN_BF16 = 0, 1
@@ -100,6 +97,8 @@ def load_library():
     lib.fp8_blockwise_gemm.restype = c_int
     lib.mx_fp4_quantize.argtypes = [i64, i64, p, c_int, p, p, p]
     lib.mx_fp4_quantize.restype = c_int
+    lib.nv_fp4_quantize.argtypes = [i64, i64, p, c_int, f, p, p, p]
+    lib.nv_fp4_quantize.restype = c_int
     lib.fp4g_status_string.argtypes = [c_int]
     lib.fp4g_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -438,6 +437,33 @@ def mx_fp4_quantize(X, codes=None, scales=None):
     xt = IN_BF16 if X.dtype == torch.bfloat16 else IN_F32
     st = lib.mx_fp4_quantize(rows, K, _ptr(X), xt, _ptr(codes), _ptr(scales), _stream(device))
     _raise_on("mx_fp4_quantize", st)
+    return codes, scales
+
+
+def nv_fp4_quantize(X, global_scale, codes=None, scales=None):
+    """NV quantizer: X [rows, K] float32 or bfloat16 (K % 16 == 0) and an fp32 global scale
+    g > 0 -> (codes [rows, K/2] uint8 packed E2M1, scales [rows, K/16] uint8 E4M3), the
+    operand layout of nv_fp4_gemm with global scale g, by the max-abs rule of
+    include/fp4gemm.h."""
+    lib = load_library()
+    device = _device_of(X)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    if X.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"X must be float32 or bfloat16, got {X.dtype}")
+    rows, K = X.shape
+    if K % 16:
+        raise ValueError(f"K={K} must be a multiple of 16")
+    _check(X, "X", X.dtype, (rows, K), device)
+    if codes is None:
+        codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=device)
+    if scales is None:
+        scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=device)
+    _check(codes, "codes", torch.uint8, (rows, K // 2), device)
+    _check(scales, "scales", torch.uint8, (rows, K // 16), device)
+    xt = IN_BF16 if X.dtype == torch.bfloat16 else IN_F32
+    st = lib.nv_fp4_quantize(rows, K, _ptr(X), xt, float(global_scale), _ptr(codes), _ptr(scales), _stream(device))
+    _raise_on("nv_fp4_quantize", st)
     return codes, scales
 
 

@@ -6,6 +6,8 @@
 
 #include <stdint.h>
 
+#include <cmath>
+
 namespace {
 
 using fp4g::FP4Args;
@@ -374,11 +376,29 @@ fp4g_status mx_fp4_quantize(int64_t rows, int64_t K, const void* X, int x_type, 
                                          static_cast<uint8_t*>(scales), reinterpret_cast<hipStream_t>(stream)));
 }
 
+fp4g_status nv_fp4_quantize(int64_t rows, int64_t K, const void* X, int x_type, float global_scale, void* codes,
+                            void* scales, void* stream) {
+  if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim) return FP4G_EINVAL;
+  if (K > 0 && rows > kMaxOut / K) return FP4G_EINVAL;
+  if (x_type != FP4G_IN_F32 && x_type != FP4G_IN_BF16) return FP4G_EINVAL;
+  if (!(global_scale > 0.0f) || !std::isfinite(global_scale)) return FP4G_EINVAL;
+  if (K % 16 != 0) return FP4G_EUNSUPPORTED;
+  if (rows == 0 || K == 0) return FP4G_OK;
+  if (!X || !codes || !scales) return FP4G_EINVAL;
+  if (!aligned(X, 16) || !aligned(codes, 8)) return FP4G_EALIGN;
+  const Range x = range_of(X, rows * K * (x_type == FP4G_IN_BF16 ? 2 : 4));
+  const Range c = range_of(codes, rows * (K / 2)), sc = range_of(scales, rows * (K / 16));
+  if (overlaps(x, c) || overlaps(x, sc) || overlaps(c, sc)) return FP4G_EINVAL;
+  return finish(fp4g::launch_nv_quantize(rows, K, X, x_type == FP4G_IN_BF16, global_scale,
+                                         static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
 const char* fp4g_status_string(int status) {
   switch (status) {
     case FP4G_OK: return "ok";
     case FP4G_EINVAL: return "invalid argument (null pointer, negative size, bad output type or D overlapping an input)";
-    case FP4G_EUNSUPPORTED: return "unsupported shape (K must be a multiple of 128, of 32 for the quantizer; GEMV needs M <= 16)";
+    case FP4G_EUNSUPPORTED: return "unsupported shape (K must be a multiple of 128, of 32 for the MX quantizer, of 16 for the NV quantizer; GEMV needs M <= 16)";
     case FP4G_EALIGN: return "misaligned pointer (operands and D need 16-byte, scales 4-byte alignment)";
     case FP4G_EHIP: return "HIP runtime error at kernel launch";
     default: return "unknown status";

@@ -76,5 +76,7 @@ hipError_t launch_zero_fill(void* D, int64_t count, bool bf16_out, hipStream_t s
 // E2M1 codes + E8M0 scales of X[rows][K] (K % 32 == 0), max-abs rule.
 hipError_t launch_mx_quantize(int64_t rows, int64_t K, const void* X, bool bf16_in, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
+hipError_t launch_nv_quantize(int64_t rows, int64_t K, const void* X, bool bf16_in, float g, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
 
 }  // namespace fp4g

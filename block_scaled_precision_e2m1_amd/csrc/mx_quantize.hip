@@ -103,7 +103,119 @@ mx_quantize_kernel(int64_t nblocks, const void* __restrict__ X, uint8_t* __restr
   }
 }
 
+// ---- NV quantizer ------------------------------------------------------------------------
+// fp32 or bf16 X[rows][K] and an fp32 global scale g -> E2M1 codes [rows][K/2] and E4M3
+// block scales [rows][K/16], the NVFP4 operand of nv_fp4_gemm (the issue page's "Scale
+// Factor Granularity": sf_vec_size 16 with Float8E4M3FN scales).  The rule, per
+// 16-element block, every decision in fp32:
+//   sv = amax / (6 g);  s = the E4M3 code nearest to sv, ties to the even code, past
+//   448 saturating to 448;  with d = e4m3(s) * g and inv = min(1 / d, FLT_MAX), each
+//   element is x * inv rounded to the nearest E2M1 value, ties to the even code,
+//   saturating at 6, zero +0;  a scale that
+//   decodes to 0 gives zero codes;  a block holding an infinity or NaN gets scale 0x7F
+//   (NaN) and zero codes.
+// 4 lanes share a block (4 elements each): one wave-wide load is still 1 KB of
+// consecutive blocks.  The two divisions per block (amax / 6g and 1 / d) are IEEE fp32
+// (correctly rounded), and the E2M1 rounding is the same hardware conversion as the MX
+// kernel's, at scale 1.
+
+// Maximum over the 4-lane quad of unsigned integers.
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  uint32_t t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  return v > t ? v : t;
+}
+
+// The E4M3FN code nearest to sv >= 0 (+inf allowed), ties to the even code, values past
+// 448 saturating to 448 (code 0x7E).  Below 2^-6 the codes are the multiples of 2^-9
+// (code 8 = 2^-6 continues into the normal range); above, the fp32 mantissa is rounded
+// to 3 bits, ties to even, a carry moving into the exponent.
+__device__ __forceinline__ uint32_t e4m3_nearest(float sv) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, sv);
+  if (u >= 0x43E00000u) return 0x7Eu;                               // sv >= 448
+  if (u < 0x3C800000u) return (uint32_t)__builtin_rintf(sv * 512.0f);   // sv < 2^-6: 0 .. 8
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  const uint32_t code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u); // biased exponent E - 127 + 7
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+template <bool BF16_IN>
+__global__ void __launch_bounds__(256)
+nv_quantize_kernel(int64_t nblocks, const void* __restrict__ X, float g, uint8_t* __restrict__ codes,
+                   uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 3;                 // position of this lane's 4 elements in the block
+  const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const float six_g = 6.0f * g;
+  // 16 blocks per wave-unit
+  for (int64_t base = wave_id * 16 * kUnroll; base < nblocks; base += nwaves * 16 * kUnroll) {
+    uint32_t bits[kUnroll][4];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t blk = min(base + u * 16 + (lane >> 2), nblocks - 1);   // clamped: in bounds
+      if constexpr (BF16_IN) {
+        typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+        const v2u w = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(static_cast<const uint16_t*>(X) + blk * 16 + sub * 4));
+        bits[u][0] = w[0] << 16;
+        bits[u][1] = w[0] & 0xFFFF0000u;
+        bits[u][2] = w[1] << 16;
+        bits[u][3] = w[1] & 0xFFFF0000u;
+      } else {
+        const v4i w = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(static_cast<const float*>(X) + blk * 16 + sub * 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bits[u][i] = (uint32_t)w[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t blk = base + u * 16 + (lane >> 2);
+      uint32_t amax = 0, bad = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a = bits[u][i] & 0x7FFFFFFFu;
+        bad |= (a >= 0x7F800000u) ? 1u : 0u;
+        amax = a > amax ? a : amax;
+      }
+      amax = quad_max(amax);
+      bad = quad_max(bad);
+      const float sv = __builtin_bit_cast(float, amax) / six_g;     // IEEE fp32 division
+      const uint32_t s = e4m3_nearest(sv);
+      const float sdec = __builtin_amdgcn_cvt_f32_fp8((int)s, 0);
+      const float d = sdec * g;
+      const float inv = __builtin_fminf(1.0f / d, 3.40282347e38f);  // one reciprocal per block; 0 * inv = 0
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = __builtin_bit_cast(float, bits[u][i]) * inv;
+      uint32_t packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], 1.0f, 1);
+      const uint32_t nonzero = ((packed & 0x7777u) + 0x7777u) & 0x8888u;   // bit 3 of a nibble: magnitude != 0
+      packed &= nonzero | 0x7777u;
+      if (bad || sdec == 0.0f) packed = 0;
+      if (blk < nblocks) {
+        *reinterpret_cast<uint16_t*>(codes + blk * 8 + sub * 2) = (uint16_t)packed;
+        if (sub == 0) scales[blk] = bad ? (uint8_t)0x7F : (uint8_t)s;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_nv_quantize(int64_t rows, int64_t K, const void* X, bool bf16_in, float g, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s) {
+  const int64_t nblocks = rows * (K / 16);
+  const int64_t units = ceil_div(nblocks, 16 * kUnroll);         // wave-iterations of work
+  const int64_t wgs = ceil_div(units, 4);                          // 4 waves per workgroup
+  const unsigned grid = (unsigned)(wgs < device_cus() * 8 ? wgs : device_cus() * 8);
+  if (bf16_in)
+    hipLaunchKernelGGL(nv_quantize_kernel<true>, dim3(grid), dim3(256), 0, s, nblocks, X, g, codes, scales);
+  else
+    hipLaunchKernelGGL(nv_quantize_kernel<false>, dim3(grid), dim3(256), 0, s, nblocks, X, g, codes, scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_mx_quantize(int64_t rows, int64_t K, const void* X, bool bf16_in, uint8_t* codes,
                               uint8_t* scales, hipStream_t s) {

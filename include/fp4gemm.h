@@ -241,6 +241,27 @@ fp4g_status fp4_gemv_prepacked(int64_t M, int64_t N, int64_t K,
 fp4g_status mx_fp4_quantize(int64_t rows, int64_t K, const void *X, int x_type,
                             void *codes, void *scales, void *stream);
 
+/* NV quantizer: X[rows][K] (fp32 or bf16 by x_type) and an fp32 global scale g ->
+ * E2M1 codes [rows][K/2] (low nibble = even k) and E4M3 scales [rows][K/16], the
+ * operand of nv_fp4_gemm with global scale g (16-element E4M3 blocks: the issue
+ * page's "Scale Factor Granularity").  The pages fix no rounding rule; the rule is
+ * max-abs per 16-element block, every step in IEEE fp32:
+ *   sv = max|x| / (6 * g)   (6 * g first, then the division),
+ *   s  = the E4M3 code nearest to sv, ties to the even code, values past 448
+ *        saturating to 448 (0x7E),
+ *   code = the E2M1 value nearest to x * inv, with inv = min(1 / (e4m3(s) * g),
+ *          FLT_MAX) (one reciprocal per block), ties to the even mantissa bit,
+ *          magnitudes past 6 saturating to 6; a zero result is +0;
+ *   a scale that decodes to 0 gives all-zero codes; a block holding an infinity or
+ *   NaN gets scale 0x7F (NaN) and zero codes.
+ * The caller chooses g (for example max|X| / (448 * 6), which puts the largest block
+ * scale near the top of the E4M3 range); it must be finite and positive
+ * (FP4G_EINVAL otherwise).  Requires rows*K <= 2^50 (FP4G_EINVAL) and K a multiple
+ * of 16 (FP4G_EUNSUPPORTED); X 16-byte and codes 8-byte aligned; the three buffers
+ * must not overlap.  rows == 0 or K == 0 is a no-op. */
+fp4g_status nv_fp4_quantize(int64_t rows, int64_t K, const void *X, int x_type, float global_scale,
+                            void *codes, void *scales, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *fp4g_status_string(int status);
 

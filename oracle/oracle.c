@@ -33,6 +33,7 @@
  * Return value: 0 on success, -1 on an argument error (K not a multiple of V
  * or of 2, null pointer, negative size).
  */
+#include <float.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -419,10 +420,11 @@ int oracle_mx_quantize(int64_t rows, int64_t K, const float *x, uint8_t *codes, 
  *   s  = the E4M3 code nearest to sv, a tie going to the even code, values past
  *        448 saturating to 448 (code 0x7E); found by trying every finite
  *        non-negative code through oracle_e4m3fn;
- *   if s decodes to 0 every code is +0; otherwise, with d = e4m3(s) * g (fp32),
- *   each element becomes y = x / d (fp32), rounded to the nearest E2M1 value as
- *   in oracle_mx_quantize (ties to the even mantissa bit, saturating at 6, zero
- *   encoded +0).
+ *   if s decodes to 0 every code is +0; otherwise, with d = e4m3(s) * g and
+ *   inv = min(1 / d, FLT_MAX) (fp32; one reciprocal per block, clamped so that
+ *   0 * inv stays 0), each element becomes y = x * inv (fp32), rounded to the
+ *   nearest E2M1 value as in oracle_mx_quantize (ties to the even mantissa bit,
+ *   saturating at 6, zero encoded +0).
  * A block holding an infinity or NaN gets the NaN scale 0x7F and zero codes.
  *
  * x [rows][K] fp32, codes [rows][K/2], scales [rows][K/16].  Returns 0, or -1 on
@@ -472,10 +474,12 @@ int oracle_nv_quantize(int64_t rows, int64_t K, const float *x, float g, uint8_t
                 continue;
             }
             const float d = sdec * g;
+            float inv = 1.0f / d;
+            if (inv > FLT_MAX) inv = FLT_MAX;
             for (int i = 0; i < 16; i += 2) {
                 unsigned nib[2];
                 for (int h = 0; h < 2; ++h) {
-                    const float y = blk[i + h] / d;
+                    const float y = blk[i + h] * inv;
                     unsigned c = e2m1_nearest_magnitude(fabs((double)y));
                     if (c != 0 && y < 0.0f) c |= 8u;
                     nib[h] = c;

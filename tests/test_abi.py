@@ -34,7 +34,8 @@ def test_header_declares_the_operations():
                                             "fp4_gemv_prepack", "fp4_gemv_prepacked",
                                             "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
                                             "nv_fp4_gemm_batched", "w4a8_gemm_batched",
-                                            "mx_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string"])
+                                            "mx_fp4_quantize", "nv_fp4_quantize", "fp8_blockwise_gemm",
+                                            "fp4g_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -150,6 +151,23 @@ def test_quantizer_validation(lib):
     assert q(4, 64, A_, 0, A_ + 512, SB_, None) == EINVAL            # codes inside X (1 KB of fp32)
     assert q(4, 64, A_, 1, B_, B_ + 64, None) == EINVAL              # scales inside codes
     assert q(1 << 30, 1 << 30, A_, 0, B_, SB_, None) == EINVAL       # rows*K above 2^50
+
+
+def test_nv_quantizer_validation(lib):
+    q = lib.nv_fp4_quantize
+    assert q(0, 64, None, 0, 1.0, None, None, None) == OK             # empty: nothing read
+    assert q(4, 0, None, 1, 1.0, None, None, None) == OK
+    assert q(-1, 64, A_, 0, 1.0, B_, SB_, None) == EINVAL
+    assert q(4, 64, A_, 2, 1.0, B_, SB_, None) == EINVAL              # bad input type
+    for g in (0.0, -2.0, float("inf"), float("nan")):                 # global scale finite and > 0
+        assert q(4, 64, A_, 0, g, B_, SB_, None) == EINVAL
+    assert q(4, 40, A_, 0, 1.0, B_, SB_, None) == EUNSUP              # K % 16
+    assert q(4, 64, None, 0, 1.0, B_, SB_, None) == EINVAL
+    assert q(4, 64, A_ + 4, 0, 1.0, B_, SB_, None) == EALIGN
+    assert q(4, 64, A_, 0, 1.0, B_ + 4, SB_, None) == EALIGN          # codes 8-byte aligned
+    assert q(4, 64, A_, 0, 1.0, A_ + 512, SB_, None) == EINVAL        # codes inside X
+    assert q(4, 64, A_, 1, 1.0, B_, B_ + 64, None) == EINVAL          # scales inside codes
+    assert q(1 << 30, 1 << 30, A_, 0, 1.0, B_, SB_, None) == EINVAL   # rows*K above 2^50
 
 
 W_ = 0x10000000     # fake workspace address, far from the operands

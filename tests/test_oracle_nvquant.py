@@ -3,8 +3,9 @@ with a caller-supplied fp32 global scale g).
 
 The rule (a reading: the pages fix none) is written out in oracle.c: per 16-element
 block, sv = amax / (6 g) in fp32, the scale is the E4M3 code nearest to sv (ties to
-the even code, saturating at 448), and each element is x / (e4m3(s) g) in fp32 rounded
-to the nearest E2M1 value (ties to the even mantissa bit, saturating at 6, zero +0).
+the even code, saturating at 448), and each element is x * min(1 / (e4m3(s) g), FLT_MAX)
+in fp32, rounded to the nearest E2M1 value (ties to the even mantissa bit, saturating at
+6, zero +0).
 Each pin checks it against something other than the oracle's own search:
 - the E4M3 values printed by the format's definition (0x38 = 1, 0x7E = 448, ...) and
   exact round trips of all 126 positive finite scale codes;
