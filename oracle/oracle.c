@@ -436,7 +436,7 @@ static unsigned e4m3_nearest_code(float sv) {
     double best_d = INFINITY;
     for (unsigned c = 0; c <= 0x7E; ++c) {
         const double d = fabs((double)sv - oracle_e4m3fn(c));
-        if (d < best_d || (d == best_d && (c & 1u) == 0 && (best & 1u) == 1)) {
+        if (d < best_d || (d == best_d && !(c & 1u) && (best & 1u))) {
             best = c;
             best_d = d;
         }
@@ -456,8 +456,11 @@ int oracle_nv_quantize(int64_t rows, int64_t K, const float *x, float g, uint8_t
             int finite = 1;
             float amax = 0.0f;
             for (int i = 0; i < 16; ++i) {
-                if (!isfinite(blk[i])) finite = 0;
-                else if (fabsf(blk[i]) > amax) amax = fabsf(blk[i]);
+                if (!isfinite(blk[i])) {
+                    finite = 0;
+                    continue;
+                }
+                if (fabsf(blk[i]) > amax) amax = fabsf(blk[i]);
             }
             if (!finite) {
                 scales[r * nb + b] = 0x7F;
@@ -484,7 +487,7 @@ int oracle_nv_quantize(int64_t rows, int64_t K, const float *x, float g, uint8_t
                     if (c != 0 && y < 0.0f) c |= 8u;
                     nib[h] = c;
                 }
-                out[i / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
+                out[i >> 1] = (uint8_t)(nib[0] | (nib[1] << 4));
             }
         }
     }

@@ -19,6 +19,7 @@ from tests import test_oracle_codecs as codecs
 from tests import test_oracle_pins as pins
 from tests import test_oracle_quant as quant
 from tests import test_oracle_fp8b as fp8b
+from tests import test_oracle_nvquant as nvquant
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -58,6 +59,13 @@ MUTANTS = {
     "quant-negative-zero": ("if (c != 0 && y < 0.0) c |= 8u;", "if (y < 0.0) c |= 8u;"),
     "quant-nibble-order": ("out[i / 2] = (uint8_t)(nib[0] | (nib[1] << 4));", "out[i / 2] = (uint8_t)(nib[1] | (nib[0] << 4));"),
     "quant-no-nonfinite-check": ("if (!isfinite(blk[i])) finite = 0;", "if (0) finite = 0;"),
+    "nvq-ties-to-odd": ("!(c & 1u) && (best & 1u)", "(c & 1u) && !(best & 1u)"),
+    "nvq-six-g": ("const float six_g = 6.0f * g;", "const float six_g = 4.0f * g;"),
+    "nvq-no-saturation": ("if (sv >= 448.0f) return 0x7E;", "if (0) return 0x7E;"),
+    "nvq-block-offset": ("const float *blk = x + r * K + 16 * b;", "const float *blk = x + r * K + 8 * b;"),
+    "nvq-global-scale-dropped": ("const float d = sdec * g;", "const float d = sdec;"),
+    "nvq-nonfinite-scale": ("scales[r * nb + b] = 0x7F;", "scales[r * nb + b] = 0xFF;"),
+    "nvq-element-saturation": ("if (y >= 6.0) return 7;", "if (0) return 7;"),
     "fp8b-group-size": ("#define FP8_BLOCK 128", "#define FP8_BLOCK 64"),
     "fp8b-b-scale-row": ("const double sc = (double)sA[m * G + g] * (double)sB[n * G + g];",
                          "const double sc = (double)sA[m * G + g] * (double)sB[m * G + g];"),
@@ -71,7 +79,7 @@ MUTANTS = {
 def _quick_pins():
     """(callable, kwargs) for every quick pin, over all of its parametrisations."""
     out = []
-    for mod in (codecs, pins, quant, fp8b):
+    for mod in (codecs, pins, quant, fp8b, nvquant):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue

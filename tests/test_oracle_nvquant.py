@@ -42,7 +42,7 @@ def dequant(codes, scales, g):
     return mag * s * np.float64(np.float32(g))
 
 
-def test_e4m3_table_anchors():
+def test_e4m3_table_anchors(oracle_lib):
     assert E4[0x38] == 1.0 and E4[0x7E] == 448.0 and E4[0x01] == 2.0 ** -9
     assert E4[0x28] == 0.25 and E4[0x48] == 4.0 and E4[0x08] == 2.0 ** -6
     assert np.all(np.diff(E4) > 0)
