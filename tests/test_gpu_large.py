@@ -87,6 +87,24 @@ def test_quantizer_input_past_2_to_31_elements():
     torch.cuda.empty_cache()
 
 
+def test_nv_quantizer_input_past_2_to_31_elements():
+    rows, K = 1 << 16, 1 << 16                    # 2^32 fp32 inputs (16 GiB)
+    print(f"case large nv_fp4_quantize {rows}x{K}", flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(13)
+    X = torch.randn((rows, K), generator=g, device=DEV, dtype=torch.float32)
+    gs = float(X.abs().max()) / (448.0 * 6.0)
+    codes, scales = fp4.nv_fp4_quantize(X, gs)
+    torch.cuda.synchronize(DEV)
+    sel = np.array([0, 1, rows // 2, rows - 2, rows - 1])
+    idx = torch.from_numpy(sel).to(DEV)
+    c_ref, s_ref = oracle.nv_quantize(X[idx].cpu().numpy(), gs)
+    assert np.array_equal(scales[idx].cpu().numpy(), s_ref)
+    assert np.array_equal(codes[idx].cpu().numpy(), c_ref)
+    del X, codes, scales
+    torch.cuda.empty_cache()
+
+
 def far_points(M, N, rng):
     ms, ns = spread(M, N, 2000, rng)
     assert int(ms[-1]) * N + int(ns[-1]) > 2 ** 31
