@@ -25,7 +25,7 @@ import torch
 
 __all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm",
            "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked",
-           "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
+           "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3", "w4a8_gemm_prepacked",
            "nv_fp4_gemm_batched", "w4a8_gemm_batched", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "nv_fp4_quantize",
            "fp8_blockwise_gemm", "fp4g_status_string",
            "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
@@ -35,7 +35,7 @@ _LIB_PATH = os.path.join(_HERE, "libfp4gemm.so")
 SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm",
            "nv_fp4_gemm_batched", "w4a8_gemm", "w4a8_gemm_batched", "fp4_gemv",
            "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked",
-           "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
+           "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3", "w4a8_gemm_prepacked",
            "mx_fp4_quantize", "nv_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string")
 
 OUT_F32, OUT_BF16 = 0, 1
@@ -81,6 +81,8 @@ def load_library():
     lib.w4a8_prepack_size.restype = c_int
     lib.w4a8_prepack.argtypes = [i64, i64, p, p, p, p, p]
     lib.w4a8_prepack.restype = c_int
+    lib.w4a8_prepack_e4m3.argtypes = [i64, i64, p, p, i64, p, p, p]
+    lib.w4a8_prepack_e4m3.restype = c_int
     lib.w4a8_gemm_prepacked.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.w4a8_gemm_prepacked.restype = c_int
     lib.nv_fp4_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, f, p, p, f, p, c_int, p]
@@ -336,6 +338,29 @@ def w4a8_prepack(B, sB):
     Sp = torch.empty(sb // 4, dtype=torch.float32, device=device)
     st = lib.w4a8_prepack(N, K, _ptr(B), _ptr(sB), _ptr(Bp), _ptr(Sp), _stream(device))
     _raise_on("w4a8_prepack", st)
+    return Bp, Sp
+
+
+def w4a8_prepack_e4m3(B, sB8, scale_stride=1):
+    """Re-pack W4A8 weights B [N, K/2] (INT4) with E4M3 group scales for
+    w4a8_gemm_prepacked: sB8 uint8 [N, K/128] (scale_stride 1) or [N, K/128, 8] (the
+    Array<E4M3, 8> packing, scale_stride 8); returns (Bp uint8, Sp float32)."""
+    lib = load_library()
+    device = _device_of(B)
+    if B.dim() != 2:
+        raise ValueError("B must be 2-D")
+    N, K = B.shape[0], B.shape[1] * 2
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    if scale_stride not in (1, 8):
+        raise ValueError("scale_stride must be 1 or 8")
+    _check(B, "B", torch.uint8, (N, K // 2), device)
+    _check(sB8, "sB8", torch.uint8, (N, K // 128) if scale_stride == 1 else (N, K // 128, 8), device)
+    wb, sb = w4a8_prepack_size(N, K)
+    Bp = torch.empty(wb, dtype=torch.uint8, device=device)
+    Sp = torch.empty(sb // 4, dtype=torch.float32, device=device)
+    st = lib.w4a8_prepack_e4m3(N, K, _ptr(B), _ptr(sB8), int(scale_stride), _ptr(Bp), _ptr(Sp), _stream(device))
+    _raise_on("w4a8_prepack_e4m3", st)
     return Bp, Sp
 
 

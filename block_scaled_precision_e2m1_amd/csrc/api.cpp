@@ -339,6 +339,25 @@ fp4g_status w4a8_prepack(int64_t N, int64_t K, const void* B, const void* sB, vo
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
+fp4g_status w4a8_prepack_e4m3(int64_t N, int64_t K, const void* B, const void* sB8, int64_t scale_stride, void* Bp,
+                              void* Sp, void* stream) {
+  if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim) return FP4G_EINVAL;
+  if (scale_stride != 1 && scale_stride != 8) return FP4G_EINVAL;
+  if (K % 128 != 0) return FP4G_EUNSUPPORTED;
+  if (N == 0 || K == 0) return FP4G_OK;
+  if (!B || !sB8 || !Bp || !Sp) return FP4G_EINVAL;
+  if (!aligned(B, 16) || !aligned(Bp, 16) || !aligned(Sp, 4)) return FP4G_EALIGN;
+  int64_t wb = 0, sb = 0;
+  fp4g::w4a8_prepack_sizes(N, K, &wb, &sb);
+  const Range ib = range_of(B, N * (K / 2)), is = range_of(sB8, N * (K / 128) * scale_stride);
+  const Range ob = range_of(Bp, wb), os = range_of(Sp, sb);
+  if (overlaps(ob, os) || overlaps(ob, ib) || overlaps(ob, is) || overlaps(os, ib) || overlaps(os, is))
+    return FP4G_EINVAL;
+  return finish(fp4g::launch_w4a8_prepack_e4m3(N, K, static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(sB8),
+                                               (int)scale_stride, static_cast<uint8_t*>(Bp), static_cast<float*>(Sp),
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
 fp4g_status w4a8_gemm_prepacked(int64_t M, int64_t N, int64_t K, const void* A, const float* sa, const void* Bp,
                                 const void* Sp, void* D, int d_type, void* stream) {
   bool empty = false;

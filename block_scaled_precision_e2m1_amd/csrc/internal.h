@@ -67,6 +67,8 @@ hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t s);
 void w4a8_prepack_sizes(int64_t N, int64_t K, int64_t* weight_bytes, int64_t* scale_bytes);
 hipError_t launch_w4a8_prepack(int64_t N, int64_t K, const uint8_t* B, const uint16_t* sB, uint8_t* Bp, float* Sp,
                                hipStream_t s);
+hipError_t launch_w4a8_prepack_e4m3(int64_t N, int64_t K, const uint8_t* B, const uint8_t* sB8, int stride,
+                                    uint8_t* Bp, float* Sp, hipStream_t s);
 hipError_t launch_w4a8_gemm_prepacked(const W4A8Args& a, const float* Sp, hipStream_t s);
 // The same ring kernel on plain INT4 weights and bf16 scales (K % 256 == 0, sB 4-byte aligned).
 hipError_t launch_w4a8_ring(const W4A8Args& a, hipStream_t s);

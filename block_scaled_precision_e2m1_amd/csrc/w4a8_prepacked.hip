@@ -107,6 +107,20 @@ w4a8_prepack_scales_kernel(int64_t units, int N, int G, int64_t Np, const uint16
   }
 }
 
+// The same Sp from E4M3 group scales: scale (n, kg) is the byte sB8[(n * G + kg) * stride],
+// stride 1 for a plain [N][K/128] array or 8 for the Hopper post's Array<float_e4m3_t, 8>
+// packing (section "The W4A8 kernel: the same four definitions, with the operands
+// swapped": each FP8 scale stored as an array of 8 elements; the first is read).  Every
+// E4M3 value is exact in fp32; a NaN code stays NaN.
+__global__ void __launch_bounds__(256)
+w4a8_prepack_e4m3_scales_kernel(int64_t units, int N, int G, int64_t Np, const uint8_t* __restrict__ sB8,
+                                int stride, float* __restrict__ Sp) {
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256) {
+    const int64_t n = u % Np, kg = u / Np;
+    Sp[u] = n < N ? __builtin_amdgcn_cvt_f32_fp8((int)sB8[(n * G + kg) * stride], 0) : 0.0f;
+  }
+}
+
 // PACKED: Bw is Bp and Sw is Sp as laid out above.  Otherwise Bw is the plain
 // w4a8_gemm weight B [N][K/2] and Sw its bf16 group scales sB [N][K/128] (K % 256 == 0,
 // sB 4-byte aligned): a wave copies its 16 rows x 64 bytes of the group with the
@@ -323,6 +337,21 @@ hipError_t launch_w4a8_prepack(int64_t N, int64_t K, const uint8_t* B, const uin
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(w4a8_prepack_scales_kernel, dim3(gs), dim3(256), 0, s, su, (int)N, (int)G, Np, sB, Sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_prepack_e4m3(int64_t N, int64_t K, const uint8_t* B, const uint8_t* sB8, int stride,
+                                    uint8_t* Bp, float* Sp, hipStream_t s) {
+  const int64_t G16 = ceil_div(N, 16), G = K / 128, Np = 16 * G16;
+  const int64_t cap = device_cus() * 8;
+  const int64_t wu = G16 * G * 64, su = G * Np;
+  const unsigned gw = (unsigned)(ceil_div(wu, 256) < cap ? ceil_div(wu, 256) : cap);
+  const unsigned gs = (unsigned)(ceil_div(su, 256) < cap ? ceil_div(su, 256) : cap);
+  hipLaunchKernelGGL(w4a8_prepack_weights_kernel, dim3(gw), dim3(256), 0, s, wu, (int)N, (int)G, K / 2, B, Bp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(w4a8_prepack_e4m3_scales_kernel, dim3(gs), dim3(256), 0, s, su, (int)N, (int)G, Np, sB8, stride,
+                     Sp);
   return hipGetLastError();
 }
 

@@ -161,6 +161,20 @@ fp4g_status w4a8_gemm_prepacked(int64_t M, int64_t N, int64_t K,
                                 const void *Bp, const void *Sp,
                                 void *D, int d_type, void *stream);
 
+/* The same pre-packed weights from E4M3 group scales instead of bf16 ones: the FP8
+ * scale type of the Hopper post's W4A8 kernel (section "The W4A8 kernel: the same four
+ * definitions, with the operands swapped", where each FP8 scale is stored as
+ * Array<float_e4m3_t, 8>).  Scale (n, g) is the E4M3 byte sB8[(n * (K/128) + g) *
+ * scale_stride]: scale_stride 1 for a plain [N][K/128] array, 8 for that Array<8>
+ * packing (the first of the 8 bytes is read).  Bp is as from w4a8_prepack and Sp
+ * holds the scales widened to fp32 (exact; a NaN code stays NaN), so
+ * w4a8_gemm_prepacked computes
+ *   D[m][n] = sa[m] * sum_g e4m3(scale(n, g)) * sum_{k in g} e4m3(A[m][k]) * int4(B[n][k]).
+ * scale_stride other than 1 or 8 is FP4G_EINVAL; alignment and overlap rules as for
+ * w4a8_prepack (sB8 needs no alignment). */
+fp4g_status w4a8_prepack_e4m3(int64_t N, int64_t K, const void *B, const void *sB8, int64_t scale_stride,
+                              void *Bp, void *Sp, void *stream);
+
 /* FP8 blockwise-scaled GEMM, the FP8 starting point of the issue page ("What
  * Works"; "Scale Factor Granularity": FP8 scales cover 128 elements of K):
  *   D[m][n] = sum_g sA[m][g] * sB[n][g] * sum_{k in group g} e4m3(A[m][k]) * e4m3(B[n][k])

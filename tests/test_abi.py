@@ -32,7 +32,8 @@ def test_header_declares_the_operations():
     assert declared_functions() == sorted(["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size",
                                             "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "fp4_gemv_prepack_size",
                                             "fp4_gemv_prepack", "fp4_gemv_prepacked",
-                                            "w4a8_prepack_size", "w4a8_prepack", "w4a8_gemm_prepacked",
+                                            "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3",
+                                            "w4a8_gemm_prepacked",
                                             "nv_fp4_gemm_batched", "w4a8_gemm_batched",
                                             "mx_fp4_quantize", "nv_fp4_quantize", "fp8_blockwise_gemm",
                                             "fp4g_status_string"])
@@ -168,6 +169,17 @@ def test_nv_quantizer_validation(lib):
     assert q(4, 64, A_, 0, 1.0, A_ + 512, SB_, None) == EINVAL        # codes inside X
     assert q(4, 64, A_, 1, 1.0, B_, B_ + 64, None) == EINVAL          # scales inside codes
     assert q(1 << 30, 1 << 30, A_, 0, 1.0, B_, SB_, None) == EINVAL   # rows*K above 2^50
+
+
+def test_w4a8_prepack_e4m3_validation(lib):
+    f = lib.w4a8_prepack_e4m3
+    assert f(0, 128, None, None, 1, None, None, None) == OK           # empty: nothing touched
+    assert f(4, 128, A_, SB_, 2, B_, D_, None) == EINVAL              # stride 1 or 8 only
+    assert f(4, 192, A_, SB_, 1, B_, D_, None) == EUNSUP
+    assert f(4, 128, A_, None, 8, B_, D_, None) == EINVAL
+    assert f(4, 128, A_ + 8, SB_, 1, B_, D_, None) == EALIGN
+    assert f(4, 128, A_, SB_, 1, B_, D_ + 2, None) == EALIGN          # Sp 4-byte aligned
+    assert f(4, 128, A_, SB_, 8, A_ + 16, D_, None) == EINVAL          # Bp over B
 
 
 W_ = 0x10000000     # fake workspace address, far from the operands

@@ -110,3 +110,66 @@ def test_edge_cases():
     Bp, Sp = fp4.w4a8_prepack(torch.zeros((20, 64), dtype=torch.uint8, device=DEV),
                               torch.zeros((20, 1), dtype=torch.bfloat16, device=DEV))
     assert fp4.w4a8_gemm_prepacked(A, sa, Bp, Sp, 20).shape == (0, 20)
+
+
+# ---- E4M3 group scales (w4a8_prepack_e4m3) ------------------------------------------------
+# Every E4M3 value is exactly a bf16 value, so the oracle's W4A8 product with the scales
+# written as bf16 bit patterns is the product with E4M3 scales.
+
+def e4m3_as_bf16_bits(codes):
+    v = np.array([oracle.e4m3fn(int(c)) for c in codes.ravel()], np.float32).reshape(codes.shape)
+    bits = v.view(np.uint32)
+    assert not np.any(bits[np.isfinite(v)] & 0xFFFF), "an E4M3 value that bf16 does not hold"
+    return (bits >> 16).astype(np.uint16)
+
+
+def e4m3_scales(N, G, rng):
+    """Codes of the workload's scale range (about 0.005 .. 0.05): 0x0A (2^-7 * 1.25) .. 0x1D."""
+    return rng.integers(0x0A, 0x1E, (N, G)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("stride", [1, 8])
+@pytest.mark.parametrize("NK", [(16, 128), (100, 640), (777, 2048)])
+def test_prepack_e4m3_matches_definition(NK, stride):
+    N, K = NK
+    G = K // 128
+    print(f"case w4a8 prepack e4m3 {N}x{K} stride {stride}", flush=True)
+    rng = np.random.default_rng(N + K + stride)
+    d = datagen.make_shape("w4a8", 4, N, K, seed=N + K)
+    s8 = rng.integers(0, 256, (N, G)).astype(np.uint8)               # every code, NaN and negative included
+    packed = np.repeat(s8[:, :, None], 8, axis=2) if stride == 8 else s8
+    if stride == 8:
+        packed[:, :, 1:] = rng.integers(0, 256, (N, G, 7))             # only the first byte counts
+    t = up(d)
+    Bp, Sp = fp4.w4a8_prepack_e4m3(t["B"], torch.from_numpy(np.ascontiguousarray(packed)).to(DEV), stride)
+    torch.cuda.synchronize(DEV)
+    Bo, _ = oracle.w4a8_prepack(d["B"], d["sB"])
+    assert np.array_equal(Bp.cpu().numpy(), Bo)
+    G16 = -(-N // 16)
+    want = np.zeros((G, 16 * G16), np.float32)
+    want[:, :N] = np.array([[oracle.e4m3fn(int(c)) for c in row] for row in s8], np.float32).T
+    got = Sp.cpu().numpy().reshape(G, 16 * G16)
+    nan = np.isnan(want)                                               # codes 0x7F and 0xFF
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))   # -0 included
+
+
+@pytest.mark.parametrize("stride", [1, 8])
+@pytest.mark.parametrize("shape", [(7, 33, 256), (100, 300, 384), (256, 1024, 2048)])
+def test_prepacked_gemm_e4m3_scales_matches_oracle(shape, stride):
+    M, N, K = shape
+    G = K // 128
+    print(f"case w4a8 prepacked e4m3 {M}x{N}x{K} stride {stride}", flush=True)
+    rng = np.random.default_rng(M + N + K)
+    d = datagen.make_shape("w4a8", M, N, K, seed=M + 5 * N + K)
+    s8 = e4m3_scales(N, G, rng)
+    d["sB"] = e4m3_as_bf16_bits(s8)
+    packed = np.ascontiguousarray(np.repeat(s8[:, :, None], 8, axis=2) if stride == 8 else s8)
+    t = up(d)
+    Bp, Sp = fp4.w4a8_prepack_e4m3(t["B"], torch.from_numpy(packed).to(DEV), stride)
+    D = fp4.w4a8_gemm_prepacked(t["A"], t["sa"], Bp, Sp, N, out_dtype=torch.float32)
+    torch.cuda.synchronize(DEV)
+    ref, S = oracle.w4a8_gemm(d["A"], d["sa"], d["B"], d["sB"])
+    r = oracle.parity_ratio(D.cpu().numpy().astype(np.float64), ref, S, "f32")
+    print(f"  max |err|/tol = {r:.3f}", flush=True)
+    assert r <= 1.0
