@@ -567,8 +567,13 @@ int64_t mxfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t re
 hipError_t launch_mxfp4_gemm_batched(const FP4Args& a, int64_t L, int64_t S, float* P, hipStream_t s) {
   const bool k256 = a.K % 256 == 0;
   if (S > 1) {
-    hipError_t e = k256 ? launch_cfg<128, 128, 64, 64, 256, 2, true>(a, L, (int)S, P, s)
-                        : launch_cfg<128, 128, 64, 64, 128, 4, true>(a, L, (int)S, P, s);
+    hipError_t e;
+    if (a.M <= 64)   // 64-row tiles: no half-empty 128-row tiles (64 x 8192 x 8192: 18.6 -> 17.8 us)
+      e = k256 ? launch_cfg<64, 128, 32, 64, 256, 2, true>(a, L, (int)S, P, s)
+               : launch_cfg<64, 128, 32, 64, 128, 4, true>(a, L, (int)S, P, s);
+    else
+      e = k256 ? launch_cfg<128, 128, 64, 64, 256, 2, true>(a, L, (int)S, P, s)
+               : launch_cfg<128, 128, 64, 64, 128, 4, true>(a, L, (int)S, P, s);
     if (e != hipSuccess) return e;
     return launch_reduce(a, L, (int)S, P, s);
   }
