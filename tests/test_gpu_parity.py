@@ -392,6 +392,23 @@ def test_fp8b_shapes(shape, out):
     check_full("fp8b", d, out)
 
 
+# Shapes with at least one 256 x 128 tile per CU, which take the large-tile kernel:
+# ragged in M and N with an odd number of K groups, and a single K group.
+F8_BIG = [(4300, 2100, 384, "bf16"), (4096, 2048, 128, "f32")]
+
+
+@pytest.mark.parametrize("shape", F8_BIG, ids=[f"{m}x{n}x{k}-{o}" for m, n, k, o in F8_BIG])
+def test_fp8b_big_tile_config_full(shape):
+    M, N, K, out = shape
+    d = datagen.make_shape("fp8b", M, N, K, seed=M + N + K)
+    if out == "f32":                              # scales over many octaves, one negative
+        rng = np.random.default_rng(K)
+        d["sA"] = (d["sA"] * np.ldexp(1.0, rng.integers(-20, 20, d["sA"].shape))).astype(np.float32)
+        d["sB"][1000, 0] = -d["sB"][1000, 0]
+    print(f"case fp8b big tiles {M}x{N}x{K} {out}", flush=True)
+    check_full("fp8b", d, out)
+
+
 def test_fp8b_workload_sampled():
     d = datagen.make("fp8_block_4096")
     print("case fp8b 4096^3 seed 0", flush=True)
