@@ -181,7 +181,7 @@ UTIL_KERNELS = [("mxfp4_gemm_8192x8192x8192", "mxfp4_gemm_kernel<256, 256, 128, 
                 ("w4a8_256x8192x8192", "w4a8p_gemm_kernel<64, false",
                  ["w4a8_gemm.hip", "w4a8_prepacked.hip", "common.hpp"]),
                 ("w4a8_256x8192x8192_prepacked", "w4a8p_gemm_kernel<64, true", ["w4a8_prepacked.hip", "common.hpp"]),
-                ("fp8_blockwise_4096", "fp8b_gemm_kernel<", ["fp8b_gemm.hip", "common.hpp"]),
+                ("fp8_blockwise_4096", "fp8b_gemm_big_kernel<", ["fp8b_gemm.hip", "common.hpp"]),
                 ("nvfp4_1024", "nvfp4_gemm_kernel<", ["nvfp4_gemm.hip", "common.hpp"]),
                 ("mx_quantize_8192x8192_f32", "mx_quantize_kernel<", ["mx_quantize.hip", "common.hpp"])]
 UTIL_METRICS = ("MfmaUtil", "LdsUtil", "VALUBusy", "LdsBankConflict")
