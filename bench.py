@@ -102,8 +102,24 @@ def src_digest(*names):
 
 
 # Counter summaries: (profile name, kernel-name prefix in the trace, sources of the kernel).
-COUNTED = [("mxfp4_gemm_8192", "fp4g::(anonymous namespace)::mxfp4_gemm_kernel", ["mxfp4_gemm.hip", "common.hpp"]),
-           ("fp4_gemv_8x14336x4096", "fp4g::(anonymous namespace)::fp4_gemv_kernel", ["fp4_gemv.hip", "common.hpp"])]
+_NS = "fp4g::(anonymous namespace)::"
+COUNTED = [("mxfp4_gemm_8192", _NS + "mxfp4_gemm_kernel", ["mxfp4_gemm.hip", "common.hpp"]),
+           ("fp4_gemv_8x14336x4096", _NS + "fp4_gemv_kernel", ["fp4_gemv.hip", "common.hpp"]),
+           ("w4a8_256x8192x8192", _NS + "w4a8p_gemm_kernel<64, false",
+            ["w4a8_gemm.hip", "w4a8_prepacked.hip", "common.hpp"]),
+           ("w4a8_prepacked_256x8192x8192", _NS + "w4a8p_gemm_kernel<64, true", ["w4a8_prepacked.hip", "common.hpp"]),
+           ("nvfp4_gemm_1024", _NS + "nvfp4_gemm_kernel<", ["nvfp4_gemm.hip", "common.hpp"]),
+           ("fp8_blockwise_4096", _NS + "fp8b_gemm_big_kernel<", ["fp8b_gemm.hip", "common.hpp"]),
+           ("mx_quantize_8192x8192_f32", _NS + "mx_quantize_kernel<", ["mx_quantize.hip", "common.hpp"]),
+           ("nv_quantize_8192x8192_f32", _NS + "nv_quantize_kernel<", ["mx_quantize.hip", "common.hpp"])]
+# The kernels that the counter runs cover: `bench.py --only` + this list.
+COUNTED_ONLY = "mx8192 gemv w4a8 w4a8p nv1024 fp8b quant nvquant copy"
+
+
+def traffic_of(name):
+    """traffic_from_profile for a COUNTED entry."""
+    src = next(src for n, _, src in COUNTED if n == name)
+    return traffic_from_profile(name, src, None)
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -122,7 +138,7 @@ def traffic_from_profile(name, kernel_src, launches_bytes):
 
 def summarize_counters(fetch_dir, write_dir, command):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
-    `bench.py --only mx8192 gemv copy --no-graph` into profiles/<name>_counters.txt.
+    `bench.py --only <COUNTED_ONLY> --no-graph` into profiles/<name>_counters.txt.
     The counters are scaled by what they read for the 512 MiB device copy (which
     reads and writes exactly 512 MiB): bytes = counter * (copy bytes / copy counter)."""
     import csv
@@ -349,7 +365,8 @@ def bench_fp8b(steps, warmup, dev):
     D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     fn = lambda: fp4.fp8_blockwise_gemm(t["A"], t["sA"], t["B"], t["sB"], out=D)
     mean_ms, _ = time_launches(fn, steps, warmup, dev)
-    return {"ms": mean_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12}
+    bytes_alg = d["A"].nbytes + d["sA"].nbytes + d["B"].nbytes + d["sB"].nbytes + M * N * 2
+    return {"ms": mean_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12, "bytes": bytes_alg}
 
 
 def bench_skinny(steps, warmup, dev, L=1, M=128, N=8192, K=8192):
@@ -522,8 +539,9 @@ def main():
             "metric": "TFLOP/s", "value": w["tflops"], "ms_per_launch": w["ms"],
             "cache": f"cold ({w['copies']} rotating weight copies)",
             "roofline": {"bound": "mfma", "achieved": w["tflops"], "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
-                         "frac": w["tflops"] / PEAK_TFLOPS["fp8"], "traffic": None},
-            "hbm": {"achieved": w["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": w["gbs"] / PEAK_HBM_GBS}}
+                         "frac": w["tflops"] / PEAK_TFLOPS["fp8"], "traffic": traffic_of("w4a8_256x8192x8192")},
+            "hbm": {"achieved": w["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": w["gbs"] / PEAK_HBM_GBS},
+            "algorithmic_bytes": w["bytes"]}
     if "w4a8p" in only:
         log("bench: prepacked w4a8 256x8192x8192 ...")
         w = bench_w4a8_prepacked(args.steps, args.warmup, dev)
@@ -533,15 +551,18 @@ def main():
             "cache": f"cold ({w['copies']} rotating weight copies)",
             "weights": "re-packed once at load time (w4a8_prepack), not timed",
             "roofline": {"bound": "mfma", "achieved": w["tflops"], "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
-                         "frac": w["tflops"] / PEAK_TFLOPS["fp8"], "traffic": None},
-            "hbm": {"achieved": w["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": w["gbs"] / PEAK_HBM_GBS}}
+                         "frac": w["tflops"] / PEAK_TFLOPS["fp8"],
+                         "traffic": traffic_of("w4a8_prepacked_256x8192x8192")},
+            "hbm": {"achieved": w["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": w["gbs"] / PEAK_HBM_GBS},
+            "algorithmic_bytes": w["bytes"]}
     if "nv1024" in only:
         n = bench_nv1024(args.steps, args.warmup, dev)
         log(f"bench: nvfp4 1024^3 {n['ms'] * 1e3:.1f} us/launch, {n['tflops']:.0f} TFLOP/s")
         also["nvfp4_1024"] = {"metric": "TFLOP/s", "value": n["tflops"], "ms_per_launch": n["ms"],
                               "roofline": {"bound": "mfma", "achieved": n["tflops"], "peak": PEAK_TFLOPS["bf16"],
                                            "unit": "TFLOP/s", "frac": n["tflops"] / PEAK_TFLOPS["bf16"],
-                                           "traffic": None}}
+                                           "traffic": traffic_of("nvfp4_gemm_1024")},
+                              "algorithmic_bytes": 3276808}
     if "fp8b" in only:
         log("bench: fp8 blockwise 4096^3 ...")
         f = bench_fp8b(args.steps, args.warmup, dev)
@@ -549,7 +570,8 @@ def main():
         also["fp8_blockwise_4096"] = {
             "metric": "TFLOP/s", "value": f["tflops"], "ms_per_launch": f["ms"],
             "roofline": {"bound": "mfma", "achieved": f["tflops"], "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
-                         "frac": f["tflops"] / PEAK_TFLOPS["fp8"], "traffic": None}}
+                         "frac": f["tflops"] / PEAK_TFLOPS["fp8"], "traffic": traffic_of("fp8_blockwise_4096")},
+            "algorithmic_bytes": f["bytes"]}
     if "quant" in only:
         log("bench: mx quantize 8192x8192 fp32 ...")
         q = bench_quant(args.steps, args.warmup, dev)
@@ -557,7 +579,7 @@ def main():
         also["mx_quantize_8192x8192_f32"] = {
             "metric": "HBM GB/s", "value": q["gbs"], "ms_per_launch": q["ms"],
             "roofline": {"bound": "hbm", "achieved": q["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": q["gbs"] / PEAK_HBM_GBS, "traffic": None},
+                         "frac": q["gbs"] / PEAK_HBM_GBS, "traffic": traffic_of("mx_quantize_8192x8192_f32")},
             "algorithmic_bytes": q["bytes"]}
     if "nvquant" in only:
         log("bench: nv quantize 8192x8192 fp32 ...")
@@ -566,7 +588,7 @@ def main():
         also["nv_quantize_8192x8192_f32"] = {
             "metric": "HBM GB/s", "value": q["gbs"], "ms_per_launch": q["ms"],
             "roofline": {"bound": "hbm", "achieved": q["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": q["gbs"] / PEAK_HBM_GBS, "traffic": None},
+                         "frac": q["gbs"] / PEAK_HBM_GBS, "traffic": traffic_of("nv_quantize_8192x8192_f32")},
             "algorithmic_bytes": q["bytes"]}
     if "skinny" in only:
         log("bench: mxfp4 batched/split-K 128x8192x8192 (cold weights) ...")

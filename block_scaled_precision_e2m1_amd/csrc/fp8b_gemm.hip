@@ -240,7 +240,14 @@ fp8b_gemm_big_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const f
   const int T = tiles_m * tiles_n;
   int lin = blockIdx.x;
   if ((T & 7) == 0) lin = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
-  const int m0 = (lin / tiles_n) * GBM, n0 = (lin % tiles_n) * GBN;
+  // Consecutive ids go to the 8 XCDs in turn: regroup so each XCD owns a contiguous
+  // range of ids. Then walk groups of 4 tile rows column by column, so the 32 tiles
+  // that one XCD runs at once form a 4 x 8 block: per 128-element group they share 4 A
+  // and 8 B slices in that XCD's L2 instead of 1 and 32 (4096^3: 139 against 291 MB
+  // fetched per launch, 115 against 117.5 us on the same box).
+  const int grp = lin / (4 * tiles_n), first = 4 * grp;
+  const int gm = min(tiles_m - first, 4), r = lin - grp * 4 * tiles_n;
+  const int m0 = (first + r % gm) * GBM, n0 = (r / gm) * GBN;
   const int G = K / 128;
 
   // Copy c of an operand covers its rows 8c .. 8c+7: A copies 4w .. 4w+3, B copies 2w, 2w+1.
