@@ -150,6 +150,15 @@ nv_quantize_kernel(int64_t nblocks, const void* __restrict__ X, float g, uint8_t
   const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
   const float six_g = 6.0f * g;
+  // The reciprocal 1 / (e4m3(s) * g) takes one of 127 values per call: the workgroup
+  // computes them once into LDS (the same fp32 operations as per block, so the same
+  // bits) and every block looks its value up instead of dividing.
+  __shared__ float inv_tab[128];
+  if (threadIdx.x < 128) {
+    const float d = __builtin_amdgcn_cvt_f32_fp8((int)threadIdx.x, 0) * g;
+    inv_tab[threadIdx.x] = __builtin_fminf(1.0f / d, 3.40282347e38f);
+  }
+  __syncthreads();
   // 16 blocks per wave-unit
   for (int64_t base = wave_id * 16 * kUnroll; base < nblocks; base += nwaves * 16 * kUnroll) {
     uint32_t bits[kUnroll][4];
@@ -183,9 +192,7 @@ nv_quantize_kernel(int64_t nblocks, const void* __restrict__ X, float g, uint8_t
       bad = quad_max(bad);
       const float sv = __builtin_bit_cast(float, amax) / six_g;     // IEEE fp32 division
       const uint32_t s = e4m3_nearest(sv);
-      const float sdec = __builtin_amdgcn_cvt_f32_fp8((int)s, 0);
-      const float d = sdec * g;
-      const float inv = __builtin_fminf(1.0f / d, 3.40282347e38f);  // one reciprocal per block; 0 * inv = 0
+      const float inv = inv_tab[s];                                 // min(1 / (e4m3(s) g), FLT_MAX); 0 * inv = 0
       float y[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[i] = __builtin_bit_cast(float, bits[u][i]) * inv;
@@ -193,7 +200,7 @@ nv_quantize_kernel(int64_t nblocks, const void* __restrict__ X, float g, uint8_t
       packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], 1.0f, 1);
       const uint32_t nonzero = ((packed & 0x7777u) + 0x7777u) & 0x8888u;   // bit 3 of a nibble: magnitude != 0
       packed &= nonzero | 0x7777u;
-      if (bad || sdec == 0.0f) packed = 0;
+      if (bad || s == 0) packed = 0;
       if (blk < nblocks) {
         *reinterpret_cast<uint16_t*>(codes + blk * 8 + sub * 2) = (uint16_t)packed;
         if (sub == 0) scales[blk] = bad ? (uint8_t)0x7F : (uint8_t)s;
