@@ -475,7 +475,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue launches eagerly instead of replaying a HIP graph (for counter runs)")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/*_counters.txt from two rocprofv3 --pmc runs, then exit")
+                    help="write profiles/*_counters.txt from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
+                         f"of `bench.py --only {COUNTED_ONLY} --no-graph`, then exit")
     ap.add_argument("--counters-command", default="", help="the profiling command, recorded with --counters")
     ap.add_argument("--util", metavar="UTIL_DIR",
                     help="write profiles/utilisation_counters.txt from a rocprofv3 --pmc run of "
