@@ -393,8 +393,10 @@ def test_fp8b_shapes(shape, out):
 
 
 # Shapes with at least one 256 x 128 tile per CU, which take the large-tile kernel:
-# ragged in M and N with an odd number of K groups, and a single K group.
-F8_BIG = [(4300, 2100, 384, "bf16"), (4096, 2048, 128, "f32")]
+# ragged in M and N with an odd number of K groups (289 tiles: no per-XCD regrouping),
+# a single K group, and 9 tile rows x 32 (288 tiles: the last group of 4 tile rows
+# holds one).
+F8_BIG = [(4300, 2100, 384, "bf16"), (4096, 2048, 128, "f32"), (2304, 4096, 128, "bf16")]
 
 
 @pytest.mark.parametrize("shape", F8_BIG, ids=[f"{m}x{n}x{k}-{o}" for m, n, k, o in F8_BIG])
