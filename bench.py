@@ -103,8 +103,14 @@ def src_digest(*names):
 
 # Counter summaries: (profile name, kernel-name prefix in the trace, sources of the kernel).
 _NS = "fp4g::(anonymous namespace)::"
-COUNTED = [("mxfp4_gemm_8192", _NS + "mxfp4_gemm_kernel", ["mxfp4_gemm.hip", "common.hpp"]),
+COUNTED = [("mxfp4_gemm_8192", _NS + "mxfp4_gemm_kernel<256, 256, 128, 128, 256, 2, true, false>",
+            ["mxfp4_gemm.hip", "common.hpp"]),
            ("fp4_gemv_8x14336x4096", _NS + "fp4_gemv_kernel", ["fp4_gemv.hip", "common.hpp"]),
+           ("fp4_gemv_prepacked_8x14336x4096", _NS + "fp4_gemv_prepacked_kernel<",
+            ["fp4_gemv_prepacked.hip", "common.hpp"]),
+           ("mxfp4_split_k_128x8192x8192", _NS + "mxfp4_gemm_kernel<128, 128, 64, 64, 256, 2, false, true>",
+            ["mxfp4_gemm.hip", "common.hpp"]),
+           ("mxfp4_split_k_reduce_128x8192x8192", _NS + "splitk_reduce_kernel<", ["mxfp4_gemm.hip", "common.hpp"]),
            ("w4a8_256x8192x8192", _NS + "w4a8p_gemm_kernel<64, false",
             ["w4a8_gemm.hip", "w4a8_prepacked.hip", "common.hpp"]),
            ("w4a8_prepacked_256x8192x8192", _NS + "w4a8p_gemm_kernel<64, true", ["w4a8_prepacked.hip", "common.hpp"]),
@@ -113,7 +119,7 @@ COUNTED = [("mxfp4_gemm_8192", _NS + "mxfp4_gemm_kernel", ["mxfp4_gemm.hip", "co
            ("mx_quantize_8192x8192_f32", _NS + "mx_quantize_kernel<", ["mx_quantize.hip", "common.hpp"]),
            ("nv_quantize_8192x8192_f32", _NS + "nv_quantize_kernel<", ["mx_quantize.hip", "common.hpp"])]
 # The kernels that the counter runs cover: `bench.py --only` + this list.
-COUNTED_ONLY = "mx8192 gemv w4a8 w4a8p nv1024 fp8b quant nvquant copy"
+COUNTED_ONLY = "mx8192 gemv gemvp w4a8 w4a8p nv1024 fp8b quant nvquant skinny copy"
 
 
 def traffic_of(name):
@@ -530,7 +536,7 @@ def main():
             "cache": f"cold ({g['copies']} rotating weight copies)",
             "weights": "re-packed once at load time (fp4_gemv_prepack), not timed",
             "roofline": {"bound": "hbm", "achieved": g["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": g["gbs"] / PEAK_HBM_GBS, "traffic": None},
+                         "frac": g["gbs"] / PEAK_HBM_GBS, "traffic": traffic_of("fp4_gemv_prepacked_8x14336x4096")},
             "algorithmic_bytes": g["bytes"]}
     if "w4a8" in only:
         log("bench: w4a8 256x8192x8192 ...")
@@ -596,12 +602,16 @@ def main():
         k = bench_skinny(args.steps, args.warmup, dev)
         log(f"bench: mxfp4 128x8192x8192 split {k['auto']['splits']}: {k['auto']['ms'] * 1e3:.1f} us "
             f"({k['auto']['tflops']:.0f} TFLOP/s); unsplit {k['none']['ms'] * 1e3:.1f} us")
+        # the split kernel and its reduction together, when both have current counters
+        ts, tr = traffic_of("mxfp4_split_k_128x8192x8192"), traffic_of("mxfp4_split_k_reduce_128x8192x8192")
+        split_traffic = ts + tr if ts is not None and tr is not None else None
         also["mxfp4_split_k_128x8192x8192"] = {
             "metric": "TFLOP/s", "value": k["auto"]["tflops"], "ms_per_launch": k["auto"]["ms"],
             "splits": k["auto"]["splits"], "unsplit_ms_per_launch": k["none"]["ms"],
             "cache": f"cold ({k['copies']} rotating weight copies)",
             "roofline": {"bound": "mfma", "achieved": k["auto"]["tflops"], "peak": PEAK_TFLOPS["fp4"],
-                         "unit": "TFLOP/s", "frac": k["auto"]["tflops"] / PEAK_TFLOPS["fp4"], "traffic": None}}
+                         "unit": "TFLOP/s", "frac": k["auto"]["tflops"] / PEAK_TFLOPS["fp4"],
+                         "traffic": split_traffic}}
     if "copy" in only:
         c = bench_copy(dev)
         log(f"bench: copy 512 MiB {c['ms'] * 1e3:.1f} us, {c['gbs']:.0f} GB/s (read+write)")
