@@ -361,11 +361,19 @@ def parity_ratio(D_gpu, D, S, out_dtype: str, rel: float = REL_TOL) -> float:
 
     Where the exact result is NaN (a NaN scale code reached it) the GPU value must be
     NaN too; those positions then carry no error term.  A NaN where the exact result
-    is finite fails (returns inf)."""
+    is finite fails (returns inf).
+
+    S must be non-negative and finite wherever the exact result is finite: it is a
+    sum of magnitudes, so a negative or non-finite S (or ``rel``) means the
+    reference itself is wrong, and this raises ValueError instead of comparing.  A zero tolerance (S = 0 with fp32 output: every product is zero)
+    requires the GPU value to equal the exact one."""
     D_gpu = np.asarray(D_gpu, dtype=np.float64)
     D = np.asarray(D, dtype=np.float64)
-    if D_gpu.shape != D.shape:
-        raise ValueError(f"shape mismatch {D_gpu.shape} vs {D.shape}")
+    S = np.asarray(S, dtype=np.float64)
+    if D_gpu.shape != D.shape or S.shape != D.shape:
+        raise ValueError(f"shape mismatch {D_gpu.shape} / {D.shape} / {S.shape}")
+    if not (np.isfinite(rel) and rel > 0):
+        raise ValueError(f"relative tolerance must be positive and finite, got {rel}")
     if D.size == 0:
         return 0.0
     nan_ref = np.isnan(D)
@@ -374,5 +382,11 @@ def parity_ratio(D_gpu, D, S, out_dtype: str, rel: float = REL_TOL) -> float:
     ok = ~nan_ref
     if not ok.any():
         return 0.0
-    tol = tolerance(D[ok], np.asarray(S, dtype=np.float64)[ok], out_dtype, rel)
-    return float(np.max(np.abs(D_gpu[ok] - D[ok]) / tol))
+    if not np.all(np.isfinite(S[ok])) or np.any(S[ok] < 0):
+        raise ValueError("S is negative or not finite where D is finite: the reference is invalid")
+    tol = tolerance(D[ok], S[ok], out_dtype, rel)
+    err = np.abs(D_gpu[ok] - D[ok])
+    zero = tol == 0
+    if np.any(zero & (err != 0)):
+        return float("inf")
+    return float(np.max(np.where(zero, 0.0, err / np.where(zero, 1.0, tol))))

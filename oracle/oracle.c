@@ -33,7 +33,6 @@
  * Return value: 0 on success, -1 on an argument error (K not a multiple of V
  * or of 2, null pointer, negative size).
  */
-#include <float.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -91,11 +90,15 @@ static unsigned nibble(const uint8_t *row, int64_t k) {
     return (k & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 0xFu);
 }
 
-/* ---- block-scaled FP4 contraction, generic over (V, scale decoder) ------ */
+/* ---- one output element of each product ------------------------------------
+ *
+ * Each routine below computes one D[m][n] and its S[m][n] from the operand rows it
+ * is given.  The full products and the sampled entry point both call them, so every
+ * product is written out once. */
 
 typedef double (*scale_fn)(unsigned);
 
-/* One output element of the block-scaled FP4 product (rows m of A, n of B). */
+/* Block-scaled FP4: sum_k (e2m1(a_k) * scale(sfa[k/V])) * (e2m1(b_k) * scale(sfb[k/V])). */
 static void fp4_dot(int64_t K, int64_t V, scale_fn dec_scale,
                     const uint8_t *arow, const uint8_t *sfarow,
                     const uint8_t *brow, const uint8_t *sfbrow,
@@ -112,34 +115,88 @@ static void fp4_dot(int64_t K, int64_t V, scale_fn dec_scale,
     *s = mag;
 }
 
-static int fp4_gemm_rows(int64_t M, int64_t N, int64_t K, int64_t V, scale_fn dec,
-                         const uint8_t *A, const uint8_t *sfA,
-                         const uint8_t *B, const uint8_t *sfB,
-                         int64_t row0, int64_t row1, double *D, double *S) {
-    if (M < 0 || N < 0 || K < 0 || (K % V) != 0 || (K % 2) != 0) return -1;
+/* MXFP4: V = 32, E8M0 scales. */
+static void mx_dot(int64_t K, const uint8_t *arow, const uint8_t *sfarow,
+                   const uint8_t *brow, const uint8_t *sfbrow, double *d, double *s) {
+    fp4_dot(K, 32, oracle_e8m0, arow, sfarow, brow, sfbrow, d, s);
+}
+
+/* NVFP4: V = 16, E4M3 scales, then the product of the two fp32 global scales
+ * (exact in fp64: two 24-bit significands) multiplies D, and its magnitude S. */
+static void nv_dot(int64_t K, const uint8_t *arow, const uint8_t *sfarow, double gA,
+                   const uint8_t *brow, const uint8_t *sfbrow, double gB, double *d, double *s) {
+    double dd, ss;
+    fp4_dot(K, 16, oracle_e4m3fn, arow, sfarow, brow, sfbrow, &dd, &ss);
+    const double g = gA * gB;
+    *d = dd * g;
+    *s = ss * fabs(g);
+}
+
+/* W4A8: sa * sum_g bf16(sB[g]) * sum_{k in group g} e4m3(a_k) * int4(b_k), groups of
+ * 128 consecutive K elements.  S is the same sum with every factor in absolute value. */
+#define W4A8_GROUP 128
+static void w4a8_dot(int64_t K, const uint8_t *arow, double row_scale,
+                     const uint8_t *brow, const uint16_t *sbrow, double *d, double *s) {
+    double acc = 0.0, mag = 0.0;
+    for (int64_t g = 0; g < K / W4A8_GROUP; ++g) {
+        double w4_part = 0.0, w4_part_mag = 0.0;
+        for (int64_t k = g * W4A8_GROUP; k < (g + 1) * W4A8_GROUP; ++k) {
+            double p = oracle_e4m3fn(arow[k]) * (double)oracle_int4(nibble(brow, k));
+            w4_part += p;
+            w4_part_mag += fabs(p);
+        }
+        double gs = oracle_bf16(sbrow[g]);
+        acc += gs * w4_part;
+        mag += fabs(gs) * w4_part_mag;
+    }
+    *d = row_scale * acc;
+    *s = fabs(row_scale) * mag;
+}
+
+/* FP8 blockwise: sum_g sA[g] * sB[g] * sum_{k in group g} e4m3(a_k) * e4m3(b_k), groups
+ * of 128 consecutive K elements, one fp32 scale per row per group. */
+#define FP8_BLOCK 128
+static void fp8b_dot(int64_t K, const uint8_t *arow, const float *sarow,
+                     const uint8_t *brow, const float *sbrow, double *d, double *s) {
+    double acc = 0.0, mag = 0.0;
+    for (int64_t g = 0; g < K / FP8_BLOCK; ++g) {
+        double fp8_part = 0.0, fp8_part_mag = 0.0;
+        for (int64_t k = g * FP8_BLOCK; k < (g + 1) * FP8_BLOCK; ++k) {
+            double p = oracle_e4m3fn(arow[k]) * oracle_e4m3fn(brow[k]);
+            fp8_part += p;
+            fp8_part_mag += fabs(p);
+        }
+        const double sc = (double)sarow[g] * (double)sbrow[g];
+        acc += sc * fp8_part;
+        mag += fabs(sc) * fp8_part_mag;
+    }
+    *d = acc;
+    *s = mag;
+}
+
+/* ---- full products (rows [row0, row1) of D and S, written to D[0 .. (row1-row0)*N)) -- */
+
+static int check_rows(int64_t M, int64_t N, int64_t K, int64_t kdiv, const void *A, const void *sfA,
+                      const void *B, const void *sfB, int64_t row0, int64_t row1, double *D, double *S) {
+    if (M < 0 || N < 0 || K < 0 || (K % kdiv) != 0) return -1;
     if (row0 < 0 || row1 > M || row0 > row1) return -1;
     if ((M && N && K) && (!A || !sfA || !B || !sfB)) return -1;
     if ((row1 > row0 && N) && (!D || !S)) return -1;
-    const int64_t a_ld = K / 2, s_ld = K / V;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t m = row0; m < row1; ++m) {
-        for (int64_t n = 0; n < N; ++n) {
-            double d, s;
-            fp4_dot(K, V, dec, A + m * a_ld, sfA + m * s_ld, B + n * a_ld, sfB + n * s_ld, &d, &s);
-            D[(m - row0) * N + n] = d;
-            S[(m - row0) * N + n] = s;
-        }
-    }
     return 0;
 }
 
-/* MXFP4: V = 32, E8M0 scales.  Rows [row0, row1) of D and S are written to
- * D[0 .. (row1-row0)*N).  The M <= 16 GEMV is the same operation. */
+/* MXFP4: V = 32, E8M0 scales.  The M <= 16 GEMV is the same operation. */
 int oracle_mx_gemm_rows(int64_t M, int64_t N, int64_t K,
                         const uint8_t *A, const uint8_t *sfA,
                         const uint8_t *B, const uint8_t *sfB,
                         int64_t row0, int64_t row1, double *D, double *S) {
-    return fp4_gemm_rows(M, N, K, 32, oracle_e8m0, A, sfA, B, sfB, row0, row1, D, S);
+    if (check_rows(M, N, K, 32, A, sfA, B, sfB, row0, row1, D, S)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = row0; m < row1; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            mx_dot(K, A + m * (K / 2), sfA + m * (K / 32), B + n * (K / 2), sfB + n * (K / 32),
+                   &D[(m - row0) * N + n], &S[(m - row0) * N + n]);
+    return 0;
 }
 
 int oracle_mx_gemm(int64_t M, int64_t N, int64_t K,
@@ -153,13 +210,12 @@ int oracle_nv_gemm_rows(int64_t M, int64_t N, int64_t K,
                         const uint8_t *A, const uint8_t *sfA, double gA,
                         const uint8_t *B, const uint8_t *sfB, double gB,
                         int64_t row0, int64_t row1, double *D, double *S) {
-    int rc = fp4_gemm_rows(M, N, K, 16, oracle_e4m3fn, A, sfA, B, sfB, row0, row1, D, S);
-    if (rc) return rc;
-    const double g = gA * gB;
-    for (int64_t i = 0; i < (row1 - row0) * N; ++i) {
-        D[i] *= g;
-        S[i] *= fabs(g);
-    }
+    if (check_rows(M, N, K, 16, A, sfA, B, sfB, row0, row1, D, S)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = row0; m < row1; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            nv_dot(K, A + m * (K / 2), sfA + m * (K / 16), gA, B + n * (K / 2), sfB + n * (K / 16), gB,
+                   &D[(m - row0) * N + n], &S[(m - row0) * N + n]);
     return 0;
 }
 
@@ -169,41 +225,17 @@ int oracle_nv_gemm(int64_t M, int64_t N, int64_t K,
     return oracle_nv_gemm_rows(M, N, K, A, sfA, gA, B, sfB, gB, 0, M, D, S);
 }
 
-/* W4A8: D[m][n] = sa[m] * sum_g bf16(sB[n][g]) * sum_{k in group g}
- * e4m3(A[m][k]) * int4(B[n][k]), groups of G = 128 consecutive K elements.
- * S is the same sum with every product in absolute value. */
-#define W4A8_GROUP 128
+/* W4A8: A [M][K] E4M3 codes, sa [M] fp32, B [N][K/2] INT4, sB [N][K/128] bf16 bits. */
 int oracle_w4a8_gemm_rows(int64_t M, int64_t N, int64_t K,
                           const uint8_t *A, const float *sa,
                           const uint8_t *B, const uint16_t *sB,
                           int64_t row0, int64_t row1, double *D, double *S) {
-    if (M < 0 || N < 0 || K < 0 || (K % W4A8_GROUP) != 0) return -1;
-    if (row0 < 0 || row1 > M || row0 > row1) return -1;
-    if ((M && N && K) && (!A || !sa || !B || !sB)) return -1;
-    if ((row1 > row0 && N) && (!D || !S)) return -1;
-    const int64_t G = K / W4A8_GROUP;
+    if (check_rows(M, N, K, W4A8_GROUP, A, sa, B, sB, row0, row1, D, S)) return -1;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t m = row0; m < row1; ++m) {
-        const uint8_t *arow = A + m * K;
-        const double row_scale = (double)sa[m];
-        for (int64_t n = 0; n < N; ++n) {
-            const uint8_t *brow = B + n * (K / 2);
-            double acc = 0.0, mag = 0.0;
-            for (int64_t g = 0; g < G; ++g) {
-                double part = 0.0, part_mag = 0.0;
-                for (int64_t k = g * W4A8_GROUP; k < (g + 1) * W4A8_GROUP; ++k) {
-                    double p = oracle_e4m3fn(arow[k]) * (double)oracle_int4(nibble(brow, k));
-                    part += p;
-                    part_mag += fabs(p);
-                }
-                double gs = oracle_bf16(sB[n * G + g]);
-                acc += gs * part;
-                mag += fabs(gs) * part_mag;
-            }
-            D[(m - row0) * N + n] = row_scale * acc;
-            S[(m - row0) * N + n] = fabs(row_scale) * mag;
-        }
-    }
+    for (int64_t m = row0; m < row1; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            w4a8_dot(K, A + m * K, (double)sa[m], B + n * (K / 2), sB + n * (K / W4A8_GROUP),
+                     &D[(m - row0) * N + n], &S[(m - row0) * N + n]);
     return 0;
 }
 
@@ -220,37 +252,16 @@ int oracle_w4a8_gemm(int64_t M, int64_t N, int64_t K,
  * carries one fp32 scale per 128 consecutive K elements, and
  *   D[m][n] = sum_g sA[m][g] * sB[n][g] * sum_{k in group g} e4m3(A[m][k]) * e4m3(B[n][k]).
  * A [M][K] and B [N][K] are E4M3 codes (K-major), sA [M][K/128], sB [N][K/128]. */
-#define FP8_BLOCK 128
 int oracle_fp8b_gemm_rows(int64_t M, int64_t N, int64_t K,
                           const uint8_t *A, const float *sA,
                           const uint8_t *B, const float *sB,
                           int64_t row0, int64_t row1, double *D, double *S) {
-    if (M < 0 || N < 0 || K < 0 || (K % FP8_BLOCK) != 0) return -1;
-    if (row0 < 0 || row1 > M || row0 > row1) return -1;
-    if ((M && N && K) && (!A || !sA || !B || !sB)) return -1;
-    if ((row1 > row0 && N) && (!D || !S)) return -1;
-    const int64_t G = K / FP8_BLOCK;
+    if (check_rows(M, N, K, FP8_BLOCK, A, sA, B, sB, row0, row1, D, S)) return -1;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t m = row0; m < row1; ++m) {
-        const uint8_t *arow = A + m * K;
-        for (int64_t n = 0; n < N; ++n) {
-            const uint8_t *brow = B + n * K;
-            double acc = 0.0, mag = 0.0;
-            for (int64_t g = 0; g < G; ++g) {
-                double part = 0.0, part_mag = 0.0;
-                for (int64_t k = g * FP8_BLOCK; k < (g + 1) * FP8_BLOCK; ++k) {
-                    double p = oracle_e4m3fn(arow[k]) * oracle_e4m3fn(brow[k]);
-                    part += p;
-                    part_mag += fabs(p);
-                }
-                const double sc = (double)sA[m * G + g] * (double)sB[n * G + g];
-                acc += sc * part;
-                mag += fabs(sc) * part_mag;
-            }
-            D[(m - row0) * N + n] = acc;
-            S[(m - row0) * N + n] = mag;
-        }
-    }
+    for (int64_t m = row0; m < row1; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            fp8b_dot(K, A + m * K, sA + m * (K / FP8_BLOCK), B + n * K, sB + n * (K / FP8_BLOCK),
+                     &D[(m - row0) * N + n], &S[(m - row0) * N + n]);
     return 0;
 }
 
@@ -265,70 +276,29 @@ int oracle_sampled(int kind, int64_t M, int64_t N, int64_t K,
                    const int64_t *ms, const int64_t *ns, int64_t count,
                    double *D, double *S) {
     if (count < 0 || (count && (!ms || !ns || !D || !S))) return -1;
+    if (kind < 0 || kind > 3 || K < 0) return -1;
+    const int64_t kdiv = kind == 0 ? 32 : kind == 1 ? 16 : 128;
+    if (K % kdiv) return -1;
     for (int64_t i = 0; i < count; ++i)
         if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
-    int bad = 0;
-#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+    const uint8_t *a8 = (const uint8_t *)A, *b8 = (const uint8_t *)B;
+#pragma omp parallel for schedule(dynamic, 16)
     for (int64_t i = 0; i < count; ++i) {
         const int64_t m = ms[i], n = ns[i];
-        double d = 0.0, s = 0.0;
-        if (kind == 0) {
-            if (K % 32) { bad = 1; continue; }
-            fp4_dot(K, 32, oracle_e8m0, (const uint8_t *)A + m * (K / 2),
-                    (const uint8_t *)sfA + m * (K / 32), (const uint8_t *)B + n * (K / 2),
-                    (const uint8_t *)sfB + n * (K / 32), &d, &s);
-        } else if (kind == 1) {
-            if (K % 16) { bad = 1; continue; }
-            fp4_dot(K, 16, oracle_e4m3fn, (const uint8_t *)A + m * (K / 2),
-                    (const uint8_t *)sfA + m * (K / 16), (const uint8_t *)B + n * (K / 2),
-                    (const uint8_t *)sfB + n * (K / 16), &d, &s);
-            d *= gA * gB;
-            s *= fabs(gA * gB);
-        } else if (kind == 2) {
-            if (K % W4A8_GROUP) { bad = 1; continue; }
-            /* one row of one column: reuse the row routine on a 1x1 view */
-            const uint8_t *arow = (const uint8_t *)A + m * K;
-            const uint8_t *brow = (const uint8_t *)B + n * (K / 2);
-            const uint16_t *srow = (const uint16_t *)sfB + n * (K / W4A8_GROUP);
-            double acc = 0.0, mag = 0.0;
-            for (int64_t g = 0; g < K / W4A8_GROUP; ++g) {
-                double part = 0.0, part_mag = 0.0;
-                for (int64_t k = g * W4A8_GROUP; k < (g + 1) * W4A8_GROUP; ++k) {
-                    double p = oracle_e4m3fn(arow[k]) * (double)oracle_int4(nibble(brow, k));
-                    part += p;
-                    part_mag += fabs(p);
-                }
-                double gs = oracle_bf16(srow[g]);
-                acc += gs * part;
-                mag += fabs(gs) * part_mag;
-            }
-            double rs = (double)((const float *)sfA)[m];
-            d = rs * acc;
-            s = fabs(rs) * mag;
-        } else if (kind == 3) {
-            if (K % FP8_BLOCK) { bad = 1; continue; }
-            const uint8_t *arow = (const uint8_t *)A + m * K;
-            const uint8_t *brow = (const uint8_t *)B + n * K;
-            const int64_t G = K / FP8_BLOCK;
-            for (int64_t g = 0; g < G; ++g) {
-                double part = 0.0, part_mag = 0.0;
-                for (int64_t k = g * FP8_BLOCK; k < (g + 1) * FP8_BLOCK; ++k) {
-                    double p = oracle_e4m3fn(arow[k]) * oracle_e4m3fn(brow[k]);
-                    part += p;
-                    part_mag += fabs(p);
-                }
-                const double sc = (double)((const float *)sfA)[m * G + g] * (double)((const float *)sfB)[n * G + g];
-                d += sc * part;
-                s += fabs(sc) * part_mag;
-            }
-        } else {
-            bad = 1;
-            continue;
-        }
-        D[i] = d;
-        S[i] = s;
+        if (kind == 0)
+            mx_dot(K, a8 + m * (K / 2), (const uint8_t *)sfA + m * (K / 32), b8 + n * (K / 2),
+                   (const uint8_t *)sfB + n * (K / 32), &D[i], &S[i]);
+        else if (kind == 1)
+            nv_dot(K, a8 + m * (K / 2), (const uint8_t *)sfA + m * (K / 16), gA, b8 + n * (K / 2),
+                   (const uint8_t *)sfB + n * (K / 16), gB, &D[i], &S[i]);
+        else if (kind == 2)
+            w4a8_dot(K, a8 + m * K, (double)((const float *)sfA)[m], b8 + n * (K / 2),
+                     (const uint16_t *)sfB + n * (K / W4A8_GROUP), &D[i], &S[i]);
+        else
+            fp8b_dot(K, a8 + m * K, (const float *)sfA + m * (K / FP8_BLOCK), b8 + n * K,
+                     (const float *)sfB + n * (K / FP8_BLOCK), &D[i], &S[i]);
     }
-    return bad ? -1 : 0;
+    return 0;
 }
 
 /* ---- MX quantizer: fp32 -> E2M1 codes + E8M0 block scales ---------------
@@ -414,28 +384,35 @@ int oracle_mx_quantize(int64_t rows, int64_t K, const float *x, uint8_t *codes, 
  * per 16 consecutive K elements (the issue page's "Scale Factor Granularity":
  * sf_vec_size 16 with Float8E4M3FN scales) and one fp32 global scale g per
  * tensor, supplied by the caller.  The pages fix no rounding rule; the reading
- * taken is max-abs, with every decision taken in fp32 (the precision of the
- * device kernel), per block with amax = max |x|:
- *   sv = amax / (6 * g)                 (two fp32 operations: 6 * g, then amax / it)
- *   s  = the E4M3 code nearest to sv, a tie going to the even code, values past
- *        448 saturating to 448 (code 0x7E); found by trying every finite
- *        non-negative code through oracle_e4m3fn;
- *   if s decodes to 0 every code is +0; otherwise, with d = e4m3(s) * g and
- *   inv = min(1 / d, FLT_MAX) (fp32; one reciprocal per block, clamped so that
- *   0 * inv stays 0), each element becomes y = x * inv (fp32), rounded to the
- *   nearest E2M1 value as in oracle_mx_quantize (ties to the even mantissa bit,
- *   saturating at 6, zero encoded +0).
+ * taken is max-abs with round-to-nearest on exact real quotients, per block with
+ * amax = max |x|:
+ *   s = the E4M3 code nearest to amax / (6 g), a tie going to the even code,
+ *       values past 448 saturating to 448 (code 0x7E);
+ *   if s decodes to 0 every code is +0; otherwise each element becomes the E2M1
+ *       value nearest to x / (e4m3(s) g), a tie going to the even mantissa bit,
+ *       magnitudes past 6 saturating to 6, a zero result encoded +0.
  * A block holding an infinity or NaN gets the NaN scale 0x7F and zero codes.
+ *
+ * Both quotients are taken in fp64, and that decides every code exactly.  The
+ * operands are fp32 (24-bit significands), e4m3(s) has 4 significant bits and 6
+ * has 2, so 6 g and e4m3(s) g are exact in fp64.  A rounding boundary of the
+ * grid (an E4M3 midpoint, 5 bits, or an E2M1 midpoint, 3 bits) times the divisor
+ * has at most 31 significant bits; amax or x differs from it by zero or by at
+ * least 2^-32 of its size, while the fp64 quotient is off by at most 2^-53 of its
+ * size.  So the fp64 quotient lies on the same side of every boundary as the
+ * exact one, and equals a boundary exactly when the exact quotient does.  The
+ * nearest value is then found by trying every candidate (differences of
+ * neighbouring grid values from a quotient between them are exact in fp64).
  *
  * x [rows][K] fp32, codes [rows][K/2], scales [rows][K/16].  Returns 0, or -1 on
  * bad arguments (K not a multiple of 16, g not finite and positive). */
-static unsigned e4m3_nearest_code(float sv) {
+static unsigned e4m3_nearest_code(double sv) {
     /* saturation first: far above 448 every distance rounds to the same double */
-    if (sv >= 448.0f) return 0x7E;
+    if (sv >= 448.0) return 0x7E;
     unsigned best = 0;
     double best_d = INFINITY;
     for (unsigned c = 0; c <= 0x7E; ++c) {
-        const double d = fabs((double)sv - oracle_e4m3fn(c));
+        const double d = fabs(sv - oracle_e4m3fn(c));
         if (d < best_d || (d == best_d && !(c & 1u) && (best & 1u))) {
             best = c;
             best_d = d;
@@ -448,43 +425,39 @@ int oracle_nv_quantize(int64_t rows, int64_t K, const float *x, float g, uint8_t
     if (rows < 0 || K < 0 || K % 16 || !(g > 0.0f) || !isfinite(g)) return -1;
     if (rows && K && (!x || !codes || !scales)) return -1;
     const int64_t nb = K / 16;
+    const double gd = (double)g;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < nb; ++b) {
             const float *blk = x + r * K + 16 * b;
             uint8_t *out = codes + r * (K / 2) + 8 * b;
             int finite = 1;
-            float amax = 0.0f;
+            double amax = 0.0;
             for (int i = 0; i < 16; ++i) {
                 if (!isfinite(blk[i])) {
                     finite = 0;
                     continue;
                 }
-                if (fabsf(blk[i]) > amax) amax = fabsf(blk[i]);
+                if (fabs((double)blk[i]) > amax) amax = fabs((double)blk[i]);
             }
             if (!finite) {
                 scales[r * nb + b] = 0x7F;
                 memset(out, 0, 8);
                 continue;
             }
-            const float six_g = 6.0f * g;
-            const float sv = amax / six_g;
-            const unsigned s = e4m3_nearest_code(sv);
+            const unsigned s = e4m3_nearest_code(amax / (6.0 * gd));
             scales[r * nb + b] = (uint8_t)s;
-            const float sdec = (float)oracle_e4m3fn(s);
-            if (sdec == 0.0f) {
+            const double divisor = oracle_e4m3fn(s) * gd;
+            if (divisor == 0.0) {
                 memset(out, 0, 8);
                 continue;
             }
-            const float d = sdec * g;
-            float inv = 1.0f / d;
-            if (inv > FLT_MAX) inv = FLT_MAX;
             for (int i = 0; i < 16; i += 2) {
                 unsigned nib[2];
                 for (int h = 0; h < 2; ++h) {
-                    const float y = blk[i + h] * inv;
-                    unsigned c = e2m1_nearest_magnitude(fabs((double)y));
-                    if (c != 0 && y < 0.0f) c |= 8u;
+                    const double q = (double)blk[i + h] / divisor;
+                    unsigned c = e2m1_nearest_magnitude(fabs(q));
+                    if (c != 0 && q < 0.0) c |= 8u;
                     nib[h] = c;
                 }
                 out[i >> 1] = (uint8_t)(nib[0] | (nib[1] << 4));

@@ -36,18 +36,28 @@ def test_group_scales_weight_their_own_group(oracle_lib):
     assert np.allclose(D, ref, rtol=1e-13, atol=0.0)
 
 
-def test_exact_rational_brute_force(oracle_lib):
+@pytest.mark.parametrize("signs", ["positive", "negative"])
+def test_exact_rational_brute_force(oracle_lib, signs):
     d = datagen.make_shape("fp8b", 2, 3, 256, seed=5)
+    if signs == "negative":
+        d["sA"][0, 1] *= -1
+        d["sB"][1, 0] *= -1
+        d["sB"][2, :] *= -1
     a, b = e4m3_values(d["A"]), e4m3_values(d["B"])
     D, S = oracle_lib.fp8b_gemm(d["A"], d["sA"], d["B"], d["sB"])
     for m in range(2):
         for n in range(3):
             exact = Fraction(0)
+            mag = Fraction(0)
             for k in range(256):
                 g = k // 128
-                exact += (Fraction(float(d["sA"][m, g])) * Fraction(float(d["sB"][n, g])) *
-                          Fraction(a[m, k]) * Fraction(b[n, k]))
-            assert abs(Fraction(D[m, n]) - exact) <= Fraction(1e-14) * Fraction(S[m, n])
+                t = (Fraction(float(d["sA"][m, g])) * Fraction(float(d["sB"][n, g])) *
+                     Fraction(a[m, k]) * Fraction(b[n, k]))
+                exact += t
+                mag += abs(t)
+            assert abs(Fraction(D[m, n]) - exact) <= Fraction(1e-14) * mag
+            assert abs(Fraction(S[m, n]) - mag) <= Fraction(1e-14) * mag
+    assert np.all(S >= np.abs(D))
 
 
 def test_group_boundary_straddle(oracle_lib):
@@ -72,8 +82,11 @@ def test_transpose_identity(oracle_lib):
 @pytest.mark.parametrize("seed", [7, 8])
 def test_sampled_equals_full(oracle_lib, seed):
     d = datagen.make_shape("fp8b", 6, 5, 384, seed=seed)
+    d["sA"][::2] *= -1            # negative scales: S must stay a sum of magnitudes
+    d["sB"][:, 1] *= -1
     D, S = oracle_lib.fp8b_gemm(d["A"], d["sA"], d["B"], d["sB"])
     ms = np.array([0, 5, 3, 2])
     ns = np.array([4, 0, 2, 2])
     Ds, Ss = oracle_lib.sampled("fp8b", d, ms, ns)
     assert np.array_equal(Ds, D[ms, ns]) and np.array_equal(Ss, S[ms, ns])
+    assert np.all(Ss >= np.abs(Ds)) and np.all(S >= np.abs(D))

@@ -46,13 +46,13 @@ MUTANTS = {
     "b-scale-from-a": (
         "double b_hat = oracle_e2m1(nibble(brow, k)) * dec_scale(sfbrow[k / V]);",
         "double b_hat = oracle_e2m1(nibble(brow, k)) * dec_scale(sfarow[k / V]);"),
-    "w4a8-group-scale-index": ("double gs = oracle_bf16(sB[n * G + g]);", "double gs = oracle_bf16(sB[n * G]);"),
-    "w4a8-row-scale-dropped": ("D[(m - row0) * N + n] = row_scale * acc;", "D[(m - row0) * N + n] = acc;"),
+    "w4a8-group-scale-index": ("double gs = oracle_bf16(sbrow[g]);", "double gs = oracle_bf16(sbrow[0]);"),
+    "w4a8-row-scale-dropped": ("*d = row_scale * acc;", "*d = acc;"),
     "w4a8-group-size": ("#define W4A8_GROUP 128", "#define W4A8_GROUP 64"),
-    "nv-global-scale-half": ("D[i] *= g;", "D[i] *= gA;"),
+    "nv-global-scale-half": ("*d = dd * g;", "*d = dd * gA;"),
     "b-row-stride": (
-        "fp4_dot(K, V, dec, A + m * a_ld, sfA + m * s_ld, B + n * a_ld, sfB + n * s_ld, &d, &s);",
-        "fp4_dot(K, V, dec, A + m * a_ld, sfA + m * s_ld, B + n * a_ld, sfB + m * s_ld, &d, &s);"),
+        "mx_dot(K, A + m * (K / 2), sfA + m * (K / 32), B + n * (K / 2), sfB + n * (K / 32),",
+        "mx_dot(K, A + m * (K / 2), sfA + m * (K / 32), B + n * (K / 2), sfB + m * (K / 32),"),
     "abs-sum-signed": ("mag += fabs(p);\n    }\n    *d = acc;", "mag += p;\n    }\n    *d = acc;"),
     "quant-exponent-offset": ("e = ex - 1 - 2 + 127;", "e = ex - 2 + 127;"),
     "quant-ties-to-odd": ("(c & 1u) == 0 && (best & 1u) == 1", "(c & 1u) == 1 && (best & 1u) == 0"),
@@ -60,19 +60,40 @@ MUTANTS = {
     "quant-nibble-order": ("out[i / 2] = (uint8_t)(nib[0] | (nib[1] << 4));", "out[i / 2] = (uint8_t)(nib[1] | (nib[0] << 4));"),
     "quant-no-nonfinite-check": ("if (!isfinite(blk[i])) finite = 0;", "if (0) finite = 0;"),
     "nvq-ties-to-odd": ("!(c & 1u) && (best & 1u)", "(c & 1u) && !(best & 1u)"),
-    "nvq-six-g": ("const float six_g = 6.0f * g;", "const float six_g = 4.0f * g;"),
-    "nvq-no-saturation": ("if (sv >= 448.0f) return 0x7E;", "if (0) return 0x7E;"),
+    "nvq-six-g": ("e4m3_nearest_code(amax / (6.0 * gd))", "e4m3_nearest_code(amax / (4.0 * gd))"),
+    "nvq-no-saturation": ("if (sv >= 448.0) return 0x7E;", "if (0) return 0x7E;"),
     "nvq-block-offset": ("const float *blk = x + r * K + 16 * b;", "const float *blk = x + r * K + 8 * b;"),
-    "nvq-global-scale-dropped": ("const float d = sdec * g;", "const float d = sdec;"),
+    "nvq-global-scale-dropped": ("const double divisor = oracle_e4m3fn(s) * gd;",
+                                 "const double divisor = oracle_e4m3fn(s);"),
+    # the rule is on exact quotients: fp32 arithmetic in either decision must be caught
+    "nvq-scale-fp32-quotient": ("e4m3_nearest_code(amax / (6.0 * gd))",
+                                "e4m3_nearest_code((double)((float)amax / (6.0f * g)))"),
+    "nvq-element-fp32-reciprocal": ("const double q = (double)blk[i + h] / divisor;",
+                                    "const double q = (double)(blk[i + h] * (1.0f / (float)divisor));"),
+    "nvq-element-fp32-quotient": ("const double q = (double)blk[i + h] / divisor;",
+                                  "const double q = (double)(blk[i + h] / (float)divisor);"),
     "nvq-nonfinite-scale": ("scales[r * nb + b] = 0x7F;", "scales[r * nb + b] = 0xFF;"),
     "nvq-element-saturation": ("if (y >= 6.0) return 7;", "if (0) return 7;"),
+    "nvq-negative-zero": ("if (c != 0 && q < 0.0) c |= 8u;", "if (q < 0.0) c |= 8u;"),
     "fp8b-group-size": ("#define FP8_BLOCK 128", "#define FP8_BLOCK 64"),
-    "fp8b-b-scale-row": ("const double sc = (double)sA[m * G + g] * (double)sB[n * G + g];",
-                         "const double sc = (double)sA[m * G + g] * (double)sB[m * G + g];"),
-    "fp8b-scale-group-shift": ("const double sc = (double)sA[m * G + g] * (double)sB[n * G + g];",
-                               "const double sc = (double)sA[m * G + g] * (double)sB[n * G + (g + 1) % G];"),
-    "fp8b-b-row-stride": ("const uint8_t *brow = B + n * K;\n            double acc = 0.0, mag = 0.0;",
-                          "const uint8_t *brow = B + n * (K / 2);\n            double acc = 0.0, mag = 0.0;"),
+    "fp8b-b-scale-row": ("const double sc = (double)sarow[g] * (double)sbrow[g];",
+                         "const double sc = (double)sarow[g] * (double)sarow[g];"),
+    "fp8b-scale-group-shift": ("const double sc = (double)sarow[g] * (double)sbrow[g];",
+                               "const double sc = (double)sarow[g] * (double)sbrow[(g + 1) % (K / FP8_BLOCK)];"),
+    "fp8b-b-row-stride": ("fp8b_dot(K, A + m * K, sA + m * (K / FP8_BLOCK), B + n * K,",
+                          "fp8b_dot(K, A + m * K, sA + m * (K / FP8_BLOCK), B + n * (K / 2),"),
+    # S is a sum of magnitudes: dropping any absolute value must be caught (with a
+    # negative scale, S would come out smaller than |D| or negative)
+    "nv-S-global-fabs": ("*s = ss * fabs(g);", "*s = ss * g;"),
+    "w4a8-S-product-fabs": ("w4_part_mag += fabs(p);", "w4_part_mag += p;"),
+    "w4a8-S-group-fabs": ("mag += fabs(gs) * w4_part_mag;", "mag += gs * w4_part_mag;"),
+    "w4a8-S-row-fabs": ("*s = fabs(row_scale) * mag;", "*s = row_scale * mag;"),
+    "fp8b-S-product-fabs": ("fp8_part_mag += fabs(p);", "fp8_part_mag += p;"),
+    "fp8b-S-scale-fabs": ("mag += fabs(sc) * fp8_part_mag;", "mag += sc * fp8_part_mag;"),
+    "sampled-nv-global-scale": ("nv_dot(K, a8 + m * (K / 2), (const uint8_t *)sfA + m * (K / 16), gA,",
+                                "nv_dot(K, a8 + m * (K / 2), (const uint8_t *)sfA + m * (K / 16), 1.0,"),
+    "sampled-w4a8-row-scale-row": ("w4a8_dot(K, a8 + m * K, (double)((const float *)sfA)[m],",
+                                   "w4a8_dot(K, a8 + m * K, (double)((const float *)sfA)[n % M],"),
 }
 
 

@@ -55,19 +55,33 @@ def exact_fp4(A, sfA, B, sfB, V, scale_table, g=Fraction(1)):
     return D
 
 
-def exact_w4a8(A, sa, B, sB):
+def exact_fp4_mag(A, sfA, B, sfB, V, scale_table, g=Fraction(1)):
+    """S = sum_k |a_hat * b_hat| * |g| for the block-scaled FP4 product, exactly."""
+    a = unpack_nibbles(A)
+    b = unpack_nibbles(B)
+    M, K = a.shape
+    N = b.shape[0]
+    return [[sum((abs(Fraction(E2M1[a[m, k]]) * Fraction(scale_table[sfA[m, k // V]])
+                      * Fraction(E2M1[b[n, k]]) * Fraction(scale_table[sfB[n, k // V]]))
+                  for k in range(K)), Fraction(0)) * abs(g)
+             for n in range(N)] for m in range(M)]
+
+
+def exact_w4a8(A, sa, B, sB, magnitude=False):
+    """D (or, with magnitude=True, S = the same sum over |every factor|), exactly."""
     q = unpack_nibbles(B)
     M, K = A.shape
     N = q.shape[0]
+    f = abs if magnitude else (lambda v: v)
     D = [[Fraction(0)] * N for _ in range(M)]
     for m in range(M):
         for n in range(N):
             tot = Fraction(0)
             for g in range(K // 128):
-                part = sum((Fraction(E4M3[A[m, k]]) * _int4(q[n, k])
+                part = sum((f(Fraction(E4M3[A[m, k]]) * _int4(q[n, k]))
                             for k in range(128 * g, 128 * g + 128)), Fraction(0))
-                tot += Fraction(_bf16(sB[n, g])) * part
-            D[m][n] = Fraction(float(sa[m])) * tot
+                tot += f(Fraction(_bf16(sB[n, g]))) * part
+            D[m][n] = f(Fraction(float(sa[m]))) * tot
     return D
 
 
@@ -97,21 +111,32 @@ def test_mx_bruteforce_fraction(oracle_lib, K, seed):
 def test_nv_bruteforce_fraction(oracle_lib, K, g):
     rng = np.random.default_rng(K)
     d = random_nv(2, 3, K, rng, gA=g[0], gB=g[1])
-    # also use the full finite E4M3 range for the scales, subnormals included
+    # also use the full finite E4M3 range for the scales, subnormals included, and
+    # negative scale codes in B
     d["sfA"] = rng.integers(0, 0x7F, d["sfA"].shape, dtype=np.uint8)
+    d["sfB"] = d["sfB"] | (rng.integers(0, 2, d["sfB"].shape, dtype=np.uint8) << 7)
     D, S = oracle_lib.nv_gemm(d["A"], d["sfA"], d["gA"], d["B"], d["sfB"], d["gB"])
-    ref = exact_fp4(d["A"], d["sfA"], d["B"], d["sfB"], 16, E4M3,
-                    Fraction(float(d["gA"])) * Fraction(float(d["gB"])))
+    g_exact = Fraction(float(d["gA"])) * Fraction(float(d["gB"]))
+    ref = exact_fp4(d["A"], d["sfA"], d["B"], d["sfB"], 16, E4M3, g_exact)
     _assert_exact(D, ref)
+    # S carries |gA * gB| and |every scale|: negative scale codes are in sfA's range
+    _assert_exact(S, exact_fp4_mag(d["A"], d["sfA"], d["B"], d["sfB"], 16, E4M3, g_exact))
+    assert np.all(S >= np.abs(D))
 
 
 @pytest.mark.parametrize("K", [128, 256])
-def test_w4a8_bruteforce_fraction(oracle_lib, K):
+@pytest.mark.parametrize("signs", ["positive", "negative"])
+def test_w4a8_bruteforce_fraction(oracle_lib, K, signs):
     rng = np.random.default_rng(K + 7)
     d = random_w4a8(2, 3, K, rng)
+    if signs == "negative":
+        # a negative row scale, and group scales of either sign (bf16 sign bit)
+        d["sa"][0] = -d["sa"][0]
+        d["sB"] = d["sB"] | (rng.integers(0, 2, d["sB"].shape).astype(np.uint16) << 15)
+        d["sB"][0, 0] |= 0x8000
     D, S = oracle_lib.w4a8_gemm(d["A"], d["sa"], d["B"], d["sB"])
-    ref = exact_w4a8(d["A"], d["sa"], d["B"], d["sB"])
-    _assert_exact(D, ref)
+    _assert_exact(D, exact_w4a8(d["A"], d["sa"], d["B"], d["sB"]))
+    _assert_exact(S, exact_w4a8(d["A"], d["sa"], d["B"], d["sB"], magnitude=True))
     assert np.all(S >= np.abs(D))
 
 
@@ -371,16 +396,21 @@ def test_nibble_order_low_is_even_k(oracle_lib):
 
 @pytest.mark.parametrize("kind", ["mx", "nv", "w4a8"])
 def test_sampled_outputs_equal_full_product(oracle_lib, kind):
-    """The sampled entry point evaluates the same definition at chosen (m, n)."""
+    """The sampled entry point evaluates the same definition at chosen (m, n), also
+    with negative scales (S must stay the sum of magnitudes)."""
     rng = np.random.default_rng(51)
     if kind == "mx":
         d = random_mx(9, 11, 256, rng)
     elif kind == "nv":
         d = random_nv(9, 11, 256, rng, gA=1.5, gB=-0.25)
+        d["sfA"][::2] |= 0x80
     else:
         d = random_w4a8(9, 11, 256, rng)
+        d["sa"][::3] *= -1
+        d["sB"][1::2] |= 0x8000
     D, S = oracle_lib.run(kind, d)
     ms = rng.integers(0, 9, 40)
     ns = rng.integers(0, 11, 40)
     Ds, Ss = oracle_lib.sampled(kind, d, ms, ns)
     assert np.array_equal(Ds, D[ms, ns]) and np.array_equal(Ss, S[ms, ns])
+    assert np.all(Ss >= np.abs(Ds)) and np.all(S >= np.abs(D))

@@ -36,3 +36,30 @@ def test_ratio_pass_fail_and_nan():
     g5 = g.copy()
     g5[1, 0] = np.nan            # NaN where a finite value is required
     assert oracle.parity_ratio(g5, D, S, "f32") == float("inf")
+
+
+def test_ratio_rejects_invalid_tolerance():
+    D = np.array([1.0, 2.0])
+    for S in (np.array([10.0, -1.0]), np.array([10.0, np.nan]), np.array([np.inf, 1.0])):
+        for out in ("f32", "bf16"):
+            try:
+                oracle.parity_ratio(D, D, S, out)
+            except ValueError:
+                continue
+            raise AssertionError(f"accepted S = {S} for {out}")
+    for rel in (0.0, -1e-5, np.nan, np.inf):
+        try:
+            oracle.parity_ratio(D, D, np.array([1.0, 1.0]), "f32", rel=rel)
+        except ValueError:
+            continue
+        raise AssertionError(f"accepted rel = {rel}")
+
+
+def test_zero_tolerance_needs_exact_match():
+    D = np.array([0.0, 3.0])
+    S = np.array([0.0, 10.0])
+    assert oracle.parity_ratio(np.array([0.0, 3.0]), D, S, "f32") == 0.0
+    assert oracle.parity_ratio(np.array([-0.0, 3.0]), D, S, "f32") == 0.0
+    assert oracle.parity_ratio(np.array([1e-30, 3.0]), D, S, "f32") == float("inf")
+    # bf16 output always has the ulp term, so S = 0 still has a positive bar
+    assert oracle.parity_ratio(np.array([2.0 ** -134, 3.0]), D, S, "bf16") <= 1.0
