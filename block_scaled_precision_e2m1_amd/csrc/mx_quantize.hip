@@ -107,17 +107,30 @@ mx_quantize_kernel(int64_t nblocks, const void* __restrict__ X, uint8_t* __restr
 // fp32 or bf16 X[rows][K] and an fp32 global scale g -> E2M1 codes [rows][K/2] and E4M3
 // block scales [rows][K/16], the NVFP4 operand of nv_fp4_gemm (the issue page's "Scale
 // Factor Granularity": sf_vec_size 16 with Float8E4M3FN scales).  The rule, per
-// 16-element block, every decision in fp32:
-//   sv = amax / (6 g);  s = the E4M3 code nearest to sv, ties to the even code, past
-//   448 saturating to 448;  with d = e4m3(s) * g and inv = min(1 / d, FLT_MAX), each
-//   element is x * inv rounded to the nearest E2M1 value, ties to the even code,
-//   saturating at 6, zero +0;  a scale that
-//   decodes to 0 gives zero codes;  a block holding an infinity or NaN gets scale 0x7F
-//   (NaN) and zero codes.
+// 16-element block, on exact real quotients:
+//   s = the E4M3 code nearest to amax / (6 g), ties to the even code, past 448
+//   saturating to 448;  each element is the E2M1 value nearest to x / (e4m3(s) g), ties
+//   to the even code, saturating at 6, zero +0;  a scale that decodes to 0 gives zero
+//   codes;  a block holding an infinity or NaN gets scale 0x7F (NaN) and zero codes.
 // 4 lanes share a block (4 elements each): one wave-wide load is still 1 KB of
-// consecutive blocks.  The two divisions per block (amax / 6g and 1 / d) are IEEE fp32
-// (correctly rounded), and the E2M1 rounding is the same hardware conversion as the MX
-// kernel's, at scale 1.
+// consecutive blocks.
+//
+// Fast path in fp32, exact decisions where fp32 could decide wrongly:
+//  * Scale: sv = amax / fl(6 g) is within 2 ulps of the exact quotient.  Every E4M3
+//    rounding boundary has an fp32 mantissa whose low 19 bits are zero, so an sv more
+//    than 64 ulps from such a value decides like the exact quotient.  Otherwise (and
+//    when 6 g overflows fp32) the code comes from the fp64 quotient, which decides
+//    exactly: 6 g is exact in fp64, and a boundary times 6 g has at most 31 significant
+//    bits, so amax differs from it by zero or by at least 2^-32 of its size, far more
+//    than the fp64 quotient's rounding.
+//  * Elements: y = x * inv with inv = fl(1 / fl(e4m3(s) g)) from an LDS table (127
+//    values per call) is within 3 fp32 roundings of the exact quotient, so the exact
+//    quotient lies between y (1 - 2^-20) and y (1 + 2^-20).  Rounding to E2M1 is
+//    monotone: when both ends give the same codes (one hardware conversion per pair),
+//    so does the exact quotient.  When they differ, when e4m3(s) g is not a normal fp32
+//    (the table holds -1 there), or when the scale saturated (|y| may then overflow),
+//    the lane's four codes come from fp64 quotients x / (e4m3(s) g), exact for the same
+//    reason as the scale's (a boundary times the divisor has at most 31 bits).
 
 // Maximum over the 4-lane quad of unsigned integers.
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
@@ -141,6 +154,32 @@ __device__ __forceinline__ uint32_t e4m3_nearest(float sv) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// The same rounding of the fp64 quotient amax / (6 g): exact (see above).
+__device__ __noinline__ uint32_t e4m3_nearest_exact(float amax, float g) {
+  const double q = (double)amax / (6.0 * (double)g);
+  if (q >= 448.0) return 0x7Eu;
+  if (q < 0x1p-6) return (uint32_t)__builtin_rint(q * 512.0);          // 0 .. 8, ties to even
+  const uint64_t u = __builtin_bit_cast(uint64_t, q);
+  const uint64_t r = u + 0xFFFFFFFFFFFFull + ((u >> 49) & 1u);        // 3 of 52 mantissa bits kept
+  const uint32_t code = (uint32_t)((((r >> 52) - 1016u) << 3) | ((r >> 49) & 7u));   // E - 1023 + 7
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// The E2M1 code nearest to the fp64 quotient x / d (d = e4m3(s) g exactly), ties to the
+// even code, saturating at 6, zero +0: the count of rounding boundaries strictly below
+// |q|, moved up by one on a tie whose lower neighbour is odd.
+__device__ __noinline__ uint32_t e2m1_nearest_exact(float x, double d) {
+  const double q = (double)x / d;
+  const double a = __builtin_fabs(q);
+  uint32_t c = (uint32_t)(a > 0.25) + (uint32_t)(a > 0.75) + (uint32_t)(a > 1.25) + (uint32_t)(a > 1.75) +
+               (uint32_t)(a > 2.5) + (uint32_t)(a > 3.5) + (uint32_t)(a > 5.0);
+  const double bound = c == 0 ? 0.25 : c == 1 ? 0.75 : c == 2 ? 1.25 : c == 3 ? 1.75 : c == 4 ? 2.5
+                     : c == 5 ? 3.5 : 5.0;
+  if (c < 7 && a == bound && (c & 1u)) c += 1;
+  if (c != 0 && q < 0.0) c |= 8u;
+  return c;
+}
+
 template <bool BF16_IN>
 __global__ void __launch_bounds__(256)
 nv_quantize_kernel(int64_t nblocks, const void* __restrict__ X, float g, uint8_t* __restrict__ codes,
@@ -150,13 +189,13 @@ nv_quantize_kernel(int64_t nblocks, const void* __restrict__ X, float g, uint8_t
   const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
   const float six_g = 6.0f * g;
-  // The reciprocal 1 / (e4m3(s) * g) takes one of 127 values per call: the workgroup
-  // computes them once into LDS (the same fp32 operations as per block, so the same
-  // bits) and every block looks its value up instead of dividing.
+  const bool six_g_finite = six_g <= 3.40282347e38f;
+  // 1 / (e4m3(s) g) for the 127 finite codes, -1 where e4m3(s) g is not a normal fp32
+  // (s = 0 included); the workgroup computes them once into LDS.
   __shared__ float inv_tab[128];
   if (threadIdx.x < 128) {
     const float d = __builtin_amdgcn_cvt_f32_fp8((int)threadIdx.x, 0) * g;
-    inv_tab[threadIdx.x] = __builtin_fminf(1.0f / d, 3.40282347e38f);
+    inv_tab[threadIdx.x] = (d >= 1.17549435e-38f && d <= 3.40282347e38f) ? 1.0f / d : -1.0f;
   }
   __syncthreads();
   // 16 blocks per wave-unit
@@ -190,14 +229,31 @@ nv_quantize_kernel(int64_t nblocks, const void* __restrict__ X, float g, uint8_t
       }
       amax = quad_max(amax);
       bad = quad_max(bad);
-      const float sv = __builtin_bit_cast(float, amax) / six_g;     // IEEE fp32 division
-      const uint32_t s = e4m3_nearest(sv);
-      const float inv = inv_tab[s];                                 // min(1 / (e4m3(s) g), FLT_MAX); 0 * inv = 0
-      float y[4];
+      const float amax_f = __builtin_bit_cast(float, amax);
+      const float sv = amax_f / six_g;
+      uint32_t s = e4m3_nearest(sv);
+      const uint32_t usv = __builtin_bit_cast(uint32_t, sv);
+      if (!bad && amax != 0 && (!six_g_finite || ((usv + 0x40u) & 0x7FFFFu) <= 0x80u))
+        s = e4m3_nearest_exact(amax_f, g);
+      const float inv = inv_tab[s];
+      const float inv_lo = inv * (1.0f - 0x1p-20f), inv_hi = inv * (1.0f + 0x1p-20f);
+      float ylo[4], yhi[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = __builtin_bit_cast(float, bits[u][i]) * inv;
-      uint32_t packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
-      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], 1.0f, 1);
+      for (int i = 0; i < 4; ++i) {
+        ylo[i] = __builtin_bit_cast(float, bits[u][i]) * inv_lo;
+        yhi[i] = __builtin_bit_cast(float, bits[u][i]) * inv_hi;
+      }
+      uint32_t packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ylo[0], ylo[1], 1.0f, 0);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, ylo[2], ylo[3], 1.0f, 1);
+      uint32_t packed_hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, yhi[0], yhi[1], 1.0f, 0);
+      packed_hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed_hi, yhi[2], yhi[3], 1.0f, 1);
+      if (!bad && s != 0 && ((packed ^ packed_hi) & 0xFFFFu || inv < 0.0f || s == 0x7Eu)) {
+        const double d = (double)__builtin_amdgcn_cvt_f32_fp8((int)s, 0) * (double)g;
+        packed = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          packed |= e2m1_nearest_exact(__builtin_bit_cast(float, bits[u][i]), d) << (4 * i);
+      }
       const uint32_t nonzero = ((packed & 0x7777u) + 0x7777u) & 0x8888u;   // bit 3 of a nibble: magnitude != 0
       packed &= nonzero | 0x7777u;
       if (bad || s == 0) packed = 0;

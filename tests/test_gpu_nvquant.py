@@ -1,8 +1,9 @@
 """GPU parity of the NV quantizer (nv_fp4_quantize) against the CPU oracle.
 
-The outputs are bytes (E2M1 codes and E4M3 scales), so the bar is bit-exact.  Both
-sides take every decision in IEEE fp32 (6 * g, amax / 6g, e4m3(s) * g, 1 / d, x * inv,
-each correctly rounded), so no tolerance enters.
+The outputs are bytes (E2M1 codes and E4M3 scales), so the bar is bit-exact.  The rule
+rounds exact real quotients (amax / 6g for the scale, x / (e4m3(s) g) for the codes);
+the oracle decides them in fp64, the kernel in fp32 with an fp64 fallback near every
+rounding boundary, so the boundary blocks below exercise that fallback.
 """
 import numpy as np
 import pytest
@@ -11,6 +12,7 @@ import torch
 import block_scaled_precision_e2m1_amd as fp4
 import datagen
 import oracle
+from tests.test_oracle_nvquant import _boundary_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +93,36 @@ def test_special_values_and_boundaries():
     bad = np.nonzero((c != c_ref).any(axis=1))[0]
     assert not len(bad), f"code rows differ: {bad}: gpu {c[bad[:3]]} oracle {c_ref[bad[:3]]} x {x[bad[:3]]}"
     assert s[0, 0] == 0x7F and s[1, 0] == 0x7F and s[2, 0] == 0 and not c[3].any()
+
+
+@pytest.mark.parametrize("g", [1.0, 0.1, 0.37, 3.0e-3, 1.7e-39, 4.0e-43, 2.5e35, 1.0e38, 3.0e38])
+def test_boundary_blocks_match_oracle(g):
+    """Blocks on and one fp32 ulp around every rounding boundary of both grids (where
+    fp32 arithmetic alone would decide some codes differently from the exact rule),
+    for global scales from the fp32 subnormal range to past FLT_MAX / 6."""
+    g = np.float32(g)
+    print(f"case nv quantize boundary blocks g={g}", flush=True)
+    rng = np.random.default_rng(int(g.view(np.uint32)))
+    x = np.stack(_boundary_blocks(rng, g))
+    for dt in (torch.float32,):
+        c, s = quantize_gpu(x, float(g), dt)
+        c_ref, s_ref = oracle.nv_quantize(x, g)
+        assert np.array_equal(s, s_ref), f"scale rows differ: {np.nonzero(s != s_ref)[0][:5]}"
+        bad = np.nonzero((c != c_ref).any(axis=1))[0]
+        assert not len(bad), f"code rows differ: {bad[:5]}: gpu {c[bad[:2]]} oracle {c_ref[bad[:2]]}"
+
+
+def test_random_blocks_wide_range_match_oracle():
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((512, 256)) * np.ldexp(1.0, rng.integers(-20, 20, (512, 1)))).astype(np.float32)
+    x[3, :16] = 0.0
+    x[5, 16:32] *= np.float32(1e-35)
+    print("case nv quantize wide-range random blocks", flush=True)
+    for g in (tensor_scale(x), 0.01, 7.3e-40, 1.2e38):
+        c, s = quantize_gpu(x, g)
+        c_ref, s_ref = oracle.nv_quantize(x, g)
+        assert np.array_equal(s, s_ref), f"scales differ at g={g}"
+        assert np.array_equal(c, c_ref), f"codes differ at g={g}"
 
 
 def test_workload_size_sampled_rows():
