@@ -64,7 +64,7 @@ fp4g_status check_fp4_operands(int64_t M, int64_t N, int64_t K, int V, const voi
 fp4g_status finish(hipError_t e) { return e == hipSuccess ? FP4G_OK : FP4G_EHIP; }
 
 fp4g_status run_fp4(int which, int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
-                    float g, const void* B, const void* sfB, void* D, int d_type, void* stream) {
+                    float ga, float gb, const void* B, const void* sfB, void* D, int d_type, void* stream) {
   const int V = (which == 1) ? 16 : 32;
   bool empty = false;
   fp4g_status st = check_common(M, N, K, d_type, D, &empty);
@@ -76,7 +76,8 @@ fp4g_status run_fp4(int which, int64_t M, int64_t N, int64_t K, const void* A, c
   const bool bf16 = d_type == FP4G_OUT_BF16;
   if (K == 0) return finish(fp4g::launch_zero_fill(D, M * N, bf16, s));
   FP4Args a{M, N, K, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(sfA),
-            static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(sfB), g, D, bf16};
+            static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(sfB), 1.0f, D, bf16};
+  if (which == 1) fp4g::split_global_scale(ga, gb, &a.gscale, &a.gscale_exp);
   if (which == 0) return finish(fp4g::launch_mxfp4_gemm(a, s));
   if (which == 1) return finish(fp4g::launch_nvfp4_gemm(a, s));
   return finish(fp4g::launch_fp4_gemv(a, s));
@@ -120,7 +121,8 @@ fp4g_status nv_fp4_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K, cons
   for (const Range& r : ins)
     if (overlaps(d, r)) return FP4G_EINVAL;
   FP4Args a{M, N, K, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(sfA),
-            static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(sfB), global_a * global_b, D, bf16, L};
+            static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(sfB), 1.0f, D, bf16, L};
+  fp4g::split_global_scale(global_a, global_b, &a.gscale, &a.gscale_exp);
   return finish(fp4g::launch_nvfp4_gemm(a, s));
 }
 
@@ -203,18 +205,18 @@ fp4g_status mx_fp4_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K, cons
 
 fp4g_status mx_fp4_gemm(int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
                         const void* B, const void* sfB, void* D, int d_type, void* stream) {
-  return run_fp4(0, M, N, K, A, sfA, 1.0f, B, sfB, D, d_type, stream);
+  return run_fp4(0, M, N, K, A, sfA, 1.0f, 1.0f, B, sfB, D, d_type, stream);
 }
 
 fp4g_status nv_fp4_gemm(int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
                         float global_a, const void* B, const void* sfB, float global_b, void* D,
                         int d_type, void* stream) {
-  return run_fp4(1, M, N, K, A, sfA, global_a * global_b, B, sfB, D, d_type, stream);
+  return run_fp4(1, M, N, K, A, sfA, global_a, global_b, B, sfB, D, d_type, stream);
 }
 
 fp4g_status fp4_gemv(int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
                      const void* B, const void* sfB, void* D, int d_type, void* stream) {
-  return run_fp4(2, M, N, K, A, sfA, 1.0f, B, sfB, D, d_type, stream);
+  return run_fp4(2, M, N, K, A, sfA, 1.0f, 1.0f, B, sfB, D, d_type, stream);
 }
 
 fp4g_status w4a8_gemm(int64_t M, int64_t N, int64_t K, const void* A, const float* sa,

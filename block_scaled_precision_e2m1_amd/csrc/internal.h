@@ -14,11 +14,18 @@ struct FP4Args {            // MXFP4 / NVFP4 / GEMV
   const uint8_t* sfA;       // [M][K/V]
   const uint8_t* B;         // [N][K/2]
   const uint8_t* sfB;       // [N][K/V]
-  float gscale;             // NVFP4: global_a * global_b; unused otherwise
+  float gscale;             // NVFP4: global_a * global_b = ldexp(gscale, gscale_exp); 1 otherwise
   void* D;                  // [M][N]
   bool bf16_out;
   int64_t L = 1;            // NVFP4: problems stored back to back (grid dimension y)
+  int gscale_exp = 0;       // NVFP4: gscale is the product of the two fp32 significands and
+                            // gscale_exp the sum of the exponents, so no pair of finite
+                            // scales overflows or flushes before it meets the accumulator
 };
+
+// Split global_a * global_b into an fp32 significand product in [0.25, 1) (one rounding)
+// and a power-of-two exponent, applied in the epilogue as ldexp(acc * m, e).
+void split_global_scale(float global_a, float global_b, float* m, int* e);
 
 struct W4A8Args {
   int64_t M, N, K;

@@ -14,7 +14,9 @@
 // v_cvt_scalef32_pk_f16_fp4 (which widens two codes and multiplies them by the
 // power of two of its fp32 scale operand: 2^e) and one v_pk_mul_f16 by (m, m).
 // The folded tiles are written to LDS and consumed by v_mfma_f32_16x16x32_f16
-// with fp32 accumulation; gA*gB multiplies the accumulator in the epilogue.
+// with fp32 accumulation; gA*gB multiplies the accumulator in the epilogue, as an fp32
+// significand product and a power of two, ldexp(acc * gm, ge), so that scale pairs whose
+// fp32 product would overflow or flush to zero still give every representable D.
 //
 // Structure: one workgroup per BM x BN tile, 4 or 8 waves of WM x WN; 128 K elements
 // (64 packed bytes, two scale dwords) per row per step; packed tiles are prefetched
@@ -64,7 +66,7 @@ __device__ __forceinline__ void fold8(uint32_t w, float pow2, h2 mant, uint32_t*
 template <int BM, int BN, int WM, int WN, bool BF16>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
-                  const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, float gscale,
+                  const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, float gscale, int gexp,
                   void* __restrict__ D) {
   constexpr int NWN = BN / WN;
   constexpr int NT = (BM / WM) * NWN * 64;
@@ -197,7 +199,7 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int m = m0 + wm * WM + i * 16 + 4 * slot + t;
-        if (m < M && n < N) store_out<BF16>(D, (int64_t)m * N + n, acc[i][j][t] * gscale);
+        if (m < M && n < N) store_out<BF16>(D, (int64_t)m * N + n, __builtin_ldexpf(acc[i][j][t] * gscale, gexp));
       }
     }
 }
@@ -210,14 +212,21 @@ hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
   const dim3 grid((unsigned)tiles, (unsigned)a.L);
   if (a.bf16_out)
     hipLaunchKernelGGL((nvfp4_gemm_kernel<BM, BN, WM, WN, true>), grid, dim3(NT), 0, s, (int)a.M,
-                       (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.gscale, a.D);
+                       (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.gscale, a.gscale_exp, a.D);
   else
     hipLaunchKernelGGL((nvfp4_gemm_kernel<BM, BN, WM, WN, false>), grid, dim3(NT), 0, s, (int)a.M,
-                       (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.gscale, a.D);
+                       (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.gscale, a.gscale_exp, a.D);
   return hipGetLastError();
 }
 
 }  // namespace
+
+void split_global_scale(float global_a, float global_b, float* m, int* e) {
+  int ea = 0, eb = 0;
+  const float fa = __builtin_frexpf(global_a, &ea), fb = __builtin_frexpf(global_b, &eb);
+  *m = fa * fb;
+  *e = ea + eb;
+}
 
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s) {
   if (a.L * ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256) return launch_cfg<128, 128, 64, 64>(a, s);

@@ -151,6 +151,24 @@ def test_mxfp4_big_tile_multi_item_sampled(shape, out):
     check_sampled("mx", d, out, mt, nt, D=D)
 
 
+def test_mxfp4_headline_config_full_output():
+    """The configuration the benchmark times (256 x 256 tiles, 256-element K stages,
+    a persistent grid with 4 tiles per workgroup and the per-XCD tile order) compared
+    element by element with the oracle over the whole 8192 x 8192 output, fp32 and
+    bf16, on workload-distributed inputs (K = 256 keeps the oracle to about 20 s)."""
+    M, N, K = 8192, 8192, 256
+    print(f"case mx {M}x{N}x{K} full output, seed 31", flush=True)
+    d = datagen.make_shape("mx", M, N, K, seed=31, dist="gaussian")
+    t = up(d)
+    D32 = as_np(run("mx", d, "f32", t))
+    D16 = as_np(run("mx", d, "bf16", t))
+    ref, S = oracle.run("mx", d)
+    for D, out in ((D32, "f32"), (D16, "bf16")):
+        r = oracle.parity_ratio(D, ref, S, out)
+        print(f"  {out}: max |err|/tol = {r:.3g}", flush=True)
+        assert r <= 1.0, f"mx {M}x{N}x{K} {out}: max |err|/tol = {r}"
+
+
 def test_mxfp4_8192_sampled_and_repeatable():
     d = datagen.make("mxfp4_8192")
     print("case mxfp4_8192 seed 0", flush=True)
@@ -331,6 +349,33 @@ def test_nvfp4_full_scale_range_including_subnormals():
     d["sfB"] = (rng.integers(0, 0x7F, d["sfB"].shape, dtype=np.uint8) | (rng.integers(0, 2, d["sfB"].shape, dtype=np.uint8) << 7))
     d.update({"M": 96, "N": 80, "K": 256})
     check_full("nv", d, "f32")
+
+
+@pytest.mark.parametrize("case", ["underflow", "overflow"])
+def test_nvfp4_global_scales_whose_product_leaves_fp32(case):
+    """global_a * global_b below the fp32 normal range (precision lost in a subnormal)
+    or past FLT_MAX, while D itself is an ordinary fp32 value: the epilogue applies the
+    pair as an fp32 significand product and a power of two, so D keeps the bar."""
+    rng = np.random.default_rng(29)
+    M, N, K = 64, 80, 256
+    d = datagen.random_nv(M, N, K, rng)
+    if case == "underflow":
+        d["gA"], d["gB"] = np.float32(1.37e-21), np.float32(-2.91e-21)      # product ~ -4e-42
+        d["sfA"] = rng.integers(0x60, 0x7F, d["sfA"].shape, dtype=np.uint8)
+        d["sfB"] = rng.integers(0x60, 0x7F, d["sfB"].shape, dtype=np.uint8)
+    else:
+        d["gA"], d["gB"] = np.float32(3.1e25), np.float32(1.6e14)           # product ~ 5e39
+        d["sfA"] = rng.integers(0x01, 0x05, d["sfA"].shape, dtype=np.uint8)
+        d["sfB"] = rng.integers(0x01, 0x05, d["sfB"].shape, dtype=np.uint8)
+        small = np.array([0, 1, 2, 8, 9, 10], np.uint8)                     # |e2m1| <= 1
+        d["A"] = datagen.pack_nibbles(rng.choice(small, (M, K)))
+        d["B"] = datagen.pack_nibbles(rng.choice(small, (N, K)))
+    d.update({"M": M, "N": N, "K": K})
+    ref, _ = oracle.run("nv", d)
+    assert np.all(np.abs(ref) < 3.0e38) and np.max(np.abs(ref)) > 1.2e-38
+    print(f"case nv global scales {case}", flush=True)
+    for out in ("f32", "bf16"):
+        check_full("nv", d, out)
 
 
 def test_nvfp4_nan_scale_codes():
