@@ -23,7 +23,8 @@ import os
 
 import torch
 
-__all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm",
+__all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_batched_noalloc", "mx_fp4_gemm_workspace_size",
+           "nv_fp4_gemm",
            "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked",
            "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3", "w4a8_gemm_prepacked",
            "nv_fp4_gemm_batched", "w4a8_gemm_batched", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "nv_fp4_quantize",
@@ -32,7 +33,8 @@ __all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfp4gemm.so")
-SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size", "nv_fp4_gemm",
+SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_batched_noalloc", "mx_fp4_gemm_workspace_size",
+           "nv_fp4_gemm",
            "nv_fp4_gemm_batched", "w4a8_gemm", "w4a8_gemm_batched", "fp4_gemv",
            "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked",
            "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3", "w4a8_gemm_prepacked",
@@ -69,6 +71,8 @@ def load_library():
     lib.mx_fp4_gemm.restype = c_int
     lib.mx_fp4_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, p, p, p, c_int, i64, p, ctypes.c_size_t, p]
     lib.mx_fp4_gemm_batched.restype = c_int
+    lib.mx_fp4_gemm_batched_noalloc.argtypes = [i64, i64, i64, i64, p, p, p, p, p, c_int, i64, p]
+    lib.mx_fp4_gemm_batched_noalloc.restype = c_int
     lib.mx_fp4_gemm_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.mx_fp4_gemm_workspace_size.restype = c_int
     lib.fp4_gemv_prepack_size.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
@@ -223,6 +227,33 @@ def mx_fp4_gemm_batched(A, sfA, B, sfB, out=None, out_dtype=torch.bfloat16, spli
                                  _ptr(workspace), workspace.numel(), _stream(device))
     _raise_on("mx_fp4_gemm_batched", st)
     return D
+
+
+def mx_fp4_gemm_batched_noalloc(A, sfA, B, sfB, out, splits=0):
+    """mx_fp4_gemm_batched without a workspace: a split of K uses the library's own 32 MiB
+    scratch on this GPU, so the call allocates nothing (``out`` [L, M, N] float32 or
+    bfloat16 must be given).  Calls that overlap in time on one GPU race on that scratch.
+    A requested split that needs more than the scratch holds raises Fp4GemmError."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 3 or B.dim() != 3:
+        raise ValueError("A and B must be 3-D [L, rows, K/2]")
+    L, M, K = A.shape[0], A.shape[1], A.shape[2] * 2
+    N = B.shape[1]
+    if K % 32:
+        raise ValueError(f"K={K} must be a multiple of 32")
+    _check(A, "A", torch.uint8, (L, M, K // 2), device)
+    _check(sfA, "sfA", torch.uint8, (L, M, K // 32), device)
+    _check(B, "B", torch.uint8, (L, N, K // 2), device)
+    _check(sfB, "sfB", torch.uint8, (L, N, K // 32), device)
+    if out is None or out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be a float32 or bfloat16 tensor [L, M, N]")
+    _check(out, "out", out.dtype, (L, M, N), device)
+    dt = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    st = lib.mx_fp4_gemm_batched_noalloc(L, M, N, K, _ptr(A), _ptr(sfA), _ptr(B), _ptr(sfB), _ptr(out), dt,
+                                         splits, _stream(device))
+    _raise_on("mx_fp4_gemm_batched_noalloc", st)
+    return out
 
 
 def fp4_gemv(A, sfA, B, sfB, out=None, out_dtype=torch.bfloat16):

@@ -203,6 +203,48 @@ fp4g_status mx_fp4_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K, cons
   return finish(fp4g::launch_mxfp4_gemm_batched(a, L, S, static_cast<float*>(workspace), s));
 }
 
+fp4g_status mx_fp4_gemm_batched_noalloc(int64_t L, int64_t M, int64_t N, int64_t K, const void* A,
+                                        const void* sfA, const void* B, const void* sfB, void* D,
+                                        int d_type, int64_t splits, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_batched_sizes(L, M, N, K, splits, &empty);
+  if (st != FP4G_OK) return st;
+  if (d_type != FP4G_OUT_F32 && d_type != FP4G_OUT_BF16) return FP4G_EINVAL;
+  if (empty) return FP4G_OK;
+  if (!D) return FP4G_EINVAL;
+  if (!aligned(D, 16)) return FP4G_EALIGN;
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, L * M * N, bf16, s));
+  if (!A || !sfA || !B || !sfB) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16)) return FP4G_EALIGN;
+  if (!aligned(sfA, 4) || !aligned(sfB, 4)) return FP4G_EALIGN;
+  const Range d = range_of(D, L * M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, L * M * (K / 2)), range_of(sfA, L * M * (K / 32)),
+                        range_of(B, L * N * (K / 2)), range_of(sfB, L * N * (K / 32))};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  // The split: an explicit request must fit the library's scratch (rejected otherwise);
+  // the automatic choice is limited to what fits.
+  const int64_t per_split = L * M * N * 4;
+  const int64_t fits = fp4g::kScratchBytes / per_split;
+  int64_t S = 1;
+  if (splits > 1) {
+    S = fp4g::mxfp4_gemm_splits(L, M, N, K, splits, fp4g::kMaxSplits);
+    if (S > 1 && S > fits) return FP4G_EUNSUPPORTED;
+  } else if (splits == 0) {
+    S = fp4g::mxfp4_gemm_splits(L, M, N, K, 0, fits);
+  }
+  float* P = nullptr;
+  if (S > 1) {
+    const hipError_t e = fp4g::scratch_pointer(&P);
+    if (e != hipSuccess || !P) return FP4G_EHIP;
+  }
+  FP4Args a{M, N, K, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(sfA),
+            static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(sfB), 1.0f, D, bf16};
+  return finish(fp4g::launch_mxfp4_gemm_batched(a, L, S, P, s));
+}
+
 fp4g_status mx_fp4_gemm(int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
                         const void* B, const void* sfB, void* D, int d_type, void* stream) {
   return run_fp4(0, M, N, K, A, sfA, 1.0f, 1.0f, B, sfB, D, d_type, stream);

@@ -80,6 +80,11 @@ hipError_t launch_w4a8_gemm_prepacked(const W4A8Args& a, const float* Sp, hipStr
 // The same ring kernel on plain INT4 weights and bf16 scales (K % 256 == 0, sB 4-byte aligned).
 hipError_t launch_w4a8_ring(const W4A8Args& a, hipStream_t s);
 hipError_t launch_fp8b_gemm(const Fp8bArgs& a, hipStream_t s);
+// Library-held scratch (scratch.hip): kScratchBytes of device memory per GPU, for the
+// allocation-free split-K entry point.  scratch_pointer returns the current device's
+// address of it (looked up once per device; never the array's host-side name).
+constexpr int64_t kScratchBytes = (int64_t)32 << 20;
+hipError_t scratch_pointer(float** out);
 // D[M][N] = 0 (the empty-K product); never uses hipMemset so it can be captured.
 hipError_t launch_zero_fill(void* D, int64_t count, bool bf16_out, hipStream_t s);
 // E2M1 codes + E8M0 scales of X[rows][K] (K % 32 == 0), max-abs rule.

@@ -34,8 +34,12 @@
  * Calls are asynchronous: each entry point validates its arguments on the
  * host, then enqueues its kernel on `stream` (a hipStream_t; NULL is the
  * default stream) and returns.  Faults inside a kernel surface at the
- * caller's next synchronisation.  The library allocates no memory, keeps no
- * per-call state, and may be called from several threads at once.
+ * caller's next synchronisation.  The library allocates no memory and keeps no
+ * per-call state.  The only state it keeps is per device and set on first use:
+ * the compute-unit count (queried once, to size grids), and, for
+ * mx_fp4_gemm_batched_noalloc, the address of its scratch array.  Entry points
+ * may be called from several threads at once, except that calls of
+ * mx_fp4_gemm_batched_noalloc that overlap on one GPU share its scratch.
  * Validation failures return a status code and launch nothing.
  *
  * Sizes (all entry points): M, N, K >= 0 and below 2^31, and M*N (L*M*N for
@@ -114,6 +118,27 @@ fp4g_status mx_fp4_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K,
  * in mx_fp4_gemm_batched (FP4G_EINVAL, FP4G_EUNSUPPORTED; bytes may not be NULL). */
 fp4g_status mx_fp4_gemm_workspace_size(int64_t L, int64_t M, int64_t N, int64_t K,
                                        int64_t splits, size_t *bytes);
+
+/* mx_fp4_gemm_batched for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, layouts, kernels and results, with no workspace argument.  A split of K
+ * keeps its fp32 partial sums in a scratch array that the library holds in every GPU's
+ * memory it runs on (32 MiB per GPU, until the process ends; its address is looked up
+ * once per device on the first call with that device current).  The call allocates
+ * nothing.
+ *   splits  0: the library chooses s, limited to what the scratch holds
+ *           (L*s*M*N*4 <= 32 MiB); 1: no split; s > 1: s slices (clamped to 16 and to
+ *           the number of K stages as in mx_fp4_gemm_batched), rejected with
+ *           FP4G_EUNSUPPORTED when L*s*M*N*4 exceeds 32 MiB.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap in time on
+ * one GPU (other streams, other host threads) race on it and must be serialised by the
+ * caller.  The partial sums are written in full before they are read, so nothing needs
+ * clearing between calls.  Validation and other statuses as for mx_fp4_gemm_batched;
+ * FP4G_EHIP also when the scratch address cannot be obtained. */
+fp4g_status mx_fp4_gemm_batched_noalloc(int64_t L, int64_t M, int64_t N, int64_t K,
+                                        const void *A, const void *sfA,
+                                        const void *B, const void *sfB,
+                                        void *D, int d_type, int64_t splits, void *stream);
 
 /* NVFP4 GEMM: V = 16, E4M3 scales, then D *= global_a * global_b.
  *   A [M][K/2], sfA [M][K/16], B [N][K/2], sfB [N][K/16], D [M][N]. */

@@ -29,7 +29,8 @@ def lib():
 
 
 def test_header_declares_the_operations():
-    assert declared_functions() == sorted(["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_workspace_size",
+    assert declared_functions() == sorted(["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_batched_noalloc",
+                                            "mx_fp4_gemm_workspace_size",
                                             "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "fp4_gemv_prepack_size",
                                             "fp4_gemv_prepack", "fp4_gemv_prepacked",
                                             "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3",
@@ -205,6 +206,27 @@ def test_batched_validation(lib):
     assert mxb(lib, 2, 4, 4, 1024, splits=2, ws=W_ + 8, wsb=4096) == EALIGN
     assert mxb(lib, 2, 4, 4, 1024, splits=2, ws=D_, wsb=4096) == EINVAL   # overlaps D
     assert mxb(lib, 2, 4, 4, 1024, splits=2, ws=B_, wsb=4096) == EINVAL   # overlaps B
+
+
+def test_noalloc_validation(lib):
+    f = lib.mx_fp4_gemm_batched_noalloc
+
+    def call(L, M, N, K, A=A_, sA=SA_, B=B_, sB=SB_, D=D_, dt=1, splits=0):
+        return f(L, M, N, K, A, sA, B, sB, D, dt, splits, None)
+
+    assert call(-1, 4, 4, 128) == EINVAL
+    assert call(2, 4, 4, 128, splits=-1) == EINVAL
+    assert call(2, 4, 4, 192) == EUNSUP
+    assert call(2, 4, 4, 128, dt=3) == EINVAL
+    assert call(0, 4, 4, 128, A=None, sA=None, B=None, sB=None, D=None) == OK
+    assert call(2, 4, 4, 128, A=None) == EINVAL
+    assert call(2, 4, 4, 128, sB=SB_ + 2) == EALIGN
+    assert call(2, 4, 4, 1024, D=A_ + 2048) == EINVAL
+    # an explicit split whose partial sums exceed the 32 MiB scratch is refused before
+    # any device call: 1 x 512 x 4096 x 8192 at s = 5 needs 40 MiB (operands 1 GiB apart)
+    far = dict(A=1 << 30, sA=2 << 30, B=3 << 30, sB=4 << 30, D=5 << 30)
+    assert call(1, 512, 4096, 8192, splits=5, **far) == EUNSUP
+    assert call(2, 1024, 1024, 8192, splits=16, **far) == EUNSUP
 
 
 def test_nv_and_w4a8_batched_validation(lib):
