@@ -151,7 +151,20 @@ fp4g_status nv_fp4_gemm(int64_t M, int64_t N, int64_t K,
  *   D[m][n] = sa[m] * sum_g bf16(sB[n][g]) * sum_{k in group g} e4m3(A[m][k]) * int4(B[n][k])
  *   with groups of 128 consecutive K elements.
  *   A [M][K] bytes, sa [M] fp32, B [N][K/2] bytes, sB [N][K/128] bf16 (raw
- *   16-bit patterns), D [M][N]. */
+ *   16-bit patterns), D [M][N].
+ * Accuracy (also for w4a8_gemm_prepacked and w4a8_gemm_batched).  The products run on
+ * the scaled FP8 matrix instruction, which truncates: in every aligned run of 8
+ * consecutive K elements it drops from each product the part below 2^(E - 13), E the
+ * largest exponent sum e(a) + e(w) of the run's products (e = the E4M3 exponent field,
+ * -6 for subnormals; measured on gfx950).  Weights enter it as the two exact parts
+ * v = q mod 8 and -8 [q < 0] when K % 256 == 0 and for pre-packed weights, else as the
+ * one E4M3 value q.  With S = sum of |products| and H = the sum over runs of
+ * |product| mod 2^(E - 13) (every scale folded into both):
+ *   |D - D_exact| <= 1e-5 * S + H       (plus one bf16 ulp of D_exact for bf16 output).
+ * H is zero when the activation exponents inside every run of 8 span at most 6
+ * binades; for N(0,1)-like activations scaled into the E4M3 range it stays near
+ * 1e-6 * S.  Activations whose runs mix far more binades can reach H up to about
+ * 8e-4 * S in the worst case (one product per run 2^14 times the others). */
 fp4g_status w4a8_gemm(int64_t M, int64_t N, int64_t K,
                       const void *A, const float *sa,
                       const void *B, const void *sB,
@@ -205,7 +218,13 @@ fp4g_status w4a8_prepack_e4m3(int64_t N, int64_t K, const void *B, const void *s
  *   D[m][n] = sum_g sA[m][g] * sB[n][g] * sum_{k in group g} e4m3(A[m][k]) * e4m3(B[n][k])
  *   with groups of 128 consecutive K elements and one fp32 scale per row per group.
  *   A [M][K] bytes and B [N][K] bytes of E4M3 codes (K-major), sA [M][K/128] and
- *   sB [N][K/128] fp32, D [M][N].  Scales need 4-byte alignment. */
+ *   sB [N][K/128] fp32, D [M][N].  Scales need 4-byte alignment.
+ * Accuracy: as for w4a8_gemm, |D - D_exact| <= 1e-5 * S + H with H the FP8
+ * instruction's truncation over aligned runs of 8 products (|a b| mod 2^(E - 13), E the
+ * run's largest exponent sum, scales folded in).  H is zero when every product of a run
+ * is a multiple of its unit, for example when both operands' exponents inside every run
+ * span at most 3 binades; for N(0,1) operands quantized per 128-block it stays below
+ * 1e-5 * S. */
 fp4g_status fp8_blockwise_gemm(int64_t M, int64_t N, int64_t K,
                                const void *A, const float *sA,
                                const void *B, const float *sB,

@@ -120,10 +120,10 @@ def sample_rows(t, ms, ns, a_keys, b_keys):
     return d, ir, ic
 
 
-def check_points(D, d, kind, ir, ic, ms, ns, rel=oracle.REL_TOL):
+def check_points(D, d, kind, ir, ic, ms, ns, extra=None):
     ref, S = oracle.sampled(kind, d, ir, ic)
     got = D[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)].float().cpu().numpy().astype(np.float64)
-    r = oracle.parity_ratio(got, ref, S, "bf16", rel)
+    r = oracle.parity_ratio(got, ref, S, "bf16", extra=extra)
     assert r <= 1.0, f"max |err|/tol = {r}"
 
 
@@ -198,6 +198,7 @@ def test_fp8_blockwise_output_past_2_to_31_elements():
     torch.cuda.synchronize(DEV)
     ms, ns = far_points(M, N, np.random.default_rng(43))
     d, ir, ic = sample_rows(t, ms, ns, ("A", "sA"), ("B", "sB"))
-    check_points(D, d, "fp8b", ir, ic, ms, ns, rel=4e-5)
+    # codes uniform over 0..0x77 (all binades): the FP8 instruction's truncation bound applies
+    check_points(D, d, "fp8b", ir, ic, ms, ns, extra=oracle.fp8_truncation_bound("fp8b", d, ir, ic))
     del D
     torch.cuda.empty_cache()
