@@ -66,6 +66,11 @@ typedef enum {
     FP4G_EHIP = 4          /* the HIP runtime rejected the launch */
 } fp4g_status;
 
+/* Output type of D.  Entry points take it as `int d_type` (and the quantizers' input
+ * type as `int x_type`), the enums' underlying type: callers from C, ctypes and other
+ * foreign-function layers may pass any int, every value is validated
+ * (FP4G_EINVAL unless it names an enumerator), and in the C++ implementation an enum
+ * parameter holding a value outside its enumerators would be undefined. */
 typedef enum {
     FP4G_OUT_F32 = 0,
     FP4G_OUT_BF16 = 1
@@ -231,8 +236,12 @@ fp4g_status fp8_blockwise_gemm(int64_t M, int64_t N, int64_t K,
                                void *D, int d_type, void *stream);
 
 /* MXFP4 GEMV for decode (few tokens): the MXFP4 GEMM with 1 <= M <= 16 and the
- * same layouts, tuned for streaming the weight operand B once from HBM.
- * M > 16 returns FP4G_EUNSUPPORTED. */
+ * same layouts, tuned for streaming the weight operand B once from HBM.  The cute-rs
+ * page lists the MXFP4 GEMV among its next steps ("Where to Go Next"); the Hopper
+ * CUTLASS/CuTe DSL blog post sizes the token tile from 16 for this decode regime and
+ * swaps the operands so the weights fill the instruction's wide side (sections "What
+ * changes in the W4A8 builder" and "The W4A8 kernel: the same four definitions, with
+ * the operands swapped").  M > 16 returns FP4G_EUNSUPPORTED. */
 fp4g_status fp4_gemv(int64_t M, int64_t N, int64_t K,
                      const void *A, const void *sfA,
                      const void *B, const void *sfB,
