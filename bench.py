@@ -43,6 +43,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def fp4_device_cus(dev):
+    return torch.cuda.get_device_properties(dev).multi_processor_count
+
+
 def to_dev(d, dev):
     out = {}
     for k, v in d.items():
@@ -127,6 +131,8 @@ def traffic_of(name):
     src = next(src for n, _, src in COUNTED if n == name)
     return traffic_from_profile(name, src, None)
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+TRAFFIC_SOURCE = ("committed rocprofv3 counter summary (profiles/<kernel>_counters.txt: FETCH_SIZE and WRITE_SIZE "
+                  "scaled by a 512 MiB device copy), used only while the kernel's source hash matches; null otherwise")
 
 
 def traffic_from_profile(name, kernel_src, launches_bytes):
@@ -263,8 +269,17 @@ def bench_mx8192(steps, warmup, dev):
     flops = 2.0 * M * N * K
     tf = flops / (mean_ms * 1e-3) / 1e12
     bytes_alg = d["A"].nbytes + d["sfA"].nbytes + d["B"].nbytes + d["sfB"].nbytes + M * N * 2
+    # The shader clock the GEMM runs at, averaged over 200 back-to-back launches (outside
+    # the timed region).
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(50):
+            fn()
+    g.replay()
+    torch.cuda.synchronize(dev)
+    ghz = shader_clock_over(lambda: [g.replay() for _ in range(4)], dev)
     return d, {"ms": mean_ms, "wall_s": wall, "tflops": tf, "flops": flops,
-               "bytes": bytes_alg}
+               "bytes": bytes_alg, "D": D, "ghz": ghz}
 
 
 def bench_gemv(steps, warmup, dev):
@@ -290,7 +305,7 @@ def bench_gemv(steps, warmup, dev):
     bytes_alg = d["A"].nbytes + d["sfA"].nbytes + wbytes + M * N * 2
     gbs = bytes_alg / (mean_ms * 1e-3) / 1e9
     return {"ms": mean_ms, "eager_ms": eager_ms, "gbs": gbs, "bytes": bytes_alg, "copies": copies,
-            "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12}
+            "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12, "d": d, "D": D}
 
 
 def bench_gemv_prepacked(steps, warmup, dev):
@@ -323,7 +338,7 @@ def bench_w4a8(steps, warmup, dev):
     flops = 2.0 * M * N * K
     bytes_alg = d["A"].nbytes + d["sa"].nbytes + wbytes + M * N * 2
     return {"ms": mean_ms, "tflops": flops / (mean_ms * 1e-3) / 1e12,
-            "gbs": bytes_alg / (mean_ms * 1e-3) / 1e9, "bytes": bytes_alg, "copies": copies}
+            "gbs": bytes_alg / (mean_ms * 1e-3) / 1e9, "bytes": bytes_alg, "copies": copies, "d": d, "D": D}
 
 
 def bench_w4a8_prepacked(steps, warmup, dev):
@@ -352,7 +367,7 @@ def bench_nv1024(steps, warmup, dev):
     D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     fn = lambda: fp4.nv_fp4_gemm(t["A"], t["sfA"], 1.0, t["B"], t["sfB"], 1.0, out=D)
     mean_ms, _ = time_launches(fn, steps, warmup, dev)
-    return {"ms": mean_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12}
+    return {"ms": mean_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12, "d": d, "D": D}
 
 
 def bench_mx256(steps, warmup, dev):
@@ -361,7 +376,7 @@ def bench_mx256(steps, warmup, dev):
     D = torch.empty((256, 256), dtype=torch.float32, device=dev)
     fn = lambda: fp4.mx_fp4_gemm(t["A"], t["sfA"], t["B"], t["sfB"], out=D)
     mean_ms, _ = time_launches(fn, steps, warmup, dev)
-    return {"ms": mean_ms, "tflops": 2.0 * 256 ** 3 / (mean_ms * 1e-3) / 1e12}
+    return {"ms": mean_ms, "tflops": 2.0 * 256 ** 3 / (mean_ms * 1e-3) / 1e12, "d": d, "D": D}
 
 
 def bench_fp8b(steps, warmup, dev):
@@ -372,7 +387,7 @@ def bench_fp8b(steps, warmup, dev):
     fn = lambda: fp4.fp8_blockwise_gemm(t["A"], t["sA"], t["B"], t["sB"], out=D)
     mean_ms, _ = time_launches(fn, steps, warmup, dev)
     bytes_alg = d["A"].nbytes + d["sA"].nbytes + d["B"].nbytes + d["sB"].nbytes + M * N * 2
-    return {"ms": mean_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12, "bytes": bytes_alg}
+    return {"ms": mean_ms, "tflops": 2.0 * M * N * K / (mean_ms * 1e-3) / 1e12, "bytes": bytes_alg, "d": d, "D": D}
 
 
 def bench_skinny(steps, warmup, dev, L=1, M=128, N=8192, K=8192):
@@ -441,12 +456,106 @@ def bench_copy(dev, mib=512):
     return {"bytes_each_way": n, "ms": ms, "gbs": 2 * n / (ms * 1e-3) / 1e9}
 
 
+# ---- measured ceilings and the shader clock ------------------------------------------------
+
+PROBE_LIB = os.path.join(ROOT, "block_scaled_precision_e2m1_amd", "libfp4probe.so")
+
+
+def measure_peaks(dev, cus):
+    """The FP4 matrix pipe's attainable rate (all CUs, one wave per SIMD, 12 independent
+    32x32x64 chains on random operand bits) with the shader clock it held, and the HBM
+    read rate of a 1 GiB stream (past the 256 MB last-level cache)."""
+    import ctypes
+    lib = _probe_lib()
+    if lib is None:
+        return None
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    grid, iters, chains = cus, 100000, 12
+    sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(grid * 4, dtype=torch.int64, device=dev)
+    run = lambda: lib.fp4p_mfma_probe(grid, iters, 12345, sink.data_ptr(), clocks.data_ptr(), stream)
+    if run():
+        return None
+    ms, _ = time_launches(run, 3, 1, dev, graph=False)
+    c = clocks.view(grid, 4).cpu().numpy().astype(np.float64)
+    ghz = float(np.median((c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / 100e6))) / 1e9
+    flops = grid * 4 * iters * chains * 2.0 * 32 * 32 * 64
+    n = 1 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev).fill_(3)
+    rgrid = cus * 8
+    rsink = torch.empty(rgrid * 256, dtype=torch.int32, device=dev)
+    rrun = lambda: lib.fp4p_read_probe(rgrid, buf.data_ptr(), n, rsink.data_ptr(), stream)
+    if rrun():
+        return None
+    rms, _ = time_launches(rrun, 5, 1, dev, graph=False)
+    del buf
+    return {"fp4_mfma": {"tflops": flops / (ms * 1e-3) / 1e12, "peak": PEAK_TFLOPS["fp4"],
+                         "frac_of_peak": flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["fp4"], "shader_ghz": ghz,
+                         "probe": f"{cus} workgroups x 4 waves, {chains} independent scaled FP4 32x32x64 chains "
+                                  f"per wave, random operand bits, {iters} rounds"},
+            "hbm_read": {"gbs": n / (rms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "frac_of_peak": n / (rms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "probe": "1 GiB read once per launch with 16-byte non-temporal loads, 5 launches"}}
+
+
+def _probe_lib():
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.fp4p_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    lib.fp4p_read_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fp4p_timestamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def shader_clock_over(run, dev):
+    """Average shader clock (GHz) over `run()` (kernels enqueued on the current stream):
+    one-wave kernels before and after read the shader clock counter and the 100 MHz
+    counter."""
+    import ctypes
+    lib = _probe_lib()
+    if lib is None:
+        return None
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ts = torch.zeros(4, dtype=torch.int64, device=dev)
+    if lib.fp4p_timestamp(ts.data_ptr(), stream):
+        return None
+    run()
+    if lib.fp4p_timestamp(ts.data_ptr() + 16, stream):
+        return None
+    torch.cuda.synchronize(dev)
+    t = ts.cpu().numpy().astype(np.float64)
+    return float((t[2] - t[0]) / ((t[3] - t[1]) / 100e6) / 1e9)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_threads():
     n = len(os.sched_getaffinity(0))
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit():
         n = min(n, int(env))
     return max(1, n)
+
+
+def parity_of_headline(d, D, rows):
+    """Parity of the benched 8192^3 output on the oracle's baseline rows (computed again
+    here, outside the baseline's timing, so the baseline times the oracle alone)."""
+    import oracle
+    rows = min(rows, 64)
+    ref, S = oracle.mx_gemm(d["A"], d["sfA"], d["B"], d["sfB"], rows=(0, rows))
+    Dg = D[:rows].float().cpu().numpy().astype(np.float64)
+    return {"max_err_over_tol": oracle.parity_ratio(Dg, ref, S, "bf16"), "rows": rows, "out": "bf16"}
 
 
 def cpu_baseline(d, budget_s=15.0):
@@ -465,9 +574,54 @@ def cpu_baseline(d, budget_s=15.0):
     oracle.mx_gemm(d["A"], d["sfA"], d["B"], d["sfB"], rows=(0, rows))
     secs = time.perf_counter() - t0
     return {"value": 2.0 * rows * N * K / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "rows": rows,
             "sample": f"rows 0..{rows - 1} of the 8192^3 MXFP4 GEMM (all 8192 columns, full K), "
                       f"{secs:.1f} s on {threads} threads"}
+
+
+def _median_time(fn, repeats=3):
+    ts, out = [], None
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        out = fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), out
+
+
+def oracle_leg(results):
+    """After all GPU timing: for each benchmarked workload, the oracle's time on a bounded
+    sample of the same inputs (median of 3 runs; whole rows, all columns, full K) and the
+    parity ratio max |D_gpu - D| / tol of the benched output on those rows (the bar of the
+    oracle module: 1e-5 S, plus one bf16 ulp for bf16 output, plus the FP8 instruction's
+    truncation bound for the FP8 blockwise GEMM)."""
+    import oracle
+    threads = cpu_threads()
+    oracle.set_threads(threads)
+    out = {}
+    # name -> (kind, rows of the sample, output type, FLOPs per row)
+    plan = {"mxfp4_256_f32": ("mx", 256, "f32", 2.0 * 256 * 256),
+            "nvfp4_1024": ("nv", 1024, "bf16", 2.0 * 1024 * 1024),
+            "mxfp4_gemv_8x14336x4096": ("mx", 8, "bf16", 2.0 * 14336 * 4096),
+            "w4a8_256x8192x8192": ("w4a8", 8, "bf16", 2.0 * 8192 * 8192),
+            "fp8_blockwise_4096": ("fp8b", 16, "bf16", 2.0 * 4096 * 4096)}
+    for name, (kind, rows, od, flops_row) in plan.items():
+        r = results.get(name)
+        if r is None:
+            continue
+        d = r["d"]
+        secs, (ref, S) = _median_time(lambda: oracle.run(kind, d, rows=(0, rows)))
+        Dg = r["D"][:rows].float().cpu().numpy().astype(np.float64)
+        extra = None
+        if kind == "fp8b":
+            sub = dict(d, A=d["A"][:rows], sA=d["sA"][:rows])
+            extra = oracle.fp8_truncation_bound("fp8b", sub)
+        out[name] = {"cpu_baseline": {"value": rows * flops_row / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
+                                      "kind": "oracle", "seconds": secs,
+                                      "sample": f"rows 0..{rows - 1} (all columns, full K), median of 3 runs"},
+                     "parity": {"max_err_over_tol": oracle.parity_ratio(Dg, ref, S, od, extra=extra),
+                                "rows": rows, "out": od}}
+        log(f"bench: oracle {name}: {secs:.2f} s for {rows} rows; parity {out[name]['parity']['max_err_over_tol']:.3g}")
+    return out
 
 
 def main():
@@ -476,7 +630,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: mx8192 gemv gemvp w4a8 w4a8p nv1024 mx256 quant nvquant fp8b skinny copy")
+                    help="subset of: mx8192 gemv gemvp w4a8 w4a8p nv1024 mx256 quant nvquant fp8b skinny copy peaks")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue launches eagerly instead of replaying a HIP graph (for counter runs)")
@@ -506,17 +660,22 @@ def main():
     dev = torch.device("cuda:0")
     fp4.load_library()
     only = set(args.only) if args.only else {"mx8192", "gemv", "gemvp", "w4a8", "w4a8p", "nv1024", "mx256",
-                                             "quant", "nvquant", "fp8b", "skinny"}
+                                             "quant", "nvquant", "fp8b", "skinny", "peaks"}
     also = {}
     head = None
     d8192 = None
+    kept = {}          # outputs and inputs of the benched workloads, for the oracle leg
+    clock_ghz = None
     if "mx8192" in only:
         log("bench: mxfp4 8192^3 ...")
         d8192, head = bench_mx8192(args.steps, args.warmup, dev)
+        clock_ghz = head["ghz"]
+        log(f"bench: shader clock under the GEMM {clock_ghz} GHz")
         log(f"bench: mxfp4 8192^3 {head['ms'] * 1e3:.1f} us/launch, {head['tflops']:.0f} TFLOP/s")
     if "gemv" in only:
         log("bench: gemv 8x14336x4096 (cold) ...")
         g = bench_gemv(max(args.steps, 100), args.warmup, dev)
+        kept["mxfp4_gemv_8x14336x4096"] = g
         log(f"bench: gemv {g['ms'] * 1e3:.2f} us/launch, {g['gbs']:.0f} GB/s "
             f"(eager launches: {g['eager_ms'] * 1e3:.2f} us)")
         traffic = traffic_from_profile("fp4_gemv_8x14336x4096", ["fp4_gemv.hip", "common.hpp"], g["bytes"])
@@ -541,6 +700,7 @@ def main():
     if "w4a8" in only:
         log("bench: w4a8 256x8192x8192 ...")
         w = bench_w4a8(args.steps, args.warmup, dev)
+        kept["w4a8_256x8192x8192"] = w
         log(f"bench: w4a8 {w['ms'] * 1e3:.1f} us/launch, {w['tflops']:.0f} TFLOP/s, {w['gbs']:.0f} GB/s")
         also["w4a8_256x8192x8192"] = {
             "metric": "TFLOP/s", "value": w["tflops"], "ms_per_launch": w["ms"],
@@ -564,6 +724,7 @@ def main():
             "algorithmic_bytes": w["bytes"]}
     if "nv1024" in only:
         n = bench_nv1024(args.steps, args.warmup, dev)
+        kept["nvfp4_1024"] = n
         log(f"bench: nvfp4 1024^3 {n['ms'] * 1e3:.1f} us/launch, {n['tflops']:.0f} TFLOP/s")
         also["nvfp4_1024"] = {"metric": "TFLOP/s", "value": n["tflops"], "ms_per_launch": n["ms"],
                               "roofline": {"bound": "mfma", "achieved": n["tflops"], "peak": PEAK_TFLOPS["bf16"],
@@ -573,6 +734,7 @@ def main():
     if "fp8b" in only:
         log("bench: fp8 blockwise 4096^3 ...")
         f = bench_fp8b(args.steps, args.warmup, dev)
+        kept["fp8_blockwise_4096"] = f
         log(f"bench: fp8 blockwise 4096^3 {f['ms'] * 1e3:.1f} us/launch, {f['tflops']:.0f} TFLOP/s")
         also["fp8_blockwise_4096"] = {
             "metric": "TFLOP/s", "value": f["tflops"], "ms_per_launch": f["ms"],
@@ -618,7 +780,15 @@ def main():
         also["copy_512MiB"] = c
     if "mx256" in only:
         s = bench_mx256(args.steps, args.warmup, dev)
+        kept["mxfp4_256_f32"] = s
         also["mxfp4_256_f32"] = {"metric": "TFLOP/s", "value": s["tflops"], "ms_per_launch": s["ms"]}
+    peaks = None
+    if "peaks" in only:
+        log("bench: measured ceilings (FP4 matrix pipe, HBM read) ...")
+        peaks = measure_peaks(dev, fp4_device_cus(dev))
+        if peaks:
+            log(f"bench: FP4 MFMA-only {peaks['fp4_mfma']['tflops']:.0f} TFLOP/s at "
+                f"{peaks['fp4_mfma']['shader_ghz']:.2f} GHz; HBM read {peaks['hbm_read']['gbs']:.0f} GB/s")
 
     line = {"metric": "TFLOP/s MXFP4 GEMM 8192^3 (% MFMA peak); FP4 GEMV HBM GB/s (% of 8 TB/s)",
             "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -632,10 +802,28 @@ def main():
         line["roofline"] = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_TFLOPS["fp4"],
                             "unit": "TFLOP/s", "frac": head["tflops"] / PEAK_TFLOPS["fp4"],
                             "traffic": traffic_from_profile("mxfp4_gemm_8192", ["mxfp4_gemm.hip", "common.hpp"],
-                                                            head["bytes"])}
+                                                            head["bytes"]),
+                            "traffic_source": TRAFFIC_SOURCE, "shader_ghz_during_run": clock_ghz}
+        if peaks:
+            line["roofline"]["measured_peak"] = peaks["fp4_mfma"]
         if not args.no_cpu:
             log("bench: cpu oracle baseline ...")
             line["cpu_baseline"] = cpu_baseline(d8192)
+            line["cpu_baseline"]["cpu_model"] = cpu_model()
+            line["parity"] = parity_of_headline(d8192, head["D"], line["cpu_baseline"]["rows"])
+    if peaks:
+        for key in ("mxfp4_gemv_8x14336x4096", "mxfp4_gemv_8x14336x4096_prepacked", "mx_quantize_8192x8192_f32",
+                    "nv_quantize_8192x8192_f32"):
+            if key in also:
+                also[key]["roofline"]["measured_peak"] = peaks["hbm_read"]
+        also["measured_peaks"] = peaks
+    if not args.no_cpu and kept:
+        for name, res in oracle_leg(kept).items():
+            if name in also:
+                also[name].update(res)
+    for entry in also.values():
+        if isinstance(entry, dict) and isinstance(entry.get("roofline"), dict):
+            entry["roofline"]["traffic_source"] = TRAFFIC_SOURCE
     # MFMA / LDS / VALU utilisation of each kernel from the committed counter run
     # (null when the kernel changed since the counters were taken).
     if "roofline" in line:

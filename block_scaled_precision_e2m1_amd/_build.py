@@ -61,7 +61,24 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe(cc)
     return LIB
+
+
+PROBE_SRC = os.path.join(HERE, "probe", "peak_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libfp4probe.so")
+
+
+def build_probe(cc=None) -> str:
+    """The benchmark's measurement kernels (matrix-pipe and HBM-read ceilings): a separate
+    shared library, not part of the operations' ABI."""
+    cc = cc or hipcc()
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([cc] + COMMON + ["-shared", "-x", "hip", PROBE_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
