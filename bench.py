@@ -506,28 +506,37 @@ def _probe_lib():
     lib.fp4p_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p]
     lib.fp4p_read_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
-    lib.fp4p_timestamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fp4p_timestamp.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
 def shader_clock_over(run, dev):
     """Average shader clock (GHz) over `run()` (kernels enqueued on the current stream):
-    one-wave kernels before and after read the shader clock counter and the 100 MHz
-    counter."""
+    kernels with one workgroup per CU before and after record each XCC's shader clock
+    counter and the 100 MHz counter; the median over XCCs of their clocks."""
     import ctypes
     lib = _probe_lib()
     if lib is None:
         return None
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    ts = torch.zeros(4, dtype=torch.int64, device=dev)
-    if lib.fp4p_timestamp(ts.data_ptr(), stream):
+    grid = fp4_device_cus(dev)
+    ts = torch.zeros((2, grid, 3), dtype=torch.int64, device=dev)
+    if lib.fp4p_timestamp(grid, ts[0].data_ptr(), stream):
         return None
     run()
-    if lib.fp4p_timestamp(ts.data_ptr() + 16, stream):
+    if lib.fp4p_timestamp(grid, ts[1].data_ptr(), stream):
         return None
     torch.cuda.synchronize(dev)
-    t = ts.cpu().numpy().astype(np.float64)
-    return float((t[2] - t[0]) / ((t[3] - t[1]) / 100e6) / 1e9)
+    t = ts.cpu().numpy()
+    clocks = []
+    for x in np.unique(t[0, :, 0]):
+        a, b = t[0][t[0, :, 0] == x], t[1][t[1, :, 0] == x]
+        if len(a) and len(b):
+            dt = float(np.median(b[:, 1]) - np.median(a[:, 1]))
+            dr = float(np.median(b[:, 2]) - np.median(a[:, 2]))
+            if dr > 0:
+                clocks.append(dt / (dr / 100e6) / 1e9)
+    return float(np.median(clocks)) if clocks else None
 
 
 def cpu_model():

@@ -6,9 +6,9 @@
 //     the matrix pipe alone at the clock the chip holds under it.  Wave 0 of each
 //     workgroup records the shader clock counter and the 100 MHz constant counter at its
 //     start and end, which give the clock the matrix pipe ran at.
-//   fp4p_timestamp: one lane writes the shader clock counter and the 100 MHz constant
-//     counter; two of them around a run of kernels on one stream give the average shader
-//     clock over that run.
+//   fp4p_timestamp: every workgroup writes its XCC id, the shader clock counter and the
+//     100 MHz constant counter; two of them around a run of kernels on one stream give
+//     the average shader clock of each XCC over that run.
 //   fp4p_read_probe: streams `bytes` from device memory with 16-byte non-temporal loads
 //     (each byte once, every lane in flight with several loads), the attainable read
 //     rate of HBM for a buffer past the 256 MB last-level cache.
@@ -79,10 +79,16 @@ __global__ void __launch_bounds__(256) read_probe_kernel(const v4i* __restrict__
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
+// Each workgroup (one per CU) records its XCC (hardware register XCC_ID, 4 bits), the
+// shader clock counter and the 100 MHz counter.  The shader clock counters of different
+// XCCs are not aligned with one another, so clocks are taken per XCC.
 __global__ void timestamp_kernel(uint64_t* out) {
   if (threadIdx.x == 0) {
-    out[0] = __builtin_amdgcn_s_memtime();
-    out[1] = __builtin_amdgcn_s_memrealtime();
+    const uint64_t t = __builtin_amdgcn_s_memtime(), r = __builtin_amdgcn_s_memrealtime();
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u;   // XCC_ID[3:0]
+    out[3 * blockIdx.x + 0] = xcc;
+    out[3 * blockIdx.x + 1] = t;
+    out[3 * blockIdx.x + 2] = r;
   }
 }
 
@@ -90,10 +96,11 @@ __global__ void timestamp_kernel(uint64_t* out) {
 
 extern "C" {
 
-// out: 2 uint64 of device memory (shader clock counter, 100 MHz counter).
-int fp4p_timestamp(uint64_t* out, void* stream) {
-  if (!out) return 1;
-  hipLaunchKernelGGL(timestamp_kernel, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), out);
+// out: 3 * grid uint64 of device memory: per workgroup (XCC id, shader clock counter,
+// 100 MHz counter).
+int fp4p_timestamp(int grid, uint64_t* out, void* stream) {
+  if (grid <= 0 || !out) return 1;
+  hipLaunchKernelGGL(timestamp_kernel, dim3(grid), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), out);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
