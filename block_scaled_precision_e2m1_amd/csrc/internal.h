@@ -79,6 +79,12 @@ hipError_t launch_w4a8_prepack_e4m3(int64_t N, int64_t K, const uint8_t* B, cons
 hipError_t launch_w4a8_gemm_prepacked(const W4A8Args& a, const float* Sp, hipStream_t s);
 // The same ring kernel on plain INT4 weights and bf16 scales (K % 256 == 0, sB 4-byte aligned).
 hipError_t launch_w4a8_ring(const W4A8Args& a, hipStream_t s);
+// Decode GEMV for 1 <= M <= 16 tokens and K <= 16384 (w4a8_gemv_fits): weights in the
+// 16-row slot of the FP8 instruction, tokens padded to 16.  Sp null: plain weights and
+// bf16 scales (a.B, a.sB, batch a.L); otherwise a.B is the pre-packed weight buffer and
+// Sp its fp32 scales.
+bool w4a8_gemv_fits(int64_t M, int64_t K);
+hipError_t launch_w4a8_gemv(const W4A8Args& a, const float* Sp, hipStream_t s);
 hipError_t launch_fp8b_gemm(const Fp8bArgs& a, hipStream_t s);
 // Library-held scratch (scratch.hip): kScratchBytes of device memory per GPU, for the
 // allocation-free split-K entry point.  scratch_pointer returns the current device's

@@ -357,6 +357,7 @@ hipError_t launch_w4a8_prepack_e4m3(int64_t N, int64_t K, const uint8_t* B, cons
 
 // a.B is the packed weight buffer; Sp the packed fp32 scales.
 hipError_t launch_w4a8_gemm_prepacked(const W4A8Args& a, const float* Sp, hipStream_t s) {
+  if (w4a8_gemv_fits(a.M, a.K)) return launch_w4a8_gemv(a, Sp, s);        // decode: a 16-token tile
   // 64-token tiles: two workgroups share a CU (79 KB of LDS, at most 256 registers).
   return launch_bm<64, true>(a, Sp, s);
 }
