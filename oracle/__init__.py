@@ -386,10 +386,13 @@ def _w4a8_row_bound(amag, aexp, q, split):
     """Per-run losses [N, K/8] of one activation row against all weight rows."""
     ea = np.where(amag > 0, aexp, -np.inf)
     if split:
-        # the two exact FP8 parts of q = v - 8 s: v = q mod 8 in 0..7 and the sign part 8 s
+        # the two exact FP8 parts of q = v - 8 s: v = q mod 8 in 0..7 and the sign part 8 s;
+        # v as its E4M3 value (split 1) or as the subnormal code v * 2^-9 scaled by 2^9,
+        # exponent field -6 + 9 = 3 for every v (split 2)
         v = q & 7
         sgn = (q < 0).astype(np.float64)
-        lv = _run_loss(amag[None, :] * v, ea[None, :] + _INT_EXP[v])
+        ev = np.where(v > 0, 3.0, -np.inf) if split == 2 else _INT_EXP[v]
+        lv = _run_loss(amag[None, :] * v, ea[None, :] + ev)
         ls = _run_loss(8.0 * amag[None, :] * sgn, np.where(sgn > 0, ea[None, :] + 3.0, -np.inf))
         return lv + ls
     aq = np.abs(q)
@@ -399,9 +402,12 @@ def _w4a8_row_bound(amag, aexp, q, split):
 def fp8_truncation_bound_np(kind, inputs, ms=None, ns=None, split=True):
     """The truncation bound H of the FP8 matrix instruction (see above) for the outputs of
     a W4A8 ("w4a8") or FP8 blockwise ("fp8b") product: the full [M][N] array, or the
-    pairs (ms[i], ns[i]).  W4A8 with split=True takes the weights as the two exact FP8
-    parts v = q mod 8 and -8 [q < 0] (the pipelined kernel, K % 256 == 0); with
-    split=False as one E4M3 value q (the kernel for other K)."""
+    pairs (ms[i], ns[i]).  W4A8 with split=True (or 1) takes the weights as the two
+    exact FP8 parts v = q mod 8 and -8 [q < 0], v as its E4M3 value (the pipelined GEMM
+    kernel, K % 256 == 0); split=2 the same parts with v as the subnormal code v * 2^-9
+    scaled by 2^9 (the decode kernel, M <= 16); split=False as one E4M3 value q (the
+    GEMM kernel for other K)."""
+    split = _split_mode(split)
     mag, ex = _e4m3_exponents()
     A = _u8(inputs["A"])
     amag, aexp = mag[A], ex[A]
@@ -444,9 +450,17 @@ def fp8_truncation_bound_np(kind, inputs, ms=None, ns=None, split=True):
     raise ValueError(kind)
 
 
+def _split_mode(split):
+    mode = int(split)
+    if mode not in (0, 1, 2) or (not isinstance(split, (bool, int, np.integer))):
+        raise ValueError(f"split must be False, True, 0, 1 or 2, not {split!r}")
+    return mode
+
+
 def fp8_truncation_bound(kind, inputs, ms=None, ns=None, split=True):
     """The same bound from oracle.c (plain C over all host threads): the full [M][N]
     array, or the pairs (ms[i], ns[i]).  fp8_truncation_bound_np is the numpy form."""
+    split = _split_mode(split)
     A, B = _u8(inputs["A"]), _u8(inputs["B"])
     M, N, K = A.shape[0], B.shape[0], A.shape[1]
     if kind == "w4a8":
@@ -462,13 +476,13 @@ def fp8_truncation_bound(kind, inputs, ms=None, ns=None, split=True):
     lib = _load()
     if ms is None:
         H = np.empty((M, N), np.float64)
-        rc = lib.oracle_fp8_bound(code, int(split), M, N, K, _ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb),
+        rc = lib.oracle_fp8_bound(code, split, M, N, K, _ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb),
                                   0, M, None, None, 0, _ptr(H))
     else:
         ms = np.ascontiguousarray(ms, dtype=np.int64)
         ns = np.ascontiguousarray(ns, dtype=np.int64)
         H = np.empty(ms.shape[0], np.float64)
-        rc = lib.oracle_fp8_bound(code, int(split), M, N, K, _ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb),
+        rc = lib.oracle_fp8_bound(code, split, M, N, K, _ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb),
                                   0, 0, _ptr(ms), _ptr(ns), ms.shape[0], _ptr(H))
     if rc:
         raise ValueError("oracle_fp8_bound: bad arguments")

@@ -312,7 +312,9 @@ int oracle_sampled(int kind, int64_t M, int64_t N, int64_t K,
  * 2^(E - 13); H sums those magnitudes over every run with the scales folded in, which
  * bounds the error of the sum.
  * W4A8 weights enter either as one E4M3 value q (split = 0) or as the two exact parts
- * v = q mod 8 and -8 [q < 0], each its own instruction (split = 1). */
+ * v = q mod 8 and -8 [q < 0], each its own instruction, with v as the E4M3 value v
+ * (split = 1) or as the subnormal code v, worth v * 2^-9, scaled by 2^9 in the
+ * instruction (split = 2): its exponent field is then -6 + 9 = 3 whatever v is. */
 static int e4m3_exp_field(unsigned c) {
     const unsigned E = (c >> 3) & 15u;
     return E == 0 ? -6 : (int)E - 7;
@@ -354,7 +356,7 @@ static double fp8_bound_one(int kind, int split, int64_t K, const uint8_t *arow,
                     const int q = oracle_int4(nibble(brow, k));
                     const int v = q & 7, neg = q < 0;
                     p1[i] = am * v;
-                    e1[i] = ea + int_exp_field(v);
+                    e1[i] = split == 2 ? ea + 3 : ea + int_exp_field(v);
                     p2[i] = neg ? 8.0 * am : 0.0;
                     e2[i] = ea + 3;
                 } else {
@@ -384,7 +386,8 @@ int oracle_fp8_bound(int kind, int split, int64_t M, int64_t N, int64_t K,
                      const uint8_t *A, const void *sfA, const uint8_t *B, const void *sfB,
                      int64_t row0, int64_t row1, const int64_t *ms, const int64_t *ns, int64_t count,
                      double *H) {
-    if ((kind != 2 && kind != 3) || M < 0 || N < 0 || K < 0 || K % 128 || !H) return -1;
+    if ((kind != 2 && kind != 3) || split < 0 || split > 2 || M < 0 || N < 0 || K < 0 || K % 128 || !H)
+        return -1;
     const int64_t b_ld = kind == 3 ? K : K / 2;
     if (ms) {
         for (int64_t i = 0; i < count; ++i)

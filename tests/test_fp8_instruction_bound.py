@@ -10,7 +10,9 @@ E4M3 exponent field, -6 for subnormals), then added.  These pins check, on the C
   every binade inside each run), never loses more than H, and loses exactly H on a
   constructed case where every loss has one sign (so H is tight);
 - H is zero when the exponents inside every run are close enough that nothing is
-  truncated, the regime in which the plain 1e-5 * S bar applies.
+  truncated, the regime in which the plain 1e-5 * S bar applies;
+- the subnormal form of the W4A8 weight part v (split=2) charges more than the E4M3
+  form (split=1) on the same inputs, since every nonzero v then counts with exponent 3.
 """
 import math
 from fractions import Fraction
@@ -65,8 +67,10 @@ def model_w4a8(d, m, n, split):
                 a = Fraction(E4M3[A[m, k]])
                 ea = exp_field(A[m, k])
                 if split:
+                    # v as its E4M3 value (split 1) or as the subnormal code v * 2^-9
+                    # scaled by 2^9, whose exponent field is -6 + 9 = 3 (split 2)
                     v, s = int(q[k]) & 7, int(q[k] < 0)
-                    run1.append((a * v, ea + int_exp(v)))
+                    run1.append((a * v, ea + (3 if split == 2 else int_exp(v))))
                     run2.append((-8 * a * s, ea + 3))
                 else:
                     run1.append((a * int(q[k]), ea + int_exp(abs(int(q[k])))))
@@ -125,7 +129,7 @@ def wide_fp8b(M, N, K, seed):
 
 
 @pytest.mark.parametrize("kind", ["w4a8", "fp8b"])
-@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("split", [True, False, 2])
 def test_c_and_numpy_forms_agree(oracle_lib, kind, split):
     d = wide_w4a8(9, 11, 256, 1) if kind == "w4a8" else wide_fp8b(9, 11, 256, 1)
     H = oracle_lib.fp8_truncation_bound(kind, d, split=split)
@@ -135,7 +139,7 @@ def test_c_and_numpy_forms_agree(oracle_lib, kind, split):
     assert np.array_equal(oracle_lib.fp8_truncation_bound(kind, d, ms, ns, split=split), H[ms, ns])
 
 
-@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("split", [True, False, 2])
 def test_w4a8_model_loss_within_bound(oracle_lib, split):
     d = wide_w4a8(3, 4, 256, 2)
     H = oracle_lib.fp8_truncation_bound("w4a8", d, split=split)
@@ -184,7 +188,7 @@ def test_bound_vanishes_for_narrow_runs(oracle_lib):
     E = np.repeat(lo, 8, axis=1) + rng.integers(0, 7, (M, K))   # spread <= 6 inside a run
     d["A"] = ((E << 3) | rng.integers(0, 8, (M, K)) | (rng.integers(0, 2, (M, K)) << 7)).astype(np.uint8)
     assert not np.isnan(E4M3[d["A"]]).any()
-    for split in (True, False):
+    for split in (True, False, 2):
         assert not oracle_lib.fp8_truncation_bound("w4a8", d, split=split).any()
     f = datagen.random_fp8b(M, N, K, rng)
     Ea = np.repeat(rng.integers(1, 11, (M, K // 8)), 8, axis=1) + rng.integers(0, 4, (M, K))
@@ -192,3 +196,25 @@ def test_bound_vanishes_for_narrow_runs(oracle_lib):
     f["A"] = ((Ea << 3) | rng.integers(0, 8, (M, K))).astype(np.uint8)
     f["B"] = ((Eb << 3) | rng.integers(0, 8, (N, K))).astype(np.uint8)
     assert not oracle_lib.fp8_truncation_bound("fp8b", f).any()
+
+
+def test_subnormal_weight_part_widens_the_window(oracle_lib):
+    """split=2 counts every nonzero v with exponent field 3 (the largest the E4M3 form
+    reaches is 2, for v = 4..7): on activations over every binade its H is at least the
+    E4M3 form's everywhere and larger somewhere; runs whose activations all share one
+    exponent lose nothing in either form."""
+    d = wide_w4a8(4, 6, 256, 7)
+    H1 = oracle_lib.fp8_truncation_bound("w4a8", d, split=True)
+    H2 = oracle_lib.fp8_truncation_bound("w4a8", d, split=2)
+    assert (H2 >= H1).all() and (H2 > H1).any()
+    d["A"][:] = 0x38                                   # every activation 1.0
+    assert not oracle_lib.fp8_truncation_bound("w4a8", d, split=2).any()
+
+
+def test_split_mode_is_validated(oracle_lib):
+    d = wide_w4a8(2, 2, 128, 8)
+    for bad in (3, -1, "subnormal", 1.5):
+        with pytest.raises(ValueError):
+            oracle_lib.fp8_truncation_bound("w4a8", d, split=bad)
+        with pytest.raises(ValueError):
+            oracle_lib.fp8_truncation_bound_np("w4a8", d, split=bad)

@@ -96,6 +96,8 @@ MUTANTS = {
     "fp8-bound-run-length": ("group += run_loss(p1, e1, 8) + run_loss(p2, e2, 8);",
                              "group += run_loss(p1, e1, 4) + run_loss(p2, e2, 4);"),
     "fp8-bound-sign-part-dropped": ("p2[i] = neg ? 8.0 * am : 0.0;", "p2[i] = 0.0;"),
+    "fp8-bound-subnormal-part-exponent": ("e1[i] = split == 2 ? ea + 3 : ea + int_exp_field(v);",
+                                          "e1[i] = split == 2 ? ea + int_exp_field(v) : ea + int_exp_field(v);"),
     "fp8-bound-group-scale-dropped": ("H += fabs(oracle_bf16(((const uint16_t *)sb_row)[g])) * group;",
                                       "H += group;"),
     "sampled-nv-global-scale": ("nv_dot(K, a8 + m * (K / 2), (const uint8_t *)sfA + m * (K / 16), gA,",
