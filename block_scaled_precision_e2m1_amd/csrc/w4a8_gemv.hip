@@ -18,22 +18,32 @@
 //   * lane (r, slot) of a K group holds its 32 consecutive K elements 32*slot..+31 in
 //     both operands: 16 bytes of INT4 for weight row r and 32 bytes of FP8 for token
 //     r, so every aligned run of 8 instruction elements is 8 consecutive K;
-//   * the weights reach LDS through global->LDS copies: plain weights [N][K/2] in
-//     whole-line 1 KB copies of RPI rows x ST*64 bytes, their 16-byte units XOR-
-//     swizzled by row so the 16-row ds_read_b128 hits distinct bank groups; pre-packed
-//     weights (w4a8_prepacked.hip: the 16 x 128 operand of one instruction stored lane
-//     by lane) in one 1 KB copy per K group, with their fp32 scales beside them;
-//   * every load is issued up front and waited for once: a decode GEMV is one pass
-//     over a cold weight stream, and what matters is how many bytes are in flight;
-//   * each weight dword becomes two exact FP8 operands, E4M3(v) and -s * 2^-6 scaled
-//     by 2^9 in the instruction, for q = v - 8s (v the low 3 bits, s bit 3), so two
-//     chained instructions over the same tokens give the group's INT4 product; the
-//     group's partial tile is folded into the fp32 accumulator times sB[n][g];
+//   * the weights reach LDS through 1 KB global->LDS copies issued in K-group order:
+//     plain weights [N][K/2] as 8 rows x 128 bytes (two groups, whole lines), their
+//     16-byte units XOR-swizzled by row so the 16-row ds_read_b128 is conflict-free;
+//     pre-packed weights (w4a8_prepacked.hip: the 16 x 128 operand of one instruction
+//     stored lane by lane) as one copy per group, with their fp32 scales beside them;
+//   * every load is issued up front (tokens, scales, then the weight copies in the order
+//     they are used), so the whole weight stream is in flight at once, and each row
+//     group's next two K groups are multiplied as soon as their copies land (counted
+//     vmcnt waits): the conversion and the instructions overlap the rest of the stream;
+//   * each INT4 q = v - 8s (v the low 3 bits, s bit 3) becomes two exact FP8 parts:
+//     its low 3 bits as they are, the E4M3 subnormal code v (v * 2^-9), and the code
+//     0x88 (-2^-6) where s = 1, both scaled by 2^9 in the instruction, so two chained
+//     instructions over the same tokens give the group's INT4 product with two VALU
+//     operations per four weights (plus one shift per eight); it is folded into the fp32
+//     accumulator times sB[n][g].  As a subnormal code, every nonzero v enters the
+//     instruction's truncation window with exponent field -6 + 9 = 3;
+//   * plain weights stay in their byte order (element 2j in the low nibble of byte j,
+//     2j+1 in the high one): the tokens are permuted to match instead, once per group for
+//     every row group, so both operands list each run of 8 K elements even-first;
 //   * the 8 partial tiles of a row group are summed through LDS (reusing the weight
 //     area) in wave order, so results are run-to-run identical, then scaled by sa[m].
 // K groups past K (the last segment of a ragged K) read clamped in-bounds addresses and
-// are given zero tokens and zero scales; rows past N read row N-1 (plain) or the zero
-// padding rows (pre-packed) and are not stored.
+// are given zero scales; rows past N read row N-1 (plain) or the zero padding rows
+// (pre-packed) and are not stored.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.h"
 
@@ -43,35 +53,51 @@ namespace {
 constexpr int WAVES = 8;
 constexpr int kMaxGroups = 128;             // K <= 16384: 8 waves x 16 groups
 
-// E4M3 codes of 0..7 as a v_perm_b32 table: selector k picks byte k of {hi:lo}.
-constexpr uint32_t kE4M3Lo = 0x44403800u;   // 0, 1, 2, 3
-constexpr uint32_t kE4M3Hi = 0x4E4C4A48u;   // 4, 5, 6, 7
-constexpr int kScale2p9 = 0x88888888;       // E8M0 136 = 2^9 in every byte
+constexpr int kScale2p9 = 0x88888888;          // E8M0 136 = 2^9 in every byte
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t u16) { return __builtin_bit_cast(float, u16 << 16); }
 
-template <int NJ, int RG, bool PACKED, bool BF16>
+// Calls f(integral_constant<int, I>) for I = B .. E-1 (each a compile-time constant).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// SCL selects how the group scales arrive: kSclPacked, fp32 Sp of the pre-packed layout
+// copied into LDS; kSclPairs, bf16 scales copied into LDS as dwords (two groups of one
+// row; K/128 even); kSclSingle, one bf16 load per scale into registers (K/128 odd, where
+// rows of scales are not dword aligned).
+constexpr int kSclPacked = 0, kSclPairs = 1, kSclSingle = 2;
+
+template <int NJ, int RG, int QG, int SCL, bool BF16>
 __global__ void __launch_bounds__(WAVES * 64)
 w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sa,
                  const uint8_t* __restrict__ Bw, const void* __restrict__ Sw, void* __restrict__ D) {
+  constexpr bool PACKED = SCL == kSclPacked;
   constexpr int ST = 4 * NJ;                 // K groups (64 bytes of INT4 per row) per wave
-  constexpr int SEG = ST * 64;               // plain: bytes per row per wave
-  constexpr int UPR = SEG / 16;              // plain: 16-byte units per row segment
-  constexpr int RPI = 64 / UPR;              // plain: rows per 1 KB copy
-  constexpr int ROWS = 16 * RG;
-  constexpr int NI = PACKED ? RG * ST : ROWS / RPI;        // weight copies per wave
-  constexpr int SOFF = RG * ST * 1024;       // pre-packed: fp32 scales after the weights
-  constexpr int WBYTES = PACKED ? SOFF + RG * ST * 64 : ROWS * SEG;
+  static_assert(QG == 2 || QG == 4 || QG == 8, "groups per copy block");
+  static_assert(ST % QG == 0, "whole blocks per segment");
+  constexpr int NC = RG * ST;                // 1 KB weight copies per wave
+  constexpr int SOFF = NC * 1024;            // the scales after the weights
+  // Pre-packed: [ST][16*RG] fp32.  Pairs: [ST/2][16*RG] dwords, in whole 256-byte copies.
+  constexpr int PAIR_COPIES = (RG * ST * 8 + 63) / 64;
+  constexpr int SBYTES = PACKED ? NC * 64 : SCL == kSclPairs ? PAIR_COPIES * 256 : 0;
+  constexpr int WBYTES = SOFF + SBYTES;
   constexpr int RED = WAVES * RG * 64 * 16;
-  static_assert(UPR >= 16 && UPR <= 64 && 64 % UPR == 0, "segment shape");
   static_assert(WAVES * WBYTES <= 160 * 1024 && RED <= WAVES * WBYTES, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[WAVES * WBYTES];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, slot = lane >> 4;
   const int KT = K / 128;
   const int ks0 = wave * ST;
-  const int64_t n0 = (int64_t)blockIdx.x * ROWS;
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * RG);
   const uint16_t* sB = static_cast<const uint16_t*>(Sw);
   if constexpr (!PACKED) {  // plain operands: problem blockIdx.y of a batch stored back to back
     const int64_t b = blockIdx.y;
@@ -82,133 +108,192 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
     D = static_cast<uint8_t*>(D) + b * M * N * (BF16 ? 2 : 4);
   }
   uint8_t* wl = lds + wave * WBYTES;
+  // Row swizzle of the plain weight rows in LDS: 8 units of 16 bytes per row take swz8,
+  // 16 or 32 units the row index itself.
+  auto swz = [](int row) { return QG == 2 ? swz8(row) : (row & 15); };
 
-  // ---- tokens of this wave's segment: lanes r >= M read token 0 (the same lines as
-  // lanes r = 0) and are zeroed below, as are groups past K ----
-  const int64_t trow = r < M ? r : 0;
-  v4i t0[ST], t1[ST];
-#pragma unroll
-  for (int s = 0; s < ST; ++s) {
-    const uint8_t* p = A + trow * K + (int64_t)min(ks0 + s, KT - 1) * 128 + slot * 32;
-    t0[s] = *reinterpret_cast<const v4i*>(p);
-    t1[s] = *reinterpret_cast<const v4i*>(p + 16);
-  }
-
-  // ---- weights (and, pre-packed, their scales) into this wave's LDS area ----
-  const int G16 = (N + 15) / 16;
-  if constexpr (PACKED) {
-    const int64_t Np = 16 * (int64_t)G16;
-    const float* Sp = static_cast<const float*>(Sw);
-#pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      const int64_t g16 = min(n0 / 16 + g, (int64_t)G16 - 1);
-#pragma unroll
-      for (int s = 0; s < ST; ++s) {
-        const int ks = min(ks0 + s, KT - 1);
-        lds_copy16_nt(Bw + (g16 * KT + ks) * 1024 + lane * 16, (lds_void*)(wl + (g * ST + s) * 1024));
-      }
-      // Sp[ks][16*g16 + row]: lane l copies the scale of row l%16 of group 4c + l/16
-#pragma unroll
-      for (int c = 0; c < ST / 4; ++c) {
-        const int ks = min(ks0 + 4 * c + (lane >> 4), KT - 1);
-        lds_copy4(Sp + ks * Np + g16 * 16 + r, (lds_void*)(wl + SOFF + (g * ST + 4 * c) * 64));
-      }
-    }
-  } else {
-    const int64_t ld = K / 2;
-    const int u = lane % UPR, rr = lane / UPR;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = i * RPI + rr;
-      const int gu = u ^ (row & 15);                      // global unit held by LDS unit u
-      const int ks = min(ks0 + (gu >> 2), KT - 1);
-      const int64_t grow = min(n0 + row, (int64_t)N - 1);
-      lds_copy16_nt(Bw + grow * ld + (int64_t)ks * 64 + (gu & 3) * 16, (lds_void*)(wl + i * 1024));
-    }
-  }
-
-  // ---- plain bf16 group scales: lane (r, slot) needs rows 4*slot + t of each row
-  // group, groups ks0 .. ks0+ST-1, kept as bf16 pairs (group 2j in the low half) ----
-  constexpr int SW = PACKED ? 1 : ST / 2;
-  uint32_t sr[RG][4][SW];
-  if constexpr (!PACKED) {
-    // Whole-segment vector loads when the segment lies inside the row and the row
-    // pitch and base keep them aligned: 16 bytes (8 groups), or 8 bytes for ST = 4.
-    constexpr int VB = ST >= 8 ? 16 : 8;
-    const bool vec = ks0 + ST <= KT && (KT * 2) % VB == 0 && (reinterpret_cast<uintptr_t>(sB) & (VB - 1)) == 0;
-#pragma unroll
-    for (int g = 0; g < RG; ++g) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint16_t* p = sB + min(n0 + 16 * g + 4 * slot + t, (int64_t)N - 1) * KT;
-        if (vec) {
-          if constexpr (VB == 16) {
-#pragma unroll
-            for (int c = 0; c < ST / 8; ++c) {
-              const v4i x = *reinterpret_cast<const v4i*>(p + ks0 + 8 * c);
-              sr[g][t][4 * c] = (uint32_t)x[0]; sr[g][t][4 * c + 1] = (uint32_t)x[1];
-              sr[g][t][4 * c + 2] = (uint32_t)x[2]; sr[g][t][4 * c + 3] = (uint32_t)x[3];
-            }
-          } else {
-            typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-            const v2u x = *reinterpret_cast<const v2u*>(p + ks0);
-            sr[g][t][0] = x[0]; sr[g][t][1] = x[1];
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < SW; ++j)
-            sr[g][t][j] = (uint32_t)p[min(ks0 + 2 * j, KT - 1)] | ((uint32_t)p[min(ks0 + 2 * j + 1, KT - 1)] << 16);
-        }
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);          // every load of this wave, copies included
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-
-  const bool tok = r < M;
   v4f acc[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
-  const int unit = 0x7F7F7F7F;
+  // One wave's segment.  FULL: all ST groups lie inside K and all rows inside N (every
+  // wave but those at a ragged edge), so no address is clamped and no scale masked.
+  auto segment = [&](auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
+    // ---- tokens of this wave's segment.  Lanes r >= M read token 0 (the same lines as
+    // lanes r = 0): their columns of the product are never stored.  Groups past K re-read
+    // group K/128 - 1 and are given a zero scale: that product is finite, or NaN only
+    // where a NaN token of that group already makes the stored result NaN. ----
+    // FULL: no address needs clamping, so each load is a base plus a constant offset.
+    auto kc = [&](int ks, int last) { return FULL ? ks : min(ks, last); };
+    auto rc = [&](int64_t row, int64_t last) { return FULL ? row : min(row, last); };
+    const int64_t trow = r < M ? r : 0;
+    v4i t0[ST], t1[ST];
 #pragma unroll
-  for (int s = 0; s < ST; ++s) {
-    const bool ok = ks0 + s < KT;
-    const v8i tv = tok && ok ? v8i{t0[s][0], t0[s][1], t0[s][2], t0[s][3], t1[s][0], t1[s][1], t1[s][2], t1[s][3]}
-                             : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      v4i x;
-      v4f sc;
-      if constexpr (PACKED) {
-        x = *reinterpret_cast<const v4i*>(wl + (g * ST + s) * 1024 + lane * 16);
-        sc = *reinterpret_cast<const v4f*>(wl + SOFF + (g * ST + s) * 64 + slot * 16);
-      } else {
-        const int row = 16 * g + r;
-        x = *reinterpret_cast<const v4i*>(wl + row * SEG + (((s * 4 + slot) ^ r) * 16));
-#pragma unroll
-        for (int t = 0; t < 4; ++t) sc[t] = bf16_bits_to_f32((sr[g][t][s / 2] >> (16 * (s & 1))) & 0xFFFFu);
-      }
-      v8i bv, bs;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // Elements 0..3 and 4..7 of the dword in the low nibbles of the bytes of lo and
-        // hi.  Pre-packed weights are stored that way; plain ones (byte j holds elements
-        // 2j, 2j+1) take one byte permute each of x and x >> 4.
-        const uint32_t xw = (uint32_t)x[w], xs = xw >> 4;
-        const uint32_t lo = PACKED ? xw : __builtin_amdgcn_perm(xs, xw, 0x05010400u);
-        const uint32_t hi = PACKED ? xs : __builtin_amdgcn_perm(xs, xw, 0x07030602u);
-        bv[2 * w] = (int)__builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, lo & 0x07070707u);
-        bv[2 * w + 1] = (int)__builtin_amdgcn_perm(kE4M3Hi, kE4M3Lo, hi & 0x07070707u);
-        bs[2 * w] = (int)((lo & 0x08080808u) | 0x80808080u);
-        bs[2 * w + 1] = (int)((hi & 0x08080808u) | 0x80808080u);
-      }
-      v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, tv, v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8, kFmtFp8,
-                                                                  0, unit, 0, unit);
-      part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bs, tv, part, kFmtFp8, kFmtFp8, 0, kScale2p9, 0, unit);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[g][t] = __builtin_fmaf(part[t], ok ? sc[t] : 0.0f, acc[g][t]);
+    for (int s = 0; s < ST; ++s) {
+      const uint8_t* p = A + trow * K + (int64_t)ks0 * 128 + slot * 32 + (int64_t)(kc(ks0 + s, KT - 1) - ks0) * 128;
+      t0[s] = *reinterpret_cast<const v4i*>(p);
+      t1[s] = *reinterpret_cast<const v4i*>(p + 16);
     }
-  }
+
+    // ---- group scales ----
+    const int G16 = (N + 15) / 16;
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    v2u16 sh[RG][4][SCL == kSclSingle ? ST / 2 : 1];     // two groups' bf16 per register
+    if constexpr (PACKED) {
+      // Sp[ks][16*g16 + row] -> LDS [g*ST + s][row]: lane l copies row l%16 of group 4c + l/16
+      const int64_t Np = 16 * (int64_t)G16;
+      const float* Sp = static_cast<const float*>(Sw);
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        const int64_t g16 = rc(n0 / 16 + g, (int64_t)G16 - 1);
+#pragma unroll
+        for (int c = 0; c < ST / 4; ++c) {
+          const int ks = kc(ks0 + 4 * c + (lane >> 4), KT - 1);
+          lds_copy4(Sp + ks * Np + g16 * 16 + r, (lds_void*)(wl + SOFF + (g * ST + 4 * c) * 64));
+        }
+      }
+    } else if constexpr (SCL == kSclPairs) {
+      // dword j of row `row` (groups ks0+2j, ks0+2j+1) -> LDS dword j*16*RG + row; entries
+      // past the segment (the last copy of a short segment) repeat the last one and land in
+      // the copy's own padding.
+#pragma unroll
+      for (int c = 0; c < PAIR_COPIES; ++c) {
+        const int i = min(c * 64 + lane, RG * ST * 8 - 1);
+        const int j = i / (16 * RG), row = i % (16 * RG);
+        const int ks = kc(ks0 + 2 * j, KT - 2);
+        lds_copy4(sB + rc(n0 + row, (int64_t)N - 1) * KT + ks, (lds_void*)(wl + SOFF + c * 256));
+      }
+    } else {
+      // lane (r, slot) needs rows 4*slot + t of each row group, one bf16 per group
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint16_t* p = sB + min(n0 + 16 * g + 4 * slot + t, (int64_t)N - 1) * KT;
+#pragma unroll
+          for (int j = 0; j < ST / 2; ++j) sh[g][t][j] = v2u16{p[min(ks0 + 2 * j, KT - 1)], p[min(ks0 + 2 * j + 1, KT - 1)]};
+        }
+    }
+
+    // ---- weight copies in K-group order, QG groups (one block) at a time, so blocks can
+    // be multiplied as they land.  A block of one row group is QG copies of 1 KB:
+    // pre-packed, one per group (the instruction's operand lane by lane); plain, one per
+    // CR = 16/QG rows x QG*64 bytes (whole lines of each row), each row's 16-byte units
+    // XOR-swizzled by the row so the 16-row ds_read_b128 of one group is conflict-free.
+    // The source of copy c of block b is src[g][c] plus b blocks when FULL (a constant
+    // offset); otherwise each address is clamped to the last group on its own.
+    constexpr int UPR = QG * 4;                           // plain: 16-byte units per row
+    constexpr int CR = 16 / QG;                           // plain: rows per copy
+    constexpr int64_t BSTEP = PACKED ? QG * 1024 : QG * 64;   // bytes per block along a row
+    const uint8_t* src[RG][QG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+      for (int c = 0; c < QG; ++c) {
+        if constexpr (PACKED) {
+          src[g][c] = Bw + (rc(n0 / 16 + g, (int64_t)G16 - 1) * KT + ks0 + c) * 1024 + lane * 16;
+        } else {
+          const int row = c * CR + lane / UPR;
+          const int gu = (lane % UPR) ^ swz(row);        // global unit held by LDS unit lane % UPR
+          src[g][c] = Bw + rc(n0 + 16 * g + row, (int64_t)N - 1) * (K / 2) + (int64_t)ks0 * 64 + gu * 16;
+        }
+      }
+#pragma unroll
+    for (int b = 0; b < ST / QG; ++b) {
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+#pragma unroll
+        for (int c = 0; c < QG; ++c) {
+          const uint8_t* a = src[g][c] + b * BSTEP;
+          if constexpr (!FULL) {
+            const int grp = PACKED ? c : (((lane % UPR) ^ swz(c * CR + lane / UPR)) >> 2);   // group in block
+            const int ks = ks0 + QG * b + grp;
+            if (ks > KT - 1) a -= (int64_t)(ks - (KT - 1)) * (PACKED ? 1024 : 64);
+          }
+          lds_copy16_nt(a, (lds_void*)(wl + ((b * RG + g) * QG + c) * 1024));
+        }
+      }
+    }
+
+    const int unit = 0x7F7F7F7F;
+    // 0x80808080 in a vector register, so the sign part is one v_and_or_b32 (a VOP3
+    // instruction takes no literal and at most one scalar operand here).
+    uint32_t k80;
+    asm("v_mov_b32 %0, 0x80808080" : "=v"(k80));
+    // Nothing of the arithmetic below is scheduled among the copies: a token or scale
+    // use placed between them would force a wait for every copy issued before it.
+    __builtin_amdgcn_sched_barrier(0);
+    // Block b of row group g as soon as its QG copies have landed (copies are issued in
+    // (block, row group) order), so what is left after the last copy lands is one block of
+    // one row group.
+    static_for<0, ST / QG>([&](auto b_c) {
+      constexpr int b = decltype(b_c)::value;
+      v8i tv[QG];
+      static_for<0, RG>([&](auto g_c) {
+        constexpr int g = decltype(g_c)::value;
+        wait_vmcnt<RG * ST - QG * (b * RG + g + 1)>();
+        __builtin_amdgcn_sched_barrier(0);   // token and scale uses stay after the wait
+#pragma unroll
+        for (int j = 0; j < QG; ++j) {
+          const int s = QG * b + j;
+          const bool ok = FULL || ks0 + s < KT;
+          if (g == 0) {
+            // Token operand.  Both operands list the 8 K elements of each dword of weights
+            // as its even elements, then its odd ones (the nibble order of a plain byte, low
+            // then high); pre-packed weights are already in K order (element j | element
+            // j+4 << 4).
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const v4i& tq = w < 2 ? t0[s] : t1[s];
+              const uint32_t x0 = (uint32_t)tq[2 * (w & 1)], x1 = (uint32_t)tq[2 * (w & 1) + 1];
+              tv[j][2 * w] = (int)(PACKED ? x0 : __builtin_amdgcn_perm(x1, x0, 0x06040200u));
+              tv[j][2 * w + 1] = (int)(PACKED ? x1 : __builtin_amdgcn_perm(x1, x0, 0x07050301u));
+            }
+          }
+          v4i x;
+          v4f sc;
+          uint8_t* blk = wl + (b * RG + g) * QG * 1024;
+          if constexpr (PACKED) {
+            x = *reinterpret_cast<const v4i*>(blk + j * 1024 + lane * 16);
+            sc = *reinterpret_cast<const v4f*>(wl + SOFF + (g * ST + s) * 64 + slot * 16);
+          } else {
+            x = *reinterpret_cast<const v4i*>(blk + r * (UPR * 16) + (((4 * j + slot) ^ swz(r)) << 4));
+            if constexpr (SCL == kSclPairs) {
+              const v4i d = *reinterpret_cast<const v4i*>(wl + SOFF + ((s / 2) * 16 * RG + 16 * g + 4 * slot) * 4);
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                sc[t] = __builtin_bit_cast(float, (s & 1) ? (uint32_t)d[t] & 0xFFFF0000u : (uint32_t)d[t] << 16);
+            } else {
+#pragma unroll
+              for (int t = 0; t < 4; ++t) sc[t] = bf16_bits_to_f32(sh[g][t][s / 2][s & 1]);
+            }
+          }
+          // q = v - 8s per weight as two exact FP8 codes: the low 3 bits as they are (the
+          // subnormal code v, worth v * 2^-9) and 0x88 (-2^-6) where bit 3 is set, else
+          // 0x80 (-0); both instructions scale the weights by 2^9.  Four weights per dword
+          // in the low nibbles of x and four in those of x >> 4: two VALU operations per
+          // four weights, plus the shift.
+          v8i bv, bs;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = (uint32_t)x[w], hi = lo >> 4;
+            bv[2 * w] = (int)(lo & 0x07070707u);
+            bv[2 * w + 1] = (int)(hi & 0x07070707u);
+            bs[2 * w] = (int)((lo & 0x08080808u) | k80);
+            bs[2 * w + 1] = (int)((hi & 0x08080808u) | k80);
+          }
+          v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, tv[j], v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
+                                                                      kFmtFp8, 0, kScale2p9, 0, unit);
+          part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bs, tv[j], part, kFmtFp8, kFmtFp8, 0, kScale2p9, 0,
+                                                                 unit);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[g][t] = __builtin_fmaf(part[t], ok ? sc[t] : 0.0f, acc[g][t]);
+        }
+      });
+    });
+  };
+  if (ks0 + ST <= KT && n0 + 16 * RG <= N) segment(std::true_type{});
+  else if (ks0 < KT) segment(std::false_type{});
 
   // ---- sum the WAVES partial tiles in wave order, scale by sa[m], store D[m][n] ----
   __syncthreads();
@@ -231,27 +316,29 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
   }
 }
 
-template <int NJ, int RG, bool PACKED>
+template <int NJ, int RG, int QG, int SCL>
 hipError_t launch_cfg(const W4A8Args& a, const void* S, hipStream_t s) {
   const int64_t g64 = ceil_div(a.N, 16 * RG);
   if (g64 > INT32_MAX) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)g64, PACKED ? 1u : (unsigned)a.L), block(WAVES * 64);
+  const dim3 grid((unsigned)g64, SCL == kSclPacked ? 1u : (unsigned)a.L), block(WAVES * 64);
   if (a.bf16_out)
-    hipLaunchKernelGGL((w4a8_gemv_kernel<NJ, RG, PACKED, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
+    hipLaunchKernelGGL((w4a8_gemv_kernel<NJ, RG, QG, SCL, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
                        a.A, a.sa, a.B, S, a.D);
   else
-    hipLaunchKernelGGL((w4a8_gemv_kernel<NJ, RG, PACKED, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
+    hipLaunchKernelGGL((w4a8_gemv_kernel<NJ, RG, QG, SCL, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
                        a.A, a.sa, a.B, S, a.D);
   return hipGetLastError();
 }
 
-template <bool PACKED>
+template <int SCL>
 hipError_t launch_shape(const W4A8Args& a, const void* S, hipStream_t s) {
   const int64_t KT = a.K / 128;
   // Segment of ST = 4*NJ groups per wave, WAVES segments per row: K <= WAVES*ST*128.
-  if (KT <= WAVES * 4) return launch_cfg<1, 2, PACKED>(a, S, s);     // K <= 4096: 32 rows per workgroup
-  if (KT <= WAVES * 8) return launch_cfg<2, 1, PACKED>(a, S, s);     // K <= 8192
-  return launch_cfg<4, 1, PACKED>(a, S, s);                          // K <= 16384
+  // Blocks of two groups: 8 rows x 128 bytes per plain copy.  (Blocks of 4 or 8 groups,
+  // 4 rows x 256 or 2 rows x 512 bytes per copy, measured no faster with cold weights.)
+  if (KT <= WAVES * 4) return launch_cfg<1, 2, 2, SCL>(a, S, s);     // K <= 4096: 32 rows per workgroup
+  if (KT <= WAVES * 8) return launch_cfg<2, 2, 2, SCL>(a, S, s);     // K <= 8192: 32 rows
+  return launch_cfg<4, 1, 2, SCL>(a, S, s);                          // K <= 16384: 16 rows
 }
 
 }  // namespace
@@ -260,7 +347,10 @@ bool w4a8_gemv_fits(int64_t M, int64_t K) { return M >= 1 && M <= 16 && K >= 128
 
 hipError_t launch_w4a8_gemv(const W4A8Args& a, const float* Sp, hipStream_t s) {
   if (!w4a8_gemv_fits(a.M, a.K) || a.K % 128 != 0) return hipErrorInvalidValue;
-  return Sp ? launch_shape<true>(a, Sp, s) : launch_shape<false>(a, a.sB, s);
+  if (Sp) return launch_shape<kSclPacked>(a, Sp, s);
+  // bf16 scale rows are dword aligned when K/128 is even (the C ABI aligns sB to 4 bytes)
+  if ((a.K / 128) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.sB) & 3) == 0) return launch_shape<kSclPairs>(a, a.sB, s);
+  return launch_shape<kSclSingle>(a, a.sB, s);
 }
 
 }  // namespace fp4g

@@ -4,8 +4,9 @@ w4a8_gemm, w4a8_gemm_batched and w4a8_gemm_prepacked run the 16-token decode ker
 
 Bar: the oracle module's parity rule, fp32 |D - D_exact| <= 1e-5 * S (bf16: plus one
 bf16 ulp) on the workload's activation distribution, and 1e-5 * S + H, H the FP8
-instruction's truncation bound for the two exact weight parts (split), on activations
-spread over every binade.  Shapes cover each segment configuration of the kernel
+instruction's truncation bound for the decode kernel's two exact weight parts (split=2:
+the subnormal code v * 2^-9 and the sign part), on activations spread over every
+binade.  Shapes cover each segment configuration of the kernel
 (K <= 4096, <= 8192, <= 16384), ragged K (groups past K inside a wave's segment),
 ragged N (row groups past N), and the boundaries to the 64-token kernel (M = 17,
 K = 16512).
@@ -97,14 +98,15 @@ def test_boundaries_to_the_gemm_kernel(MK):
 @pytest.mark.parametrize("K", [1024, 6016])
 def test_decode_activations_over_every_binade(K, out):
     """Activation codes spread over all binades inside every run of 8: the instruction
-    truncates, and the decode kernel (two exact weight parts) stays within 1e-5 S + H."""
+    truncates, and the decode kernel (two exact weight parts, v as a subnormal code)
+    stays within 1e-5 S + H."""
     M, N = 16, 96
     rng = np.random.default_rng(K + (out == "bf16"))
     d = datagen.make_shape("w4a8", M, N, K, seed=K + 1)
     d["A"] = rng.choice(np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8), (M, K))
     print(f"case w4a8 decode wide activations {M}x{N}x{K} {out}", flush=True)
     ref, S = oracle.run("w4a8", d)
-    H = oracle.fp8_truncation_bound("w4a8", d, split=True)
+    H = oracle.fp8_truncation_bound("w4a8", d, split=2)
     assert (H > 1e-5 * S).any()               # the regime where the bound matters
     check(d, out, extra=H)
 
@@ -161,3 +163,4 @@ def test_decode_is_run_to_run_identical():
     D2 = fp4.w4a8_gemm(t["A"], t["sa"], t["B"], t["sB"], out_dtype=torch.float32)
     torch.cuda.synchronize(DEV)
     assert torch.equal(D1, D2)
+
