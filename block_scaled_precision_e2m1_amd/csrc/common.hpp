@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fp4g {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -152,6 +154,15 @@ template <int OPSEL>
 __device__ __forceinline__ v4f mfma_fp4_16x16(v4i a, v4i b, v4f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(a), widen(b), c, kFmtFp4, kFmtFp4,
                                                           OPSEL, sa, OPSEL, sb);
+}
+
+// Calls f(integral_constant<int, I>) for I = B .. E-1 (each a compile-time constant).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Integer helpers.

@@ -61,6 +61,9 @@ hipError_t launch_mxfp4_gemm_batched(const FP4Args& a, int64_t L, int64_t S, flo
 // choice for the current device; at most `cap`, kMaxSplits and the K stage count.
 int64_t mxfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t requested, int64_t cap);
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s);
+// NVFP4 decode GEMV for 1 <= M <= 16 tokens and K <= 16384 (nvfp4_gemv_fits); batch a.L.
+bool nvfp4_gemv_fits(int64_t M, int64_t K);
+hipError_t launch_nvfp4_gemv(const FP4Args& a, hipStream_t s);
 hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s);
 // Pre-packed decode weights: sizes, the load-time re-pack, and the GEMV over them
 // (a.B is the packed weight buffer; Sp the packed scale dwords).

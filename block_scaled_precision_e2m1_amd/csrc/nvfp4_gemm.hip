@@ -26,6 +26,7 @@
 
 #include "common.hpp"
 #include "internal.h"
+#include "nv_fold.hpp"
 
 namespace fp4g {
 namespace {
@@ -39,29 +40,6 @@ constexpr int kRowH = kBK * 2;     // 256 bytes of fp16 per LDS row: 16 chunks o
 // that one MFMA fragment read touches at one logical chunk, and the 4 rows x 4 chunks
 // that 16 consecutive threads of the fold write, all land in distinct bank groups.
 __device__ __forceinline__ int swz16(int r) { return r & 15; }
-
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-
-// An E4M3 scale byte as the two factors of the fold: `pow2` (fp32; only its power
-// of two is used by the conversion) and `mant` = (m, m) in fp16 with the scale's
-// sign.  A NaN code (0x7F / 0xFF) gives mant = NaN, so the block's products are NaN.
-__device__ __forceinline__ void e4m3_split(uint32_t b, float* pow2, h2* mant) {
-  const float s = __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
-  const uint32_t u = __builtin_bit_cast(uint32_t, s);
-  uint32_t m16 = 0x3C00u | ((u >> 13) & 0x3FFu) | ((u >> 16) & 0x8000u);
-  if ((b & 0x7Fu) == 0x7Fu) m16 = 0x7E00u;
-  *pow2 = s;
-  *mant = __builtin_bit_cast(h2, m16 | (m16 << 16));
-}
-
-// 4 packed bytes (8 E2M1 codes) times one E4M3 scale -> 8 fp16 in 4 dwords.
-__device__ __forceinline__ void fold8(uint32_t w, float pow2, h2 mant, uint32_t* out) {
-  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 0) * mant);
-  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 1) * mant);
-  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 2) * mant);
-  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 3) * mant);
-}
 
 template <int BM, int BN, int WM, int WN, bool BF16>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
@@ -229,6 +207,7 @@ void split_global_scale(float global_a, float global_b, float* m, int* e) {
 }
 
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s) {
+  if (nvfp4_gemv_fits(a.M, a.K)) return launch_nvfp4_gemv(a, s);         // decode: a 16-token tile
   if (a.L * ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256) return launch_cfg<128, 128, 64, 64>(a, s);
   // Small problems: 64 x 64 tiles with 8 waves of 16 x 32, so each SIMD interleaves two
   // waves' folds, LDS traffic and MFMAs (1024^3: 7.1 us, against 8.3 us with 4 waves of

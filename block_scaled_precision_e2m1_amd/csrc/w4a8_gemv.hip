@@ -57,15 +57,6 @@ constexpr int kScale2p9 = 0x88888888;          // E8M0 136 = 2^9 in every byte
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t u16) { return __builtin_bit_cast(float, u16 << 16); }
 
-// Calls f(integral_constant<int, I>) for I = B .. E-1 (each a compile-time constant).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
 // SCL selects how the group scales arrive: kSclPacked, fp32 Sp of the pre-packed layout
@@ -231,8 +222,9 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
       v8i tv[QG];
       static_for<0, RG>([&](auto g_c) {
         constexpr int g = decltype(g_c)::value;
-        wait_vmcnt<RG * ST - QG * (b * RG + g + 1)>();
         __builtin_amdgcn_sched_barrier(0);   // token and scale uses stay after the wait
+        wait_vmcnt<RG * ST - QG * (b * RG + g + 1)>();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < QG; ++j) {
           const int s = QG * b + j;
