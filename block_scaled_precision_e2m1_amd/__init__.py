@@ -28,6 +28,8 @@ __all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_batched_noalloc", 
            "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked",
            "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3", "w4a8_gemm_prepacked",
            "nv_fp4_gemm_batched", "w4a8_gemm_batched", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "nv_fp4_quantize",
+           "nv_fp4_gemm_split", "w4a8_gemm_split", "w4a8_gemm_prepacked_split",
+           "nv_fp4_gemm_workspace_size", "w4a8_gemm_workspace_size",
            "fp8_blockwise_gemm", "fp4g_status_string",
            "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
 
@@ -38,7 +40,9 @@ SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_batched_noalloc", 
            "nv_fp4_gemm_batched", "w4a8_gemm", "w4a8_gemm_batched", "fp4_gemv",
            "fp4_gemv_prepack_size", "fp4_gemv_prepack", "fp4_gemv_prepacked",
            "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3", "w4a8_gemm_prepacked",
-           "mx_fp4_quantize", "nv_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string")
+           "mx_fp4_quantize", "nv_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string",
+           "nv_fp4_gemm_workspace_size", "w4a8_gemm_workspace_size", "nv_fp4_gemm_split", "w4a8_gemm_split",
+           "w4a8_gemm_prepacked_split")
 
 OUT_F32, OUT_BF16 = 0, 1
 IN_F32, IN_BF16 = 0, 1
@@ -92,6 +96,14 @@ def load_library():
     lib.nv_fp4_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, f, p, p, f, p, c_int, p]
     lib.nv_fp4_gemm_batched.restype = c_int
     lib.w4a8_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, p, p, p, c_int, p]
+    lib.nv_fp4_gemm_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.w4a8_gemm_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.nv_fp4_gemm_split.argtypes = [i64, i64, i64, i64, p, p, f, p, p, f, p, c_int, i64, p, ctypes.c_size_t, p]
+    lib.w4a8_gemm_split.argtypes = [i64, i64, i64, i64, p, p, p, p, p, c_int, i64, p, ctypes.c_size_t, p]
+    lib.w4a8_gemm_prepacked_split.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, i64, p, ctypes.c_size_t, p]
+    for name in ("nv_fp4_gemm_workspace_size", "w4a8_gemm_workspace_size", "nv_fp4_gemm_split", "w4a8_gemm_split",
+                 "w4a8_gemm_prepacked_split"):
+        getattr(lib, name).restype = c_int
     lib.w4a8_gemm_batched.restype = c_int
     lib.fp4_gemv.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.fp4_gemv.restype = c_int
@@ -467,6 +479,101 @@ def w4a8_gemm_batched(A, sa, B, sB, out=None, out_dtype=torch.bfloat16):
     dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
     st = lib.w4a8_gemm_batched(L, M, N, K, _ptr(A), _ptr(sa), _ptr(B), _ptr(sB), _ptr(D), dt, _stream(device))
     _raise_on("w4a8_gemm_batched", st)
+    return D
+
+
+def nv_fp4_gemm_workspace_size(L, M, N, K, splits=0) -> int:
+    """Bytes of workspace nv_fp4_gemm_split uses for these sizes on the current device."""
+    n = ctypes.c_size_t(0)
+    _raise_on("nv_fp4_gemm_workspace_size", load_library().nv_fp4_gemm_workspace_size(L, M, N, K, splits, ctypes.byref(n)))
+    return int(n.value)
+
+
+def w4a8_gemm_workspace_size(L, M, N, K, splits=0) -> int:
+    """Bytes of workspace w4a8_gemm_split (or, with L = 1, w4a8_gemm_prepacked_split) uses."""
+    n = ctypes.c_size_t(0)
+    _raise_on("w4a8_gemm_workspace_size", load_library().w4a8_gemm_workspace_size(L, M, N, K, splits, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(workspace, nbytes, device):
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _check(workspace, "workspace", torch.uint8, (workspace.numel(),), device)
+    return workspace
+
+
+def nv_fp4_gemm_split(A, sfA, global_a, B, sfB, global_b, out=None, out_dtype=torch.bfloat16, splits=0,
+                      workspace=None):
+    """nv_fp4_gemm_batched with a K split: `splits` = 0 lets the library choose, 1 never
+    splits, s > 1 asks for at most s slices.  `workspace` is a uint8 device tensor for the
+    partial products; None allocates the size the library asks for."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 3 or B.dim() != 3:
+        raise ValueError("A and B must be 3-D [L, rows, K/2]")
+    L, M, K = A.shape[0], A.shape[1], A.shape[2] * 2
+    N = B.shape[1]
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(A, "A", torch.uint8, (L, M, K // 2), device)
+    _check(sfA, "sfA", torch.uint8, (L, M, K // 16), device)
+    _check(B, "B", torch.uint8, (L, N, K // 2), device)
+    _check(sfB, "sfB", torch.uint8, (L, N, K // 16), device)
+    D = _batched_out(out, L, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    ws = _workspace(workspace, nv_fp4_gemm_workspace_size(L, M, N, K, splits) if workspace is None else 0, device)
+    st = lib.nv_fp4_gemm_split(L, M, N, K, _ptr(A), _ptr(sfA), float(global_a), _ptr(B), _ptr(sfB), float(global_b),
+                               _ptr(D), dt, splits, _ptr(ws), ws.numel(), _stream(device))
+    _raise_on("nv_fp4_gemm_split", st)
+    return D
+
+
+def w4a8_gemm_split(A, sa, B, sB, out=None, out_dtype=torch.bfloat16, splits=0, workspace=None):
+    """w4a8_gemm_batched with a K split (plain weights split only when K % 256 == 0);
+    `splits` and `workspace` as for nv_fp4_gemm_split."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 3 or B.dim() != 3:
+        raise ValueError("A and B must be 3-D")
+    L, M, K = A.shape
+    N = B.shape[1]
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(A, "A", torch.uint8, (L, M, K), device)
+    _check(sa, "sa", torch.float32, (L, M), device)
+    _check(B, "B", torch.uint8, (L, N, K // 2), device)
+    _check(sB, "sB", torch.bfloat16, (L, N, K // 128), device)
+    D = _batched_out(out, L, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    ws = _workspace(workspace, w4a8_gemm_workspace_size(L, M, N, K, splits) if workspace is None else 0, device)
+    st = lib.w4a8_gemm_split(L, M, N, K, _ptr(A), _ptr(sa), _ptr(B), _ptr(sB), _ptr(D), dt, splits, _ptr(ws),
+                             ws.numel(), _stream(device))
+    _raise_on("w4a8_gemm_split", st)
+    return D
+
+
+def w4a8_gemm_prepacked_split(A, sa, Bp, Sp, N, out=None, out_dtype=torch.bfloat16, splits=0, workspace=None):
+    """w4a8_gemm_prepacked with a K split; `splits` and `workspace` as for
+    nv_fp4_gemm_split."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 2:
+        raise ValueError("A must be 2-D")
+    M, K = A.shape
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(A, "A", torch.uint8, (M, K), device)
+    _check(sa, "sa", torch.float32, (M,), device)
+    wb, sb = w4a8_prepack_size(N, K)
+    _check(Bp, "Bp", torch.uint8, (wb,), device)
+    _check(Sp, "Sp", torch.float32, (sb // 4,), device)
+    D = _out(out, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    ws = _workspace(workspace, w4a8_gemm_workspace_size(1, M, N, K, splits) if workspace is None else 0, device)
+    st = lib.w4a8_gemm_prepacked_split(M, N, K, _ptr(A), _ptr(sa), _ptr(Bp), _ptr(Sp), _ptr(D), dt, splits,
+                                       _ptr(ws), ws.numel(), _stream(device))
+    _raise_on("w4a8_gemm_prepacked_split", st)
     return D
 
 

@@ -94,6 +94,43 @@ fp4g_status check_batched_sizes(int64_t L, int64_t M, int64_t N, int64_t K, int6
   return FP4G_OK;
 }
 
+
+// The K split of a call: `requested` (0 automatic, 1 none, s > 1 at most s) limited to
+// what `workspace_bytes` holds at per_split bytes a slice; the workspace is checked
+// against the output and the inputs.  *S = 1 when nothing is split.
+struct SplitCtx { int64_t L, M, N, K, requested; int kind; };   // kind 0 W4A8 plain, 1 W4A8 pre-packed, 2 NVFP4
+
+int64_t choose_split(const SplitCtx& c, int64_t cap) {
+  if (c.kind == 2) return fp4g::nvfp4_gemm_splits(c.L, c.M, c.N, c.K, c.requested, cap);
+  return fp4g::w4a8_gemm_splits(c.L, c.M, c.N, c.K, c.kind == 1, c.requested, cap);
+}
+
+fp4g_status split_of(const SplitCtx& c, int64_t per_split, void* workspace, size_t workspace_bytes, const Range& d,
+                     const Range* ins, int n_ins, int64_t* S) {
+  *S = 1;
+  if (c.requested == 1 || workspace_bytes == 0 || per_split == 0) return FP4G_OK;
+  if (!aligned(workspace, 16)) return FP4G_EALIGN;
+  const Range w = range_of(workspace, (int64_t)workspace_bytes);
+  if (overlaps(w, d)) return FP4G_EINVAL;
+  for (int i = 0; i < n_ins; ++i)
+    if (overlaps(w, ins[i])) return FP4G_EINVAL;
+  *S = choose_split(c, (int64_t)(workspace_bytes / (size_t)per_split));
+  return FP4G_OK;
+}
+
+fp4g_status split_workspace_size(int kind, int64_t L, int64_t M, int64_t N, int64_t K, int64_t splits,
+                                 size_t* bytes) {
+  bool empty = false;
+  const fp4g_status st = check_batched_sizes(L, M, N, K, splits, &empty);
+  if (st != FP4G_OK) return st;
+  if (!bytes) return FP4G_EINVAL;
+  *bytes = 0;
+  if (empty || K == 0 || splits == 1) return FP4G_OK;
+  const int64_t S = choose_split(SplitCtx{L, M, N, K, splits, kind}, fp4g::kMaxSplits);
+  if (S > 1) *bytes = (size_t)(L * S * M * N * 4);
+  return FP4G_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -466,6 +503,108 @@ const char* fp4g_status_string(int status) {
     case FP4G_EHIP: return "HIP runtime error at kernel launch";
     default: return "unknown status";
   }
+}
+
+fp4g_status w4a8_gemm_workspace_size(int64_t L, int64_t M, int64_t N, int64_t K, int64_t splits, size_t* bytes) {
+  // the larger of the two weight forms' needs (pre-packed weights also split K % 256 != 0)
+  return split_workspace_size(1, L, M, N, K, splits, bytes);
+}
+
+fp4g_status nv_fp4_gemm_workspace_size(int64_t L, int64_t M, int64_t N, int64_t K, int64_t splits, size_t* bytes) {
+  return split_workspace_size(2, L, M, N, K, splits, bytes);
+}
+
+fp4g_status w4a8_gemm_split(int64_t L, int64_t M, int64_t N, int64_t K, const void* A, const float* sa,
+                            const void* B, const void* sB, void* D, int d_type, int64_t splits, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_batched_sizes(L, M, N, K, splits, &empty);
+  if (st != FP4G_OK) return st;
+  if (d_type != FP4G_OUT_F32 && d_type != FP4G_OUT_BF16) return FP4G_EINVAL;
+  if (L > kMaxGridY) return FP4G_EUNSUPPORTED;
+  if (!workspace && workspace_bytes > 0) return FP4G_EINVAL;
+  if (empty) return FP4G_OK;
+  if (!D) return FP4G_EINVAL;
+  if (!aligned(D, 16)) return FP4G_EALIGN;
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, L * M * N, bf16, s));
+  if (!A || !sa || !B || !sB) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16)) return FP4G_EALIGN;
+  if (!aligned(sa, 4) || !aligned(sB, 4)) return FP4G_EALIGN;
+  const Range d = range_of(D, L * M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, L * M * K), range_of(sa, L * M * 4), range_of(B, L * N * (K / 2)),
+                        range_of(sB, L * N * (K / 128) * 2)};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  int64_t S = 1;
+  st = split_of(SplitCtx{L, M, N, K, splits, 0}, L * M * N * 4, workspace, workspace_bytes, d, ins, 4, &S);
+  if (st != FP4G_OK) return st;
+  W4A8Args a{M, N, K, static_cast<const uint8_t*>(A), sa, static_cast<const uint8_t*>(B),
+             static_cast<const uint16_t*>(sB), D, bf16, L};
+  if (S > 1) return finish(fp4g::launch_w4a8_gemm_split(a, nullptr, S, static_cast<float*>(workspace), s));
+  return finish(fp4g::launch_w4a8_gemm(a, s));
+}
+
+fp4g_status w4a8_gemm_prepacked_split(int64_t M, int64_t N, int64_t K, const void* A, const float* sa,
+                                      const void* Bp, const void* Sp, void* D, int d_type, int64_t splits,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_common(M, N, K, d_type, D, &empty);
+  if (st != FP4G_OK) return st;
+  if (splits < 0) return FP4G_EINVAL;
+  if (!workspace && workspace_bytes > 0) return FP4G_EINVAL;
+  if (empty) return FP4G_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, M * N, bf16, s));
+  if (!A || !sa || !Bp || !Sp) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(Bp, 16)) return FP4G_EALIGN;
+  if (!aligned(sa, 4) || !aligned(Sp, 4)) return FP4G_EALIGN;
+  int64_t wb = 0, sb = 0;
+  fp4g::w4a8_prepack_sizes(N, K, &wb, &sb);
+  const Range d = range_of(D, M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, M * K), range_of(sa, M * 4), range_of(Bp, wb), range_of(Sp, sb)};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  int64_t S = 1;
+  st = split_of(SplitCtx{1, M, N, K, splits, 1}, M * N * 4, workspace, workspace_bytes, d, ins, 4, &S);
+  if (st != FP4G_OK) return st;
+  W4A8Args a{M, N, K, static_cast<const uint8_t*>(A), sa, static_cast<const uint8_t*>(Bp), nullptr, D, bf16};
+  return finish(fp4g::launch_w4a8_gemm_split(a, static_cast<const float*>(Sp), S,
+                                             S > 1 ? static_cast<float*>(workspace) : nullptr, s));
+}
+
+fp4g_status nv_fp4_gemm_split(int64_t L, int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,
+                              float global_a, const void* B, const void* sfB, float global_b, void* D, int d_type,
+                              int64_t splits, void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_batched_sizes(L, M, N, K, splits, &empty);
+  if (st != FP4G_OK) return st;
+  if (d_type != FP4G_OUT_F32 && d_type != FP4G_OUT_BF16) return FP4G_EINVAL;
+  if (L > kMaxGridY) return FP4G_EUNSUPPORTED;
+  if (!workspace && workspace_bytes > 0) return FP4G_EINVAL;
+  if (empty) return FP4G_OK;
+  if (!D) return FP4G_EINVAL;
+  if (!aligned(D, 16)) return FP4G_EALIGN;
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, L * M * N, bf16, s));
+  if (!A || !sfA || !B || !sfB) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16)) return FP4G_EALIGN;
+  if (!aligned(sfA, 4) || !aligned(sfB, 4)) return FP4G_EALIGN;
+  const Range d = range_of(D, L * M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, L * M * (K / 2)), range_of(sfA, L * M * (K / 16)),
+                        range_of(B, L * N * (K / 2)), range_of(sfB, L * N * (K / 16))};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  int64_t S = 1;
+  st = split_of(SplitCtx{L, M, N, K, splits, 2}, L * M * N * 4, workspace, workspace_bytes, d, ins, 4, &S);
+  if (st != FP4G_OK) return st;
+  FP4Args a{M, N, K, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(sfA),
+            static_cast<const uint8_t*>(B), static_cast<const uint8_t*>(sfB), 1.0f, D, bf16, L};
+  fp4g::split_global_scale(global_a, global_b, &a.gscale, &a.gscale_exp);
+  return finish(fp4g::launch_nvfp4_gemm_split(a, S, S > 1 ? static_cast<float*>(workspace) : nullptr, s));
 }
 
 }  // extern "C"

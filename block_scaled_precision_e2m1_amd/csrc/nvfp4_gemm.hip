@@ -41,9 +41,12 @@ constexpr int kRowH = kBK * 2;     // 256 bytes of fp16 per LDS row: 16 chunks o
 // that 16 consecutive threads of the fold write, all land in distinct bank groups.
 __device__ __forceinline__ int swz16(int r) { return r & 15; }
 
-template <int BM, int BN, int WM, int WN, bool BF16>
+// SPLIT: the K steps are cut into S slices of KS steps (the last one shorter); work item
+// = tile * S + slice, and the slice's fp32 partial product (without the global scales)
+// goes to D = P[L][S][M][N] for launch_scaled_reduce.
+template <int BM, int BN, int WM, int WN, bool SPLIT, bool BF16>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
+nvfp4_gemm_kernel(int M, int N, int K, int S, int KS, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
                   const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, float gscale, int gexp,
                   void* __restrict__ D) {
   constexpr int NWN = BN / WN;
@@ -63,12 +66,16 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
     sfA += b * M * (K / 16);
     B += b * N * (K / 2);
     sfB += b * N * (K / 16);
-    D = static_cast<uint8_t*>(D) + b * M * N * (BF16 ? 2 : 4);
+    D = static_cast<uint8_t*>(D) + b * (SPLIT ? S : 1) * M * N * (SPLIT ? 4 : (BF16 ? 2 : 4));
   }
   const int tiles_n = (N + BN - 1) / BN;
-  const int m0 = (int)(blockIdx.x / tiles_n) * BM, n0 = (int)(blockIdx.x % tiles_n) * BN;
+  const int item = (int)blockIdx.x;
+  const int tile = SPLIT ? item / S : item, slice = SPLIT ? item % S : 0;
+  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
   const int64_t ld = K / 2, lds_ = K / 16;
-  const int KT = K / kBK;
+  const int k0 = SPLIT ? slice * KS : 0;           // this item's steps: k0 .. k0 + KT - 1
+  const int KT = SPLIT ? min(KS, K / kBK - k0) : K / kBK;
+  if constexpr (SPLIT) D = static_cast<float*>(D) + (int64_t)slice * M * N;
 
   // Thread chunk q: packed row (A rows first, then B rows), quarter c of its 64 bytes
   // (32 elements, two scales).
@@ -79,8 +86,8 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
     const int q = min(tid + i * NT, CHUNKS - 1), row = q >> 2, c = q & 3;
     const bool isA = row < BM;
     const int grow = isA ? min(m0 + row, M - 1) : min(n0 + row - BM, N - 1);
-    gsrc[i] = (isA ? A : B) + (int64_t)grow * ld + c * 16;
-    gscl[i] = (isA ? sfA : sfB) + (int64_t)grow * lds_ + c * 2;
+    gsrc[i] = (isA ? A : B) + (int64_t)grow * ld + (int64_t)k0 * 64 + c * 16;
+    gscl[i] = (isA ? sfA : sfB) + (int64_t)grow * lds_ + k0 * 8 + c * 2;
   }
 
   // Packed tiles are prefetched two steps ahead into two register buffers (RB = the
@@ -177,25 +184,39 @@ nvfp4_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int m = m0 + wm * WM + i * 16 + 4 * slot + t;
-        if (m < M && n < N) store_out<BF16>(D, (int64_t)m * N + n, __builtin_ldexpf(acc[i][j][t] * gscale, gexp));
+        if (m < M && n < N) {
+          if constexpr (SPLIT) store_out<false>(D, (int64_t)m * N + n, acc[i][j][t]);
+          else store_out<BF16>(D, (int64_t)m * N + n, __builtin_ldexpf(acc[i][j][t] * gscale, gexp));
+        }
       }
     }
 }
 
 template <int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
+hipError_t launch_cfg(const FP4Args& a, int64_t S, float* P, hipStream_t s) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  const int64_t tiles = ceil_div(a.N, BN) * ceil_div(a.M, BM);
-  if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)tiles, (unsigned)a.L);
+  const int64_t KT = a.K / kBK, KS = ceil_div(KT, S);
+  const int64_t items = ceil_div(a.N, BN) * ceil_div(a.M, BM) * S;
+  if (items > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)items, (unsigned)a.L);
+  if (S > 1) {
+    hipLaunchKernelGGL((nvfp4_gemm_kernel<BM, BN, WM, WN, true, false>), grid, dim3(NT), 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, (int)S, (int)KS, a.A, a.sfA, a.B, a.sfB, a.gscale, a.gscale_exp, P);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_scaled_reduce(a.L, a.M, a.N, (int)S, P, nullptr, a.gscale, a.gscale_exp, a.D, a.bf16_out, s);
+  }
   if (a.bf16_out)
-    hipLaunchKernelGGL((nvfp4_gemm_kernel<BM, BN, WM, WN, true>), grid, dim3(NT), 0, s, (int)a.M,
-                       (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.gscale, a.gscale_exp, a.D);
+    hipLaunchKernelGGL((nvfp4_gemm_kernel<BM, BN, WM, WN, false, true>), grid, dim3(NT), 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, 1, (int)KT, a.A, a.sfA, a.B, a.sfB, a.gscale, a.gscale_exp, a.D);
   else
-    hipLaunchKernelGGL((nvfp4_gemm_kernel<BM, BN, WM, WN, false>), grid, dim3(NT), 0, s, (int)a.M,
-                       (int)a.N, (int)a.K, a.A, a.sfA, a.B, a.sfB, a.gscale, a.gscale_exp, a.D);
+    hipLaunchKernelGGL((nvfp4_gemm_kernel<BM, BN, WM, WN, false, false>), grid, dim3(NT), 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, 1, (int)KT, a.A, a.sfA, a.B, a.sfB, a.gscale, a.gscale_exp, a.D);
   return hipGetLastError();
 }
+
+// The tile configuration for L problems of M x N (both paths take it).
+bool nv_big_tiles(int64_t L, int64_t M, int64_t N) { return L * ceil_div(M, 128) * ceil_div(N, 128) >= 256; }
 
 }  // namespace
 
@@ -206,13 +227,45 @@ void split_global_scale(float global_a, float global_b, float* m, int* e) {
   *e = ea + eb;
 }
 
-hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s) {
+hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s) { return launch_nvfp4_gemm_split(a, 1, nullptr, s); }
+
+int64_t nvfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t requested, int64_t cap) {
+  const int64_t KT = K / kBK;
+  if (L * M * N == 0 || nvfp4_gemv_fits(M, K) || KT < 2) return 1;
+  int64_t smax = KT < kMaxSplits ? KT : kMaxSplits;
+  if (cap < smax) smax = cap;
+  if (smax < 2) return 1;
+  auto slices = [&](int64_t S) { return ceil_div(KT, ceil_div(KT, S)); };   // every slice non-empty
+  if (requested > 0) return slices(requested < smax ? requested : smax);
+  // Automatic choice: an item streams its K steps at about 0.6 us each plus about 2 us of
+  // fixed cost, two items share a CU; the partial products cost a write and a read of
+  // L*M*N fp32 per slice at about 4 TB/s.  Problems that fill the chip with 128 x 128
+  // tiles are not split; a slice keeps at least 4 steps.
+  if (nv_big_tiles(L, M, N)) return 1;
+  const int64_t cus = device_cus();
+  const int64_t items = L * ceil_div(M, 64) * ceil_div(N, 64);
+  int64_t best = 1;
+  double best_t = 0;
+  for (int64_t S = 1; S <= smax; ++S) {
+    const int64_t sl = slices(S), ks = ceil_div(KT, S);
+    if (S > 1 && ks < 4) break;
+    const double rounds = (double)ceil_div(items * sl, 2 * cus);
+    double t = rounds * ((double)ks * 0.6 + 2.0);
+    if (sl > 1) t += (double)(L * M * N) * 4.0 * (double)(2 * sl) / 4.0e6;
+    if (S == 1 || t < best_t) { best = sl; best_t = t; }
+  }
+  return best;
+}
+
+hipError_t launch_nvfp4_gemm_split(const FP4Args& a, int64_t splits, float* P, hipStream_t s) {
   if (nvfp4_gemv_fits(a.M, a.K)) return launch_nvfp4_gemv(a, s);         // decode: a 16-token tile
-  if (a.L * ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256) return launch_cfg<128, 128, 64, 64>(a, s);
+  if (splits > 1 && !P) return hipErrorInvalidValue;
+  const int64_t S = splits > 1 ? splits : 1;
+  if (nv_big_tiles(a.L, a.M, a.N)) return launch_cfg<128, 128, 64, 64>(a, S, P, s);
   // Small problems: 64 x 64 tiles with 8 waves of 16 x 32, so each SIMD interleaves two
   // waves' folds, LDS traffic and MFMAs (1024^3: 7.1 us, against 8.3 us with 4 waves of
   // 32 x 32, which read a third less from LDS but fold with half as many threads).
-  return launch_cfg<64, 64, 16, 32>(a, s);
+  return launch_cfg<64, 64, 16, 32>(a, S, P, s);
 }
 
 }  // namespace fp4g

@@ -127,9 +127,12 @@ w4a8_prepack_e4m3_scales_kernel(int64_t units, int N, int G, int64_t Np, const u
 // 16-byte units XOR-swizzled by row (conflict-free reads), the conversion first puts
 // the nibbles into K order with two byte permutes per 8 weights, and the scale copy fetches
 // the aligned dword holding groups g & ~1 and (g & ~1) + 1 of each row.
-template <int BM, bool PACKED, bool BF16>
+// SPLIT: the K groups are cut into S slices of GS groups (GS even, the last slice
+// shorter); work item = tile * S + slice, and the slice's fp32 partial product (without
+// sa) goes to D = P[L][S][M][N] for launch_scaled_reduce.
+template <int BM, bool PACKED, bool SPLIT, bool BF16>
 __global__ void __launch_bounds__(256, 2)
-w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sa,
+w4a8p_gemm_kernel(int M, int N, int K, int S, int GS, const uint8_t* __restrict__ A, const float* __restrict__ sa,
                   const uint8_t* __restrict__ Bw, const void* __restrict__ Sw, void* __restrict__ D) {
   using C = QCfg<BM>;
   constexpr int FI = C::FI;
@@ -143,17 +146,22 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
     sa += b * M;
     Bw += b * N * (K / 2);
     Sw = static_cast<const uint8_t*>(Sw) + b * N * (K / 128) * 2;
-    D = static_cast<uint8_t*>(D) + b * M * N * (BF16 ? 2 : 4);
+    D = static_cast<uint8_t*>(D) + b * (SPLIT ? S : 1) * M * N * (SPLIT ? 4 : (BF16 ? 2 : 4));
   }
 
   // Tile order: the token tiles of one weight panel are adjacent (they share it in
   // L2); consecutive ids go to the 8 XCDs in turn and are regrouped per XCD.
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + QBN - 1) / QBN;
-  const int T = tiles_m * tiles_n;
+  const int T = tiles_m * tiles_n * (SPLIT ? S : 1);
   int lin = blockIdx.x;
   if ((T & 7) == 0) lin = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  const int slice = SPLIT ? lin % S : 0;
+  if constexpr (SPLIT) lin /= S;
   const int m0 = (lin % tiles_m) * BM, n0 = (lin / tiles_m) * QBN;
-  const int G = K / 128;
+  const int GA = K / 128;                          // groups of the whole K (row pitches)
+  const int g0 = SPLIT ? slice * GS : 0;           // this item's groups: g0 .. g0 + G - 1
+  const int G = SPLIT ? min(GS, GA - g0) : GA;
+  if constexpr (SPLIT) D = static_cast<float*>(D) + (int64_t)slice * M * N;
   const int G16 = (N + 15) / 16;
   const int64_t Np = 16 * (int64_t)G16;
 
@@ -162,20 +170,24 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
 #pragma unroll
   for (int i = 0; i < C::IA; ++i) {
     const int row = 8 * (wave * C::IA + i) + (lane >> 3), u = lane & 7;
-    ga[i] = A + (int64_t)min(m0 + row, M - 1) * K + ((u ^ swz8(row)) << 4);
+    ga[i] = A + (int64_t)min(m0 + row, M - 1) * K + (int64_t)g0 * 128 + ((u ^ swz8(row)) << 4);
   }
   const uint8_t* gb;
+  // The scale copy: each wave copies the scales of its own 16 weight rows into its own
+  // 256-byte slot (lanes 0..15; lanes 16..63 repeat those addresses, which the copy
+  // fetches once, into the rest of the slot).
   const uint8_t* gs;                               // scale copy source (4 bytes per lane)
   int64_t gstep_b, gstep_s;                        // bytes per K group
+  const int srow = 16 * wave + (lane & 15);
   if constexpr (PACKED) {
-    gb = Bw + (int64_t)min(n0 / 16 + wave, G16 - 1) * G * 1024 + lane * 16;
-    gs = static_cast<const uint8_t*>(Sw) + min((int64_t)n0 + lane, Np - 1) * 4;
+    gb = Bw + ((int64_t)min(n0 / 16 + wave, G16 - 1) * GA + g0) * 1024 + lane * 16;
+    gs = static_cast<const uint8_t*>(Sw) + ((int64_t)g0 * Np + min((int64_t)n0 + srow, Np - 1)) * 4;
     gstep_b = 1024;
     gstep_s = Np * 4;
   } else {
     const int rr = lane >> 2, u = lane & 3;        // LDS unit u of row rr holds global unit u ^ f(rr)
-    gb = Bw + (int64_t)min(n0 + 16 * wave + rr, N - 1) * (K / 2) + ((u ^ ((rr >> 2) & 3)) << 4);
-    gs = static_cast<const uint8_t*>(Sw) + (int64_t)min(n0 + lane, N - 1) * G * 2;
+    gb = Bw + (int64_t)min(n0 + 16 * wave + rr, N - 1) * (K / 2) + (int64_t)g0 * 64 + ((u ^ ((rr >> 2) & 3)) << 4);
+    gs = static_cast<const uint8_t*>(Sw) + ((int64_t)min(n0 + srow, N - 1) * GA + g0) * 2;   // g0 even
     gstep_b = 64;
     gstep_s = 0;                                   // the group offset is added per copy
   }
@@ -186,9 +198,8 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
 #pragma unroll
     for (int i = 0; i < C::IA; ++i) lds_copy16(ga[i] + (int64_t)gc * 128, (lds_void*)(base + (wave * C::IA + i) * 1024));
     lds_copy16(gb + (int64_t)gc * gstep_b, (lds_void*)(base + C::B_OFF + wave * 1024));
-    // every wave copies the same bytes to the same place
-    if constexpr (PACKED) lds_copy4(gs + (int64_t)gc * gstep_s, (lds_void*)(base + C::S_OFF));
-    else lds_copy4(gs + (int64_t)(gc & ~1) * 2, (lds_void*)(base + C::S_OFF));
+    if constexpr (PACKED) lds_copy4(gs + (int64_t)gc * gstep_s, (lds_void*)(base + C::S_OFF + wave * 256));
+    else lds_copy4(gs + (int64_t)(gc & ~1) * 2, (lds_void*)(base + C::S_OFF + wave * 256));
   };
 
   v4f acc[FI];
@@ -220,11 +231,11 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
     // weight operand of this wave's 16 rows, and their scales (n = 16w + 4slot + t)
     if constexpr (PACKED) {
       f.x = *reinterpret_cast<const v4i*>(base + C::B_OFF + wave * 1024 + lane * 16);
-      f.s = *reinterpret_cast<const v4f*>(base + C::S_OFF + (wave * 16 + 4 * slot) * 4);
+      f.s = *reinterpret_cast<const v4f*>(base + C::S_OFF + wave * 256 + 16 * slot);
     } else {
       f.x = *reinterpret_cast<const v4i*>(base + C::B_OFF + wave * 1024 + r * 64 + ((slot ^ ((r >> 2) & 3)) << 4));
       // g is even in set 0 and odd in set 1: the low or high bf16 of each dword
-      const v4i d = *reinterpret_cast<const v4i*>(base + C::S_OFF + (wave * 16 + 4 * slot) * 4);
+      const v4i d = *reinterpret_cast<const v4i*>(base + C::S_OFF + wave * 256 + 16 * slot);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         f.s[t] = __builtin_bit_cast(float, SET == 0 ? (uint32_t)d[t] << 16 : (uint32_t)d[t] & 0xFFFF0000u);
@@ -298,23 +309,45 @@ w4a8p_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const floa
   for (int i = 0; i < FI; ++i) {
     const int m = m0 + 16 * i + r;
     if (m < M && n < N) {
-      const float s = sa[m];
-      store_out4<BF16>(D, (int64_t)m * N + n, N - n, acc[i][0] * s, acc[i][1] * s, acc[i][2] * s, acc[i][3] * s);
+      if constexpr (SPLIT) {
+        store_out4<false>(D, (int64_t)m * N + n, N - n, acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+      } else {
+        const float s = sa[m];
+        store_out4<BF16>(D, (int64_t)m * N + n, N - n, acc[i][0] * s, acc[i][1] * s, acc[i][2] * s, acc[i][3] * s);
+      }
     }
   }
 }
 
+// Groups per K slice for `splits` slices of G groups: an even count (the plain path
+// reads its bf16 scales as dwords of two groups), at least 2.
+int w4a8_slice_groups(int64_t G, int64_t splits) {
+  const int64_t gs = (ceil_div(G, splits) + 1) & ~(int64_t)1;
+  return (int)(gs < 2 ? 2 : gs);
+}
+
 template <int BM, bool PACKED>
-hipError_t launch_bm(const W4A8Args& a, const void* S, hipStream_t s) {
-  const int64_t tiles = ceil_div(a.M, BM) * ceil_div(a.N, QBN);
-  if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)tiles, PACKED ? 1u : (unsigned)a.L);
+hipError_t launch_bm(const W4A8Args& a, const void* S, int64_t splits, float* P, hipStream_t s) {
+  const int64_t G = a.K / 128;
+  const int GS = w4a8_slice_groups(G, splits);
+  const int64_t slices = splits > 1 ? ceil_div(G, GS) : 1;   // every slice non-empty
+  if (slices > (splits > 1 ? splits : 1)) return hipErrorInvalidValue;   // P holds `splits` slices
+  const int64_t items = ceil_div(a.M, BM) * ceil_div(a.N, QBN) * slices;
+  if (items > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)items, PACKED ? 1u : (unsigned)a.L);
+  if (slices > 1) {
+    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, true, false>), grid, dim3(256), 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, (int)slices, GS, a.A, a.sa, a.B, S, P);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_scaled_reduce(PACKED ? 1 : a.L, a.M, a.N, (int)slices, P, a.sa, 1.0f, 0, a.D, a.bf16_out, s);
+  }
   if (a.bf16_out)
-    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, true>), grid, dim3(256), 0, s, (int)a.M, (int)a.N, (int)a.K,
-                       a.A, a.sa, a.B, S, a.D);
+    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, false, true>), grid, dim3(256), 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, 1, (int)G, a.A, a.sa, a.B, S, a.D);
   else
-    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, false>), grid, dim3(256), 0, s, (int)a.M, (int)a.N, (int)a.K,
-                       a.A, a.sa, a.B, S, a.D);
+    hipLaunchKernelGGL((w4a8p_gemm_kernel<BM, PACKED, false, false>), grid, dim3(256), 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, 1, (int)G, a.A, a.sa, a.B, S, a.D);
   return hipGetLastError();
 }
 
@@ -357,12 +390,48 @@ hipError_t launch_w4a8_prepack_e4m3(int64_t N, int64_t K, const uint8_t* B, cons
 
 // a.B is the packed weight buffer; Sp the packed fp32 scales.
 hipError_t launch_w4a8_gemm_prepacked(const W4A8Args& a, const float* Sp, hipStream_t s) {
-  if (w4a8_gemv_fits(a.M, a.K)) return launch_w4a8_gemv(a, Sp, s);        // decode: a 16-token tile
-  // 64-token tiles: two workgroups share a CU (79 KB of LDS, at most 256 registers).
-  return launch_bm<64, true>(a, Sp, s);
+  return launch_w4a8_gemm_split(a, Sp, 1, nullptr, s);
 }
 
 // Plain weights and bf16 scales (K % 256 == 0, sB 4-byte aligned).
-hipError_t launch_w4a8_ring(const W4A8Args& a, hipStream_t s) { return launch_bm<64, false>(a, a.sB, s); }
+hipError_t launch_w4a8_ring(const W4A8Args& a, hipStream_t s) { return launch_bm<64, false>(a, a.sB, 1, nullptr, s); }
+
+int64_t w4a8_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, bool packed, int64_t requested, int64_t cap) {
+  const int64_t G = K / 128;
+  // Only the ring kernel splits: not the decode kernel (M <= 16 fills the chip by rows)
+  // and not the plain-weight kernel for K % 256 != 0.
+  if (L * M * N == 0 || w4a8_gemv_fits(M, K) || (!packed && K % 256 != 0) || G < 4) return 1;
+  int64_t smax = G / 2 < kMaxSplits ? G / 2 : kMaxSplits;
+  if (cap < smax) smax = cap;
+  if (smax < 2) return 1;
+  auto slices = [&](int64_t S) { return ceil_div(G, w4a8_slice_groups(G, S)); };
+  if (requested > 0) return slices(requested < smax ? requested : smax);
+  // Automatic choice: a 64 x 64 item is a chain of K groups at about 0.45 us each plus
+  // about 3.5 us of fixed cost, two items share a CU; the partial products cost a write
+  // and a read of L*M*N fp32 per slice at about 4 TB/s.  The cheapest S wins; a slice
+  // keeps at least 4 groups.
+  const int64_t cus = device_cus();
+  const int64_t items = (packed ? 1 : L) * ceil_div(M, 64) * ceil_div(N, 64);
+  int64_t best = 1;
+  double best_t = 0;
+  for (int64_t S = 1; S <= smax; ++S) {
+    const int64_t sl = slices(S);
+    const int64_t gs = S == 1 ? G : w4a8_slice_groups(G, S);
+    if (S > 1 && gs < 4) break;
+    const double rounds = (double)ceil_div(items * sl, 2 * cus);
+    double t = rounds * ((double)gs * 0.45 + 3.5);
+    if (sl > 1) t += (double)(L * M * N) * 4.0 * (double)(2 * sl) / 4.0e6;
+    if (S == 1 || t < best_t) { best = sl; best_t = t; }
+  }
+  return best;
+}
+
+hipError_t launch_w4a8_gemm_split(const W4A8Args& a, const float* Sp, int64_t splits, float* P, hipStream_t s) {
+  if (w4a8_gemv_fits(a.M, a.K)) return launch_w4a8_gemv(a, Sp, s);       // decode: a 16-token tile
+  if (splits > 1 && !P) return hipErrorInvalidValue;
+  // 64-token tiles: two workgroups share a CU (79 KB of LDS, at most 256 registers).
+  if (Sp) return launch_bm<64, true>(a, Sp, splits, P, s);
+  return launch_bm<64, false>(a, a.sB, splits, P, s);
+}
 
 }  // namespace fp4g

@@ -263,6 +263,50 @@ fp4g_status w4a8_gemm_batched(int64_t L, int64_t M, int64_t N, int64_t K,
                               const void *B, const void *sB,
                               void *D, int d_type, void *stream);
 
+/* K split for the NVFP4 and W4A8 GEMMs.  A problem with too few output tiles to fill the
+ * GPU (a skinny M, a small batch) can split its K groups into S slices of consecutive
+ * groups: the plain, fixed form of dividing K among workgroups, which the stream-K tile
+ * scheduler of one variant of the running example in the Hopper CUTLASS/CuTe DSL blog
+ * post does adaptively (its introduction); each slice writes an fp32 partial product
+ * into the caller's workspace, and a second kernel sums the slices in slice order and
+ * applies the per-token scales (W4A8) or global scales (NVFP4) as the unsplit epilogue
+ * does.  Results meet the same accuracy bar as the unsplit calls.
+ *
+ * nv_fp4_gemm_split: nv_fp4_gemm_batched (same layouts, sizes and result) with a split.
+ * w4a8_gemm_split: w4a8_gemm_batched (same layouts, sizes and result) with a split;
+ *   plain weights split only when K % 256 == 0.
+ * w4a8_gemm_prepacked_split: w4a8_gemm_prepacked (same layouts and result) with a split.
+ * `splits`: 0 lets the library choose (no split when the tiles already fill the GPU), 1
+ *   never splits, s > 1 asks for at most s slices; a slice keeps at least 2 K groups
+ *   (W4A8: an even number), and S never exceeds 16 or what `workspace` holds.  With
+ *   1 <= M <= 16 the decode kernels run and nothing is split.
+ * workspace: device memory of workspace_bytes (16-byte aligned, overlapping neither D nor
+ *   any input), or NULL with workspace_bytes == 0 (no split).  S slices use L*S*M*N*4
+ *   bytes, written in full before they are read: nothing needs clearing.
+ * nv_fp4_gemm_workspace_size / w4a8_gemm_workspace_size: the workspace bytes the split
+ *   call takes for these sizes and `splits` (0 when it would not split); the W4A8 size
+ *   covers both weight forms (pass L = 1 for the pre-packed call).
+ * Statuses as for the unsplit calls; splits < 0 is FP4G_EINVAL. */
+fp4g_status nv_fp4_gemm_workspace_size(int64_t L, int64_t M, int64_t N, int64_t K, int64_t splits,
+                                       size_t *bytes);
+fp4g_status w4a8_gemm_workspace_size(int64_t L, int64_t M, int64_t N, int64_t K, int64_t splits,
+                                     size_t *bytes);
+fp4g_status nv_fp4_gemm_split(int64_t L, int64_t M, int64_t N, int64_t K,
+                              const void *A, const void *sfA, float global_a,
+                              const void *B, const void *sfB, float global_b,
+                              void *D, int d_type, int64_t splits,
+                              void *workspace, size_t workspace_bytes, void *stream);
+fp4g_status w4a8_gemm_split(int64_t L, int64_t M, int64_t N, int64_t K,
+                            const void *A, const float *sa,
+                            const void *B, const void *sB,
+                            void *D, int d_type, int64_t splits,
+                            void *workspace, size_t workspace_bytes, void *stream);
+fp4g_status w4a8_gemm_prepacked_split(int64_t M, int64_t N, int64_t K,
+                                      const void *A, const float *sa,
+                                      const void *Bp, const void *Sp,
+                                      void *D, int d_type, int64_t splits,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Pre-packed decode weights (a load-time step, like the weight re-encoding and
  * re-ordering that the Hopper CUTLASS/CuTe DSL blog post describes for W4A8 in
  * section "The W4A8 kernel: the same four definitions, with the operands

@@ -36,6 +36,8 @@ def test_header_declares_the_operations():
                                             "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3",
                                             "w4a8_gemm_prepacked",
                                             "nv_fp4_gemm_batched", "w4a8_gemm_batched",
+                                            "nv_fp4_gemm_workspace_size", "w4a8_gemm_workspace_size",
+                                            "nv_fp4_gemm_split", "w4a8_gemm_split", "w4a8_gemm_prepacked_split",
                                             "mx_fp4_quantize", "nv_fp4_quantize", "fp8_blockwise_gemm",
                                             "fp4g_status_string"])
 
@@ -314,3 +316,48 @@ def test_binding_rejects_host_tensors():
         fp4.mx_fp4_gemm(A, s, A, s)
     with pytest.raises(TypeError):
         fp4.mx_fp4_gemm(A.numpy(), s, A, s)
+
+
+def test_split_validation(lib):
+    """The K-split NVFP4 and W4A8 entry points: sizes, workspace rules (NULL with bytes,
+    alignment, overlap with D or an input) and the workspace-size query, all refused or
+    answered before any device call."""
+    nv, w4, wp = lib.nv_fp4_gemm_split, lib.w4a8_gemm_split, lib.w4a8_gemm_prepacked_split
+    W = 0x600000
+
+    def nvc(L, M, N, K, D=D_, dt=1, splits=0, ws=W, wbytes=1 << 20, A=A_):
+        return nv(L, M, N, K, A, SA_, 1.0, B_, SB_, 1.0, D, dt, splits, ws, wbytes, None)
+
+    def w4c(L, M, N, K, D=D_, dt=1, splits=0, ws=W, wbytes=1 << 20, A=A_):
+        return w4(L, M, N, K, A, SA_, B_, SB_, D, dt, splits, ws, wbytes, None)
+
+    def wpc(M, N, K, D=D_, dt=1, splits=0, ws=W, wbytes=1 << 20, A=A_):
+        return wp(M, N, K, A, SA_, B_, SB_, D, dt, splits, ws, wbytes, None)
+
+    for call in (nvc, w4c):
+        assert call(-1, 4, 4, 128) == EINVAL
+        assert call(2, 4, 4, 128, splits=-1) == EINVAL
+        assert call(2, 4, 4, 192) == EUNSUP
+        assert call(2, 4, 4, 128, dt=3) == EINVAL
+        assert call(65536, 4, 4, 128) == EUNSUP
+        assert call(0, 4, 4, 128) == OK
+        assert call(2, 64, 64, 1024, ws=None) == EINVAL                 # NULL workspace with bytes
+        assert call(2, 64, 64, 1024, A=None) == EINVAL
+        assert call(2, 64, 64, 1024, ws=W + 8) == EALIGN
+        assert call(2, 64, 64, 1024, ws=D_) == EINVAL                   # workspace over D
+        assert call(2, 64, 64, 1024, ws=B_) == EINVAL                   # workspace over B
+    assert wpc(-1, 4, 128) == EINVAL
+    assert wpc(4, 4, 128, splits=-1) == EINVAL
+    assert wpc(64, 64, 1024, ws=None) == EINVAL
+    assert wpc(64, 64, 1024, ws=W + 4) == EALIGN
+    assert wpc(64, 64, 1024, ws=SA_) == EINVAL
+    assert wpc(0, 64, 1024) == OK
+
+    n = ctypes.c_size_t(7)
+    for f in (lib.nv_fp4_gemm_workspace_size, lib.w4a8_gemm_workspace_size):
+        assert f(1, 64, 8192, 8192, 1, ctypes.byref(n)) == OK and n.value == 0     # never splits
+        assert f(1, 16, 8192, 8192, 0, ctypes.byref(n)) == OK and n.value == 0     # decode kernel
+        assert f(1, 64, 8192, 8192, 4, ctypes.byref(n)) == OK and n.value == 4 * 64 * 8192 * 4
+        assert f(1, 64, 8192, 256, 16, ctypes.byref(n)) == OK and n.value <= 2 * 64 * 8192 * 4
+        assert f(1, 64, 64, 1024, -1, ctypes.byref(n)) == EINVAL
+        assert f(1, 64, 64, 1024, 0, None) == EINVAL
