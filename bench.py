@@ -415,6 +415,45 @@ def bench_skinny(steps, warmup, dev, L=1, M=128, N=8192, K=8192):
     return out
 
 
+def bench_decode(steps, warmup, dev, N=8192, K=8192):
+    """Few-token calls on an N x K = 8192 x 8192 weight, cold rotating weight copies: the
+    16-token decode kernels (W4A8 plain and pre-packed, NVFP4) at M = 8, and the K-split
+    W4A8 and NVFP4 GEMMs at M = 64 with the library's own split."""
+    w = datagen.make_shape("w4a8", 64, N, K, seed=0)
+    n = datagen.random_nv(64, N, K, np.random.default_rng(0))
+    A8, sa = torch.from_numpy(w["A"]).to(dev), torch.from_numpy(w["sa"]).to(dev)
+    B4 = torch.from_numpy(w["B"]).to(dev)
+    sB = torch.from_numpy(w["sB"].view(np.int16)).to(dev).view(torch.bfloat16)
+    A4, sfA = torch.from_numpy(n["A"]).to(dev), torch.from_numpy(n["sfA"]).to(dev)
+    NB, sfB = torch.from_numpy(n["B"]).to(dev), torch.from_numpy(n["sfB"]).to(dev)
+    copies = int(np.ceil(320e6 / (B4.numel() + sB.numel() * 2)))
+    w_sets = [((B4.clone(), sB.clone()) if c else (B4, sB)) for c in range(copies)]
+    p_sets = [fp4.w4a8_prepack(b, s) for b, s in w_sets]
+    n_sets = [((NB.clone(), sfB.clone()) if c else (NB, sfB)) for c in range(copies)]
+    out = {"copies": copies}
+    wbytes = {"w4a8": B4.numel() + sB.numel() * 2, "w4a8_prepacked": B4.numel() + sB.numel() * 4,
+              "nvfp4": NB.numel() + sfB.numel()}
+    for M in (8, 64):
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        a8, s8, a4, f4 = A8[:M].contiguous(), sa[:M].contiguous(), A4[:M].contiguous(), sfA[:M].contiguous()
+        ws = torch.empty(max(fp4.w4a8_gemm_workspace_size(1, M, N, K), fp4.nv_fp4_gemm_workspace_size(1, M, N, K), 16),
+                         dtype=torch.uint8, device=dev)
+        fns = {"w4a8": (lambda B, s_: fp4.w4a8_gemm_split(a8[None], s8[None], B[None], s_[None], out=D[None],
+                                                           workspace=ws), w_sets),
+               "w4a8_prepacked": (lambda Bp, Sp: fp4.w4a8_gemm_prepacked_split(a8, s8, Bp, Sp, N, out=D,
+                                                                               workspace=ws), p_sets),
+               "nvfp4": (lambda B, s_: fp4.nv_fp4_gemm_split(a4[None], f4[None], 1.0, B[None], s_[None], 1.0,
+                                                              out=D[None], workspace=ws), n_sets)}
+        row = {"splits": {"w4a8": fp4.w4a8_gemm_workspace_size(1, M, N, K) // (M * N * 4) or 1,
+                          "nvfp4": fp4.nv_fp4_gemm_workspace_size(1, M, N, K) // (M * N * 4) or 1}}
+        for name, (fn, sets) in fns.items():
+            ms, _ = time_launches(fn, steps, warmup, dev, sets)
+            row[name] = {"us": ms * 1e3, "gbs": wbytes[name] / (ms * 1e-3) / 1e9,
+                         "tflops": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
+        out[M] = row
+    return out
+
+
 def bench_quant(steps, warmup, dev):
     """MX quantizer on an 8192 x 8192 fp32 activation (the GEMM's operand size): two
     input copies alternate (512 MB, past the 256 MB last-level cache)."""
@@ -639,7 +678,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: mx8192 gemv gemvp w4a8 w4a8p nv1024 mx256 quant nvquant fp8b skinny copy peaks")
+                    help="subset of: mx8192 gemv gemvp w4a8 w4a8p nv1024 mx256 quant nvquant fp8b skinny decode "
+                         "copy peaks")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue launches eagerly instead of replaying a HIP graph (for counter runs)")
@@ -669,7 +709,7 @@ def main():
     dev = torch.device("cuda:0")
     fp4.load_library()
     only = set(args.only) if args.only else {"mx8192", "gemv", "gemvp", "w4a8", "w4a8p", "nv1024", "mx256",
-                                             "quant", "nvquant", "fp8b", "skinny", "peaks"}
+                                             "quant", "nvquant", "fp8b", "skinny", "decode", "peaks"}
     also = {}
     head = None
     d8192 = None
@@ -783,6 +823,18 @@ def main():
             "roofline": {"bound": "mfma", "achieved": k["auto"]["tflops"], "peak": PEAK_TFLOPS["fp4"],
                          "unit": "TFLOP/s", "frac": k["auto"]["tflops"] / PEAK_TFLOPS["fp4"],
                          "traffic": split_traffic}}
+    if "decode" in only:
+        log("bench: decode (M = 8) and skinny (M = 64) W4A8 / NVFP4 on 8192x8192 weights (cold) ...")
+        k = bench_decode(args.steps, args.warmup, dev)
+        for M, label in ((8, "decode_8x8192x8192"), (64, "skinny_64x8192x8192")):
+            r = k[M]
+            log(f"bench: {label}: " + ", ".join(f"{n} {r[n]['us']:.1f} us" for n in ("w4a8", "w4a8_prepacked", "nvfp4")))
+            also[label] = {"metric": "us per launch", "cache": f"cold ({k['copies']} rotating weight copies)",
+                           "kernels": "16-token decode kernels" if M <= 16 else "K-split GEMMs (library's choice)",
+                           "splits": r["splits"],
+                           **{n: {"us": r[n]["us"], "weight_GBps": r[n]["gbs"], "tflops": r[n]["tflops"],
+                                  "hbm_frac": r[n]["gbs"] / PEAK_HBM_GBS}
+                              for n in ("w4a8", "w4a8_prepacked", "nvfp4")}}
     if "copy" in only:
         c = bench_copy(dev)
         log(f"bench: copy 512 MiB {c['ms'] * 1e3:.1f} us, {c['gbs']:.0f} GB/s (read+write)")
