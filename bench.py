@@ -115,15 +115,32 @@ COUNTED = [("mxfp4_gemm_8192", _NS + "mxfp4_gemm_kernel<256, 256, 128, 128, 256,
            ("mxfp4_split_k_128x8192x8192", _NS + "mxfp4_gemm_kernel<128, 128, 64, 64, 256, 2, false, true>",
             ["mxfp4_gemm.hip", "common.hpp"]),
            ("mxfp4_split_k_reduce_128x8192x8192", _NS + "splitk_reduce_kernel<", ["mxfp4_gemm.hip", "common.hpp"]),
-           ("w4a8_256x8192x8192", _NS + "w4a8p_gemm_kernel<64, false",
+           ("w4a8_256x8192x8192", _NS + "w4a8p_gemm_kernel<64, false, false",
             ["w4a8_gemm.hip", "w4a8_prepacked.hip", "common.hpp"]),
-           ("w4a8_prepacked_256x8192x8192", _NS + "w4a8p_gemm_kernel<64, true", ["w4a8_prepacked.hip", "common.hpp"]),
-           ("nvfp4_gemm_1024", _NS + "nvfp4_gemm_kernel<", ["nvfp4_gemm.hip", "common.hpp"]),
+           ("w4a8_prepacked_256x8192x8192", _NS + "w4a8p_gemm_kernel<64, true, false",
+            ["w4a8_prepacked.hip", "common.hpp"]),
+           ("nvfp4_gemm_1024", _NS + "nvfp4_gemm_kernel<64, 64, 16, 32, false",
+            ["nvfp4_gemm.hip", "nv_fold.hpp", "common.hpp"]),
            ("fp8_blockwise_4096", _NS + "fp8b_gemm_big_kernel<", ["fp8b_gemm.hip", "common.hpp"]),
            ("mx_quantize_8192x8192_f32", _NS + "mx_quantize_kernel<", ["mx_quantize.hip", "common.hpp"]),
-           ("nv_quantize_8192x8192_f32", _NS + "nv_quantize_kernel<", ["mx_quantize.hip", "common.hpp"])]
+           ("nv_quantize_8192x8192_f32", _NS + "nv_quantize_kernel<", ["mx_quantize.hip", "common.hpp"]),
+           # decode (M = 8, K = 8192: two 4-group segments per wave, two row groups) and the
+           # K-split GEMMs at M = 64 (64-row tiles, split kernel + scaled reduction)
+           ("w4a8_decode_8x8192x8192", _NS + "w4a8_gemv_kernel<2, 2, 2, 1,", ["w4a8_gemv.hip", "common.hpp"]),
+           ("w4a8_decode_prepacked_8x8192x8192", _NS + "w4a8_gemv_kernel<2, 2, 2, 0,",
+            ["w4a8_gemv.hip", "common.hpp"]),
+           ("nvfp4_decode_8x8192x8192", _NS + "nvfp4_gemv_kernel<2, 2,",
+            ["nvfp4_gemv.hip", "nv_fold.hpp", "common.hpp"]),
+           ("w4a8_split_64x8192x8192", _NS + "w4a8p_gemm_kernel<64, false, true",
+            ["w4a8_gemm.hip", "w4a8_prepacked.hip", "common.hpp"]),
+           ("w4a8_prepacked_split_64x8192x8192", _NS + "w4a8p_gemm_kernel<64, true, true",
+            ["w4a8_prepacked.hip", "common.hpp"]),
+           ("nvfp4_split_64x8192x8192", _NS + "nvfp4_gemm_kernel<64, 64, 16, 32, true",
+            ["nvfp4_gemm.hip", "nv_fold.hpp", "common.hpp"]),
+           ("split_reduce_64x8192x8192", _NS + "scaled_reduce_kernel<", ["splitk_reduce.hip", "common.hpp"]),
+           ("w4a8_fp6_256x8192x8192", _NS + "w4a8f6_gemm_kernel<", ["w4a8_fp6.hip", "common.hpp"])]
 # The kernels that the counter runs cover: `bench.py --only` + this list.
-COUNTED_ONLY = "mx8192 gemv gemvp w4a8 w4a8p nv1024 fp8b quant nvquant skinny copy"
+COUNTED_ONLY = "mx8192 gemv gemvp w4a8 w4a8p w4a8f6 nv1024 fp8b quant nvquant skinny decode copy"
 
 
 def traffic_of(name):
@@ -206,11 +223,14 @@ def summarize_counters(fetch_dir, write_dir, command):
 UTIL_KERNELS = [("mxfp4_gemm_8192x8192x8192", "mxfp4_gemm_kernel<256, 256, 128, 128, 256, 2, true, false>",
                  ["mxfp4_gemm.hip", "common.hpp"]),
                 ("mxfp4_gemv_8x14336x4096", "fp4_gemv_kernel<1, 2, true, true>", ["fp4_gemv.hip", "common.hpp"]),
-                ("w4a8_256x8192x8192", "w4a8p_gemm_kernel<64, false",
+                ("w4a8_256x8192x8192", "w4a8p_gemm_kernel<64, false, false",
                  ["w4a8_gemm.hip", "w4a8_prepacked.hip", "common.hpp"]),
-                ("w4a8_256x8192x8192_prepacked", "w4a8p_gemm_kernel<64, true", ["w4a8_prepacked.hip", "common.hpp"]),
+                ("w4a8_256x8192x8192_prepacked", "w4a8p_gemm_kernel<64, true, false",
+                 ["w4a8_prepacked.hip", "common.hpp"]),
                 ("fp8_blockwise_4096", "fp8b_gemm_big_kernel<", ["fp8b_gemm.hip", "common.hpp"]),
-                ("nvfp4_1024", "nvfp4_gemm_kernel<", ["nvfp4_gemm.hip", "common.hpp"]),
+                ("nvfp4_1024", "nvfp4_gemm_kernel<64, 64, 16, 32, false", ["nvfp4_gemm.hip", "nv_fold.hpp", "common.hpp"]),
+                ("decode_8x8192x8192_w4a8", "w4a8_gemv_kernel<2, 2, 2, 1,", ["w4a8_gemv.hip", "common.hpp"]),
+                ("decode_8x8192x8192_nvfp4", "nvfp4_gemv_kernel<2, 2,", ["nvfp4_gemv.hip", "nv_fold.hpp", "common.hpp"]),
                 ("mx_quantize_8192x8192_f32", "mx_quantize_kernel<", ["mx_quantize.hip", "common.hpp"])]
 UTIL_METRICS = ("MfmaUtil", "LdsUtil", "VALUBusy", "LdsBankConflict")
 UTIL_FILE = os.path.join(PROFILES, "utilisation_counters.txt")
@@ -360,6 +380,27 @@ def bench_w4a8_prepacked(steps, warmup, dev):
             "gbs": bytes_alg / (mean_ms * 1e-3) / 1e9, "bytes": bytes_alg, "copies": copies}
 
 
+def bench_w4a8_fp6(steps, warmup, dev):
+    """W4A8 over weights re-encoded once at load time as FP6 (w4a8_prepack_fp6), rotating
+    cold copies as for the other W4A8 kernels."""
+    d = datagen.make("w4a8_256x8192x8192")
+    M, N, K = 256, 8192, 8192
+    base = to_dev(d, dev)
+    Bp0, Sp0 = fp4.w4a8_prepack_fp6(base["B"], base["sB"])
+    wbytes = Bp0.numel() + Sp0.numel() * 4
+    copies = int(np.ceil(320e6 / wbytes))
+    sets = [((Bp0.clone(), Sp0.clone()) if c else (Bp0, Sp0)) for c in range(copies)]
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fn = lambda Bp6, Sp: fp4.w4a8_gemm_prepacked_fp6(base["A"], base["sa"], Bp6, Sp, N, out=D)
+    mean_ms, _ = time_launches(fn, steps, warmup, dev, sets)
+    flops = 2.0 * M * N * K
+    bytes_alg = d["A"].nbytes + d["sa"].nbytes + d["B"].nbytes + d["sB"].nbytes + M * N * 2
+    layout_bytes = d["A"].nbytes + d["sa"].nbytes + wbytes + M * N * 2
+    return {"ms": mean_ms, "tflops": flops / (mean_ms * 1e-3) / 1e12,
+            "gbs": bytes_alg / (mean_ms * 1e-3) / 1e9, "bytes": bytes_alg, "layout_bytes": layout_bytes,
+            "copies": copies}
+
+
 def bench_nv1024(steps, warmup, dev):
     d = datagen.make("nvfp4_1024")
     t = to_dev(d, dev)
@@ -433,6 +474,8 @@ def bench_decode(steps, warmup, dev, N=8192, K=8192):
     out = {"copies": copies}
     wbytes = {"w4a8": B4.numel() + sB.numel() * 2, "w4a8_prepacked": B4.numel() + sB.numel() * 4,
               "nvfp4": NB.numel() + sfB.numel()}
+    # per token: E4M3 codes + the fp32 row scale (W4A8); E2M1 codes + E4M3 scales (NVFP4)
+    abytes = {"w4a8": K + 4, "w4a8_prepacked": K + 4, "nvfp4": K // 2 + K // 16}
     for M in (8, 64):
         D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         a8, s8, a4, f4 = A8[:M].contiguous(), sa[:M].contiguous(), A4[:M].contiguous(), sfA[:M].contiguous()
@@ -448,10 +491,23 @@ def bench_decode(steps, warmup, dev, N=8192, K=8192):
                           "nvfp4": fp4.nv_fp4_gemm_workspace_size(1, M, N, K) // (M * N * 4) or 1}}
         for name, (fn, sets) in fns.items():
             ms, _ = time_launches(fn, steps, warmup, dev, sets)
-            row[name] = {"us": ms * 1e3, "gbs": wbytes[name] / (ms * 1e-3) / 1e9,
+            nbytes = wbytes[name] + abytes[name] * M + M * N * 2
+            row[name] = {"us": ms * 1e3, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
                          "tflops": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
         out[M] = row
     return out
+
+
+def decode_traffic(name, M):
+    """HBM bytes per call of a bench_decode row from the counter summaries: the decode
+    kernel (M = 8), or the split kernel plus its scaled reduction (M = 64)."""
+    if M <= 16:
+        return traffic_of({"w4a8": "w4a8_decode_8x8192x8192", "w4a8_prepacked": "w4a8_decode_prepacked_8x8192x8192",
+                           "nvfp4": "nvfp4_decode_8x8192x8192"}[name])
+    t = traffic_of({"w4a8": "w4a8_split_64x8192x8192", "w4a8_prepacked": "w4a8_prepacked_split_64x8192x8192",
+                    "nvfp4": "nvfp4_split_64x8192x8192"}[name])
+    r = traffic_of("split_reduce_64x8192x8192")
+    return t + r if t is not None and r is not None else None
 
 
 def bench_quant(steps, warmup, dev):
@@ -678,8 +734,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="subset of: mx8192 gemv gemvp w4a8 w4a8p nv1024 mx256 quant nvquant fp8b skinny decode "
-                         "copy peaks")
+                    help="subset of: mx8192 gemv gemvp w4a8 w4a8p w4a8f6 nv1024 mx256 quant nvquant fp8b skinny "
+                         "decode copy peaks")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue launches eagerly instead of replaying a HIP graph (for counter runs)")
@@ -708,7 +764,7 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     fp4.load_library()
-    only = set(args.only) if args.only else {"mx8192", "gemv", "gemvp", "w4a8", "w4a8p", "nv1024", "mx256",
+    only = set(args.only) if args.only else {"mx8192", "gemv", "gemvp", "w4a8", "w4a8p", "w4a8f6", "nv1024", "mx256",
                                              "quant", "nvquant", "fp8b", "skinny", "decode", "peaks"}
     also = {}
     head = None
@@ -771,6 +827,19 @@ def main():
                          "traffic": traffic_of("w4a8_prepacked_256x8192x8192")},
             "hbm": {"achieved": w["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": w["gbs"] / PEAK_HBM_GBS},
             "algorithmic_bytes": w["bytes"]}
+    if "w4a8f6" in only:
+        log("bench: fp6 w4a8 256x8192x8192 ...")
+        w = bench_w4a8_fp6(args.steps, args.warmup, dev)
+        log(f"bench: fp6 w4a8 {w['ms'] * 1e3:.1f} us/launch, {w['tflops']:.0f} TFLOP/s")
+        also["w4a8_256x8192x8192_fp6"] = {
+            "metric": "TFLOP/s", "value": w["tflops"], "ms_per_launch": w["ms"],
+            "cache": f"cold ({w['copies']} rotating weight copies)",
+            "weights": "re-encoded once at load time as FP6 E3M2 (w4a8_prepack_fp6), not timed",
+            "roofline": {"bound": "mfma", "achieved": w["tflops"], "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                         "frac": w["tflops"] / PEAK_TFLOPS["fp8"],
+                         "traffic": traffic_of("w4a8_fp6_256x8192x8192")},
+            "hbm": {"achieved": w["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": w["gbs"] / PEAK_HBM_GBS},
+            "algorithmic_bytes": w["bytes"], "layout_bytes": w["layout_bytes"]}
     if "nv1024" in only:
         n = bench_nv1024(args.steps, args.warmup, dev)
         kept["nvfp4_1024"] = n
@@ -829,12 +898,17 @@ def main():
         for M, label in ((8, "decode_8x8192x8192"), (64, "skinny_64x8192x8192")):
             r = k[M]
             log(f"bench: {label}: " + ", ".join(f"{n} {r[n]['us']:.1f} us" for n in ("w4a8", "w4a8_prepacked", "nvfp4")))
-            also[label] = {"metric": "us per launch", "cache": f"cold ({k['copies']} rotating weight copies)",
-                           "kernels": "16-token decode kernels" if M <= 16 else "K-split GEMMs (library's choice)",
-                           "splits": r["splits"],
-                           **{n: {"us": r[n]["us"], "weight_GBps": r[n]["gbs"], "tflops": r[n]["tflops"],
-                                  "hbm_frac": r[n]["gbs"] / PEAK_HBM_GBS}
-                              for n in ("w4a8", "w4a8_prepacked", "nvfp4")}}
+            entry = {"metric": "us per launch", "cache": f"cold ({k['copies']} rotating weight copies)",
+                     "kernels": "16-token decode kernels" if M <= 16 else "K-split GEMMs (library's choice)",
+                     "splits": r["splits"]}
+            for n in ("w4a8", "w4a8_prepacked", "nvfp4"):
+                entry[n] = {"us": r[n]["us"], "tflops": r[n]["tflops"], "algorithmic_bytes": r[n]["bytes"],
+                            "roofline": {"bound": "hbm", "achieved": r[n]["gbs"], "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": r[n]["gbs"] / PEAK_HBM_GBS,
+                                         "traffic": decode_traffic(n, M), "traffic_source": TRAFFIC_SOURCE}}
+                if M <= 16 and n != "w4a8_prepacked":
+                    entry[n]["roofline"]["utilisation"] = util_from_profile(f"decode_8x8192x8192_{n}")
+            also[label] = entry
     if "copy" in only:
         c = bench_copy(dev)
         log(f"bench: copy 512 MiB {c['ms'] * 1e3:.1f} us, {c['gbs']:.0f} GB/s (read+write)")

@@ -30,6 +30,7 @@ __all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_batched_noalloc", 
            "nv_fp4_gemm_batched", "w4a8_gemm_batched", "w4a8_gemm", "fp4_gemv", "mx_fp4_quantize", "nv_fp4_quantize",
            "nv_fp4_gemm_split", "w4a8_gemm_split", "w4a8_gemm_prepacked_split",
            "nv_fp4_gemm_workspace_size", "w4a8_gemm_workspace_size",
+           "w4a8_prepack_fp6_size", "w4a8_prepack_fp6", "w4a8_gemm_prepacked_fp6",
            "fp8_blockwise_gemm", "fp4g_status_string",
            "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
 
@@ -42,7 +43,7 @@ SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_batched_noalloc", 
            "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3", "w4a8_gemm_prepacked",
            "mx_fp4_quantize", "nv_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string",
            "nv_fp4_gemm_workspace_size", "w4a8_gemm_workspace_size", "nv_fp4_gemm_split", "w4a8_gemm_split",
-           "w4a8_gemm_prepacked_split")
+           "w4a8_gemm_prepacked_split", "w4a8_prepack_fp6_size", "w4a8_prepack_fp6", "w4a8_gemm_prepacked_fp6")
 
 OUT_F32, OUT_BF16 = 0, 1
 IN_F32, IN_BF16 = 0, 1
@@ -93,6 +94,13 @@ def load_library():
     lib.w4a8_prepack_e4m3.restype = c_int
     lib.w4a8_gemm_prepacked.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.w4a8_gemm_prepacked.restype = c_int
+    lib.w4a8_prepack_fp6_size.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_size_t)]
+    lib.w4a8_prepack_fp6_size.restype = c_int
+    lib.w4a8_prepack_fp6.argtypes = [i64, i64, p, p, p, p, p]
+    lib.w4a8_prepack_fp6.restype = c_int
+    lib.w4a8_gemm_prepacked_fp6.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
+    lib.w4a8_gemm_prepacked_fp6.restype = c_int
     lib.nv_fp4_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, f, p, p, f, p, c_int, p]
     lib.nv_fp4_gemm_batched.restype = c_int
     lib.w4a8_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, p, p, p, c_int, p]
@@ -382,6 +390,57 @@ def w4a8_prepack(B, sB):
     st = lib.w4a8_prepack(N, K, _ptr(B), _ptr(sB), _ptr(Bp), _ptr(Sp), _stream(device))
     _raise_on("w4a8_prepack", st)
     return Bp, Sp
+
+
+def w4a8_prepack_fp6_size(N, K):
+    """(weight bytes, scale bytes) of the FP6 re-encoded layout of an N x K W4A8 weight."""
+    wb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = load_library().w4a8_prepack_fp6_size(N, K, ctypes.byref(wb), ctypes.byref(sb))
+    _raise_on("w4a8_prepack_fp6_size", st)
+    return int(wb.value), int(sb.value)
+
+
+def w4a8_prepack_fp6(B, sB):
+    """Re-encode W4A8 weights B [N, K/2] (INT4) as FP6 and widen sB [N, K/128]
+    (bfloat16) for w4a8_gemm_prepacked_fp6; returns (Bp6 uint8, Sp float32) as flat
+    device tensors."""
+    lib = load_library()
+    device = _device_of(B)
+    if B.dim() != 2:
+        raise ValueError("B must be 2-D")
+    N, K = B.shape[0], B.shape[1] * 2
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(B, "B", torch.uint8, (N, K // 2), device)
+    _check(sB, "sB", torch.bfloat16, (N, K // 128), device)
+    wb, sb = w4a8_prepack_fp6_size(N, K)
+    Bp6 = torch.empty(wb, dtype=torch.uint8, device=device)
+    Sp = torch.empty(sb // 4, dtype=torch.float32, device=device)
+    st = lib.w4a8_prepack_fp6(N, K, _ptr(B), _ptr(sB), _ptr(Bp6), _ptr(Sp), _stream(device))
+    _raise_on("w4a8_prepack_fp6", st)
+    return Bp6, Sp
+
+
+def w4a8_gemm_prepacked_fp6(A, sa, Bp6, Sp, N, out=None, out_dtype=torch.bfloat16):
+    """w4a8_gemm with weights from w4a8_prepack_fp6 (N weight rows); returns D [M, N]."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 2:
+        raise ValueError("A must be 2-D")
+    M, K = A.shape
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(A, "A", torch.uint8, (M, K), device)
+    _check(sa, "sa", torch.float32, (M,), device)
+    wb, sb = w4a8_prepack_fp6_size(N, K)
+    _check(Bp6, "Bp6", torch.uint8, (wb,), device)
+    _check(Sp, "Sp", torch.float32, (sb // 4,), device)
+    D = _out(out, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    st = lib.w4a8_gemm_prepacked_fp6(M, N, K, _ptr(A), _ptr(sa), _ptr(Bp6), _ptr(Sp), _ptr(D), dt,
+                                     _stream(device))
+    _raise_on("w4a8_gemm_prepacked_fp6", st)
+    return D
 
 
 def w4a8_prepack_e4m3(B, sB8, scale_stride=1):

@@ -23,6 +23,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function"]
 
 
+# Per-file device flags.  w4a8_fp6.hip: the MFMA results are folded into fp32
+# accumulators by VALU after every K group, so they are wanted in VGPRs (no AGPR reads).
+DEVICE_FLAGS = {"w4a8_fp6.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -42,7 +47,7 @@ def build(verbose: bool = False) -> str:
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc] + COMMON + lang + ["-c", src, "-o", obj]
+        cmd = [cc] + COMMON + DEVICE_FLAGS.get(os.path.basename(src), []) + lang + ["-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -460,6 +460,57 @@ fp4g_status w4a8_gemm_prepacked(int64_t M, int64_t N, int64_t K, const void* A, 
   return finish(fp4g::launch_w4a8_gemm_prepacked(a, static_cast<const float*>(Sp), s));
 }
 
+fp4g_status w4a8_prepack_fp6_size(int64_t N, int64_t K, size_t* weight_bytes, size_t* scale_bytes) {
+  if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim) return FP4G_EINVAL;
+  if (K % 128 != 0) return FP4G_EUNSUPPORTED;
+  if (!weight_bytes || !scale_bytes) return FP4G_EINVAL;
+  int64_t wb = 0, sb = 0;
+  fp4g::w4a8_prepack_fp6_sizes(N, K, &wb, &sb);
+  *weight_bytes = (size_t)wb;
+  *scale_bytes = (size_t)sb;
+  return FP4G_OK;
+}
+
+fp4g_status w4a8_prepack_fp6(int64_t N, int64_t K, const void* B, const void* sB, void* Bp6, void* Sp,
+                             void* stream) {
+  if (N < 0 || K < 0 || N >= kMaxDim || K >= kMaxDim) return FP4G_EINVAL;
+  if (K % 128 != 0) return FP4G_EUNSUPPORTED;
+  if (N == 0 || K == 0) return FP4G_OK;
+  if (!B || !sB || !Bp6 || !Sp) return FP4G_EINVAL;
+  if (!aligned(B, 16) || !aligned(Bp6, 16) || !aligned(sB, 2) || !aligned(Sp, 4)) return FP4G_EALIGN;
+  int64_t wb = 0, sb = 0;
+  fp4g::w4a8_prepack_fp6_sizes(N, K, &wb, &sb);
+  const Range ib = range_of(B, N * (K / 2)), is = range_of(sB, N * (K / 128) * 2);
+  const Range ob = range_of(Bp6, wb), os = range_of(Sp, sb);
+  if (overlaps(ob, os) || overlaps(ob, ib) || overlaps(ob, is) || overlaps(os, ib) || overlaps(os, is))
+    return FP4G_EINVAL;
+  return finish(fp4g::launch_w4a8_prepack_fp6(N, K, static_cast<const uint8_t*>(B), static_cast<const uint16_t*>(sB),
+                                              static_cast<uint8_t*>(Bp6), static_cast<float*>(Sp),
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+fp4g_status w4a8_gemm_prepacked_fp6(int64_t M, int64_t N, int64_t K, const void* A, const float* sa,
+                                    const void* Bp6, const void* Sp, void* D, int d_type, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_common(M, N, K, d_type, D, &empty);
+  if (st != FP4G_OK || empty) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, M * N, bf16, s));
+  if (!fp4g::w4a8_fp6_fits(K)) return FP4G_EUNSUPPORTED;
+  if (!A || !sa || !Bp6 || !Sp) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(Bp6, 16) || !aligned(Sp, 16)) return FP4G_EALIGN;
+  if (!aligned(sa, 4)) return FP4G_EALIGN;
+  int64_t wb = 0, sb = 0;
+  fp4g::w4a8_prepack_fp6_sizes(N, K, &wb, &sb);
+  const Range d = range_of(D, M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, M * K), range_of(sa, M * 4), range_of(Bp6, wb), range_of(Sp, sb)};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  W4A8Args a{M, N, K, static_cast<const uint8_t*>(A), sa, static_cast<const uint8_t*>(Bp6), nullptr, D, bf16};
+  return finish(fp4g::launch_w4a8_gemm_prepacked_fp6(a, static_cast<const float*>(Sp), s));
+}
+
 fp4g_status mx_fp4_quantize(int64_t rows, int64_t K, const void* X, int x_type, void* codes, void* scales,
                             void* stream) {
   if (rows < 0 || K < 0 || rows >= kMaxDim || K >= kMaxDim) return FP4G_EINVAL;

@@ -80,6 +80,14 @@ hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t s);
 // Pre-packed W4A8 weights: sizes, the load-time re-pack, and the GEMM over them
 // (a.B is the packed weight buffer, a.sB unused; Sp the packed fp32 scales).
 void w4a8_prepack_sizes(int64_t N, int64_t K, int64_t* weight_bytes, int64_t* scale_bytes);
+// The fp32 group scales Sp [K/128][16*ceil(N/16)] alone (rows past N 0).
+hipError_t launch_w4a8_prepack_scales(int64_t N, int64_t K, const uint16_t* sB, float* Sp, hipStream_t s);
+// FP6 (E3M2) re-encoded W4A8 weights: sizes, the re-pack (weights and Sp), and the GEMM.
+void w4a8_prepack_fp6_sizes(int64_t N, int64_t K, int64_t* weight_bytes, int64_t* scale_bytes);
+hipError_t launch_w4a8_prepack_fp6(int64_t N, int64_t K, const uint8_t* B, const uint16_t* sB, uint8_t* Bp6,
+                                   float* Sp, hipStream_t s);
+bool w4a8_fp6_fits(int64_t K);             // K <= 2^24
+hipError_t launch_w4a8_gemm_prepacked_fp6(const W4A8Args& a, const float* Sp, hipStream_t s);
 hipError_t launch_w4a8_prepack(int64_t N, int64_t K, const uint8_t* B, const uint16_t* sB, uint8_t* Bp, float* Sp,
                                hipStream_t s);
 hipError_t launch_w4a8_prepack_e4m3(int64_t N, int64_t K, const uint8_t* B, const uint8_t* sB8, int stride,

@@ -373,6 +373,15 @@ hipError_t launch_w4a8_prepack(int64_t N, int64_t K, const uint8_t* B, const uin
   return hipGetLastError();
 }
 
+hipError_t launch_w4a8_prepack_scales(int64_t N, int64_t K, const uint16_t* sB, float* Sp, hipStream_t s) {
+  const int64_t G16 = ceil_div(N, 16), G = K / 128, Np = 16 * G16;
+  const int64_t cap = device_cus() * 8;
+  const int64_t su = G * Np;
+  const unsigned gs = (unsigned)(ceil_div(su, 256) < cap ? ceil_div(su, 256) : cap);
+  hipLaunchKernelGGL(w4a8_prepack_scales_kernel, dim3(gs), dim3(256), 0, s, su, (int)N, (int)G, Np, sB, Sp);
+  return hipGetLastError();
+}
+
 hipError_t launch_w4a8_prepack_e4m3(int64_t N, int64_t K, const uint8_t* B, const uint8_t* sB8, int stride,
                                     uint8_t* Bp, float* Sp, hipStream_t s) {
   const int64_t G16 = ceil_div(N, 16), G = K / 128, Np = 16 * G16;

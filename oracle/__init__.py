@@ -336,6 +336,58 @@ def w4a8_prepack(B, sB):
     return np.ascontiguousarray(Bp).reshape(-1), np.ascontiguousarray(sf.T).reshape(-1)
 
 
+def e3m2_code(q: int) -> int:
+    """The FP6 E3M2 code of an integer q with |q| <= 28 that the format holds exactly:
+    sign in bit 5, exponent field E in bits 4..2 (bias 3), mantissa m in bits 1..0, value
+    (-1)^s * 2^(E-3) * (1 + m/4).  Zero is code 0."""
+    if q == 0:
+        return 0
+    a = abs(int(q))
+    e = a.bit_length() - 1                      # 2^e <= a < 2^(e+1)
+    m4 = a * 4 - (4 << e)                        # (a / 2^e - 1) * 4 * 2^e
+    if m4 % (1 << e) or not (0 <= e <= 4):
+        raise ValueError(f"{q} is not exact in E3M2")
+    return (32 if q < 0 else 0) | ((e + 3) << 2) | (m4 >> e)
+
+
+def w4a8_prepack_fp6(B, sB):
+    """The FP6 re-encoded W4A8 weight layout, from its definition: every INT4 weight q
+    becomes its E3M2 code (e3m2_code); 32-row blocks g32, K groups kg of 128, lanes
+    l = 16*slot + r, halves h (rows 32*g32 + 16h + r).  Lane (h, l) holds the 32 codes of
+    its row at K = 128*kg + 64*(slot & 1) + 16*(slot >> 1) + e + (0 if e < 16 else 16),
+    code e in bits 6e..6e+5 of a 24-byte little-endian word; block (g32, kg) is 3072 bytes:
+    bytes 0..15 of the words of half 0 for lanes 0..63, the same for half 1, then bytes
+    16..23 of half 0 and half 1 per lane.  Rows past N are zero codes; the scales are
+    those of w4a8_prepack.  Returns (Bp6 uint8 flat, Sp float32 flat)."""
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    N, half = B.shape
+    K = 2 * half
+    if K % 128:
+        raise ValueError("B must be [N][K/2] with K % 128 == 0")
+    G32, KG = -(-N // 32), K // 128
+    table = np.array([e3m2_code(n - 16 if n >= 8 else n) for n in range(16)], np.uint8)
+    nib = np.zeros((32 * G32, K), np.uint8)
+    nib[:N, 0::2] = B & 0xF
+    nib[:N, 1::2] = B >> 4
+    codes = table[nib]                                          # [row][K]
+    slot = np.arange(4)[:, None]
+    e = np.arange(32)[None, :]
+    kmap = 64 * (slot & 1) + 16 * (slot >> 1) + e + np.where(e < 16, 0, 16)   # [slot][e]
+    # [g32][h][r][kg][slot][e]
+    c = codes.reshape(G32, 2, 16, KG, 128)[:, :, :, :, kmap]
+    c = c.transpose(0, 3, 1, 4, 2, 5).astype(np.uint32)       # [g32][kg][h][slot][r][e]
+    # four 6-bit codes -> three bytes, little-endian
+    c4 = c.reshape(G32, KG, 2, 4, 16, 8, 4)
+    word = c4[..., 0] | (c4[..., 1] << 6) | (c4[..., 2] << 12) | (c4[..., 3] << 18)
+    byts = np.stack([word & 0xFF, (word >> 8) & 0xFF, (word >> 16) & 0xFF], axis=-1).astype(np.uint8)
+    lanes = byts.reshape(G32, KG, 2, 64, 24)                    # [g32][kg][h][lane = 16 slot + r][24]
+    lo = lanes[..., :16].reshape(G32, KG, 2 * 64 * 16)          # half 0 lanes, then half 1 lanes
+    hi = lanes[..., 16:].transpose(0, 1, 3, 2, 4).reshape(G32, KG, 64 * 16)   # per lane: half 0, half 1
+    Bp6 = np.concatenate([lo, hi], axis=2)
+    _, Sp = w4a8_prepack(B, sB)
+    return np.ascontiguousarray(Bp6).reshape(-1), Sp
+
+
 # ---- the FP8 matrix instruction's truncation bound ---------------------------------------
 #
 # gfx950's scaled FP8 matrix instruction (the contraction behind w4a8_gemm and

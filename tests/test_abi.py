@@ -34,7 +34,8 @@ def test_header_declares_the_operations():
                                             "nv_fp4_gemm", "w4a8_gemm", "fp4_gemv", "fp4_gemv_prepack_size",
                                             "fp4_gemv_prepack", "fp4_gemv_prepacked",
                                             "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3",
-                                            "w4a8_gemm_prepacked",
+                                            "w4a8_gemm_prepacked", "w4a8_prepack_fp6_size", "w4a8_prepack_fp6",
+                                            "w4a8_gemm_prepacked_fp6",
                                             "nv_fp4_gemm_batched", "w4a8_gemm_batched",
                                             "nv_fp4_gemm_workspace_size", "w4a8_gemm_workspace_size",
                                             "nv_fp4_gemm_split", "w4a8_gemm_split", "w4a8_gemm_prepacked_split",
@@ -307,6 +308,38 @@ def test_w4a8_prepack_validation(lib):
     assert g(4, 16, 128, A_ + 4, SA_, B_, SB_, D_, 1, None) == EALIGN
     assert g(4, 16, 128, A_, SA_, B_, SB_ + 2, D_, 1, None) == EALIGN
     assert g(4, 16, 128, A_, SA_, B_, SB_, SB_ + 32, 1, None) == EINVAL   # D inside Sp (64 B)
+
+
+def test_w4a8_prepack_fp6_validation(lib):
+    wb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    f = lib.w4a8_prepack_fp6_size
+    assert f(40, 384, ctypes.byref(wb), ctypes.byref(sb)) == OK
+    assert wb.value == 2 * 3 * 3072 and sb.value == 3 * 48 * 4          # G32 = 2, G16 = 3, KG = 3
+    assert f(40, 384, None, ctypes.byref(sb)) == EINVAL
+    assert f(40, 200, ctypes.byref(wb), ctypes.byref(sb)) == EUNSUP
+    assert f(-1, 128, ctypes.byref(wb), ctypes.byref(sb)) == EINVAL
+    p = lib.w4a8_prepack_fp6
+    assert p(0, 128, None, None, None, None, None) == OK
+    assert p(4, 192, B_, SB_, A_, D_, None) == EUNSUP
+    assert p(4, 128, B_, None, A_, D_, None) == EINVAL
+    assert p(4, 128, B_ + 8, SB_, A_, D_, None) == EALIGN
+    assert p(4, 128, B_, SB_ + 1, A_, D_, None) == EALIGN
+    assert p(4, 128, B_, SB_, A_ + 8, D_, None) == EALIGN
+    assert p(4, 128, B_, SB_, A_, D_ + 2, None) == EALIGN
+    assert p(4, 128, B_, SB_, A_, B_, None) == EINVAL                   # Sp over B
+    assert p(4, 128, B_, SB_, B_, D_, None) == EINVAL                   # Bp6 over B
+    g = lib.w4a8_gemm_prepacked_fp6
+    assert g(0, 16, 128, None, None, None, None, None, 1, None) == OK
+    assert g(4, 16, 128, None, None, None, None, None, 2, None) == EINVAL   # output type
+    assert g(4, 16, 192, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
+    assert g(4, 16, 128, A_, None, B_, SB_, D_, 1, None) == EINVAL
+    assert g(4, 16, 128, A_ + 4, SA_, B_, SB_, D_, 1, None) == EALIGN
+    assert g(4, 16, 128, A_, SA_, B_ + 4, SB_, D_, 1, None) == EALIGN
+    assert g(4, 16, 128, A_, SA_, B_, SB_ + 4, D_, 1, None) == EALIGN      # Sp needs 16 bytes here
+    assert g(4, 16, 128, A_, SA_ + 2, B_, SB_, D_, 1, None) == EALIGN
+    assert g(4, 16, 128, A_, SA_, B_, SB_, D_ + 8, 1, None) == EALIGN
+    assert g(4, 16, 128, A_, SA_, B_, SB_, B_ + 1024, 1, None) == EINVAL   # D inside Bp6 (3072 B)
+    assert g(4, 16, (1 << 24) + 128, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
 
 
 def test_binding_rejects_host_tensors():
