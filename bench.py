@@ -229,6 +229,7 @@ UTIL_KERNELS = [("mxfp4_gemm_8192x8192x8192", "mxfp4_gemm_kernel<256, 256, 128, 
                  ["w4a8_prepacked.hip", "common.hpp"]),
                 ("fp8_blockwise_4096", "fp8b_gemm_big_kernel<", ["fp8b_gemm.hip", "common.hpp"]),
                 ("nvfp4_1024", "nvfp4_gemm_kernel<64, 64, 16, 32, false", ["nvfp4_gemm.hip", "nv_fold.hpp", "common.hpp"]),
+                ("w4a8_256x8192x8192_fp6", "w4a8f6_gemm_kernel<", ["w4a8_fp6.hip", "common.hpp"]),
                 ("decode_8x8192x8192_w4a8", "w4a8_gemv_kernel<2, 2, 2, 1,", ["w4a8_gemv.hip", "common.hpp"]),
                 ("decode_8x8192x8192_nvfp4", "nvfp4_gemv_kernel<2, 2,", ["nvfp4_gemv.hip", "nv_fold.hpp", "common.hpp"]),
                 ("mx_quantize_8192x8192_f32", "mx_quantize_kernel<", ["mx_quantize.hip", "common.hpp"])]
