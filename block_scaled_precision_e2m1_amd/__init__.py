@@ -31,6 +31,7 @@ __all__ = ["mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_batched_noalloc", 
            "nv_fp4_gemm_split", "w4a8_gemm_split", "w4a8_gemm_prepacked_split",
            "nv_fp4_gemm_workspace_size", "w4a8_gemm_workspace_size",
            "w4a8_prepack_fp6_size", "w4a8_prepack_fp6", "w4a8_gemm_prepacked_fp6",
+           "w4a8_fp6_workspace_size", "w4a8_gemm_prepacked_fp6_split",
            "fp8_blockwise_gemm", "fp4g_status_string",
            "Fp4GemmError", "library_path", "load_library", "SYMBOLS"]
 
@@ -43,7 +44,8 @@ SYMBOLS = ("mx_fp4_gemm", "mx_fp4_gemm_batched", "mx_fp4_gemm_batched_noalloc", 
            "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3", "w4a8_gemm_prepacked",
            "mx_fp4_quantize", "nv_fp4_quantize", "fp8_blockwise_gemm", "fp4g_status_string",
            "nv_fp4_gemm_workspace_size", "w4a8_gemm_workspace_size", "nv_fp4_gemm_split", "w4a8_gemm_split",
-           "w4a8_gemm_prepacked_split", "w4a8_prepack_fp6_size", "w4a8_prepack_fp6", "w4a8_gemm_prepacked_fp6")
+           "w4a8_gemm_prepacked_split", "w4a8_prepack_fp6_size", "w4a8_prepack_fp6", "w4a8_gemm_prepacked_fp6",
+           "w4a8_fp6_workspace_size", "w4a8_gemm_prepacked_fp6_split")
 
 OUT_F32, OUT_BF16 = 0, 1
 IN_F32, IN_BF16 = 0, 1
@@ -101,6 +103,10 @@ def load_library():
     lib.w4a8_prepack_fp6.restype = c_int
     lib.w4a8_gemm_prepacked_fp6.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, p]
     lib.w4a8_gemm_prepacked_fp6.restype = c_int
+    lib.w4a8_fp6_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.w4a8_fp6_workspace_size.restype = c_int
+    lib.w4a8_gemm_prepacked_fp6_split.argtypes = [i64, i64, i64, p, p, p, p, p, c_int, i64, p, ctypes.c_size_t, p]
+    lib.w4a8_gemm_prepacked_fp6_split.restype = c_int
     lib.nv_fp4_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, f, p, p, f, p, c_int, p]
     lib.nv_fp4_gemm_batched.restype = c_int
     lib.w4a8_gemm_batched.argtypes = [i64, i64, i64, i64, p, p, p, p, p, c_int, p]
@@ -440,6 +446,38 @@ def w4a8_gemm_prepacked_fp6(A, sa, Bp6, Sp, N, out=None, out_dtype=torch.bfloat1
     st = lib.w4a8_gemm_prepacked_fp6(M, N, K, _ptr(A), _ptr(sa), _ptr(Bp6), _ptr(Sp), _ptr(D), dt,
                                      _stream(device))
     _raise_on("w4a8_gemm_prepacked_fp6", st)
+    return D
+
+
+def w4a8_fp6_workspace_size(M, N, K, splits=0):
+    """Workspace bytes w4a8_gemm_prepacked_fp6_split takes for these sizes and `splits`."""
+    nb = ctypes.c_size_t(0)
+    st = load_library().w4a8_fp6_workspace_size(M, N, K, splits, ctypes.byref(nb))
+    _raise_on("w4a8_fp6_workspace_size", st)
+    return int(nb.value)
+
+
+def w4a8_gemm_prepacked_fp6_split(A, sa, Bp6, Sp, N, out=None, out_dtype=torch.bfloat16, splits=0, workspace=None):
+    """w4a8_gemm_prepacked_fp6 with a split of K; `splits` and `workspace` as for
+    nv_fp4_gemm_split."""
+    lib = load_library()
+    device = _device_of(A)
+    if A.dim() != 2:
+        raise ValueError("A must be 2-D")
+    M, K = A.shape
+    if K % 128:
+        raise ValueError(f"K={K} must be a multiple of 128")
+    _check(A, "A", torch.uint8, (M, K), device)
+    _check(sa, "sa", torch.float32, (M,), device)
+    wb, sb = w4a8_prepack_fp6_size(N, K)
+    _check(Bp6, "Bp6", torch.uint8, (wb,), device)
+    _check(Sp, "Sp", torch.float32, (sb // 4,), device)
+    D = _out(out, M, N, out_dtype, device)
+    dt = OUT_BF16 if D.dtype == torch.bfloat16 else OUT_F32
+    ws = _workspace(workspace, w4a8_fp6_workspace_size(M, N, K, splits) if workspace is None else 0, device)
+    st = lib.w4a8_gemm_prepacked_fp6_split(M, N, K, _ptr(A), _ptr(sa), _ptr(Bp6), _ptr(Sp), _ptr(D), dt, splits,
+                                           _ptr(ws), ws.numel(), _stream(device))
+    _raise_on("w4a8_gemm_prepacked_fp6_split", st)
     return D
 
 

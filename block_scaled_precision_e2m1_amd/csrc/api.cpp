@@ -98,10 +98,12 @@ fp4g_status check_batched_sizes(int64_t L, int64_t M, int64_t N, int64_t K, int6
 // The K split of a call: `requested` (0 automatic, 1 none, s > 1 at most s) limited to
 // what `workspace_bytes` holds at per_split bytes a slice; the workspace is checked
 // against the output and the inputs.  *S = 1 when nothing is split.
-struct SplitCtx { int64_t L, M, N, K, requested; int kind; };   // kind 0 W4A8 plain, 1 W4A8 pre-packed, 2 NVFP4
+// kind 0 W4A8 plain, 1 W4A8 pre-packed, 2 NVFP4, 3 W4A8 over FP6 weights
+struct SplitCtx { int64_t L, M, N, K, requested; int kind; };
 
 int64_t choose_split(const SplitCtx& c, int64_t cap) {
   if (c.kind == 2) return fp4g::nvfp4_gemm_splits(c.L, c.M, c.N, c.K, c.requested, cap);
+  if (c.kind == 3) return fp4g::w4a8_fp6_splits(c.M, c.N, c.K, c.requested, cap);
   return fp4g::w4a8_gemm_splits(c.L, c.M, c.N, c.K, c.kind == 1, c.requested, cap);
 }
 
@@ -624,6 +626,40 @@ fp4g_status w4a8_gemm_prepacked_split(int64_t M, int64_t N, int64_t K, const voi
   W4A8Args a{M, N, K, static_cast<const uint8_t*>(A), sa, static_cast<const uint8_t*>(Bp), nullptr, D, bf16};
   return finish(fp4g::launch_w4a8_gemm_split(a, static_cast<const float*>(Sp), S,
                                              S > 1 ? static_cast<float*>(workspace) : nullptr, s));
+}
+
+fp4g_status w4a8_fp6_workspace_size(int64_t M, int64_t N, int64_t K, int64_t splits, size_t* bytes) {
+  return split_workspace_size(3, 1, M, N, K, splits, bytes);
+}
+
+fp4g_status w4a8_gemm_prepacked_fp6_split(int64_t M, int64_t N, int64_t K, const void* A, const float* sa,
+                                          const void* Bp6, const void* Sp, void* D, int d_type, int64_t splits,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  fp4g_status st = check_common(M, N, K, d_type, D, &empty);
+  if (st != FP4G_OK) return st;
+  if (splits < 0) return FP4G_EINVAL;
+  if (!workspace && workspace_bytes > 0) return FP4G_EINVAL;
+  if (empty) return FP4G_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf16 = d_type == FP4G_OUT_BF16;
+  if (K == 0) return finish(fp4g::launch_zero_fill(D, M * N, bf16, s));
+  if (!fp4g::w4a8_fp6_fits(K)) return FP4G_EUNSUPPORTED;
+  if (!A || !sa || !Bp6 || !Sp) return FP4G_EINVAL;
+  if (!aligned(A, 16) || !aligned(Bp6, 16) || !aligned(Sp, 16)) return FP4G_EALIGN;
+  if (!aligned(sa, 4)) return FP4G_EALIGN;
+  int64_t wb = 0, sb = 0;
+  fp4g::w4a8_prepack_fp6_sizes(N, K, &wb, &sb);
+  const Range d = range_of(D, M * N * (bf16 ? 2 : 4));
+  const Range ins[4] = {range_of(A, M * K), range_of(sa, M * 4), range_of(Bp6, wb), range_of(Sp, sb)};
+  for (const Range& r : ins)
+    if (overlaps(d, r)) return FP4G_EINVAL;
+  int64_t S = 1;
+  st = split_of(SplitCtx{1, M, N, K, splits, 3}, M * N * 4, workspace, workspace_bytes, d, ins, 4, &S);
+  if (st != FP4G_OK) return st;
+  W4A8Args a{M, N, K, static_cast<const uint8_t*>(A), sa, static_cast<const uint8_t*>(Bp6), nullptr, D, bf16};
+  return finish(fp4g::launch_w4a8_gemm_prepacked_fp6_split(a, static_cast<const float*>(Sp), S,
+                                                           S > 1 ? static_cast<float*>(workspace) : nullptr, s));
 }
 
 fp4g_status nv_fp4_gemm_split(int64_t L, int64_t M, int64_t N, int64_t K, const void* A, const void* sfA,

@@ -86,7 +86,13 @@ hipError_t launch_w4a8_prepack_scales(int64_t N, int64_t K, const uint16_t* sB, 
 void w4a8_prepack_fp6_sizes(int64_t N, int64_t K, int64_t* weight_bytes, int64_t* scale_bytes);
 hipError_t launch_w4a8_prepack_fp6(int64_t N, int64_t K, const uint8_t* B, const uint16_t* sB, uint8_t* Bp6,
                                    float* Sp, hipStream_t s);
-bool w4a8_fp6_fits(int64_t K);             // K <= 2^24
+bool w4a8_fp6_fits(int64_t K);             // K <= 2^23
+// K split of the FP6 GEMM (128 x 128 tiles): the slice count S (`requested` if > 0, else
+// the library's choice; at most `cap` and kMaxSplits), and the launcher: S > 1 writes
+// the partial products to P [S][M][N] and folds them into a.D with launch_scaled_reduce.
+int64_t w4a8_fp6_splits(int64_t M, int64_t N, int64_t K, int64_t requested, int64_t cap);
+hipError_t launch_w4a8_gemm_prepacked_fp6_split(const W4A8Args& a, const float* Sp, int64_t splits, float* P,
+                                                hipStream_t s);
 hipError_t launch_w4a8_gemm_prepacked_fp6(const W4A8Args& a, const float* Sp, hipStream_t s);
 hipError_t launch_w4a8_prepack(int64_t N, int64_t K, const uint8_t* B, const uint16_t* sB, uint8_t* Bp, float* Sp,
                                hipStream_t s);

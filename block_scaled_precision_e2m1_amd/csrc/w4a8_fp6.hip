@@ -63,8 +63,8 @@ static_assert(F6_STAGES * F6_STAGE <= 160 * 1024, "LDS budget");
 static_assert((F6_STAGES - 2) * F6_LOADS < 64, "vmcnt range");
 
 constexpr int kFmtE3M2 = 3;
-// The activation copies take a 32-bit lane offset of up to 63 rows: 64 * K < 2^31.
-constexpr int64_t kFp6MaxK = int64_t(1) << 24;
+// The activation copies take a 32-bit lane offset of up to 127 rows: 128 * K < 2^31.
+constexpr int64_t kFp6MaxK = int64_t(1) << 23;
 
 __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
@@ -290,6 +290,215 @@ w4a8f6_gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const flo
   }
 }
 
+// ---- 128 x 128 tiles, with an optional split of K ------------------------------------
+// Per K group a 64 x 128 tile copies 24 KB for 8192 outputs; a 128 x 128 tile 32 KB for
+// 16384, so where the copies bound the kernel (a problem with as many 64 x 128 tiles as
+// CUs) the wider tile does the same work with a third fewer copies, and a split of K
+// keeps all CUs busy.  8 waves in a 4 x 2 grid of 32 x 64 wave tiles: wave w owns tokens
+// 32*(w & 3) .. +31 (two FP8 operands) and weight rows 64*(w >> 2) .. +63 (two 32-row
+// quarters, four FP6 operands), 8 instructions per K group.  Per stage each wave copies
+// 16 activation rows (2 KB); wave w also copies, of weight quarter w & 3, both halves'
+// dwords 0-3 (w < 4) or the dwords 4-5 and the quarter's scales (w >= 4).
+// SPLIT: the K groups are cut into S slices of GS groups (the last shorter); work item =
+// tile * S + slice, and the slice's fp32 partial product (without sa) goes to
+// D = P[S][M][N] for launch_scaled_reduce.
+constexpr int F7_BM = 128;
+constexpr int F7_BN = 128;
+constexpr int F7_STAGES = 4;
+constexpr int F7_T_OFF = 0;                // activations: 128 rows x 128 B
+constexpr int F7_W_OFF = F7_BM * 128;      // weights: 4 quarters x 3072 B
+constexpr int F7_S_OFF = F7_W_OFF + 4 * 3072;   // scales: 4 quarters x 1 KB (128 B used)
+constexpr int F7_STAGE = F7_S_OFF + 4 * 1024;
+constexpr int F7_LOADS = 4;                // copies per wave per stage
+static_assert(F7_STAGES * F7_STAGE <= 160 * 1024, "LDS budget");
+static_assert((F7_STAGES - 2) * F7_LOADS < 64, "vmcnt range");
+
+template <bool SPLIT, bool BF16>
+__global__ void __launch_bounds__(512, 1)
+w4a8f6_wide_kernel(int M, int N, int K, int S, int GS, const uint8_t* __restrict__ A,
+                   const float* __restrict__ sa, const uint8_t* __restrict__ Bp, const float* __restrict__ Sp,
+                   void* __restrict__ D) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[F7_STAGES * F7_STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tq = wave & 3, rh = wave >> 2;         // token quarter, weight-row half
+  const int cq = wave & 3, cr = wave >> 2;         // copy quarter, copy role
+  const int r = lane & 15, slot = lane >> 4;
+
+  const int tiles_m = (M + F7_BM - 1) / F7_BM, tiles_n = (N + F7_BN - 1) / F7_BN;
+  const int T = tiles_m * tiles_n * (SPLIT ? S : 1);
+  int lin = blockIdx.x;
+  if ((T & 7) == 0) lin = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  const int slice = SPLIT ? lin % S : 0;
+  if constexpr (SPLIT) lin /= S;
+  const int m0 = (lin % tiles_m) * F7_BM, n0 = (lin / tiles_m) * F7_BN;
+  const int GA = K / 128;
+  const int g0 = SPLIT ? slice * GS : 0;           // this item's groups: g0 .. g0 + G - 1
+  const int G = SPLIT ? min(GS, GA - g0) : GA;
+  const int G32 = (N + 31) / 32;
+  const int64_t Np = 16 * (int64_t)((N + 15) / 16);
+
+  // ---- copy sources (wave-uniform bases plus fixed 32-bit lane offsets; 128 * K < 2^31) ----
+  const uint8_t* ua = A + (int64_t)m0 * K + (int64_t)g0 * 128;
+  uint32_t va[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * (2 * wave + i) + (lane >> 3), u = lane & 7;
+    va[i] = (uint32_t)((min(m0 + row, M - 1) - m0) * K + ((u ^ swz8(row)) << 4));
+  }
+  const uint8_t* ub = Bp + ((int64_t)min(n0 / 32 + cq, G32 - 1) * GA + g0) * 3072 + (cr ? 2048 : 0);
+  const uint32_t vb = (uint32_t)lane * 16;
+  const int64_t srow0 = min((int64_t)n0 + 32 * cq, Np - 4);
+  const uint8_t* us = reinterpret_cast<const uint8_t*>(Sp) + ((int64_t)g0 * Np + srow0) * 4;
+  const uint32_t vs = (uint32_t)(min(srow0 + 4 * (lane & 7), Np - 4) - srow0) * 4;
+  const uint8_t* u2 = cr ? us : ub + 1024;
+  const int64_t step2 = cr ? Np * 4 : 3072;
+  const uint32_t v2 = cr ? vs : vb;
+  const int w1 = F7_W_OFF + cq * 3072 + (cr ? 2048 : 0);
+  const int w2 = cr ? F7_S_OFF + cq * 1024 : w1 + 1024;
+
+  auto issue = [&](int g, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    const int gc = min(g, G - 1);                  // past the end: re-read the last group
+    uint8_t* base = smem + SLOT * F7_STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      lds_copy16(ua + (int64_t)gc * 128 + va[i], (lds_void*)(base + F7_T_OFF + (2 * wave + i) * 1024));
+    lds_copy16(ub + (int64_t)gc * 3072 + vb, (lds_void*)(base + w1));
+    lds_copy16(u2 + (int64_t)gc * step2 + v2, (lds_void*)(base + w2));
+  };
+
+  // acc[q][h][i]: weight quarter 2rh + q, half h (16 rows), token block i (16 tokens);
+  // lane (slot, r) element t holds token 32tq + 16i + 4slot + t and weight row
+  // 64rh + 32q + 16h + r.
+  v4f acc[2][2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[q][h][i] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int unit = 0x7F7F7F7F;
+
+  static_for<0, F7_STAGES - 1>([&](auto p) { issue(p, p); });
+
+  struct Frag { v8i w[2][2]; float s[2][2]; v8i a[2]; };
+  Frag fr[2];
+  v4f part[2][2][2][2];
+  float sc[2][2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sc[1][q][h] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) part[1][q][h][i] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  auto load = [&](auto slot_c, auto set_c) {
+    constexpr int SLOT = decltype(slot_c)::value, SET = decltype(set_c)::value;
+    const uint8_t* base = smem + SLOT * F7_STAGE;
+    Frag& f = fr[SET];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int quarter = 2 * rh + q;
+      const uint8_t* wb = base + F7_W_OFF + quarter * 3072 + lane * 16;
+      const v4i w0 = *reinterpret_cast<const v4i*>(wb);
+      const v4i w1v = *reinterpret_cast<const v4i*>(wb + 1024);
+      const v4i wh = *reinterpret_cast<const v4i*>(wb + 2048);
+      f.w[q][0] = v8i{w0[0], w0[1], w0[2], w0[3], wh[0], wh[1], 0, 0};
+      f.w[q][1] = v8i{w1v[0], w1v[1], w1v[2], w1v[3], wh[2], wh[3], 0, 0};
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        f.s[q][h] = *reinterpret_cast<const float*>(base + F7_S_OFF + quarter * 1024 + (16 * h + r) * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 32 * tq + 16 * i + r;
+      const v4i a0 = *reinterpret_cast<const v4i*>(base + F7_T_OFF + row * 128 + (((2 * slot) ^ swz8(row)) << 4));
+      const v4i a1 = *reinterpret_cast<const v4i*>(base + F7_T_OFF + row * 128 + (((2 * slot + 1) ^ swz8(row)) << 4));
+      f.a[i] = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    }
+  };
+  auto fold = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[q][h][i][t] = __builtin_fmaf(part[buf][q][h][i][t], sc[buf][q][h], acc[q][h][i][t]);
+  };
+
+  auto group = [&](int g, auto j_c) {
+    constexpr int J = decltype(j_c)::value, BUF = J & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(F7_STAGES - 3) * F7_LOADS>();
+    barrier_lds();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(g + F7_STAGES - 1, std::integral_constant<int, (J + F7_STAGES - 1) % F7_STAGES>{});
+    load(std::integral_constant<int, (J + 1) % F7_STAGES>{}, std::integral_constant<int, BUF ^ 1>{});
+    const Frag& f = fr[BUF];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sc[BUF][q][h] = f.s[q][h];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          part[BUF][q][h][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              f.a[i], f.w[q][h], v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8, kFmtE3M2, 0, unit, 0, unit);
+    fold(BUF ^ 1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // a global -> LDS copy
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  wait_vmcnt<(F7_STAGES - 2) * F7_LOADS>();
+  barrier_lds();
+  load(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+  static_assert(F7_STAGES % 2 == 0, "slot parity = buffer parity");
+  int g = 0;
+  for (; g + F7_STAGES <= G; g += F7_STAGES) static_for<0, F7_STAGES>([&](auto j) { group(g + j, j); });
+  static_for<0, F7_STAGES - 1>([&](auto j) {
+    if (g + j < G) group(g + j, j);
+  });
+  if ((G - 1) & 1) fold(1);
+  else fold(0);
+  wait_vmcnt<0>();
+
+  if constexpr (SPLIT) D = static_cast<float*>(D) + (int64_t)slice * M * N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int mb = m0 + 32 * tq + 16 * i + 4 * slot;
+    v4f s4 = v4f{1.f, 1.f, 1.f, 1.f};
+    if constexpr (!SPLIT) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s4[t] = mb + t < M ? sa[mb + t] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = n0 + 64 * rh + 32 * q + 16 * h + r;
+        if (n < N) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (mb + t < M) store_out<SPLIT ? false : BF16>(D, (int64_t)(mb + t) * N + n, acc[q][h][i][t] * s4[t]);
+        }
+      }
+  }
+}
+
 }  // namespace
 
 void w4a8_prepack_fp6_sizes(int64_t N, int64_t K, int64_t* weight_bytes, int64_t* scale_bytes) {
@@ -312,8 +521,66 @@ hipError_t launch_w4a8_prepack_fp6(int64_t N, int64_t K, const uint8_t* B, const
 
 bool w4a8_fp6_fits(int64_t K) { return K <= kFp6MaxK; }
 
+// Groups per K slice for `splits` slices of G groups (at least 2).
+int fp6_slice_groups(int64_t G, int64_t splits) {
+  const int64_t gs = ceil_div(G, splits);
+  return (int)(gs < 2 ? 2 : gs);
+}
+
+int64_t w4a8_fp6_splits(int64_t M, int64_t N, int64_t K, int64_t requested, int64_t cap) {
+  const int64_t G = K / 128;
+  if (M <= 0 || N <= 0 || G < 4) return 1;
+  int64_t S;
+  if (requested > 0) {
+    S = requested;
+  } else {
+    // Split only when even the unsplit kernel's 64 x 128 tiles leave CUs idle (at one
+    // tile per CU the split's reduction costs what its wider tiles save); then enough
+    // slices of 128 x 128 tiles to give every CU an item, each slice at least 8 K groups.
+    const int64_t cus = device_cus();
+    if (ceil_div(M, F6_BM) * ceil_div(N, F6_BN) >= cus) return 1;
+    const int64_t tiles = ceil_div(M, F7_BM) * ceil_div(N, F7_BN);
+    S = ceil_div(cus, tiles);
+    if (S > G / 8) S = G / 8;
+  }
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (S > cap) S = cap;
+  if (S < 2) return 1;
+  return ceil_div(G, fp6_slice_groups(G, S));         // the slices that exist
+}
+
+hipError_t launch_w4a8_gemm_prepacked_fp6_split(const W4A8Args& a, const float* Sp, int64_t splits, float* P,
+                                                hipStream_t s) {
+  if (a.K % 128 != 0 || a.K == 0 || a.M <= 0 || a.N <= 0 || !w4a8_fp6_fits(a.K)) return hipErrorInvalidValue;
+  if (splits <= 1) return launch_w4a8_gemm_prepacked_fp6(a, Sp, s);
+  const int64_t G = a.K / 128;
+  const int GS = fp6_slice_groups(G, splits);
+  const int64_t S = ceil_div(G, GS);
+  if (S > splits || S < 2) return hipErrorInvalidValue;
+  const int64_t items = ceil_div(a.M, F7_BM) * ceil_div(a.N, F7_BN) * S;
+  if (items > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((w4a8f6_wide_kernel<true, false>), dim3((unsigned)items), dim3(512), 0, s, (int)a.M, (int)a.N,
+                     (int)a.K, (int)S, GS, a.A, a.sa, a.B, Sp, static_cast<void*>(P));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_scaled_reduce(1, a.M, a.N, (int)S, P, a.sa, 1.0f, 0, a.D, a.bf16_out, s);
+}
+
 hipError_t launch_w4a8_gemm_prepacked_fp6(const W4A8Args& a, const float* Sp, hipStream_t s) {
   if (a.K % 128 != 0 || a.K == 0 || a.M <= 0 || a.N <= 0 || !w4a8_fp6_fits(a.K)) return hipErrorInvalidValue;
+  // 64 x 128 tiles while they all run at once (one per CU); beyond that 128 x 128 tiles,
+  // which copy a third fewer bytes per output (N = K = 8192, cold weights: M = 384, 512,
+  // 1024, 2048 take 44, 44, 88, 173 us against 58, 56, 114, 226 us).
+  const int64_t wide = ceil_div(a.M, F7_BM) * ceil_div(a.N, F7_BN);
+  if (ceil_div(a.M, F6_BM) * ceil_div(a.N, F6_BN) > device_cus() && wide <= INT32_MAX) {
+    if (a.bf16_out)
+      hipLaunchKernelGGL((w4a8f6_wide_kernel<false, true>), dim3((unsigned)wide), dim3(512), 0, s, (int)a.M, (int)a.N,
+                         (int)a.K, 1, (int)(a.K / 128), a.A, a.sa, a.B, Sp, a.D);
+    else
+      hipLaunchKernelGGL((w4a8f6_wide_kernel<false, false>), dim3((unsigned)wide), dim3(512), 0, s, (int)a.M,
+                         (int)a.N, (int)a.K, 1, (int)(a.K / 128), a.A, a.sa, a.B, Sp, a.D);
+    return hipGetLastError();
+  }
   const int64_t tiles = ceil_div(a.M, F6_BM) * ceil_div(a.N, F6_BN);
   if (tiles > INT32_MAX) return hipErrorInvalidConfiguration;
   if (a.bf16_out)

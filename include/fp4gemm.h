@@ -249,7 +249,14 @@ fp4g_status w4a8_prepack_e4m3(int64_t N, int64_t K, const void *B, const void *s
  *   instruction's results equal those of the FP8 instruction on the one E4M3 value q bit
  *   for bit (measured on gfx950), so the accuracy is w4a8_gemm's for the one-value form:
  *   |D - D_exact| <= 1e-5 * S + H.  A, Bp6 and Sp 16-byte aligned, sa 4-byte; D must
- *   not overlap any input; K > 2^24 is FP4G_EUNSUPPORTED. */
+ *   not overlap any input; K > 2^23 is FP4G_EUNSUPPORTED.
+ * w4a8_gemm_prepacked_fp6_split: the same product with a split of K for problems whose
+ *   tiles cannot fill the GPU (the fp32 partial products of the slices go to `workspace`
+ *   and are then added in slice order and scaled by sa).  `splits` and `workspace` as for
+ *   w4a8_gemm_prepacked_split (a slice keeps at least 2 K groups); the result is
+ *   reproducible bit for bit for a given split and within the same bound.
+ * w4a8_fp6_workspace_size: the workspace bytes the split call takes for these sizes and
+ *   `splits` (0 when it would not split). */
 fp4g_status w4a8_prepack_fp6_size(int64_t N, int64_t K, size_t *weight_bytes, size_t *scale_bytes);
 fp4g_status w4a8_prepack_fp6(int64_t N, int64_t K, const void *B, const void *sB,
                              void *Bp6, void *Sp, void *stream);
@@ -257,6 +264,12 @@ fp4g_status w4a8_gemm_prepacked_fp6(int64_t M, int64_t N, int64_t K,
                                     const void *A, const float *sa,
                                     const void *Bp6, const void *Sp,
                                     void *D, int d_type, void *stream);
+fp4g_status w4a8_fp6_workspace_size(int64_t M, int64_t N, int64_t K, int64_t splits, size_t *bytes);
+fp4g_status w4a8_gemm_prepacked_fp6_split(int64_t M, int64_t N, int64_t K,
+                                          const void *A, const float *sa,
+                                          const void *Bp6, const void *Sp,
+                                          void *D, int d_type, int64_t splits,
+                                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* FP8 blockwise-scaled GEMM, the FP8 starting point of the issue page ("What
  * Works"; "Scale Factor Granularity": FP8 scales cover 128 elements of K):

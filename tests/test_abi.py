@@ -35,7 +35,8 @@ def test_header_declares_the_operations():
                                             "fp4_gemv_prepack", "fp4_gemv_prepacked",
                                             "w4a8_prepack_size", "w4a8_prepack", "w4a8_prepack_e4m3",
                                             "w4a8_gemm_prepacked", "w4a8_prepack_fp6_size", "w4a8_prepack_fp6",
-                                            "w4a8_gemm_prepacked_fp6",
+                                            "w4a8_gemm_prepacked_fp6", "w4a8_fp6_workspace_size",
+                                            "w4a8_gemm_prepacked_fp6_split",
                                             "nv_fp4_gemm_batched", "w4a8_gemm_batched",
                                             "nv_fp4_gemm_workspace_size", "w4a8_gemm_workspace_size",
                                             "nv_fp4_gemm_split", "w4a8_gemm_split", "w4a8_gemm_prepacked_split",
@@ -339,7 +340,18 @@ def test_w4a8_prepack_fp6_validation(lib):
     assert g(4, 16, 128, A_, SA_ + 2, B_, SB_, D_, 1, None) == EALIGN
     assert g(4, 16, 128, A_, SA_, B_, SB_, D_ + 8, 1, None) == EALIGN
     assert g(4, 16, 128, A_, SA_, B_, SB_, B_ + 1024, 1, None) == EINVAL   # D inside Bp6 (3072 B)
-    assert g(4, 16, (1 << 24) + 128, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
+    assert g(4, 16, (1 << 23) + 128, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
+    sp = lib.w4a8_gemm_prepacked_fp6_split
+    assert sp(0, 16, 128, None, None, None, None, None, 1, 0, None, 0, None) == OK
+    assert sp(4, 16, 128, A_, SA_, B_, SB_, D_, 1, -1, None, 0, None) == EINVAL      # negative split
+    assert sp(4, 16, 128, A_, SA_, B_, SB_, D_, 1, 0, None, 64, None) == EINVAL      # bytes without a workspace
+    assert sp(4, 16, 128, A_, SA_, B_, SB_ + 4, D_, 1, 0, None, 0, None) == EALIGN
+    assert sp(4, 16, 256, A_, SA_, B_, SB_, D_, 1, 2, D_ + 8, 4096, None) == EALIGN   # workspace alignment
+    assert sp(4, 16, 256, A_, SA_, B_, SB_, D_, 1, 2, A_, 4096, None) == EINVAL       # workspace over A
+    nb = ctypes.c_size_t(7)
+    assert lib.w4a8_fp6_workspace_size(256, 8192, 8192, 1, ctypes.byref(nb)) == OK and nb.value == 0
+    assert lib.w4a8_fp6_workspace_size(256, 8192, 8192, 0, None) == EINVAL
+    assert lib.w4a8_fp6_workspace_size(256, 8192, 200, 0, ctypes.byref(nb)) == EUNSUP
 
 
 def test_binding_rejects_host_tensors():

@@ -131,3 +131,84 @@ def test_edge_cases():
     Bp6, Sp = fp4.w4a8_prepack_fp6(torch.zeros((20, 64), dtype=torch.uint8, device=DEV),
                                    torch.zeros((20, 1), dtype=torch.bfloat16, device=DEV))
     assert fp4.w4a8_gemm_prepacked_fp6(A, sa, Bp6, Sp, 20).shape == (0, 20)
+
+
+# ---- 128 x 128 tiles: the unsplit wide path (tiles fill the GPU) and the K split ----
+
+WIDE = [(2048, 2048, 256), (2100, 2000, 384)]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", WIDE, ids=[f"{m}x{n}x{k}" for m, n, k in WIDE])
+def test_wide_tiles_full(shape, out):
+    """Problems with at least one 128 x 128 tile per CU run the wide kernel unsplit."""
+    M, N, K = shape
+    print(f"case w4a8 fp6 wide {M}x{N}x{K} {out}", flush=True)
+    d = datagen.make_shape("w4a8", M, N, K, seed=M + N + K)
+    D = run(d, out).float().cpu().numpy().astype(np.float64)
+    ref, S = oracle.w4a8_gemm(d["A"], d["sa"], d["B"], d["sB"])
+    r = oracle.parity_ratio(D, ref, S, out)
+    print(f"  max |err|/tol = {r:.3f}", flush=True)
+    assert r <= 1.0
+
+
+SPLITS = [(64, 200, 2048, 0), (100, 300, 1024, 2), (130, 129, 1536, 3), (256, 512, 4096, 5), (17, 64, 8192, 16),
+          (256, 1000, 640, 0)]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("case", SPLITS, ids=[f"{m}x{n}x{k}_s{s}" for m, n, k, s in SPLITS])
+def test_split(case, out):
+    M, N, K, splits = case
+    print(f"case w4a8 fp6 split {M}x{N}x{K} splits={splits} {out}", flush=True)
+    d = datagen.make_shape("w4a8", M, N, K, seed=M + 5 * N + K)
+    t = up(d)
+    Bp6, Sp = fp4.w4a8_prepack_fp6(t["B"], t["sB"])
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    D = fp4.w4a8_gemm_prepacked_fp6_split(t["A"], t["sa"], Bp6, Sp, N, out_dtype=od, splits=splits)
+    torch.cuda.synchronize(DEV)
+    ref, S = oracle.w4a8_gemm(d["A"], d["sa"], d["B"], d["sB"])
+    r = oracle.parity_ratio(D.float().cpu().numpy().astype(np.float64), ref, S, out)
+    print(f"  max |err|/tol = {r:.3f}", flush=True)
+    assert r <= 1.0
+
+
+def test_split_workload_sampled_and_repeatable():
+    """256 x 8192 x 8192 split in two (the library itself does not split it: its 64 x 128
+    tiles already give every CU one), sampled; repeated calls agree bit for bit."""
+    d = datagen.make("w4a8_256x8192x8192")
+    M, N, K = 256, 8192, 8192
+    assert fp4.w4a8_fp6_workspace_size(M, N, K) == 0
+    assert fp4.w4a8_fp6_workspace_size(M, N, K, 2) == 2 * M * N * 4
+    t = up(d)
+    Bp6, Sp = fp4.w4a8_prepack_fp6(t["B"], t["sB"])
+    D1 = fp4.w4a8_gemm_prepacked_fp6_split(t["A"], t["sa"], Bp6, Sp, N, out_dtype=torch.bfloat16, splits=2)
+    D2 = fp4.w4a8_gemm_prepacked_fp6_split(t["A"], t["sa"], Bp6, Sp, N, out_dtype=torch.bfloat16, splits=2)
+    torch.cuda.synchronize(DEV)
+    assert torch.equal(D1, D2)
+    rng = np.random.default_rng(6)
+    ms = np.concatenate([rng.integers(0, M, 20000), np.full(N, 127), np.full(N, 128), np.arange(M)])
+    ns = np.concatenate([rng.integers(0, N, 20000), np.arange(N), np.arange(N), np.full(M, 8191)])
+    Dn = D1[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)].float().cpu().numpy().astype(np.float64)
+    ref, S = oracle.sampled("w4a8", d, ms, ns)
+    r = oracle.parity_ratio(Dn, ref, S, "bf16")
+    print(f"  max |err|/tol = {r:.3f}", flush=True)
+    assert r <= 1.0
+
+
+def test_split_small_workspace_and_wide_activations():
+    """A workspace for two slices caps a request for eight; activations over every binade
+    stay within 1e-5 * S + H through the split."""
+    M, N, K = 96, 160, 2048
+    rng = np.random.default_rng(8)
+    d = datagen.make_shape("w4a8", M, N, K, seed=8)
+    d["A"] = rng.choice(np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8), (M, K))
+    H = oracle.fp8_truncation_bound("w4a8", d, split=False)
+    t = up(d)
+    Bp6, Sp = fp4.w4a8_prepack_fp6(t["B"], t["sB"])
+    ws = torch.empty(2 * M * N * 4, dtype=torch.uint8, device=DEV)
+    D = fp4.w4a8_gemm_prepacked_fp6_split(t["A"], t["sa"], Bp6, Sp, N, out_dtype=torch.float32, splits=8,
+                                          workspace=ws)
+    torch.cuda.synchronize(DEV)
+    ref, S = oracle.w4a8_gemm(d["A"], d["sa"], d["B"], d["sB"])
+    assert oracle.parity_ratio(D.cpu().numpy().astype(np.float64), ref, S, "f32", extra=H) <= 1.0
