@@ -20,8 +20,9 @@
 //
 // Structure: one workgroup per BM x BN tile, 4 or 8 waves of WM x WN; 128 K elements
 // (64 packed bytes, two scale dwords) per row per step; packed tiles are prefetched
-// into registers two steps ahead while the MFMAs of the current step run;
-// LDS rows are 256 bytes (128 fp16) with 16-byte chunks XOR-swizzled by row.
+// into registers two steps ahead; a step reads all its fragments, folds the next step
+// while they land, then runs its MFMAs; LDS rows are 256 bytes (128 fp16) with 16-byte
+// chunks XOR-swizzled by row.
 #include <type_traits>
 
 #include "common.hpp"
@@ -131,37 +132,40 @@ nvfp4_gemm_kernel(int M, int N, int K, int S, int KS, const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < FJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int st) {
+  // Step kt: all fragments of LDS buffer kt&1 are read into registers; while they land,
+  // step kt+1 is folded from register buffer (kt+1)&1 into the other LDS buffer and step
+  // kt+3 is fetched into that register buffer; then the step's MFMAs run.
+  auto step = [&](int kt, auto rb_c) {
+    __syncthreads();
+    const int st = kt & 1;
+    v8h af[4][FI], bf[4][FJ];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
       const int chunk = 4 * sub + slot;
-      v8h af[FI], bf[FJ];
 #pragma unroll
       for (int i = 0; i < FI; ++i) {
         const int row = wm * WM + i * 16 + r16;
-        af[i] = *reinterpret_cast<const v8h*>(&lds[st][row * kRowH + ((chunk ^ swz16(row)) << 4)]);
+        af[sub][i] = *reinterpret_cast<const v8h*>(&lds[st][row * kRowH + ((chunk ^ swz16(row)) << 4)]);
       }
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
         const int row = BM + wn * WN + j * 16 + r16;
-        bf[j] = *reinterpret_cast<const v8h*>(&lds[st][row * kRowH + ((chunk ^ swz16(row)) << 4)]);
+        bf[sub][j] = *reinterpret_cast<const v8h*>(&lds[st][row * kRowH + ((chunk ^ swz16(row)) << 4)]);
       }
-#pragma unroll
-      for (int i = 0; i < FI; ++i)
-#pragma unroll
-        for (int j = 0; j < FJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-  };
-  // Step kt: the MFMAs of LDS buffer kt&1; then step kt+1 is folded from register
-  // buffer (kt+1)&1 into the other LDS buffer, and step kt+3 is fetched into it.
-  auto step = [&](int kt, auto rb_c) {
-    __syncthreads();
-    compute(kt & 1);
+    __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < KT) {
       store_lds((kt + 1) & 1, rb_c);
       load_global(kt + 3, rb_c);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[sub][i], bf[sub][j], acc[i][j], 0, 0, 0);
   };
   const std::integral_constant<int, 0> R0{};
   const std::integral_constant<int, 1> R1{};
