@@ -262,7 +262,7 @@ int64_t nvfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t re
 }
 
 hipError_t launch_nvfp4_gemm_split(const FP4Args& a, int64_t splits, float* P, hipStream_t s) {
-  if (nvfp4_gemv_fits(a.M, a.K)) return launch_nvfp4_gemv(a, s);         // decode: a 16-token tile
+  if (nvfp4_gemv_fits(a.M, a.K)) return launch_nvfp4_gemv(a, s);         // decode: 16-token tiles
   if (splits > 1 && !P) return hipErrorInvalidValue;
   const int64_t S = splits > 1 ? splits : 1;
   if (nv_big_tiles(a.L, a.M, a.N)) return launch_cfg<128, 128, 64, 64>(a, S, P, s);

@@ -1,4 +1,4 @@
-// NVFP4 decode GEMV for gfx950: D[M][N] for 1 <= M <= 16 tokens, the NVFP4 product of
+// NVFP4 decode GEMV for gfx950: D[M][N] for 1 <= M <= 32 tokens, the NVFP4 product of
 // the GEMM,
 //   D[m][n] = gA * gB * sum_k e2m1(A[m,k]) e4m3(sfA[m,k/16]) * e2m1(B[n,k]) e4m3(sfB[n,k/16])
 // with one E4M3 scale per 16 K elements (the NVFP4 setup of the NVIDIA/cutlass issue "Add
@@ -9,7 +9,9 @@
 // kernel (the Hopper CUTLASS/CuTe DSL post, section "What changes in the W4A8 builder":
 // a 16-token tile for decode), 16 weight rows fill the first operand of the matrix
 // instruction and the tokens sit in the other, zero past M: accumulator lane l holds rows
-// n = 4*(l/16)+t of one 16-row weight group and token m = l%16.
+// n = 4*(l/16)+t of one 16-row weight group and token m = l%16 of a 16-token tile.  With
+// 17 to 32 tokens a second token tile multiplies the same folded weights, so each weight
+// is still read and folded once.
 //
 // gfx950 has no E4M3-per-16 block scale in its scaled FP4 instruction, so both operands
 // are folded exactly to fp16 (nv_fold.hpp) and multiplied by v_mfma_f32_16x16x32_f16
@@ -45,7 +47,7 @@ constexpr int kMaxGroups = 128;             // K <= 16384: 8 waves x 16 groups
 
 __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
-template <int NJ, int RG, bool BF16>
+template <int NJ, int RG, int TT, bool BF16>
 __global__ void __launch_bounds__(WAVES * 64)
 nvfp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
                   const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, float gscale, int gexp,
@@ -57,7 +59,8 @@ nvfp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   constexpr int SDW = RG * 16 * SROW / 4;    // scale dwords per wave
   constexpr int SC = (SDW + 63) / 64;        // dword copies (whole 256-byte copies)
   constexpr int WBYTES = SOFF + SC * 256;
-  constexpr int RED = WAVES * RG * 64 * 16;
+  constexpr int RED = WAVES * RG * TT * 64 * 16;
+  static_assert(TT == 1 || TT == 2, "token tiles");
   static_assert(WAVES * WBYTES <= 160 * 1024 && RED <= WAVES * WBYTES, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[WAVES * WBYTES];
 
@@ -78,9 +81,11 @@ nvfp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   }
   uint8_t* wl = lds + wave * WBYTES;
 
-  v4f acc[RG];
+  v4f acc[RG][TT];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int u = 0; u < TT; ++u) acc[g][u] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // One wave's segment.  FULL: all ST groups lie inside K and all rows inside N (every
   // wave but those at a ragged edge), so no address is clamped and no group masked.
@@ -92,15 +97,18 @@ nvfp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
     // ---- tokens of the segment: 16 bytes of codes and the two scale bytes of a lane's
     // 32 elements per group.  Lanes r >= M read token 0 (the same lines as lanes r = 0):
     // their columns of the product are never stored. ----
-    const int64_t trow = r < M ? r : 0;
-    v4i tc[ST];
-    uint32_t tsc[ST];
+    v4i tc[TT][ST];
+    uint32_t tsc[TT][ST];
 #pragma unroll
-    for (int s = 0; s < ST; ++s) {
-      const int ks = kc(ks0 + s);
-      tc[s] = *reinterpret_cast<const v4i*>(A + trow * ld + (int64_t)ks * 64 + slot * 16);
-      // the dword holding this lane's two scale bytes (halves: slots 2j, 2j+1)
-      tsc[s] = *reinterpret_cast<const uint32_t*>(sfA + trow * lsc + ks * 8 + (slot >> 1) * 4);
+    for (int u = 0; u < TT; ++u) {
+      const int64_t trow = 16 * u + r < M ? 16 * u + r : 0;
+#pragma unroll
+      for (int s = 0; s < ST; ++s) {
+        const int ks = kc(ks0 + s);
+        tc[u][s] = *reinterpret_cast<const v4i*>(A + trow * ld + (int64_t)ks * 64 + slot * 16);
+        // the dword holding this lane's two scale bytes (halves: slots 2j, 2j+1)
+        tsc[u][s] = *reinterpret_cast<const uint32_t*>(sfA + trow * lsc + ks * 8 + (slot >> 1) * 4);
+      }
     }
 
     // ---- weight scales: dword j of row `row` (scale bytes 4j..4j+3 of the segment) ->
@@ -145,7 +153,7 @@ nvfp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, ST / 2>([&](auto p_c) {
       constexpr int p = decltype(p_c)::value;
-      v8h ta[2][4];                                   // the pair's folded tokens
+      v8h ta[TT][2][4];                               // the pair's folded tokens
       static_for<0, RG>([&](auto g_c) {
         constexpr int g = decltype(g_c)::value;
         __builtin_amdgcn_sched_barrier(0);   // token and scale uses stay after the wait
@@ -155,20 +163,23 @@ nvfp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
         for (int h = 0; h < 2; ++h) {
           const int s = 2 * p + h;
           if (g == 0) {
-            float p0, p1;
-            h2 m0, m1;
-            const uint32_t t2 = tsc[s] >> (16 * (slot & 1));
-            e4m3_split(t2 & 0xFFu, &p0, &m0);
-            e4m3_split((t2 >> 8) & 0xFFu, &p1, &m1);
-            if (!FULL && ks0 + s >= KT) {             // a group past K adds nothing
-              m0 = h2{0, 0};
-              m1 = h2{0, 0};
-            }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              uint32_t o[4];
-              fold8((uint32_t)tc[s][q], q < 2 ? p0 : p1, q < 2 ? m0 : m1, o);
-              ta[h][q] = __builtin_bit_cast(v8h, v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]});
+            for (int u = 0; u < TT; ++u) {
+              float p0, p1;
+              h2 m0, m1;
+              const uint32_t t2 = tsc[u][s] >> (16 * (slot & 1));
+              e4m3_split(t2 & 0xFFu, &p0, &m0);
+              e4m3_split((t2 >> 8) & 0xFFu, &p1, &m1);
+              if (!FULL && ks0 + s >= KT) {           // a group past K adds nothing
+                m0 = h2{0, 0};
+                m1 = h2{0, 0};
+              }
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                uint32_t o[4];
+                fold8((uint32_t)tc[u][s][q], q < 2 ? p0 : p1, q < 2 ? m0 : m1, o);
+                ta[u][h][q] = __builtin_bit_cast(v8h, v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]});
+              }
             }
           }
           const int row = 16 * g + r;
@@ -184,7 +195,9 @@ nvfp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
             uint32_t o[4];
             fold8((uint32_t)x[q], q < 2 ? p0 : p1, q < 2 ? m0 : m1, o);
             const v8h wv = __builtin_bit_cast(v8h, v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]});
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, ta[h][q], acc[g], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < TT; ++u)
+              acc[g][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, ta[u][h][q], acc[g][u], 0, 0, 0);
           }
         }
       });
@@ -195,16 +208,19 @@ nvfp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
 
   // ---- sum the WAVES partial tiles in wave order, scale by gA*gB, store D[m][n] ----
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);   // [WAVES][RG][64 lanes][4]
+  float* red = reinterpret_cast<float*>(lds);   // [WAVES][RG * TT][64 lanes][4]
 #pragma unroll
-  for (int g = 0; g < RG; ++g) *reinterpret_cast<v4f*>(red + ((wave * RG + g) * 64 + lane) * 4) = acc[g];
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int u = 0; u < TT; ++u)
+      *reinterpret_cast<v4f*>(red + ((wave * RG * TT + g * TT + u) * 64 + lane) * 4) = acc[g][u];
   __syncthreads();
-  if (threadIdx.x < RG * 64) {
-    const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int m = l & 15;
-    v4f v = *reinterpret_cast<const v4f*>(red + (g * 64 + l) * 4);
+  if (threadIdx.x < RG * TT * 64) {
+    const int gu = threadIdx.x >> 6, l = threadIdx.x & 63;   // gu = g * TT + u
+    const int g = gu / TT, m = 16 * (gu % TT) + (l & 15);
+    v4f v = *reinterpret_cast<const v4f*>(red + (gu * 64 + l) * 4);
 #pragma unroll
-    for (int w2 = 1; w2 < WAVES; ++w2) v += *reinterpret_cast<const v4f*>(red + ((w2 * RG + g) * 64 + l) * 4);
+    for (int w2 = 1; w2 < WAVES; ++w2) v += *reinterpret_cast<const v4f*>(red + ((w2 * RG * TT + gu) * 64 + l) * 4);
     const int64_t n = n0 + 16 * g + 4 * (l >> 4);
     if (m < M && n < N) {
       const int avail = (int)min((int64_t)4, (int64_t)N - n);
@@ -215,23 +231,37 @@ nvfp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint
   }
 }
 
-template <int NJ, int RG>
-hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
+template <int NJ, int RG, int TT>
+hipError_t launch_tiles(const FP4Args& a, hipStream_t s) {
   const int64_t g64 = ceil_div(a.N, 16 * RG);
   if (g64 > INT32_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)g64, (unsigned)a.L), block(WAVES * 64);
   if (a.bf16_out)
-    hipLaunchKernelGGL((nvfp4_gemv_kernel<NJ, RG, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K, a.A,
+    hipLaunchKernelGGL((nvfp4_gemv_kernel<NJ, RG, TT, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K, a.A,
                        a.sfA, a.B, a.sfB, a.gscale, a.gscale_exp, a.D);
   else
-    hipLaunchKernelGGL((nvfp4_gemv_kernel<NJ, RG, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K, a.A,
-                       a.sfA, a.B, a.sfB, a.gscale, a.gscale_exp, a.D);
+    hipLaunchKernelGGL((nvfp4_gemv_kernel<NJ, RG, TT, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
+                       a.A, a.sfA, a.B, a.sfB, a.gscale, a.gscale_exp, a.D);
   return hipGetLastError();
+}
+
+template <int NJ, int RG>
+hipError_t launch_cfg(const FP4Args& a, hipStream_t s) {
+  if (a.M <= 16) return launch_tiles<NJ, RG, 1>(a, s);
+  // Two token tiles keep their tokens in registers: up to 8 groups per wave (K <= 8192),
+  // which nvfp4_gemv_fits admits.
+  if constexpr (NJ <= 2) return launch_tiles<NJ, RG, 2>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool nvfp4_gemv_fits(int64_t M, int64_t K) { return M >= 1 && M <= 16 && K >= 128 && K / 128 <= kMaxGroups; }
+bool nvfp4_gemv_fits(int64_t M, int64_t K) {
+  const int64_t G = K / 128;
+  if (M < 1 || K < 128) return false;
+  if (M <= 16) return G <= kMaxGroups;
+  return M <= 32 && G <= WAVES * 8;                   // two token tiles (launch_cfg)
+}
 
 hipError_t launch_nvfp4_gemv(const FP4Args& a, hipStream_t s) {
   if (!nvfp4_gemv_fits(a.M, a.K) || a.K % 128 != 0) return hipErrorInvalidValue;

@@ -210,7 +210,7 @@ hipError_t launch_cfg(const W4A8Args& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t s) {
-  if (w4a8_gemv_fits(a.M, a.K)) return launch_w4a8_gemv(a, nullptr, s);   // decode: a 16-token tile
+  if (w4a8_gemv_fits(a.M, a.K)) return launch_w4a8_gemv(a, nullptr, s);   // decode: 16-token tiles
   // The ring kernel of the pre-packed path also takes plain weights when the bf16 group
   // scales of a row pair up into aligned dwords: K % 256 == 0 (the C ABI already
   // requires sB to be 4-byte aligned; the check keeps the kernel's assumption local).

@@ -1,4 +1,4 @@
-// W4A8 decode GEMV for gfx950: D[M][N] for 1 <= M <= 16 tokens, the same product as
+// W4A8 decode GEMV for gfx950: D[M][N] for 1 <= M <= 32 tokens, the same product as
 // the W4A8 GEMM,
 //   D[m][n] = sa[m] * sum_g sB[n][g] * sum_{k in g} e4m3(A[m][k]) * int4(B[n][k]),
 // K groups of 128 elements.
@@ -9,7 +9,9 @@
 // same four definitions, with the operands swapped") the weights fill the 16-row slot
 // of the FP8 16x16x128 instruction and the tokens sit in the other slot, zero past M.
 // The product computed is D^T = B * A^T: accumulator lane l holds rows n = 4*(l/16)+t
-// of one 16-row weight group and token m = l%16.
+// of one 16-row weight group and token m = l%16 of a 16-token tile.  With 17 to 32 tokens
+// a second token tile multiplies the same converted weights (two more instructions per
+// group), so each weight is still read and converted once.
 //
 // gfx950 mapping (K <= 16384, the decode shapes), as in the MXFP4 GEMV:
 //   * one workgroup of 8 waves per RG groups of 16 weight rows; wave w owns the ST
@@ -65,7 +67,7 @@ __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) <<
 // rows of scales are not dword aligned).
 constexpr int kSclPacked = 0, kSclPairs = 1, kSclSingle = 2;
 
-template <int NJ, int RG, int QG, int SCL, bool BF16>
+template <int NJ, int RG, int QG, int SCL, int TT, bool BF16>
 __global__ void __launch_bounds__(WAVES * 64)
 w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sa,
                  const uint8_t* __restrict__ Bw, const void* __restrict__ Sw, void* __restrict__ D) {
@@ -79,7 +81,8 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
   constexpr int PAIR_COPIES = (RG * ST * 8 + 63) / 64;
   constexpr int SBYTES = PACKED ? NC * 64 : SCL == kSclPairs ? PAIR_COPIES * 256 : 0;
   constexpr int WBYTES = SOFF + SBYTES;
-  constexpr int RED = WAVES * RG * 64 * 16;
+  constexpr int RED = WAVES * RG * TT * 64 * 16;
+  static_assert(TT == 1 || TT == 2, "token tiles");
   static_assert(WAVES * WBYTES <= 160 * 1024 && RED <= WAVES * WBYTES, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[WAVES * WBYTES];
 
@@ -103,9 +106,11 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
   // 16 or 32 units the row index itself.
   auto swz = [](int row) { return QG == 2 ? swz8(row) : (row & 15); };
 
-  v4f acc[RG];
+  v4f acc[RG][TT];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int u = 0; u < TT; ++u) acc[g][u] = v4f{0.f, 0.f, 0.f, 0.f};
   // One wave's segment.  FULL: all ST groups lie inside K and all rows inside N (every
   // wave but those at a ragged edge), so no address is clamped and no scale masked.
   auto segment = [&](auto full_c) {
@@ -117,13 +122,16 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
     // FULL: no address needs clamping, so each load is a base plus a constant offset.
     auto kc = [&](int ks, int last) { return FULL ? ks : min(ks, last); };
     auto rc = [&](int64_t row, int64_t last) { return FULL ? row : min(row, last); };
-    const int64_t trow = r < M ? r : 0;
-    v4i t0[ST], t1[ST];
+    v4i t0[TT][ST], t1[TT][ST];
 #pragma unroll
-    for (int s = 0; s < ST; ++s) {
-      const uint8_t* p = A + trow * K + (int64_t)ks0 * 128 + slot * 32 + (int64_t)(kc(ks0 + s, KT - 1) - ks0) * 128;
-      t0[s] = *reinterpret_cast<const v4i*>(p);
-      t1[s] = *reinterpret_cast<const v4i*>(p + 16);
+    for (int u = 0; u < TT; ++u) {
+      const int64_t trow = 16 * u + r < M ? 16 * u + r : 0;
+#pragma unroll
+      for (int s = 0; s < ST; ++s) {
+        const uint8_t* p = A + trow * K + (int64_t)ks0 * 128 + slot * 32 + (int64_t)(kc(ks0 + s, KT - 1) - ks0) * 128;
+        t0[u][s] = *reinterpret_cast<const v4i*>(p);
+        t1[u][s] = *reinterpret_cast<const v4i*>(p + 16);
+      }
     }
 
     // ---- group scales ----
@@ -219,7 +227,7 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
     // one row group.
     static_for<0, ST / QG>([&](auto b_c) {
       constexpr int b = decltype(b_c)::value;
-      v8i tv[QG];
+      v8i tv[TT][QG];
       static_for<0, RG>([&](auto g_c) {
         constexpr int g = decltype(g_c)::value;
         __builtin_amdgcn_sched_barrier(0);   // token and scale uses stay after the wait
@@ -235,12 +243,14 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
             // then high); pre-packed weights are already in K order (element j | element
             // j+4 << 4).
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const v4i& tq = w < 2 ? t0[s] : t1[s];
-              const uint32_t x0 = (uint32_t)tq[2 * (w & 1)], x1 = (uint32_t)tq[2 * (w & 1) + 1];
-              tv[j][2 * w] = (int)(PACKED ? x0 : __builtin_amdgcn_perm(x1, x0, 0x06040200u));
-              tv[j][2 * w + 1] = (int)(PACKED ? x1 : __builtin_amdgcn_perm(x1, x0, 0x07050301u));
-            }
+            for (int u = 0; u < TT; ++u)
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                const v4i& tq = w < 2 ? t0[u][s] : t1[u][s];
+                const uint32_t x0 = (uint32_t)tq[2 * (w & 1)], x1 = (uint32_t)tq[2 * (w & 1) + 1];
+                tv[u][j][2 * w] = (int)(PACKED ? x0 : __builtin_amdgcn_perm(x1, x0, 0x06040200u));
+                tv[u][j][2 * w + 1] = (int)(PACKED ? x1 : __builtin_amdgcn_perm(x1, x0, 0x07050301u));
+              }
           }
           v4i x;
           v4f sc;
@@ -274,12 +284,15 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
             bs[2 * w] = (int)((lo & 0x08080808u) | k80);
             bs[2 * w + 1] = (int)((hi & 0x08080808u) | k80);
           }
-          v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, tv[j], v4f{0.f, 0.f, 0.f, 0.f}, kFmtFp8,
-                                                                      kFmtFp8, 0, kScale2p9, 0, unit);
-          part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bs, tv[j], part, kFmtFp8, kFmtFp8, 0, kScale2p9, 0,
-                                                                 unit);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[g][t] = __builtin_fmaf(part[t], ok ? sc[t] : 0.0f, acc[g][t]);
+          for (int u = 0; u < TT; ++u) {
+            v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, tv[u][j], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                        kFmtFp8, kFmtFp8, 0, kScale2p9, 0, unit);
+            part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bs, tv[u][j], part, kFmtFp8, kFmtFp8, 0,
+                                                                   kScale2p9, 0, unit);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[g][u][t] = __builtin_fmaf(part[t], ok ? sc[t] : 0.0f, acc[g][u][t]);
+          }
         }
       });
     });
@@ -289,16 +302,19 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
 
   // ---- sum the WAVES partial tiles in wave order, scale by sa[m], store D[m][n] ----
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);   // [WAVES][RG][64 lanes][4]
+  float* red = reinterpret_cast<float*>(lds);   // [WAVES][RG * TT][64 lanes][4]
 #pragma unroll
-  for (int g = 0; g < RG; ++g) *reinterpret_cast<v4f*>(red + ((wave * RG + g) * 64 + lane) * 4) = acc[g];
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int u = 0; u < TT; ++u)
+      *reinterpret_cast<v4f*>(red + ((wave * RG * TT + g * TT + u) * 64 + lane) * 4) = acc[g][u];
   __syncthreads();
-  if (threadIdx.x < RG * 64) {
-    const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int m = l & 15;
-    v4f v = *reinterpret_cast<const v4f*>(red + (g * 64 + l) * 4);
+  if (threadIdx.x < RG * TT * 64) {
+    const int gu = threadIdx.x >> 6, l = threadIdx.x & 63;   // gu = g * TT + u
+    const int g = gu / TT, m = 16 * (gu % TT) + (l & 15);
+    v4f v = *reinterpret_cast<const v4f*>(red + (gu * 64 + l) * 4);
 #pragma unroll
-    for (int w2 = 1; w2 < WAVES; ++w2) v += *reinterpret_cast<const v4f*>(red + ((w2 * RG + g) * 64 + l) * 4);
+    for (int w2 = 1; w2 < WAVES; ++w2) v += *reinterpret_cast<const v4f*>(red + ((w2 * RG * TT + gu) * 64 + l) * 4);
     const int64_t n = n0 + 16 * g + 4 * (l >> 4);
     if (m < M && n < N) {
       const float s = sa[m];
@@ -308,18 +324,27 @@ w4a8_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const float
   }
 }
 
-template <int NJ, int RG, int QG, int SCL>
-hipError_t launch_cfg(const W4A8Args& a, const void* S, hipStream_t s) {
+template <int NJ, int RG, int QG, int SCL, int TT>
+hipError_t launch_tiles(const W4A8Args& a, const void* S, hipStream_t s) {
   const int64_t g64 = ceil_div(a.N, 16 * RG);
   if (g64 > INT32_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)g64, SCL == kSclPacked ? 1u : (unsigned)a.L), block(WAVES * 64);
   if (a.bf16_out)
-    hipLaunchKernelGGL((w4a8_gemv_kernel<NJ, RG, QG, SCL, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
-                       a.A, a.sa, a.B, S, a.D);
+    hipLaunchKernelGGL((w4a8_gemv_kernel<NJ, RG, QG, SCL, TT, true>), grid, block, 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, a.A, a.sa, a.B, S, a.D);
   else
-    hipLaunchKernelGGL((w4a8_gemv_kernel<NJ, RG, QG, SCL, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
-                       a.A, a.sa, a.B, S, a.D);
+    hipLaunchKernelGGL((w4a8_gemv_kernel<NJ, RG, QG, SCL, TT, false>), grid, block, 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, a.A, a.sa, a.B, S, a.D);
   return hipGetLastError();
+}
+
+template <int NJ, int RG, int QG, int SCL>
+hipError_t launch_cfg(const W4A8Args& a, const void* S, hipStream_t s) {
+  if (a.M <= 16) return launch_tiles<NJ, RG, QG, SCL, 1>(a, S, s);
+  // Two token tiles keep their tokens in registers: up to 8 groups per wave with the
+  // scales in LDS (K <= 8192, K/128 even; 178-186 registers), which w4a8_gemv_fits admits.
+  if constexpr (NJ <= 2 && SCL != kSclSingle) return launch_tiles<NJ, RG, QG, SCL, 2>(a, S, s);
+  return hipErrorInvalidValue;
 }
 
 template <int SCL>
@@ -335,7 +360,12 @@ hipError_t launch_shape(const W4A8Args& a, const void* S, hipStream_t s) {
 
 }  // namespace
 
-bool w4a8_gemv_fits(int64_t M, int64_t K) { return M >= 1 && M <= 16 && K >= 128 && K / 128 <= kMaxGroups; }
+bool w4a8_gemv_fits(int64_t M, int64_t K) {
+  const int64_t G = K / 128;
+  if (M < 1 || K < 128) return false;
+  if (M <= 16) return G <= kMaxGroups;
+  return M <= 32 && G <= WAVES * 8 && G % 2 == 0;     // two token tiles (launch_cfg)
+}
 
 hipError_t launch_w4a8_gemv(const W4A8Args& a, const float* Sp, hipStream_t s) {
   if (!w4a8_gemv_fits(a.M, a.K) || a.K % 128 != 0) return hipErrorInvalidValue;

@@ -407,7 +407,7 @@ hipError_t launch_w4a8_ring(const W4A8Args& a, hipStream_t s) { return launch_bm
 
 int64_t w4a8_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, bool packed, int64_t requested, int64_t cap) {
   const int64_t G = K / 128;
-  // Only the ring kernel splits: not the decode kernel (M <= 16 fills the chip by rows)
+  // Only the ring kernel splits: not the decode kernel (M <= 32 fills the chip by rows)
   // and not the plain-weight kernel for K % 256 != 0.
   if (L * M * N == 0 || w4a8_gemv_fits(M, K) || (!packed && K % 256 != 0) || G < 4) return 1;
   int64_t smax = G / 2 < kMaxSplits ? G / 2 : kMaxSplits;
@@ -436,7 +436,7 @@ int64_t w4a8_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, bool packed
 }
 
 hipError_t launch_w4a8_gemm_split(const W4A8Args& a, const float* Sp, int64_t splits, float* P, hipStream_t s) {
-  if (w4a8_gemv_fits(a.M, a.K)) return launch_w4a8_gemv(a, Sp, s);       // decode: a 16-token tile
+  if (w4a8_gemv_fits(a.M, a.K)) return launch_w4a8_gemv(a, Sp, s);       // decode: 16-token tiles
   if (splits > 1 && !P) return hipErrorInvalidValue;
   // 64-token tiles: two workgroups share a CU (79 KB of LDS, at most 256 registers).
   if (Sp) return launch_bm<64, true>(a, Sp, splits, P, s);

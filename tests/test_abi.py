@@ -402,6 +402,9 @@ def test_split_validation(lib):
     for f in (lib.nv_fp4_gemm_workspace_size, lib.w4a8_gemm_workspace_size):
         assert f(1, 64, 8192, 8192, 1, ctypes.byref(n)) == OK and n.value == 0     # never splits
         assert f(1, 16, 8192, 8192, 0, ctypes.byref(n)) == OK and n.value == 0     # decode kernel
+        assert f(1, 32, 8192, 8192, 4, ctypes.byref(n)) == OK and n.value == 0     # two token tiles
+        assert f(1, 33, 8192, 8192, 4, ctypes.byref(n)) == OK and n.value == 4 * 33 * 8192 * 4
+        assert f(1, 17, 8192, 8448, 2, ctypes.byref(n)) == OK and n.value == 2 * 17 * 8192 * 4   # K > 8192
         assert f(1, 64, 8192, 8192, 4, ctypes.byref(n)) == OK and n.value == 4 * 64 * 8192 * 4
         assert f(1, 64, 8192, 256, 16, ctypes.byref(n)) == OK and n.value <= 2 * 64 * 8192 * 4
         assert f(1, 64, 64, 1024, -1, ctypes.byref(n)) == EINVAL

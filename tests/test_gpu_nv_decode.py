@@ -1,11 +1,13 @@
-"""GPU parity of the NVFP4 decode path: with 1 <= M <= 16 tokens and K <= 16384,
-nv_fp4_gemm and nv_fp4_gemm_batched run the 16-token decode kernel (weights in the
-16-row slot, both operands folded exactly to fp16, fp32 accumulation).
+"""GPU parity of the NVFP4 decode path: with 1 <= M <= 16 tokens and K <= 16384, and
+with 17 <= M <= 32 tokens and K <= 8192, nv_fp4_gemm and nv_fp4_gemm_batched run the
+decode kernel (weights in the 16-row slot, tokens in one or two 16-token tiles, both
+operands folded exactly to fp16, fp32 accumulation).
 
 Bar: the oracle module's parity rule, fp32 |D - D_exact| <= 1e-5 * S (bf16: plus one
 bf16 ulp).  Shapes cover each segment configuration of the kernel (K <= 4096, <= 8192,
 <= 16384), ragged K (groups past K inside a wave's segment), ragged N (row groups past
-N), every M from 1 to 16, and the boundaries to the GEMM kernel (M = 17, K = 16512);
+N), every M from 1 to 32, and the boundaries to the GEMM kernel (M = 33; M = 17 with
+K = 8320; K = 16512);
 scales cover every finite E4M3 code (subnormals and negative codes), NaN codes, and
 global scales whose product leaves fp32.
 """
@@ -50,7 +52,7 @@ def make(M, N, K, seed, gA=1.0, gB=1.0):
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
-@pytest.mark.parametrize("M", [1, 8, 16])
+@pytest.mark.parametrize("M", [1, 8, 16, 17, 32])
 def test_decode_8192_full(M, out):
     """M decode tokens against an 8192 x 8192 NVFP4 weight, every output."""
     print(f"case nv decode {M}x8192x8192 {out} seed {M}", flush=True)
@@ -59,7 +61,8 @@ def test_decode_8192_full(M, out):
 
 SHAPES = [(1, 1, 128), (2, 17, 256), (3, 40, 384), (16, 64, 1024), (5, 100, 4096), (9, 33, 4224),
           (16, 300, 6016), (4, 48, 8192), (12, 250, 8320), (16, 129, 12288), (6, 31, 16384),
-          (8, 14336, 4096)]
+          (8, 14336, 4096), (17, 40, 256), (20, 100, 4096), (32, 64, 1024), (25, 129, 6144),
+          (31, 33, 8192), (18, 300, 2432)]
 
 
 @pytest.mark.parametrize("g", [(1.0, 1.0), (2.0, -0.375)])
@@ -70,22 +73,23 @@ def test_decode_shapes(shape, g):
     check(make(M, N, K, M + 3 * N + K, *g), "f32")
 
 
-@pytest.mark.parametrize("M", list(range(1, 17)))
+@pytest.mark.parametrize("M", list(range(1, 33)))
 def test_every_token_count(M):
     print(f"case nv decode M={M} 70x1152", flush=True)
     check(make(M, 70, 1152, 200 + M), "bf16")
 
 
-@pytest.mark.parametrize("MK", [(17, 1024), (16, 16512)])
+@pytest.mark.parametrize("MK", [(32, 1024), (33, 1024), (17, 8192), (17, 8320), (16, 16512)])
 def test_boundaries_to_the_gemm_kernel(MK):
     M, K = MK
     print(f"case nv decode boundary {M}x96x{K}", flush=True)
     check(make(M, 96, K, M + K), "f32")
 
 
-def test_decode_full_scale_range_including_subnormals():
+@pytest.mark.parametrize("M", [12, 28])
+def test_decode_full_scale_range_including_subnormals(M):
     rng = np.random.default_rng(31)
-    d = make(12, 80, 2048, 31)
+    d = make(M, 80, 2048, 31)
     d["sfA"] = rng.integers(0, 0x7F, d["sfA"].shape, dtype=np.uint8)
     d["sfB"] = (rng.integers(0, 0x7F, d["sfB"].shape, dtype=np.uint8) |
                 (rng.integers(0, 2, d["sfB"].shape, dtype=np.uint8) << 7))
@@ -114,10 +118,11 @@ def test_decode_global_scales_whose_product_leaves_fp32(case):
         check(d, out)
 
 
-def test_decode_nan_scale_codes():
+@pytest.mark.parametrize("M", [8, 24])
+def test_decode_nan_scale_codes(M):
     """A NaN scale code makes every product of its block NaN: the token rows and weight
     columns that meet it come out NaN, the rest stay finite."""
-    d = make(8, 40, 4224, 41)
+    d = make(M, 40, 4224, 41)
     d["sfA"][3, 2] = 0x7F
     d["sfB"][7, 5] = 0xFF
     d["sfB"][9, 4223 // 16] = 0x7F       # in the last group: the one a ragged segment re-reads
@@ -129,8 +134,9 @@ def test_decode_nan_scale_codes():
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_decode_batched(out):
-    L, M, N, K = 3, 8, 200, 4224
+@pytest.mark.parametrize("M", [8, 20])
+def test_decode_batched(M, out):
+    L, N, K = 3, 200, 4224
     print(f"case nv decode batched L={L} {M}x{N}x{K} {out}", flush=True)
     ds = [make(M, N, K, 50 + b, 2.0, 0.5) for b in range(L)]
     t = {k: torch.stack([up(d)[k] for d in ds]) for k in ("A", "sfA", "B", "sfB")}
@@ -142,8 +148,9 @@ def test_decode_batched(out):
         assert oracle.parity_ratio(D[b], ref, S, out) <= 1.0
 
 
-def test_decode_is_run_to_run_identical():
-    d = make(16, 1000, 8192, 9)
+@pytest.mark.parametrize("M", [16, 32])
+def test_decode_is_run_to_run_identical(M):
+    d = make(M, 1000, 8192, 9)
     t = up(d)
     D1 = fp4.nv_fp4_gemm(t["A"], t["sfA"], 1.0, t["B"], t["sfB"], 1.0, out_dtype=torch.float32)
     D2 = fp4.nv_fp4_gemm(t["A"], t["sfA"], 1.0, t["B"], t["sfB"], 1.0, out_dtype=torch.float32)

@@ -1,6 +1,7 @@
-"""GPU parity of the W4A8 decode path: with 1 <= M <= 16 tokens and K <= 16384,
-w4a8_gemm, w4a8_gemm_batched and w4a8_gemm_prepacked run the 16-token decode kernel
-(weights in the 16-row slot of the FP8 instruction, tokens padded to 16).
+"""GPU parity of the W4A8 decode path: with 1 <= M <= 16 tokens and K <= 16384, and with
+17 <= M <= 32 tokens, K <= 8192 and K/128 even, w4a8_gemm, w4a8_gemm_batched and
+w4a8_gemm_prepacked run the decode kernel (weights in the 16-row slot of the FP8
+instruction, tokens padded to one or two 16-token tiles).
 
 Bar: the oracle module's parity rule, fp32 |D - D_exact| <= 1e-5 * S (bf16: plus one
 bf16 ulp) on the workload's activation distribution, and 1e-5 * S + H, H the FP8
@@ -8,7 +9,8 @@ instruction's truncation bound for the decode kernel's two exact weight parts (s
 the subnormal code v * 2^-9 and the sign part), on activations spread over every
 binade.  Shapes cover each segment configuration of the kernel
 (K <= 4096, <= 8192, <= 16384), ragged K (groups past K inside a wave's segment),
-ragged N (row groups past N), and the boundaries to the 64-token kernel (M = 17,
+ragged N (row groups past N), both token tiles (every M from 1 to 32), and the
+boundaries to the 64-token kernel (M = 33; M = 17 with K = 8320 or K/128 odd;
 K = 16512).
 """
 import numpy as np
@@ -55,7 +57,7 @@ def check(d, out, extra=None):
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
-@pytest.mark.parametrize("M", [1, 8, 16])
+@pytest.mark.parametrize("M", [1, 8, 16, 17, 32])
 def test_decode_workload_full(M, out):
     """The W4A8 workload's weights (N = K = 8192) with M decode tokens, every output."""
     print(f"case w4a8 decode {M}x8192x8192 {out} seed {M}", flush=True)
@@ -65,7 +67,8 @@ def test_decode_workload_full(M, out):
 
 SHAPES = [(1, 1, 128), (2, 17, 256), (3, 40, 384), (16, 64, 1024), (5, 100, 4096), (9, 33, 4224),
           (16, 300, 6016), (4, 48, 8192), (12, 250, 8320), (16, 129, 12288), (6, 31, 16384),
-          (11, 14336, 4096)]
+          (11, 14336, 4096), (17, 40, 256), (20, 100, 4096), (32, 64, 1024), (25, 129, 6144),
+          (31, 33, 8192), (18, 300, 2304)]
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
@@ -77,17 +80,19 @@ def test_decode_shapes(shape, out):
     check(d, out)
 
 
-@pytest.mark.parametrize("M", list(range(1, 17)))
+@pytest.mark.parametrize("M", list(range(1, 33)))
 def test_every_token_count(M):
-    """Each M from 1 to 16: lanes r >= M carry zero tokens and are not stored."""
-    print(f"case w4a8 decode M={M} 70x1152", flush=True)
-    d = datagen.make_shape("w4a8", M, 70, 1152, seed=100 + M)
+    """Each M from 1 to 32: lanes whose token is past M read token 0 and are not stored
+    (from M = 17 in the second token tile)."""
+    print(f"case w4a8 decode M={M} 70x1280", flush=True)
+    d = datagen.make_shape("w4a8", M, 70, 1280, seed=100 + M)
     check(d, "f32")
 
 
-@pytest.mark.parametrize("MK", [(17, 1024), (16, 16512)])
+@pytest.mark.parametrize("MK", [(32, 1024), (33, 1024), (17, 8192), (17, 8448), (17, 1152), (16, 16512)])
 def test_boundaries_to_the_gemm_kernel(MK):
-    """M = 17 and K = 16512 leave the decode kernel; both sides of each boundary meet the bar."""
+    """M = 33, M = 17 with K = 8448 (66 groups) or K = 1152 (an odd group count) and
+    K = 16512 leave the decode kernel; both sides of each boundary meet the bar."""
     M, K = MK
     print(f"case w4a8 decode boundary {M}x96x{K}", flush=True)
     d = datagen.make_shape("w4a8", M, 96, K, seed=M + K)
@@ -95,12 +100,13 @@ def test_boundaries_to_the_gemm_kernel(MK):
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-@pytest.mark.parametrize("K", [1024, 6016])
-def test_decode_activations_over_every_binade(K, out):
+@pytest.mark.parametrize("MK", [(16, 1024), (16, 6016), (32, 2048)])
+def test_decode_activations_over_every_binade(MK, out):
     """Activation codes spread over all binades inside every run of 8: the instruction
     truncates, and the decode kernel (two exact weight parts, v as a subnormal code)
     stays within 1e-5 S + H."""
-    M, N = 16, 96
+    M, K = MK
+    N = 96
     rng = np.random.default_rng(K + (out == "bf16"))
     d = datagen.make_shape("w4a8", M, N, K, seed=K + 1)
     d["A"] = rng.choice(np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8), (M, K))
@@ -111,9 +117,10 @@ def test_decode_activations_over_every_binade(K, out):
     check(d, out, extra=H)
 
 
-def test_decode_int4_extremes_and_signed_scales():
+@pytest.mark.parametrize("M", [8, 24])
+def test_decode_int4_extremes_and_signed_scales(M):
     """All -8 / 7 weights (both ends of the conversion), negative group and token scales."""
-    M, N, K = 8, 80, 2048
+    N, K = 80, 2048
     rng = np.random.default_rng(21)
     d = datagen.make_shape("w4a8", M, N, K, seed=21)
     q = np.where(rng.integers(0, 2, (N, K)) > 0, 7, 8).astype(np.uint8)
@@ -126,9 +133,11 @@ def test_decode_int4_extremes_and_signed_scales():
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_decode_batched(out):
-    """w4a8_gemm_batched with M <= 16: problem b on grid row b."""
-    L, M, N, K = 3, 8, 200, 4224
+@pytest.mark.parametrize("MK", [(8, 4224), (20, 4352)])
+def test_decode_batched(MK, out):
+    """w4a8_gemm_batched with M <= 32: problem b on grid row b."""
+    L, N = 3, 200
+    M, K = MK
     print(f"case w4a8 decode batched L={L} {M}x{N}x{K} {out}", flush=True)
     ds = [datagen.make_shape("w4a8", M, N, K, seed=40 + b) for b in range(L)]
     ts = [up(d) for d in ds]
@@ -156,8 +165,9 @@ def test_scales_without_vector_alignment():
         assert oracle.parity_ratio(as_np(D), ref, S, "f32") <= 1.0
 
 
-def test_decode_is_run_to_run_identical():
-    d = datagen.make_shape("w4a8", 16, 1000, 8192, seed=9)
+@pytest.mark.parametrize("M", [16, 32])
+def test_decode_is_run_to_run_identical(M):
+    d = datagen.make_shape("w4a8", M, 1000, 8192, seed=9)
     t = up(d)
     D1 = fp4.w4a8_gemm(t["A"], t["sa"], t["B"], t["sB"], out_dtype=torch.float32)
     D2 = fp4.w4a8_gemm(t["A"], t["sa"], t["B"], t["sB"], out_dtype=torch.float32)
