@@ -283,7 +283,8 @@ def mx_fp4_gemm_batched_noalloc(A, sfA, B, sfB, out, splits=0):
 
 
 def fp4_gemv(A, sfA, B, sfB, out=None, out_dtype=torch.bfloat16):
-    """MXFP4 GEMV for 1 <= M <= 16 tokens (same layouts as mx_fp4_gemm)."""
+    """MXFP4 GEMV for 1 <= M <= 16 tokens, or 17 <= M <= 32 with K <= 16384 (same layouts
+    as mx_fp4_gemm)."""
     lib, dev, M, N, K, D, dt = _fp4_common("fp4_gemv", 32, A, sfA, B, sfB, out, out_dtype)
     st = lib.fp4_gemv(M, N, K, _ptr(A), _ptr(sfA), _ptr(B), _ptr(sfB), _ptr(D), dt, _stream(dev))
     _raise_on("fp4_gemv", st)

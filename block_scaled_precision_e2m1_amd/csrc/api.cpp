@@ -69,7 +69,7 @@ fp4g_status run_fp4(int which, int64_t M, int64_t N, int64_t K, const void* A, c
   bool empty = false;
   fp4g_status st = check_common(M, N, K, d_type, D, &empty);
   if (st != FP4G_OK || empty) return st;
-  if (which == 2 && M > 16) return FP4G_EUNSUPPORTED;
+  if (which == 2 && !fp4g::fp4_gemv_fits(M, K)) return FP4G_EUNSUPPORTED;
   st = check_fp4_operands(M, N, K, V, A, sfA, B, sfB, D, d_type);
   if (st != FP4G_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -551,7 +551,7 @@ const char* fp4g_status_string(int status) {
   switch (status) {
     case FP4G_OK: return "ok";
     case FP4G_EINVAL: return "invalid argument (null pointer, negative size, bad output type or D overlapping an input)";
-    case FP4G_EUNSUPPORTED: return "unsupported shape (K must be a multiple of 128, of 32 for the MX quantizer, of 16 for the NV quantizer; GEMV needs M <= 16)";
+    case FP4G_EUNSUPPORTED: return "unsupported shape (K must be a multiple of 128, of 32 for the MX quantizer, of 16 for the NV quantizer; GEMV needs M <= 16, or M <= 32 with K <= 8192; the pre-packed GEMV M <= 16)";
     case FP4G_EALIGN: return "misaligned pointer (operands and D need 16-byte, scales 4-byte alignment)";
     case FP4G_EHIP: return "HIP runtime error at kernel launch";
     default: return "unknown status";

@@ -1,4 +1,4 @@
-// MXFP4 GEMV for decode: D[M][N] with 1 <= M <= 16 tokens, the same block-scaled
+// MXFP4 GEMV for decode: D[M][N] with 1 <= M <= 32 tokens, the same block-scaled
 // E2M1 x E8M0 product as the GEMM (section 1 of the cuda-oxide page "TMA
 // Pipelines, Tensor Cores, and ctm-rs Interop"; its "Where to Go Next" table
 // lists the MXFP4 GEMV as a workload of its own).
@@ -8,7 +8,8 @@
 // post (section "The W4A8 kernel: the same four definitions, with the operands
 // swapped"): 16 weight rows fill the 16-row slot of the MFMA and the tokens sit
 // in the other slot, zero past M.  The product computed is D^T = B * A^T; its
-// accumulator lane l holds D^T rows 4*(l/16)+t, column l%16.
+// accumulator lane l holds D^T rows 4*(l/16)+t, column l%16 of a 16-token tile.  With 17
+// to 32 tokens (K <= 16384) a second token tile multiplies the same weight fragments.
 //
 // gfx950 mapping (K <= 16384, the decode shapes):
 //   * one workgroup of 8 waves per RG groups of 16 weight rows; wave w owns the K
@@ -36,7 +37,7 @@ namespace {
 
 constexpr int WAVES = 8;
 
-template <int NJ, int RG, bool COOP, bool BF16>
+template <int NJ, int RG, int TT, bool COOP, bool BF16>
 __global__ void __launch_bounds__(WAVES * 64)
 fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
                 const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, void* __restrict__ D) {
@@ -49,7 +50,8 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
   constexpr int WBYTES = ROWS * SEG;     // LDS bytes per wave
   static_assert(UPR >= 16 && UPR <= 64 && 64 % UPR == 0, "segment shape");
   static_assert(WAVES * WBYTES <= 160 * 1024, "LDS budget");
-  static_assert(WAVES * RG * 64 * 4 * 4 <= WAVES * WBYTES, "reduction fits in the weight area");
+  static_assert(WAVES * RG * TT * 64 * 4 * 4 <= WAVES * WBYTES, "reduction fits in the weight area");
+  static_assert(TT == 1 || TT == 2, "token tiles");
   constexpr int SCL = COOP ? ROWS * ST * WAVES * 4 : 16;   // the workgroup's scale rows (K / 32 bytes each)
   static_assert(WAVES * WBYTES + SCL <= 160 * 1024, "LDS budget");
   // The cooperative copy gives each wave at most one 1 KB piece of the scale rows.
@@ -65,9 +67,8 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
   const int ks0 = wave * ST;
   uint8_t* wl = lds + wave * WBYTES;
 
-  // ---- tokens of this wave's segment (lanes r >= M and steps past K get zeros) ----
-  const bool tok = r < M;
-  const int64_t trow = tok ? r : 0;
+  // ---- tokens of this wave's segment (lanes whose token is past M, and steps past K,
+  // get zeros); tile u holds tokens 16u .. 16u+15 ----
   // Scale words of 4 consecutive steps are one 16-byte load when the segment lies
   // inside the row and rows of scales are 16-byte multiples (K % 512 == 0).
   const bool vec_scales = (K & 511) == 0;
@@ -81,26 +82,37 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
       for (int u = 0; u < 4; ++u) dst[u] = *reinterpret_cast<const int*>(rowp + min(ks + u, KT - 1) * 4);
     }
   };
-  v4i t[ST];
-  int ts[ST];
-  if (M <= 8) {
+  v4i t[TT][ST];
+  int ts[TT][ST];
+  bool tok[TT];
+  int64_t trow[TT];
+#pragma unroll
+  for (int u = 0; u < TT; ++u) {
+    tok[u] = 16 * u + r < M;
+    trow[u] = tok[u] ? 16 * u + r : 0;
+  }
+  if (TT == 1 && M <= 8) {
     // Lanes r >= 8 would only hold zeros: let them fetch the next step of token r-8,
     // then rotate each 16-lane row by 8 (DPP row_ror:8) to move it into lanes 0..7.
     const int64_t prow = min(r & 7, M - 1);
 #pragma unroll
     for (int s = 0; s < ST; s += 2) {
       const int ks = min(ks0 + s + (r >> 3), KT - 1);
-      t[s] = *reinterpret_cast<const v4i*>(A + prow * ld + (int64_t)ks * 64 + slot * 16);
+      t[0][s] = *reinterpret_cast<const v4i*>(A + prow * ld + (int64_t)ks * 64 + slot * 16);
     }
   } else {
 #pragma unroll
-    for (int s = 0; s < ST; ++s) {
-      const int ks = min(ks0 + s, KT - 1);
-      t[s] = *reinterpret_cast<const v4i*>(A + trow * ld + (int64_t)ks * 64 + slot * 16);
-    }
+    for (int u = 0; u < TT; ++u)
+#pragma unroll
+      for (int s = 0; s < ST; ++s) {
+        const int ks = min(ks0 + s, KT - 1);
+        t[u][s] = *reinterpret_cast<const v4i*>(A + trow[u] * ld + (int64_t)ks * 64 + slot * 16);
+      }
   }
 #pragma unroll
-  for (int q = 0; q < ST / 4; ++q) load_words(sfA + trow * lsc, q, ts + 4 * q);
+  for (int u = 0; u < TT; ++u)
+#pragma unroll
+    for (int q = 0; q < ST / 4; ++q) load_words(sfA + trow[u] * lsc, q, ts[u] + 4 * q);
 
   // ---- weight copies: copy i covers rows i*RPI .. i*RPI+RPI-1 of the segment ----
   {
@@ -151,45 +163,52 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
     }
   }
 
-  if (M <= 8) {
+  if (TT == 1 && M <= 8) {
 #pragma unroll
     for (int s = 0; s < ST; s += 2) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[s + 1][e] = __builtin_amdgcn_mov_dpp(t[s][e], 0x128, 0xF, 0xF, false);
+      for (int e = 0; e < 4; ++e) t[0][s + 1][e] = __builtin_amdgcn_mov_dpp(t[0][s][e], 0x128, 0xF, 0xF, false);
     }
   }
 #pragma unroll
-  for (int s = 0; s < ST; ++s) {
-    const bool ok = tok && ks0 + s < KT;
-    ts[s] = ok ? (ts[s] >> (8 * slot)) & 255 : 127;
-    if (!ok) t[s] = v4i{0, 0, 0, 0};
-  }
+  for (int u = 0; u < TT; ++u)
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+      const bool ok = tok[u] && ks0 + s < KT;
+      ts[u][s] = ok ? (ts[u][s] >> (8 * slot)) & 255 : 127;
+      if (!ok) t[u][s] = v4i{0, 0, 0, 0};
+    }
 
-  v4f acc[RG];
+  v4f acc[RG][TT];
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
-    acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
     const int row = 16 * g + r;
+#pragma unroll
+    for (int u = 0; u < TT; ++u) acc[g][u] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < ST; ++s) {
       const v4i w = *reinterpret_cast<const v4i*>(wl + row * SEG + (((s * 4 + slot) ^ (row & 15)) * 16));
       const int wsc = ks0 + s < KT ? (ws[g][s] >> (8 * slot)) & 255 : 127;
-      acc[g] = mfma_fp4_16x16<0>(w, t[s], acc[g], wsc, ts[s]);
+#pragma unroll
+      for (int u = 0; u < TT; ++u) acc[g][u] = mfma_fp4_16x16<0>(w, t[u][s], acc[g][u], wsc, ts[u][s]);
     }
   }
 
   // ---- sum the WAVES partial tiles in wave order, store D[m][n] ----
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);   // [WAVES][RG][64 lanes][4]
+  float* red = reinterpret_cast<float*>(lds);   // [WAVES][RG * TT][64 lanes][4]
 #pragma unroll
-  for (int g = 0; g < RG; ++g) *reinterpret_cast<v4f*>(red + ((wave * RG + g) * 64 + lane) * 4) = acc[g];
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int u = 0; u < TT; ++u)
+      *reinterpret_cast<v4f*>(red + ((wave * RG * TT + g * TT + u) * 64 + lane) * 4) = acc[g][u];
   __syncthreads();
-  if (threadIdx.x < RG * 64) {
-    const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int m = l & 15;
-    v4f v = *reinterpret_cast<const v4f*>(red + (g * 64 + l) * 4);
+  if (threadIdx.x < RG * TT * 64) {
+    const int gu = threadIdx.x >> 6, l = threadIdx.x & 63;   // gu = g * TT + u
+    const int g = gu / TT, m = 16 * (gu % TT) + (l & 15);
+    v4f v = *reinterpret_cast<const v4f*>(red + (gu * 64 + l) * 4);
 #pragma unroll
-    for (int w2 = 1; w2 < WAVES; ++w2) v += *reinterpret_cast<const v4f*>(red + ((w2 * RG + g) * 64 + l) * 4);
+    for (int w2 = 1; w2 < WAVES; ++w2) v += *reinterpret_cast<const v4f*>(red + ((w2 * RG * TT + gu) * 64 + l) * 4);
     const int64_t n = n0 + 16 * g + 4 * (l >> 4);
     if (m < M && n < N) {
       const int avail = (int)min((int64_t)4, (int64_t)N - n);
@@ -264,16 +283,16 @@ fp4_gemv_long_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const u
   }
 }
 
-template <int NJ, int RG, bool COOP>
+template <int NJ, int RG, int TT, bool COOP>
 hipError_t launch_segmented(const FP4Args& a, hipStream_t s) {
   const int64_t g64 = ceil_div(a.N, 16 * RG);
   if (g64 > INT32_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)g64), block(WAVES * 64);
   if (a.bf16_out)
-    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, COOP, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
+    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, TT, COOP, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
                        a.A, a.sfA, a.B, a.sfB, a.D);
   else
-    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, COOP, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
+    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, TT, COOP, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
                        a.A, a.sfA, a.B, a.sfB, a.D);
   return hipGetLastError();
 }
@@ -282,12 +301,19 @@ template <int NJ, int RG>
 hipError_t launch_segmented(const FP4Args& a, hipStream_t s) {
   // Cooperative scale copies need 16-byte aligned scale rows and whole segments.
   const bool coop = a.K % (WAVES * 4 * NJ * 128) == 0 && (reinterpret_cast<uintptr_t>(a.sfB) & 15) == 0;
-  return coop ? launch_segmented<NJ, RG, true>(a, s) : launch_segmented<NJ, RG, false>(a, s);
+  if (a.M <= 16) return coop ? launch_segmented<NJ, RG, 1, true>(a, s) : launch_segmented<NJ, RG, 1, false>(a, s);
+  // A second token tile keeps its tokens in registers: up to 16 steps per wave (K <= 16384).
+  if constexpr (NJ <= 4)
+    return coop ? launch_segmented<NJ, RG, 2, true>(a, s) : launch_segmented<NJ, RG, 2, false>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+bool fp4_gemv_fits(int64_t M, int64_t K) { return M >= 1 && (M <= 16 || (M <= 32 && K <= WAVES * 16 * 128)); }
+
 hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s) {
+  if (!fp4_gemv_fits(a.M, a.K)) return hipErrorInvalidValue;
   const int64_t KT = a.K / 128;
   // Segment of ST = 4*NJ steps per wave, WAVES segments per row: K <= WAVES*ST*128.
   if (KT <= WAVES * 4) return launch_segmented<1, 2>(a, s);     // K <= 4096: 32 rows per workgroup

@@ -62,13 +62,16 @@ hipError_t launch_mxfp4_gemm_batched(const FP4Args& a, int64_t L, int64_t S, flo
 int64_t mxfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t requested, int64_t cap);
 hipError_t launch_nvfp4_gemm(const FP4Args& a, hipStream_t s);
 // K-split NVFP4: nvfp4_gemm_splits gives the slice count S the launcher uses (as for
-// w4a8_gemm_splits); with S > 1 the partial products go to P [L][S][M][N].  M <= 16 runs
-// the decode kernel (no split, P unused).
+// w4a8_gemm_splits); with S > 1 the partial products go to P [L][S][M][N].  Shapes the
+// decode kernel takes (nvfp4_gemv_fits) run it (no split, P unused).
 int64_t nvfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t requested, int64_t cap);
 hipError_t launch_nvfp4_gemm_split(const FP4Args& a, int64_t splits, float* P, hipStream_t s);
-// NVFP4 decode GEMV for 1 <= M <= 16 tokens and K <= 16384 (nvfp4_gemv_fits); batch a.L.
+// NVFP4 decode GEMV for 1 <= M <= 16 tokens and K <= 16384, or 17 <= M <= 32 and
+// K <= 8192 (nvfp4_gemv_fits); batch a.L.
 bool nvfp4_gemv_fits(int64_t M, int64_t K);
 hipError_t launch_nvfp4_gemv(const FP4Args& a, hipStream_t s);
+// MXFP4 decode GEMV (L = 1) for 1 <= M <= 16 tokens, or 17 <= M <= 32 and K <= 8192.
+bool fp4_gemv_fits(int64_t M, int64_t K);
 hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s);
 // Pre-packed decode weights: sizes, the load-time re-pack, and the GEMV over them
 // (a.B is the packed weight buffer; Sp the packed scale dwords).
@@ -105,14 +108,16 @@ hipError_t launch_w4a8_ring(const W4A8Args& a, hipStream_t s);
 // the slice count S the launcher uses (`requested` slices if > 0, else its own choice;
 // at most `cap` and kMaxSplits); with S > 1 the partial products go to the fp32 buffer
 // P [L][S][M][N] and launch_scaled_reduce folds them into a.D.  Sp non-null: pre-packed
-// weights (L = 1).  M <= 16 runs the decode kernel (no split, P unused).
+// weights (L = 1).  Shapes the decode kernel takes (w4a8_gemv_fits) run it (no split,
+// P unused).
 int64_t w4a8_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, bool packed, int64_t requested, int64_t cap);
 hipError_t launch_w4a8_gemm_split(const W4A8Args& a, const float* Sp, int64_t splits, float* P, hipStream_t s);
 // D[b][m][n] = ldexp((sum_s P[b][s][m][n]) * (rs ? rs[b][m] : 1) * gm, ge), slices in order.
 hipError_t launch_scaled_reduce(int64_t L, int64_t M, int64_t N, int S, const float* P, const float* rs, float gm,
                                 int ge, void* D, bool bf16_out, hipStream_t s);
-// Decode GEMV for 1 <= M <= 16 tokens and K <= 16384 (w4a8_gemv_fits): weights in the
-// 16-row slot of the FP8 instruction, tokens padded to 16.  Sp null: plain weights and
+// Decode GEMV for 1 <= M <= 16 tokens and K <= 16384, or 17 <= M <= 32, K <= 8192 and
+// K/128 even (w4a8_gemv_fits): weights in the 16-row slot of the FP8 instruction, tokens
+// padded to one or two 16-token tiles.  Sp null: plain weights and
 // bf16 scales (a.B, a.sB, batch a.L); otherwise a.B is the pre-packed weight buffer and
 // Sp its fp32 scales.
 bool w4a8_gemv_fits(int64_t M, int64_t K);

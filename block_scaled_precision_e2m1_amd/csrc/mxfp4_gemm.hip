@@ -536,6 +536,14 @@ hipError_t launch_reduce(const FP4Args& a, int64_t L, int S, const float* P, hip
 // K stages of the 128 x 128 configuration that the split path uses.
 int64_t split_stages(int64_t K) { return K % 256 == 0 ? K / 256 : K / 128; }
 
+// One problem of a few tokens runs the decode GEMV instead of the GEMM tiles: 1 to 32
+// tokens where fp4_gemv takes them and K >= 4096.  Measured against the GEMM with its
+// automatic K split (cold weights, M = 1 ... 32): 7.5-10.0 against 13.6-15.3 us at
+// N = 14336, K = 4096; 4.7-6.3 against 9.6-11.1 us at N = K = 4096; 9.1-15.7 against
+// 14.5-15.9 us at N = K = 8192; at K = 1024 the GEMM was faster (4.5-5.2 against
+// 4.8-7.4 us at N = 2048).
+bool decode_route(int64_t L, int64_t M, int64_t K) { return L == 1 && K >= 4096 && fp4_gemv_fits(M, K); }
+
 }  // namespace
 
 int64_t mxfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t requested, int64_t cap) {
@@ -544,6 +552,7 @@ int64_t mxfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t re
   if (cap < smax) smax = cap;
   if (smax < 2 || L * M * N == 0) return 1;
   if (requested > 0) return requested < smax ? requested : smax;
+  if (decode_route(L, M, K)) return 1;
   // Automatic choice.  Problems that already fill the chip with 256 x 256 tiles are not
   // split.  Otherwise model the time of the 128 x 128 path as (rounds of work items over
   // the CUs) x (stages per item + a fixed cost per item) plus the reduction's HBM
@@ -565,6 +574,7 @@ int64_t mxfp4_gemm_splits(int64_t L, int64_t M, int64_t N, int64_t K, int64_t re
 }
 
 hipError_t launch_mxfp4_gemm_batched(const FP4Args& a, int64_t L, int64_t S, float* P, hipStream_t s) {
+  if (S <= 1 && decode_route(L, a.M, a.K)) return launch_fp4_gemv(a, s);
   const bool k256 = a.K % 256 == 0;
   if (S > 1) {
     hipError_t e;

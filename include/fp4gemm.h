@@ -61,7 +61,8 @@ extern "C" {
 typedef enum {
     FP4G_OK = 0,
     FP4G_EINVAL = 1,       /* null pointer, negative or too large size, bad enum, D overlaps an input */
-    FP4G_EUNSUPPORTED = 2, /* K not a multiple of 128 (of 32 for the quantizer), or GEMV with M > 16 */
+    FP4G_EUNSUPPORTED = 2, /* K not a multiple of 128 (of 32 for the quantizer), or GEMV with M > 32
+                              (M > 16 with K > 16384; the pre-packed GEMV M > 16) */
     FP4G_EALIGN = 3,       /* operand / output not 16-byte aligned, scales not 4-byte aligned */
     FP4G_EHIP = 4          /* the HIP runtime rejected the launch */
 } fp4g_status;
@@ -82,7 +83,10 @@ typedef enum {
 } fp4g_in;
 
 /* MXFP4 GEMM: V = 32, E8M0 scales.
- *   A [M][K/2], sfA [M][K/32], B [N][K/2], sfB [N][K/32], D [M][N] of d_type. */
+ *   A [M][K/2], sfA [M][K/32], B [N][K/2], sfB [N][K/32], D [M][N] of d_type.
+ * With 1 <= M <= 32 in fp4_gemv's range and K >= 4096 (also mx_fp4_gemm_batched with
+ * L = 1 and its automatic split) it runs the decode GEMV kernel; the result bar is the
+ * same. */
 fp4g_status mx_fp4_gemm(int64_t M, int64_t N, int64_t K,
                         const void *A, const void *sfA,
                         const void *B, const void *sfB,
@@ -290,13 +294,15 @@ fp4g_status fp8_blockwise_gemm(int64_t M, int64_t N, int64_t K,
                                const void *B, const float *sB,
                                void *D, int d_type, void *stream);
 
-/* MXFP4 GEMV for decode (few tokens): the MXFP4 GEMM with 1 <= M <= 16 and the
- * same layouts, tuned for streaming the weight operand B once from HBM.  The cute-rs
- * page lists the MXFP4 GEMV among its next steps ("Where to Go Next"); the Hopper
- * CUTLASS/CuTe DSL blog post sizes the token tile from 16 for this decode regime and
- * swaps the operands so the weights fill the instruction's wide side (sections "What
+/* MXFP4 GEMV for decode (few tokens): the MXFP4 GEMM with 1 <= M <= 16 (any K), or
+ * 17 <= M <= 32 with K <= 16384 (a second 16-token tile over the same weight fragments),
+ * and the same layouts, tuned for streaming the weight operand B once from HBM.  The
+ * cute-rs page lists the MXFP4 GEMV among its next steps ("Where to Go Next"); the
+ * Hopper CUTLASS/CuTe DSL blog post sizes the token tile from 16 for this decode regime
+ * and swaps the operands so the weights fill the instruction's wide side (sections "What
  * changes in the W4A8 builder" and "The W4A8 kernel: the same four definitions, with
- * the operands swapped").  M > 16 returns FP4G_EUNSUPPORTED. */
+ * the operands swapped").  Other M (or M > 16 with K > 16384) return
+ * FP4G_EUNSUPPORTED. */
 fp4g_status fp4_gemv(int64_t M, int64_t N, int64_t K,
                      const void *A, const void *sfA,
                      const void *B, const void *sfB,

@@ -122,7 +122,9 @@ def test_empty_outputs_are_noops(lib):
 
 
 def test_gemv_token_limit(lib):
-    assert lib.fp4_gemv(17, 64, 128, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
+    # 1..16 tokens at any K, 17..32 tokens at K <= 16384 (the second token tile)
+    assert lib.fp4_gemv(33, 64, 128, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
+    assert lib.fp4_gemv(17, 64, 16512, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
     assert lib.fp4_gemv(4, 64, 96, A_, SA_, B_, SB_, D_, 1, None) == EUNSUP
 
 
@@ -261,6 +263,8 @@ def test_workspace_size(lib):
     assert f(1, 64, 64, 8192, 100, ctypes.byref(n)) == OK and n.value == 16 * 64 * 64 * 4   # clamped
     assert f(1, 64, 64, 640, 100, ctypes.byref(n)) == OK and n.value == 5 * 64 * 64 * 4     # K/128 stages
     assert f(1, 8192, 8192, 8192, 0, ctypes.byref(n)) == OK and n.value == 0     # fills the GPU
+    assert f(1, 32, 8192, 4096, 0, ctypes.byref(n)) == OK and n.value == 0       # the decode GEMV
+    assert f(1, 32, 8192, 4096, 4, ctypes.byref(n)) == OK and n.value == 4 * 32 * 8192 * 4   # asked to split
     assert f(1, 64, 8192, 8192, 0, ctypes.byref(n)) == OK
     assert n.value > 0 and n.value % (64 * 8192 * 4) == 0 and n.value <= 16 * 64 * 8192 * 4
 

@@ -272,7 +272,23 @@ def test_gemv_decode_workload_full():
     check_full("gemv", d, "bf16")
 
 
-@pytest.mark.parametrize("M", [1, 3, 8, 13, 16])
+@pytest.mark.parametrize("M", [17, 32])
+def test_gemv_two_token_tiles_workload_weights(M):
+    """The decode workload's weight shape (N = 14336, K = 4096) with 17 and 32 tokens:
+    the second token tile, every output."""
+    d = datagen.make_shape("gemv", M, 14336, 4096, seed=M, dist="gaussian")
+    print(f"case gemv {M}x14336x4096", flush=True)
+    check_full("gemv", d, "bf16")
+
+
+def test_gemv_every_token_count_to_32():
+    """Each M from 1 to 32 on one shape (lanes whose token is past M are not stored)."""
+    for M in range(1, 33):
+        d = datagen.make_shape("gemv", M, 70, 1152, seed=300 + M)
+        check_full("gemv", d, "f32")
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 13, 16, 17, 24, 32])
 @pytest.mark.parametrize("NK", [(1, 128), (17, 384), (1000, 256), (4101, 1152)])
 def test_gemv_shapes(M, NK):
     N, K = NK
@@ -281,10 +297,11 @@ def test_gemv_shapes(M, NK):
 
 
 @pytest.mark.parametrize("MNK", [(8, 300, 5120), (16, 257, 8192), (5, 130, 14336), (3, 70, 16384),
-                                 (8, 40, 16512), (16, 1000, 4096), (1, 33, 12800)])
+                                 (8, 40, 16512), (16, 1000, 4096), (1, 33, 12800), (20, 300, 5120),
+                                 (32, 257, 8192), (17, 130, 14336), (29, 70, 16384), (32, 1000, 4096)])
 def test_gemv_long_k(MNK):
     # K past one 4096-element pass: segments of 8 and 16 steps per wave, a ragged last
-    # segment, and K beyond 16384 (the streaming kernel).
+    # segment, K beyond 16384 (the streaming kernel), and the second token tile.
     M, N, K = MNK
     d = datagen.make_shape("gemv", M, N, K, seed=M + N + K)
     print(f"case gemv {M}x{N}x{K}", flush=True)
@@ -304,6 +321,24 @@ def test_gemv_scale_rows_not_16_byte_aligned():
     D = as_np(fp4.fp4_gemv(t["A"], t["sfA"], t["B"], sfB, out_dtype=torch.float32))
     ref, S = oracle.run("mx", d)
     assert oracle.parity_ratio(D, ref, S, "f32") <= 1.0
+
+
+@pytest.mark.parametrize("M", [1, 8, 17, 32])
+def test_mxfp4_few_tokens_run_the_gemv(M):
+    """mx_fp4_gemm with 1 to 32 tokens and K >= 4096 runs the decode GEMV: the result is
+    fp4_gemv's bit for bit and meets the bar, and mx_fp4_gemm_batched with L = 1 and the
+    automatic split takes the same path without a workspace."""
+    N, K = 300, 4096
+    d = datagen.make_shape("mx", M, N, K, seed=M, dist="gaussian")
+    t = up(d)
+    D1 = fp4.mx_fp4_gemm(t["A"], t["sfA"], t["B"], t["sfB"], out_dtype=torch.float32)
+    D2 = fp4.fp4_gemv(t["A"], t["sfA"], t["B"], t["sfB"], out_dtype=torch.float32)
+    D3 = fp4.mx_fp4_gemm_batched(*(t[k][None] for k in ("A", "sfA", "B", "sfB")), out_dtype=torch.float32)[0]
+    torch.cuda.synchronize(DEV)
+    assert fp4.mx_fp4_gemm_workspace_size(1, M, N, K) == 0
+    assert torch.equal(D1, D2) and torch.equal(D1, D3)
+    ref, S = oracle.run("mx", d)
+    assert oracle.parity_ratio(as_np(D1), ref, S, "f32") <= 1.0
 
 
 def test_gemv_matches_gemm():
@@ -507,8 +542,8 @@ def test_invalid_calls_raise():
     d = datagen.make_shape("mx", 4, 4, 256, seed=1)
     t = up(d)
     with pytest.raises(fp4.Fp4GemmError):
-        fp4.fp4_gemv(torch.zeros((17, 128), dtype=torch.uint8, device=DEV),
-                     torch.zeros((17, 8), dtype=torch.uint8, device=DEV), t["B"], t["sfB"])
+        fp4.fp4_gemv(torch.zeros((33, 128), dtype=torch.uint8, device=DEV),
+                     torch.zeros((33, 8), dtype=torch.uint8, device=DEV), t["B"], t["sfB"])
     with pytest.raises(TypeError):
         fp4.mx_fp4_gemm(t["A"].to(torch.int8), t["sfA"], t["B"], t["sfB"])
     with pytest.raises(ValueError):
