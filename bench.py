@@ -109,7 +109,7 @@ def src_digest(*names):
 _NS = "fp4g::(anonymous namespace)::"
 COUNTED = [("mxfp4_gemm_8192", _NS + "mxfp4_gemm_kernel<256, 256, 128, 128, 256, 2, true, false>",
             ["mxfp4_gemm.hip", "common.hpp"]),
-           ("fp4_gemv_8x14336x4096", _NS + "fp4_gemv_kernel", ["fp4_gemv.hip", "common.hpp"]),
+           ("fp4_gemv_8x14336x4096", _NS + "fp4_gemv_kernel<1, 2, 1,", ["fp4_gemv.hip", "common.hpp"]),
            ("fp4_gemv_prepacked_8x14336x4096", _NS + "fp4_gemv_prepacked_kernel<",
             ["fp4_gemv_prepacked.hip", "common.hpp"]),
            ("mxfp4_split_k_128x8192x8192", _NS + "mxfp4_gemm_kernel<128, 128, 64, 64, 256, 2, false, true>",
@@ -124,12 +124,18 @@ COUNTED = [("mxfp4_gemm_8192", _NS + "mxfp4_gemm_kernel<256, 256, 128, 128, 256,
            ("fp8_blockwise_4096", _NS + "fp8b_gemm_big_kernel<", ["fp8b_gemm.hip", "common.hpp"]),
            ("mx_quantize_8192x8192_f32", _NS + "mx_quantize_kernel<", ["mx_quantize.hip", "common.hpp"]),
            ("nv_quantize_8192x8192_f32", _NS + "nv_quantize_kernel<", ["mx_quantize.hip", "common.hpp"]),
-           # decode (M = 8, K = 8192: two 4-group segments per wave, two row groups) and the
-           # K-split GEMMs at M = 64 (64-row tiles, split kernel + scaled reduction)
-           ("w4a8_decode_8x8192x8192", _NS + "w4a8_gemv_kernel<2, 2, 2, 1,", ["w4a8_gemv.hip", "common.hpp"]),
-           ("w4a8_decode_prepacked_8x8192x8192", _NS + "w4a8_gemv_kernel<2, 2, 2, 0,",
+           # decode (M = 8, K = 8192: two 4-group segments per wave, two row groups; M = 32:
+           # the same with two token tiles) and the K-split GEMMs at M = 64 (64-row tiles,
+           # split kernel + scaled reduction)
+           ("w4a8_decode_8x8192x8192", _NS + "w4a8_gemv_kernel<2, 2, 2, 1, 1,", ["w4a8_gemv.hip", "common.hpp"]),
+           ("w4a8_decode_prepacked_8x8192x8192", _NS + "w4a8_gemv_kernel<2, 2, 2, 0, 1,",
             ["w4a8_gemv.hip", "common.hpp"]),
-           ("nvfp4_decode_8x8192x8192", _NS + "nvfp4_gemv_kernel<2, 2,",
+           ("nvfp4_decode_8x8192x8192", _NS + "nvfp4_gemv_kernel<2, 2, 1,",
+            ["nvfp4_gemv.hip", "nv_fold.hpp", "common.hpp"]),
+           ("w4a8_decode_32x8192x8192", _NS + "w4a8_gemv_kernel<2, 2, 2, 1, 2,", ["w4a8_gemv.hip", "common.hpp"]),
+           ("w4a8_decode_prepacked_32x8192x8192", _NS + "w4a8_gemv_kernel<2, 2, 2, 0, 2,",
+            ["w4a8_gemv.hip", "common.hpp"]),
+           ("nvfp4_decode_32x8192x8192", _NS + "nvfp4_gemv_kernel<2, 2, 2,",
             ["nvfp4_gemv.hip", "nv_fold.hpp", "common.hpp"]),
            ("w4a8_split_64x8192x8192", _NS + "w4a8p_gemm_kernel<64, false, true",
             ["w4a8_gemm.hip", "w4a8_prepacked.hip", "common.hpp"]),
@@ -222,7 +228,7 @@ def summarize_counters(fetch_dir, write_dir, command):
 # Utilisation counters: (workload key, kernel-name prefix, sources of the kernel).
 UTIL_KERNELS = [("mxfp4_gemm_8192x8192x8192", "mxfp4_gemm_kernel<256, 256, 128, 128, 256, 2, true, false>",
                  ["mxfp4_gemm.hip", "common.hpp"]),
-                ("mxfp4_gemv_8x14336x4096", "fp4_gemv_kernel<1, 2, true, true>", ["fp4_gemv.hip", "common.hpp"]),
+                ("mxfp4_gemv_8x14336x4096", "fp4_gemv_kernel<1, 2, 1, true, true>", ["fp4_gemv.hip", "common.hpp"]),
                 ("w4a8_256x8192x8192", "w4a8p_gemm_kernel<64, false, false",
                  ["w4a8_gemm.hip", "w4a8_prepacked.hip", "common.hpp"]),
                 ("w4a8_256x8192x8192_prepacked", "w4a8p_gemm_kernel<64, true, false",
@@ -230,8 +236,8 @@ UTIL_KERNELS = [("mxfp4_gemm_8192x8192x8192", "mxfp4_gemm_kernel<256, 256, 128, 
                 ("fp8_blockwise_4096", "fp8b_gemm_big_kernel<", ["fp8b_gemm.hip", "common.hpp"]),
                 ("nvfp4_1024", "nvfp4_gemm_kernel<64, 64, 16, 32, false", ["nvfp4_gemm.hip", "nv_fold.hpp", "common.hpp"]),
                 ("w4a8_256x8192x8192_fp6", "w4a8f6_gemm_kernel<", ["w4a8_fp6.hip", "common.hpp"]),
-                ("decode_8x8192x8192_w4a8", "w4a8_gemv_kernel<2, 2, 2, 1,", ["w4a8_gemv.hip", "common.hpp"]),
-                ("decode_8x8192x8192_nvfp4", "nvfp4_gemv_kernel<2, 2,", ["nvfp4_gemv.hip", "nv_fold.hpp", "common.hpp"]),
+                ("decode_8x8192x8192_w4a8", "w4a8_gemv_kernel<2, 2, 2, 1, 1,", ["w4a8_gemv.hip", "common.hpp"]),
+                ("decode_8x8192x8192_nvfp4", "nvfp4_gemv_kernel<2, 2, 1,", ["nvfp4_gemv.hip", "nv_fold.hpp", "common.hpp"]),
                 ("mx_quantize_8192x8192_f32", "mx_quantize_kernel<", ["mx_quantize.hip", "common.hpp"])]
 UTIL_METRICS = ("MfmaUtil", "LdsUtil", "VALUBusy", "LdsBankConflict")
 UTIL_FILE = os.path.join(PROFILES, "utilisation_counters.txt")
@@ -459,8 +465,9 @@ def bench_skinny(steps, warmup, dev, L=1, M=128, N=8192, K=8192):
 
 def bench_decode(steps, warmup, dev, N=8192, K=8192):
     """Few-token calls on an N x K = 8192 x 8192 weight, cold rotating weight copies: the
-    16-token decode kernels (W4A8 plain and pre-packed, NVFP4) at M = 8, and the K-split
-    W4A8 and NVFP4 GEMMs at M = 64 with the library's own split."""
+    decode kernels (W4A8 plain and pre-packed, NVFP4) at M = 8 (one 16-token tile) and
+    M = 32 (two), and the K-split W4A8 and NVFP4 GEMMs at M = 64 with the library's own
+    split."""
     w = datagen.make_shape("w4a8", 64, N, K, seed=0)
     n = datagen.random_nv(64, N, K, np.random.default_rng(0))
     A8, sa = torch.from_numpy(w["A"]).to(dev), torch.from_numpy(w["sa"]).to(dev)
@@ -477,7 +484,7 @@ def bench_decode(steps, warmup, dev, N=8192, K=8192):
               "nvfp4": NB.numel() + sfB.numel()}
     # per token: E4M3 codes + the fp32 row scale (W4A8); E2M1 codes + E4M3 scales (NVFP4)
     abytes = {"w4a8": K + 4, "w4a8_prepacked": K + 4, "nvfp4": K // 2 + K // 16}
-    for M in (8, 64):
+    for M in (8, 32, 64):
         D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         a8, s8, a4, f4 = A8[:M].contiguous(), sa[:M].contiguous(), A4[:M].contiguous(), sfA[:M].contiguous()
         ws = torch.empty(max(fp4.w4a8_gemm_workspace_size(1, M, N, K), fp4.nv_fp4_gemm_workspace_size(1, M, N, K), 16),
@@ -501,10 +508,10 @@ def bench_decode(steps, warmup, dev, N=8192, K=8192):
 
 def decode_traffic(name, M):
     """HBM bytes per call of a bench_decode row from the counter summaries: the decode
-    kernel (M = 8), or the split kernel plus its scaled reduction (M = 64)."""
-    if M <= 16:
-        return traffic_of({"w4a8": "w4a8_decode_8x8192x8192", "w4a8_prepacked": "w4a8_decode_prepacked_8x8192x8192",
-                           "nvfp4": "nvfp4_decode_8x8192x8192"}[name])
+    kernel (M = 8 and 32), or the split kernel plus its scaled reduction (M = 64)."""
+    if M <= 32:
+        return traffic_of({"w4a8": f"w4a8_decode_{M}x8192x8192", "w4a8_prepacked": f"w4a8_decode_prepacked_{M}x8192x8192",
+                           "nvfp4": f"nvfp4_decode_{M}x8192x8192"}[name])
     t = traffic_of({"w4a8": "w4a8_split_64x8192x8192", "w4a8_prepacked": "w4a8_prepacked_split_64x8192x8192",
                     "nvfp4": "nvfp4_split_64x8192x8192"}[name])
     r = traffic_of("split_reduce_64x8192x8192")
@@ -894,13 +901,14 @@ def main():
                          "unit": "TFLOP/s", "frac": k["auto"]["tflops"] / PEAK_TFLOPS["fp4"],
                          "traffic": split_traffic}}
     if "decode" in only:
-        log("bench: decode (M = 8) and skinny (M = 64) W4A8 / NVFP4 on 8192x8192 weights (cold) ...")
+        log("bench: decode (M = 8, 32) and skinny (M = 64) W4A8 / NVFP4 on 8192x8192 weights (cold) ...")
         k = bench_decode(args.steps, args.warmup, dev)
-        for M, label in ((8, "decode_8x8192x8192"), (64, "skinny_64x8192x8192")):
+        for M, label in ((8, "decode_8x8192x8192"), (32, "decode_32x8192x8192"), (64, "skinny_64x8192x8192")):
             r = k[M]
             log(f"bench: {label}: " + ", ".join(f"{n} {r[n]['us']:.1f} us" for n in ("w4a8", "w4a8_prepacked", "nvfp4")))
             entry = {"metric": "us per launch", "cache": f"cold ({k['copies']} rotating weight copies)",
-                     "kernels": "16-token decode kernels" if M <= 16 else "K-split GEMMs (library's choice)",
+                     "kernels": ("decode kernels, one 16-token tile" if M <= 16 else
+                                 "decode kernels, two 16-token tiles" if M <= 32 else "K-split GEMMs (library's choice)"),
                      "splits": r["splits"]}
             for n in ("w4a8", "w4a8_prepacked", "nvfp4"):
                 entry[n] = {"us": r[n]["us"], "tflops": r[n]["tflops"], "algorithmic_bytes": r[n]["bytes"],
