@@ -37,7 +37,11 @@ namespace {
 
 constexpr int WAVES = 8;
 
-template <int NJ, int RG, int TT, bool COOP, bool BF16>
+// HALF (M <= 8, one token tile): lanes 8..15 fetch the next step of tokens 0..7.  It is a
+// template parameter, not a test of M in the kernel: with both forms in one kernel the
+// compiler merges their token registers where the branches join, and the moves it puts
+// there wait for the token loads before a single weight copy has been issued.
+template <int NJ, int RG, int TT, bool HALF, bool COOP, bool BF16>
 __global__ void __launch_bounds__(WAVES * 64)
 fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
                 const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, void* __restrict__ D) {
@@ -52,6 +56,7 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
   static_assert(WAVES * WBYTES <= 160 * 1024, "LDS budget");
   static_assert(WAVES * RG * TT * 64 * 4 * 4 <= WAVES * WBYTES, "reduction fits in the weight area");
   static_assert(TT == 1 || TT == 2, "token tiles");
+  static_assert(!HALF || TT == 1, "the half-row token fetch is for one tile");
   constexpr int SCL = COOP ? ROWS * ST * WAVES * 4 : 16;   // the workgroup's scale rows (K / 32 bytes each)
   static_assert(WAVES * WBYTES + SCL <= 160 * 1024, "LDS budget");
   // The cooperative copy gives each wave at most one 1 KB piece of the scale rows.
@@ -91,7 +96,7 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
     tok[u] = 16 * u + r < M;
     trow[u] = tok[u] ? 16 * u + r : 0;
   }
-  if (TT == 1 && M <= 8) {
+  if constexpr (HALF) {
     // Lanes r >= 8 would only hold zeros: let them fetch the next step of token r-8,
     // then rotate each 16-lane row by 8 (DPP row_ror:8) to move it into lanes 0..7.
     const int64_t prow = min(r & 7, M - 1);
@@ -163,7 +168,7 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
     }
   }
 
-  if (TT == 1 && M <= 8) {
+  if constexpr (HALF) {
 #pragma unroll
     for (int s = 0; s < ST; s += 2) {
 #pragma unroll
@@ -283,28 +288,33 @@ fp4_gemv_long_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const u
   }
 }
 
-template <int NJ, int RG, int TT, bool COOP>
+template <int NJ, int RG, int TT, bool HALF, bool COOP>
 hipError_t launch_segmented(const FP4Args& a, hipStream_t s) {
   const int64_t g64 = ceil_div(a.N, 16 * RG);
   if (g64 > INT32_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)g64), block(WAVES * 64);
   if (a.bf16_out)
-    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, TT, COOP, true>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
-                       a.A, a.sfA, a.B, a.sfB, a.D);
+    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, TT, HALF, COOP, true>), grid, block, 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
   else
-    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, TT, COOP, false>), grid, block, 0, s, (int)a.M, (int)a.N, (int)a.K,
-                       a.A, a.sfA, a.B, a.sfB, a.D);
+    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, TT, HALF, COOP, false>), grid, block, 0, s, (int)a.M, (int)a.N,
+                       (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
   return hipGetLastError();
+}
+
+template <int NJ, int RG, int TT, bool HALF>
+hipError_t launch_segmented(const FP4Args& a, bool coop, hipStream_t s) {
+  return coop ? launch_segmented<NJ, RG, TT, HALF, true>(a, s) : launch_segmented<NJ, RG, TT, HALF, false>(a, s);
 }
 
 template <int NJ, int RG>
 hipError_t launch_segmented(const FP4Args& a, hipStream_t s) {
   // Cooperative scale copies need 16-byte aligned scale rows and whole segments.
   const bool coop = a.K % (WAVES * 4 * NJ * 128) == 0 && (reinterpret_cast<uintptr_t>(a.sfB) & 15) == 0;
-  if (a.M <= 16) return coop ? launch_segmented<NJ, RG, 1, true>(a, s) : launch_segmented<NJ, RG, 1, false>(a, s);
+  if (a.M <= 8) return launch_segmented<NJ, RG, 1, true>(a, coop, s);
+  if (a.M <= 16) return launch_segmented<NJ, RG, 1, false>(a, coop, s);
   // A second token tile keeps its tokens in registers: up to 16 steps per wave (K <= 16384).
-  if constexpr (NJ <= 4)
-    return coop ? launch_segmented<NJ, RG, 2, true>(a, s) : launch_segmented<NJ, RG, 2, false>(a, s);
+  if constexpr (NJ <= 4) return launch_segmented<NJ, RG, 2, false>(a, coop, s);
   return hipErrorInvalidValue;
 }
 
