@@ -551,7 +551,7 @@ const char* fp4g_status_string(int status) {
   switch (status) {
     case FP4G_OK: return "ok";
     case FP4G_EINVAL: return "invalid argument (null pointer, negative size, bad output type or D overlapping an input)";
-    case FP4G_EUNSUPPORTED: return "unsupported shape (K must be a multiple of 128, of 32 for the MX quantizer, of 16 for the NV quantizer; GEMV needs M <= 16, or M <= 32 with K <= 8192; the pre-packed GEMV M <= 16)";
+    case FP4G_EUNSUPPORTED: return "unsupported shape (K must be a multiple of 128, of 32 for the MX quantizer, of 16 for the NV quantizer; GEMV needs M <= 16, or M <= 32 with K <= 16384; the pre-packed GEMV M <= 16)";
     case FP4G_EALIGN: return "misaligned pointer (operands and D need 16-byte, scales 4-byte alignment)";
     case FP4G_EHIP: return "HIP runtime error at kernel launch";
     default: return "unknown status";

@@ -70,7 +70,7 @@ hipError_t launch_nvfp4_gemm_split(const FP4Args& a, int64_t splits, float* P, h
 // K <= 8192 (nvfp4_gemv_fits); batch a.L.
 bool nvfp4_gemv_fits(int64_t M, int64_t K);
 hipError_t launch_nvfp4_gemv(const FP4Args& a, hipStream_t s);
-// MXFP4 decode GEMV (L = 1) for 1 <= M <= 16 tokens, or 17 <= M <= 32 and K <= 8192.
+// MXFP4 decode GEMV (L = 1) for 1 <= M <= 16 tokens, or 17 <= M <= 32 and K <= 16384.
 bool fp4_gemv_fits(int64_t M, int64_t K);
 hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s);
 // Pre-packed decode weights: sizes, the load-time re-pack, and the GEMV over them
