@@ -130,7 +130,8 @@ mx_quantize_kernel(int64_t nblocks, const void* __restrict__ X, uint8_t* __restr
 //    so does the exact quotient.  When they differ, when e4m3(s) g is not a normal fp32
 //    (the table holds -1 there), or when the scale saturated (|y| may then overflow),
 //    the lane's four codes come from fp64 quotients x / (e4m3(s) g), exact for the same
-//    reason as the scale's (a boundary times the divisor has at most 31 bits).
+//    reason as the scale's (a boundary times the divisor has at most 31 bits); where
+//    only the two ends differ, one fused multiply-add per element settles it (below).
 
 // Maximum over the 4-lane quad of unsigned integers.
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
@@ -248,11 +249,39 @@ nv_quantize_kernel(int64_t nblocks, const void* __restrict__ X, float g, uint8_t
       uint32_t packed_hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, yhi[0], yhi[1], 1.0f, 0);
       packed_hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed_hi, yhi[2], yhi[3], 1.0f, 1);
       if (!bad && s != 0 && ((packed ^ packed_hi) & 0xFFFFu || inv < 0.0f || s == 0x7Eu)) {
-        const double d = (double)__builtin_amdgcn_cvt_f32_fp8((int)s, 0) * (double)g;
-        packed = 0;
+        const float se = __builtin_amdgcn_cvt_f32_fp8((int)s, 0);
+        bool tiny = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          packed |= e2m1_nearest_exact(__builtin_bit_cast(float, bits[u][i]), d) << (4 * i);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t a = bits[u][i] & 0x7FFFFFFFu;
+          tiny |= a != 0 && a < 0x0D800000u;             // 0 < |x| < 2^-100
+        }
+        if (inv < 0.0f || s == 0x7Eu || tiny) {
+          const double d = (double)se * (double)g;
+          packed = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            packed |= e2m1_nearest_exact(__builtin_bit_cast(float, bits[u][i]), d) << (4 * i);
+        } else {
+          // The two ends of the bracket give adjacent magnitudes k and k+1 (the bracket is far
+          // narrower than the spacing of the E2M1 values), so the exact quotient is decided
+          // by the boundary between them, b_k: |x| against b_k * e4m3(s) * g.  b_k * e4m3(s)
+          // has at most 7 significant bits (exact in fp32), and one fused multiply-add gives
+          // the sign of b_k e4m3(s) g - |x| exactly (|x| >= 2^-100 keeps a nonzero difference
+          // above the fp32 underflow); zero is a tie, settled to the even magnitude.
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t kl = (packed >> (4 * i)) & 7u, kh = (packed_hi >> (4 * i)) & 7u;
+            if (kl != kh) {
+              const float b = kl == 0 ? 0.25f : kl == 1 ? 0.75f : kl == 2 ? 1.25f : kl == 3 ? 1.75f
+                            : kl == 4 ? 2.5f : kl == 5 ? 3.5f : 5.0f;
+              const float ax = __builtin_bit_cast(float, bits[u][i] & 0x7FFFFFFFu);
+              const float r = __builtin_fmaf(b * se, g, -ax);
+              const uint32_t k = r > 0.0f ? kl : r < 0.0f ? kh : ((kl & 1u) ? kh : kl);
+              packed = (packed & ~(7u << (4 * i))) | (k << (4 * i));
+            }
+          }
+        }
       }
       const uint32_t nonzero = ((packed & 0x7777u) + 0x7777u) & 0x8888u;   // bit 3 of a nibble: magnitude != 0
       packed &= nonzero | 0x7777u;
