@@ -756,9 +756,13 @@ def main():
                          "MfmaUtil LdsUtil LdsBankConflict VALUBusy, then exit")
     args = ap.parse_args()
     if args.counters:
+        if not args.counters_command:
+            ap.error("--counters needs --counters-command: the profiling command the summary records")
         summarize_counters(args.counters[0], args.counters[1], args.counters_command)
         return
     if args.util:
+        if not args.counters_command:
+            ap.error("--util needs --counters-command: the profiling command the summary records")
         summarize_util(args.util, args.counters_command)
         return
     global USE_GRAPH
