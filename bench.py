@@ -768,7 +768,7 @@ def main():
     global USE_GRAPH
     USE_GRAPH = not args.no_graph
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
