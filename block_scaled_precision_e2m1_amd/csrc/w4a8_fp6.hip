@@ -42,9 +42,10 @@
 // the texture path about 16 cycles for its 64 lanes, so the 24 copies of a group take
 // about as long as its 256 cycles of matrix work per SIMD even from L2, and the weights,
 // read once from HBM and shared by the four token tiles of a panel, arrive at about
-// 2 TB/s with the bytes the ring keeps in flight.  A copy-only version of the kernel takes
-// 28 us of its 31.  A deeper ring (6 slots instead of 4) gained 2 us; K-major weight blocks
-// and a ninth wave gathering the next groups' weight lines into L2 gained nothing or lost.
+// 2 TB/s.  A copy-only version of the kernel takes 28 us of its 31.  A deeper ring (6 slots
+// instead of 4) gained 2 us, but one more group of lead in the same slots gained nothing;
+// K-major weight blocks and a ninth wave gathering the next groups' weight lines into L2
+// gained nothing or lost.
 #include "common.hpp"
 #include "internal.h"
 
