@@ -491,8 +491,8 @@ splitk_reduce_kernel(int64_t MN, int L, int S, const float* __restrict__ P, void
     const int64_t b = u / per, i = (u - b * per) * W;
     const float* p = P + b * S * MN + i;
     if constexpr (VEC) {
-      v4f acc = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
-      for (int s = 1; s < S; ++s) acc += __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + s * MN));
+      v4f acc = *reinterpret_cast<const v4f*>(p);
+      for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const v4f*>(p + s * MN);
       store_out4<BF16>(D, b * MN + i, 4, acc[0], acc[1], acc[2], acc[3]);
     } else {
       float acc = p[0];

@@ -4,7 +4,8 @@
 //   D[b][m][n] = ldexp((sum_s P[b][s][m][n]) * rs[b][m] * gm, ge),
 // rs the W4A8 per-token scales (absent for NVFP4: 1) and gm * 2^ge the NVFP4 global
 // scale pair (1 for W4A8).  One pass over the partials: four consecutive n per lane when
-// N % 4 == 0, streamed once (nontemporal loads).
+// N % 4 == 0.  Plain loads: the partials were written just before and may still sit in
+// the caches (nontemporal loads measured about 1% slower).
 #include "common.hpp"
 #include "internal.h"
 
@@ -22,13 +23,13 @@ scaled_reduce_kernel(int64_t M, int64_t N, int L, int S, const float* __restrict
     const float* p = P + b * S * MN + i;
     const float sc = (rs ? rs[b * M + i / N] : 1.0f) * gm;
     if constexpr (VEC) {
-      v4f acc = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
-      for (int s = 1; s < S; ++s) acc += __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + s * MN));
+      v4f acc = *reinterpret_cast<const v4f*>(p);
+      for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const v4f*>(p + s * MN);
       store_out4<BF16>(D, b * MN + i, 4, __builtin_ldexpf(acc[0] * sc, ge), __builtin_ldexpf(acc[1] * sc, ge),
                        __builtin_ldexpf(acc[2] * sc, ge), __builtin_ldexpf(acc[3] * sc, ge));
     } else {
-      float acc = __builtin_nontemporal_load(p);
-      for (int s = 1; s < S; ++s) acc += __builtin_nontemporal_load(p + s * MN);
+      float acc = p[0];
+      for (int s = 1; s < S; ++s) acc += p[s * MN];
       store_out<BF16>(D, b * MN + i, __builtin_ldexpf(acc * sc, ge));
     }
   }
