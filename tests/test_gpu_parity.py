@@ -171,6 +171,31 @@ def test_mxfp4_headline_config_full_output():
         assert r <= 1.0, f"mx {M}x{N}x{K} {out}: max |err|/tol = {r}"
 
 
+def test_w4a8_workload_full_output_all_paths():
+    """The W4A8 workload (256 x 8192 x 8192) compared element by element with the oracle
+    over the whole output for the three W4A8 paths the benchmark times: plain INT4
+    weights (the ring kernel), INT4 weights pre-packed by w4a8_prepack, and weights
+    re-encoded as FP6 E3M2 by w4a8_prepack_fp6 (64 x 128 tiles, one per CU), fp32 and bf16
+    outputs.  One oracle pass (about 20 s on 16 threads) serves all six comparisons."""
+    d = datagen.make("w4a8_256x8192x8192")
+    M, N, K = d["M"], d["N"], d["K"]
+    print(f"case w4a8 {M}x{N}x{K} full output, three paths", flush=True)
+    t = up(d)
+    Bp, Sp = fp4.w4a8_prepack(t["B"], t["sB"])
+    B6, S6 = fp4.w4a8_prepack_fp6(t["B"], t["sB"])
+    outs = {}
+    for od, name in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+        outs[("plain", name)] = as_np(fp4.w4a8_gemm(t["A"], t["sa"], t["B"], t["sB"], out_dtype=od))
+        outs[("prepacked", name)] = as_np(fp4.w4a8_gemm_prepacked(t["A"], t["sa"], Bp, Sp, N, out_dtype=od))
+        outs[("fp6", name)] = as_np(fp4.w4a8_gemm_prepacked_fp6(t["A"], t["sa"], B6, S6, N, out_dtype=od))
+    torch.cuda.synchronize(DEV)
+    ref, S = oracle.run("w4a8", d)
+    for (path, name), D in outs.items():
+        r = oracle.parity_ratio(D, ref, S, name)
+        print(f"  {path} {name}: max |err|/tol = {r:.3g}", flush=True)
+        assert r <= 1.0, f"w4a8 {path} {M}x{N}x{K} {name}: max |err|/tol = {r}"
+
+
 def test_mxfp4_8192_sampled_and_repeatable():
     d = datagen.make("mxfp4_8192")
     print("case mxfp4_8192 seed 0", flush=True)
