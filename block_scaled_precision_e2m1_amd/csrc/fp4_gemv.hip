@@ -327,7 +327,13 @@ hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s) {
   const int64_t KT = a.K / 128;
   // Segment of ST = 4*NJ steps per wave, WAVES segments per row: K <= WAVES*ST*128.
   if (KT <= WAVES * 4) return launch_segmented<1, 2>(a, s);     // K <= 4096: 32 rows per workgroup
-  if (KT <= WAVES * 8) return launch_segmented<2, 1>(a, s);     // K <= 8192
+  if (KT <= WAVES * 8) {                                         // K <= 8192
+    // 32 rows per workgroup halve the token re-reads (each workgroup reads all M x K
+    // tokens), which pays with more than 8 tokens while one workgroup per CU covers N;
+    // otherwise 16 rows keep two workgroups, and so more bytes, in flight per CU.
+    if (a.M > 8 && ceil_div(a.N, 32) <= device_cus()) return launch_segmented<2, 2>(a, s);
+    return launch_segmented<2, 1>(a, s);
+  }
   if (KT <= WAVES * 16) return launch_segmented<4, 1>(a, s);    // K <= 16384
   const int64_t g64 = ceil_div(a.N, 16);
   if (g64 > INT32_MAX) return hipErrorInvalidConfiguration;

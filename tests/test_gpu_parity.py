@@ -323,10 +323,13 @@ def test_gemv_shapes(M, NK):
 
 @pytest.mark.parametrize("MNK", [(8, 300, 5120), (16, 257, 8192), (5, 130, 14336), (3, 70, 16384),
                                  (8, 40, 16512), (16, 1000, 4096), (1, 33, 12800), (20, 300, 5120),
-                                 (32, 257, 8192), (17, 130, 14336), (29, 70, 16384), (32, 1000, 4096)])
+                                 (32, 257, 8192), (17, 130, 14336), (29, 70, 16384), (32, 1000, 4096),
+                                 (16, 8192, 8192), (32, 8192, 6144), (9, 8224, 8192), (16, 8224, 8192)])
 def test_gemv_long_k(MNK):
     # K past one 4096-element pass: segments of 8 and 16 steps per wave, a ragged last
-    # segment, K beyond 16384 (the streaming kernel), and the second token tile.
+    # segment, K beyond 16384 (the streaming kernel), and the second token tile.  At K <=
+    # 8192 with more than 8 tokens, 32 rows per workgroup while ceil(N / 32) workgroups fit
+    # the CUs (N = 8192) and 16 rows beyond (N = 8224 on 256 CUs).
     M, N, K = MNK
     d = datagen.make_shape("gemv", M, N, K, seed=M + N + K)
     print(f"case gemv {M}x{N}x{K}", flush=True)
