@@ -389,7 +389,9 @@ fp4g_status w4a8_gemm_prepacked_split(int64_t M, int64_t N, int64_t K,
  *   is a no-op.
  * fp4_gemv_prepacked: fp4_gemv (1 <= M <= 16 tokens, same A, sfA and D layouts
  *   and result) with the weights given as Bp and Sp.  Bp 16-byte and Sp 4-byte
- *   aligned; D must not overlap any input.  M > 16 returns FP4G_EUNSUPPORTED. */
+ *   aligned; D must not overlap any input.  M > 16 returns FP4G_EUNSUPPORTED.
+ *   Measured on MI355X with cold weights it is the faster of the two at K >= 8192
+ *   (row pitches of 4 KB and more), and fp4_gemv at K <= 4096. */
 fp4g_status fp4_gemv_prepack_size(int64_t N, int64_t K, size_t *weight_bytes, size_t *scale_bytes);
 fp4g_status fp4_gemv_prepack(int64_t N, int64_t K, const void *B, const void *sfB,
                              void *Bp, void *Sp, void *stream);
