@@ -228,7 +228,7 @@ def summarize_counters(fetch_dir, write_dir, command):
 # Utilisation counters: (workload key, kernel-name prefix, sources of the kernel).
 UTIL_KERNELS = [("mxfp4_gemm_8192x8192x8192", "mxfp4_gemm_kernel<256, 256, 128, 128, 256, 2, true, false>",
                  ["mxfp4_gemm.hip", "common.hpp"]),
-                ("mxfp4_gemv_8x14336x4096", "fp4_gemv_kernel<1, 2, 1, true, true, true>", ["fp4_gemv.hip", "common.hpp"]),
+                ("mxfp4_gemv_8x14336x4096", "fp4_gemv_kernel<1, 2, 1, true, true, true, 8>", ["fp4_gemv.hip", "common.hpp"]),
                 ("w4a8_256x8192x8192", "w4a8p_gemm_kernel<64, false, false",
                  ["w4a8_gemm.hip", "w4a8_prepacked.hip", "common.hpp"]),
                 ("w4a8_256x8192x8192_prepacked", "w4a8p_gemm_kernel<64, true, false",

@@ -12,10 +12,10 @@
 // to 32 tokens (K <= 16384) a second token tile multiplies the same weight fragments.
 //
 // gfx950 mapping (K <= 16384, the decode shapes):
-//   * one workgroup of 8 waves per RG groups of 16 weight rows; wave w owns the K
-//     segment of ST = 4*NJ consecutive 128-element steps starting at w*ST, for all
-//     of the workgroup's rows, so its token fragments are loaded once and reused
-//     for every row group;
+//   * one workgroup of NWV waves (8; 4 at 7168 < K <= 8192) per RG groups of 16 weight
+//     rows; wave w owns the K segment of ST = 4*NJ consecutive 128-element steps
+//     starting at w*ST, for all of the workgroup's rows, so its token fragments are
+//     loaded once and reused for every row group;
 //   * the weights reach LDS through global->LDS copies (global_load_lds_dwordx4)
 //     that read whole 128-byte lines: each 1 KB copy covers RPI rows x ST*64 bytes.
 //     A row's 16-byte units are XOR-swizzled by the row index (the copy lane picks
@@ -37,12 +37,13 @@ namespace {
 
 constexpr int WAVES = 8;
 
-// HALF (M <= 8, one token tile): lanes 8..15 fetch the next step of tokens 0..7.  It is a
-// template parameter, not a test of M in the kernel: with both forms in one kernel the
-// compiler merges their token registers where the branches join, and the moves it puts
-// there wait for the token loads before a single weight copy has been issued.
-template <int NJ, int RG, int TT, bool HALF, bool COOP, bool BF16>
-__global__ void __launch_bounds__(WAVES * 64)
+// NWV waves per workgroup.  HALF (M <= 8, one token tile): lanes 8..15 fetch the next step
+// of tokens 0..7.  It is a template parameter, not a test of M in the kernel: with both
+// forms in one kernel the compiler merges their token registers where the branches join,
+// and the moves it puts there wait for the token loads before a single weight copy has
+// been issued.
+template <int NJ, int RG, int TT, bool HALF, bool COOP, bool BF16, int NWV>
+__global__ void __launch_bounds__(NWV * 64)
 fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sfA,
                 const uint8_t* __restrict__ B, const uint8_t* __restrict__ sfB, void* __restrict__ D) {
   constexpr int ST = 4 * NJ;             // steps (128 K elements, 64 bytes) per wave
@@ -53,15 +54,14 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
   constexpr int NI = ROWS / RPI;         // copies per wave
   constexpr int WBYTES = ROWS * SEG;     // LDS bytes per wave
   static_assert(UPR >= 16 && UPR <= 64 && 64 % UPR == 0, "segment shape");
-  static_assert(WAVES * WBYTES <= 160 * 1024, "LDS budget");
-  static_assert(WAVES * RG * TT * 64 * 4 * 4 <= WAVES * WBYTES, "reduction fits in the weight area");
+  static_assert(NWV * WBYTES <= 160 * 1024, "LDS budget");
+  static_assert(NWV * RG * TT * 64 * 4 * 4 <= NWV * WBYTES, "reduction fits in the weight area");
   static_assert(TT == 1 || TT == 2, "token tiles");
   static_assert(!HALF || TT == 1, "the half-row token fetch is for one tile");
-  constexpr int SCL = COOP ? ROWS * ST * WAVES * 4 : 16;   // the workgroup's scale rows (K / 32 bytes each)
-  static_assert(WAVES * WBYTES + SCL <= 160 * 1024, "LDS budget");
+  constexpr int SCL = COOP ? ROWS * ST * NWV * 4 : 16;   // the workgroup's scale rows (K / 32 bytes each)
+  static_assert(NWV * WBYTES + SCL <= 160 * 1024, "LDS budget");
   // The cooperative copy gives each wave at most one 1 KB piece of the scale rows.
-  static_assert(!COOP || (SCL + 1023) / 1024 <= WAVES, "one scale piece per wave at most");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[WAVES * WBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NWV * WBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t scl[SCL];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -141,9 +141,9 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
     const int64_t total = (int64_t)N * lsc;
     const int64_t first = n0 * lsc;
     const int pieces = (int)((min((int64_t)ROWS * lsc, total - first) + 1023) / 1024);
-    if (wave < pieces) {
-      const int64_t off = min(first + wave * 1024 + lane * 16, total - 16);
-      lds_copy16(sfB + off, (lds_void*)(scl + wave * 1024));
+    for (int pc = wave; pc < pieces; pc += NWV) {
+      const int64_t off = min(first + pc * 1024 + lane * 16, total - 16);
+      lds_copy16(sfB + off, (lds_void*)(scl + pc * 1024));
     }
   } else {
 #pragma unroll
@@ -199,9 +199,9 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
     }
   }
 
-  // ---- sum the WAVES partial tiles in wave order, store D[m][n] ----
+  // ---- sum the NWV partial tiles in wave order, store D[m][n] ----
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);   // [WAVES][RG * TT][64 lanes][4]
+  float* red = reinterpret_cast<float*>(lds);   // [NWV][RG * TT][64 lanes][4]
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
@@ -213,7 +213,7 @@ fp4_gemv_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const uint8_
     const int g = gu / TT, m = 16 * (gu % TT) + (l & 15);
     v4f v = *reinterpret_cast<const v4f*>(red + (gu * 64 + l) * 4);
 #pragma unroll
-    for (int w2 = 1; w2 < WAVES; ++w2) v += *reinterpret_cast<const v4f*>(red + ((w2 * RG * TT + gu) * 64 + l) * 4);
+    for (int w2 = 1; w2 < NWV; ++w2) v += *reinterpret_cast<const v4f*>(red + ((w2 * RG * TT + gu) * 64 + l) * 4);
     const int64_t n = n0 + 16 * g + 4 * (l >> 4);
     if (m < M && n < N) {
       const int avail = (int)min((int64_t)4, (int64_t)N - n);
@@ -288,33 +288,33 @@ fp4_gemv_long_kernel(int M, int N, int K, const uint8_t* __restrict__ A, const u
   }
 }
 
-template <int NJ, int RG, int TT, bool HALF, bool COOP>
+template <int NJ, int RG, int TT, bool HALF, bool COOP, int NWV>
 hipError_t launch_segmented(const FP4Args& a, hipStream_t s) {
   const int64_t g64 = ceil_div(a.N, 16 * RG);
   if (g64 > INT32_MAX) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)g64), block(WAVES * 64);
+  const dim3 grid((unsigned)g64), block(NWV * 64);
   if (a.bf16_out)
-    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, TT, HALF, COOP, true>), grid, block, 0, s, (int)a.M, (int)a.N,
+    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, TT, HALF, COOP, true, NWV>), grid, block, 0, s, (int)a.M, (int)a.N,
                        (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
   else
-    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, TT, HALF, COOP, false>), grid, block, 0, s, (int)a.M, (int)a.N,
+    hipLaunchKernelGGL((fp4_gemv_kernel<NJ, RG, TT, HALF, COOP, false, NWV>), grid, block, 0, s, (int)a.M, (int)a.N,
                        (int)a.K, a.A, a.sfA, a.B, a.sfB, a.D);
   return hipGetLastError();
 }
 
-template <int NJ, int RG, int TT, bool HALF>
+template <int NJ, int RG, int TT, bool HALF, int NWV>
 hipError_t launch_segmented(const FP4Args& a, bool coop, hipStream_t s) {
-  return coop ? launch_segmented<NJ, RG, TT, HALF, true>(a, s) : launch_segmented<NJ, RG, TT, HALF, false>(a, s);
+  return coop ? launch_segmented<NJ, RG, TT, HALF, true, NWV>(a, s) : launch_segmented<NJ, RG, TT, HALF, false, NWV>(a, s);
 }
 
-template <int NJ, int RG>
+template <int NJ, int RG, int NWV = WAVES>
 hipError_t launch_segmented(const FP4Args& a, hipStream_t s) {
   // Cooperative scale copies need 16-byte aligned scale rows and whole segments.
-  const bool coop = a.K % (WAVES * 4 * NJ * 128) == 0 && (reinterpret_cast<uintptr_t>(a.sfB) & 15) == 0;
-  if (a.M <= 8) return launch_segmented<NJ, RG, 1, true>(a, coop, s);
-  if (a.M <= 16) return launch_segmented<NJ, RG, 1, false>(a, coop, s);
+  const bool coop = a.K % (NWV * 4 * NJ * 128) == 0 && (reinterpret_cast<uintptr_t>(a.sfB) & 15) == 0;
+  if (a.M <= 8) return launch_segmented<NJ, RG, 1, true, NWV>(a, coop, s);
+  if (a.M <= 16) return launch_segmented<NJ, RG, 1, false, NWV>(a, coop, s);
   // A second token tile keeps its tokens in registers: up to 16 steps per wave (K <= 16384).
-  if constexpr (NJ <= 4) return launch_segmented<NJ, RG, 2, false>(a, coop, s);
+  if constexpr (NJ <= 4) return launch_segmented<NJ, RG, 2, false, NWV>(a, coop, s);
   return hipErrorInvalidValue;
 }
 
@@ -328,6 +328,14 @@ hipError_t launch_fp4_gemv(const FP4Args& a, hipStream_t s) {
   // Segment of ST = 4*NJ steps per wave, WAVES segments per row: K <= WAVES*ST*128.
   if (KT <= WAVES * 4) return launch_segmented<1, 2>(a, s);     // K <= 4096: 32 rows per workgroup
   if (KT <= WAVES * 8) {                                         // K <= 8192
+    if (KT > WAVES * 7) {
+      // 7168 < K <= 8192: 4 waves of 16 steps, so each copy reads 1 KB of one row.  Two
+      // rows x 512 bytes per copy at this row pitch (4 KB at K = 8192) streamed 3-12%
+      // slower.  32 rows per workgroup (half the token re-reads) while ceil(N/32)
+      // workgroups take at most two rounds of the CUs and there are more than 8 tokens.
+      if (a.M > 8 && ceil_div(a.N, 32) <= 2 * device_cus()) return launch_segmented<4, 2, 4>(a, s);
+      return launch_segmented<4, 1, 4>(a, s);
+    }
     // 32 rows per workgroup halve the token re-reads (each workgroup reads all M x K
     // tokens), which pays with more than 8 tokens while one workgroup per CU covers N;
     // otherwise 16 rows keep two workgroups, and so more bytes, in flight per CU.

@@ -324,12 +324,17 @@ def test_gemv_shapes(M, NK):
 @pytest.mark.parametrize("MNK", [(8, 300, 5120), (16, 257, 8192), (5, 130, 14336), (3, 70, 16384),
                                  (8, 40, 16512), (16, 1000, 4096), (1, 33, 12800), (20, 300, 5120),
                                  (32, 257, 8192), (17, 130, 14336), (29, 70, 16384), (32, 1000, 4096),
-                                 (16, 8192, 8192), (32, 8192, 6144), (9, 8224, 8192), (16, 8224, 8192)])
+                                 (16, 8192, 8192), (32, 8192, 6144), (9, 8224, 8192), (16, 8224, 8192),
+                                 (1, 8192, 8192), (8, 300, 7296), (24, 1000, 7680), (16, 16416, 8192),
+                                 (32, 4100, 8192), (12, 8224, 6144)])
 def test_gemv_long_k(MNK):
     # K past one 4096-element pass: segments of 8 and 16 steps per wave, a ragged last
-    # segment, K beyond 16384 (the streaming kernel), and the second token tile.  At K <=
-    # 8192 with more than 8 tokens, 32 rows per workgroup while ceil(N / 32) workgroups fit
-    # the CUs (N = 8192) and 16 rows beyond (N = 8224 on 256 CUs).
+    # segment, K beyond 16384 (the streaming kernel), and the second token tile.  At 4096
+    # < K <= 7168, 8 waves, with 32 rows per workgroup for more than 8 tokens while
+    # ceil(N / 32) workgroups fit the CUs (N = 8192 of K = 6144) and 16 rows beyond (N = 8224
+    # on 256 CUs); at 7168 < K <= 8192, 4 waves of 16 steps, 32 rows for more than 8 tokens
+    # while ceil(N / 32) is at most twice the CUs (N = 8192, 4100) and 16 rows beyond
+    # (N = 16416 on 256 CUs), with a ragged last segment at K = 7296 and 7680.
     M, N, K = MNK
     d = datagen.make_shape("gemv", M, N, K, seed=M + N + K)
     print(f"case gemv {M}x{N}x{K}", flush=True)
